@@ -1,0 +1,488 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage it follows.  None of them re-types the oracle's formula:
+they use the pages' printed worked examples, hand-worked values, identities stated on
+the pages, closed forms, brute force on tiny inputs, and library routines (torch's
+scaled_dot_product_attention, numpy's lexsort, torch's float8 / bfloat16 casts).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sa_synth
+from oracle import oracle as orc
+from tests._util import tiny, all_rows, full_idx, rand_f32
+from tests.conftest import golden
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+# ------------------------------------------------------------------ codecs
+
+def test_e4m3_decoder_matches_torch_float8_and_spot_values():
+    # OCP e4m3fn: 0x7e = 448 (max finite), 0x38 = 1.0, 0x08 = 2^-6 (min normal), 0x01 = 2^-9.
+    spot = {0x7E: 448.0, 0x38: 1.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x00: 0.0, 0xB8: -1.0, 0xFE: -448.0,
+            0x40: 2.0, 0x3C: 1.5}
+    for code, val in spot.items():
+        assert orc.decode(orc.E4M3, code) == val
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for code in range(256):
+        got = orc.decode(orc.E4M3, code)
+        if code in (0x7F, 0xFF):
+            assert math.isnan(got) and math.isnan(ref[code])
+        else:
+            assert got == ref[code], hex(code)
+
+
+def test_bf16_decoder_matches_torch_bfloat16():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    for b, r in zip(bits[:4096], ref):
+        g = orc.decode(orc.BF16, int(b))
+        assert (math.isnan(g) and math.isnan(r)) or g == r
+    assert orc.decode(orc.BF16, 0x3F80) == 1.0 and orc.decode(orc.BF16, 0xC000) == -2.0
+
+
+def test_synth_encoders_round_trip_and_match_torch():
+    # every finite e4m3 code survives decode -> encode; RNE fp32 -> e4m3 agrees with torch
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.int64)
+    vals = np.array([orc.decode(orc.E4M3, int(c)) for c in codes])
+    enc = sa_synth.encode(vals, sa_synth.E4M3).astype(np.int64)
+    same = (enc == codes) | ((codes == 0x80) & (enc == 0x80))
+    assert same.all()
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(20000) * 40).astype(np.float32)
+    x = x[np.abs(x) < 440]
+    mine = sa_synth.encode(x.astype(np.float64), sa_synth.E4M3)
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (mine == theirs).all()
+    b16 = sa_synth.encode(x.astype(np.float64), sa_synth.BF16)
+    tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (b16 == tb).all()
+
+
+# -------------------------------------------------------------- visibility
+
+def test_causal_pair_count_six_positions():
+    # "Understanding LLMs" ch. 26 §26.4: causal length 6 allows 1+2+...+6 = 21 pairs (self included)
+    g = golden("pair_counts.txt")
+    n = int(g["n"])
+    W = tiny(Q=np.zeros((1, 1, n, 1)), K=np.zeros((1, 1, n, 1)), V=np.zeros((1, 1, n, 1)), k=n)
+    assert orc.count_visible(W) == g["causal_pairs"]
+    assert orc.count_visible(W, causal=0) == n * n
+    for n2 in (1, 7, 64):
+        W2 = tiny(Q=np.zeros((1, 1, n2, 1)), K=np.zeros((1, 1, n2, 1)), V=np.zeros((1, 1, n2, 1)), k=n2)
+        assert orc.count_visible(W2) == n2 * (n2 + 1) // 2
+
+
+def test_window_candidate_pair_counts():
+    # §26.4 example 26.3 and exercise 3: windows {i-1, i} -> 11 pairs, {i-2..i} -> 15 pairs
+    # (per row 1,2,3,3,3,3).  Window index lists pass through the oracle's mask unchanged.
+    g = golden("pair_counts.txt")
+    n = int(g["n"])
+    for width, key in ((2, "window2_pairs"), (3, "window3_pairs")):
+        idx = np.array([[j if j >= 0 else -1 for j in range(i - width + 1, i + 1)] for i in range(n)], np.int32)
+        Q = np.ones((1, 1, n, 1)); K = np.zeros((1, 1, n, 1)); V = np.ones((1, 1, n, 1))
+        W = tiny(Q=Q, K=K, V=V, k=width)
+        O, lse = orc.attend(W, idx)
+        # equal logits: LSE = ln(count), so the per-row counts come back out of the softmax
+        counts = np.rint(np.exp(lse[:, 0])).astype(int)
+        assert counts.sum() == g[key]
+        if width == 3:
+            assert list(counts) == [int(x) for x in g["window3_rows"]]
+
+
+# ------------------------------------------------------------ indexer score
+
+def _hand_indexer():
+    g = golden("indexer_hand.txt")
+    q = np.array([[g["q0"], g["q1"]]])[None]  # [1,1,2,3]
+    keys = np.array(g["keys"])[None]  # [1,4,3]
+    w = np.array(g["w"])[None, None]
+    return g, tiny(q_idx=q, k_idx=keys, w=w, causal=0, k=2)
+
+
+def test_indexer_score_hand_worked_example():
+    g, W = _hand_indexer()
+    r = orc.scores(W)[0]
+    assert np.array_equal(r, np.array(g["scores"]))
+
+
+def test_indexer_relu_identity_from_resmisa():
+    # "PaperTrace 2.2 · Fine-grained indexing", §3.2 (ResMiSA): ReLU(z) = z + ReLU(-z).
+    # Hence r(q) - r(-q) = sum_h w_h <q_h, k>, the unclipped linear term, computed here by
+    # a plain matmul.  A dropped head, a sign slip or a transposed operand breaks it.
+    rng = np.random.default_rng(3)
+    B, n, H, d = 2, 40, 5, 16
+    q = rand_f32(rng, (B, n, H, d)); kk = rand_f32(rng, (B, n, d))
+    w = (rng.standard_normal((B, n, H))).astype(np.float32)  # any sign
+    Wp = tiny(q_idx=q, k_idx=kk, w=w, causal=0)
+    Wm = tiny(q_idx=-q, k_idx=kk, w=w, causal=0)
+    diff = orc.scores(Wp) - orc.scores(Wm)
+    lin = np.einsum("bih,bihd,bjd->bij", w.astype(np.float64), q.astype(np.float64), kk.astype(np.float64))
+    assert np.allclose(diff, lin.reshape(B * n, n), rtol=1e-12, atol=1e-10)
+
+
+def test_indexer_single_head_positive_reduces_to_dot_and_argsort():
+    # One head, w = 1, all dot products positive: r = <q, k>, and the top-k is numpy's
+    # stable descending argsort of the plain dot products.
+    rng = np.random.default_rng(4)
+    n, d, k = 50, 8, 7
+    q = np.abs(rand_f32(rng, (1, n, 1, d))) + 0.1
+    kk = np.abs(rand_f32(rng, (1, n, d))) + 0.1
+    W = tiny(q_idx=q, k_idx=kk, w=np.ones((1, n, 1)), causal=0, k=k)
+    r = orc.scores(W)
+    dots = q[0, :, 0, :].astype(np.float64) @ kk[0].astype(np.float64).T
+    assert np.allclose(r, dots, rtol=1e-12)
+    idx, *_ = orc.select(W, r)
+    for i in range(n):
+        top = np.sort(np.argsort(-dots[i], kind="stable")[:k])
+        assert np.array_equal(idx[i], top)
+
+
+def test_indexer_positive_homogeneity():
+    # ReLU(a z) = a ReLU(z) for a > 0: scaling k or w by a > 0 scales r by a, set unchanged.
+    W = sa_synth.make_config(0)
+    rows = np.arange(0, 256, 17, dtype=np.int32)
+    base = orc.scores(W, rows)
+    W2 = dict(W); W2["k_idx"] = (W["k_idx"] * np.float32(4.0)).astype(np.float32)
+    W3 = dict(W); W3["w"] = (W["w"] * np.float32(0.5)).astype(np.float32)
+    assert np.allclose(orc.scores(W2, rows), 4.0 * base, rtol=1e-12)
+    assert np.allclose(orc.scores(W3, rows), 0.5 * base, rtol=1e-12)
+    i1, *_ = orc.select(W, base, rows)
+    i2, *_ = orc.select(W2, orc.scores(W2, rows), rows)
+    assert np.array_equal(i1, i2)
+
+
+def test_indexer_brute_force_tiny_against_python_loops():
+    # Brute force in pure Python on a tiny problem with causal mask and padding.
+    rng = np.random.default_rng(5)
+    B, n, H, d = 2, 9, 3, 4
+    q = rand_f32(rng, (B, n, H, d)); kk = rand_f32(rng, (B, n, d)); w = rng.random((B, n, H)).astype(np.float32)
+    W = tiny(q_idx=q, k_idx=kk, w=w, causal=1, kv_len=[9, 6])
+    r = orc.scores(W).reshape(B, n, n)
+    for b in range(B):
+        for i in range(n):
+            for j in range(n):
+                vis = i < W["kv_len"][b] and j < W["kv_len"][b] and j <= i
+                if not vis:
+                    assert r[b, i, j] == -np.inf
+                    continue
+                tot = 0.0
+                for h in range(H):
+                    z = sum(float(q[b, i, h, t]) * float(kk[b, j, t]) for t in range(d))
+                    tot += float(w[b, i, h]) * max(z, 0.0)
+                assert abs(tot - r[b, i, j]) <= 1e-12 * max(1.0, abs(tot))
+
+
+# ------------------------------------------------------------------ select
+
+def test_select_hand_example_tie_goes_to_lower_position():
+    g, W = _hand_indexer()
+    r = orc.scores(W)
+    idx, sk, skp1, nsel = orc.select(W, r, k=2)
+    assert list(idx[0]) == [int(x) for x in g["select_k2"]]
+    assert sk[0] == 2.0 and skp1[0] == 2.0  # the cutoff margin is zero: an exact tie
+    idx3, *_ = orc.select(W, r, k=3)
+    assert list(idx3[0]) == [int(x) for x in g["select_k3"]]
+
+
+def test_select_tie_on_cobs_toy_keys():
+    g = golden("tie_cobs_keys.txt")
+    W = tiny(q_idx=np.array(g["q"])[None, None, None], k_idx=np.array(g["keys"])[None],
+             w=np.ones((1, 1, 1)), causal=0, k=2)
+    r = orc.scores(W)
+    assert list(r[0]) == [float(x) for x in g["scores"]]
+    idx, *_ = orc.select(W, r)
+    assert list(idx[0]) == [int(x) for x in g["select_k2"]]
+
+
+def test_select_matches_lexsort_with_many_ties():
+    # Library routine: numpy lexsort by (position asc) within (score desc).
+    rng = np.random.default_rng(6)
+    n, k = 200, 37
+    W = tiny(q_idx=np.zeros((1, n, 1, 1)), k_idx=np.zeros((1, n, 1)), w=np.zeros((1, n, 1)), causal=1, k=k)
+    sc = rng.integers(0, 6, size=(n, n)).astype(np.float64)  # heavy exact ties
+    sc[np.triu_indices(n, 1)] = -np.inf
+    idx, sk, skp1, nsel = orc.select(W, sc)
+    for i in range(n):
+        vis = np.arange(i + 1)
+        order = np.lexsort((vis, -sc[i, : i + 1]))
+        want = np.sort(order[: min(k, i + 1)])
+        got = idx[i][idx[i] >= 0]
+        assert np.array_equal(got, want)
+        assert nsel[i] == min(k, i + 1)
+
+
+def test_select_causal_rows_shorter_than_k_are_padded_not_repeated():
+    # Fine-grained indexing §2.1: with t < k only t+1 real positions exist; the other slots
+    # are explicitly invalid, never repeats of position 0.
+    W = sa_synth.make_config(0)
+    idx, *_ = orc.select(W, orc.scores(W))
+    for i in range(W["n_q"]):
+        valid = idx[i][idx[i] >= 0]
+        assert valid.size == min(W["k"], i + 1)
+        assert np.array_equal(idx[i][: valid.size], valid)
+        assert (idx[i][valid.size:] == -1).all()
+        assert len(set(valid.tolist())) == valid.size
+        if i < W["k"]:
+            assert np.array_equal(valid, np.arange(i + 1))
+
+
+def test_select_sliced_merge_equals_global():
+    # Fine-grained indexing §2.1: slice the history, keep local top-k per slice, merge
+    # keeping k of 2k; the result equals the global top-k.
+    rng = np.random.default_rng(7)
+    n, k = 300, 20
+    W = tiny(q_idx=np.zeros((1, 1, 1, 1)), k_idx=np.zeros((1, n, 1)), w=np.zeros((1, 1, 1)), causal=0, k=k)
+    sc = np.round(rng.standard_normal((1, n)) * 3, 1)  # some ties
+    gidx, *_ = orc.select(W, sc)
+    for slice_len in (1, 7, 64, 150, 300):
+        cur = np.full((1, n), -np.inf)
+        for s0 in range(0, n, slice_len):
+            part = np.full((1, n), -np.inf)
+            part[0, s0:s0 + slice_len] = sc[0, s0:s0 + slice_len]
+            lidx, *_ = orc.select(W, part)
+            both = cur.copy()
+            keep = lidx[0][lidx[0] >= 0]
+            both[0, keep] = sc[0, keep]
+            m, *_ = orc.select(W, both)
+            cur = np.full((1, n), -np.inf)
+            mk = m[0][m[0] >= 0]
+            cur[0, mk] = sc[0, mk]
+        final = np.where(np.isfinite(cur[0]))[0]
+        assert np.array_equal(final, gidx[0])
+
+
+def test_select_stable_under_perturbation_below_half_margin():
+    # Fine-grained indexing §3.1 eq. (9): if every score moves by less than delta_k / 2
+    # the top-k set is unchanged.
+    W = sa_synth.make_config(0)
+    rows = all_rows(W)
+    sc = orc.scores(W)
+    idx, sk, skp1, nsel = orc.select(W, sc)
+    rng = np.random.default_rng(8)
+    for r in rows[rows >= W["k"]]:
+        delta = sk[r] - skp1[r]
+        assert delta >= 0
+        if delta == 0:
+            continue
+        noise = rng.uniform(-0.49, 0.49, size=sc.shape[1]) * delta
+        pert = sc[r:r + 1] + noise
+        i2, *_ = orc.select(W, pert, rows=np.array([r], np.int32))
+        assert np.array_equal(i2[0], idx[r])
+
+
+# --------------------------------------------------------------- attention
+
+def _attn_tiny(q, keys, vals, scale=1.0, causal=0):
+    keys = np.asarray(keys, dtype=np.float64)
+    vals = np.asarray(vals, dtype=np.float64)
+    if vals.ndim == 1:
+        vals = vals[:, None]
+    Q = np.asarray(q, dtype=np.float64).reshape(1, 1, -1, keys.shape[-1])
+    W = tiny(Q=Q, K=keys[None, None], V=vals[None, None], causal=causal, scale=scale, k=keys.shape[0])
+    return W
+
+
+def test_attention_lsh_toy_printed_numbers():
+    g = golden("lsh_toy.txt")
+    xs = [g["x1"], g["x2"], g["x3"], g["x4"]]
+    W = _attn_tiny([g["x2"]], xs, np.eye(4))
+    dots = [float(np.dot(np.float32(g["x2"]), np.float32(x))) for x in xs]
+    for d_, key in zip(dots, ("dot_x1", "dot_x2", "dot_x3", "dot_x4")):
+        assert abs(d_ - g[key]) < 1e-6
+    O, lse = orc.attend(W, np.arange(4, dtype=np.int32)[None])
+    assert abs(math.exp(lse[0, 0]) - g["expsum_all"]) <= g["expsum_tol"]
+    O2, lse2 = orc.attend(W, np.array([[0, 1, -1, -1]], np.int32))
+    kept = math.exp(lse2[0, 0] - lse[0, 0])
+    assert abs((1 - kept) - g["dropped_mass"]) <= g["dropped_tol"]
+    # V = identity exposes the probabilities; they sum to one
+    assert abs(O[0, 0].sum() - 1.0) < 1e-12
+    assert abs(O[0, 0][2:].sum() - g["dropped_mass"]) <= g["dropped_tol"]
+
+
+def test_attention_kmeans_toy_printed_weights():
+    g = golden("kmeans_toy.txt")
+    ks = [g["k1"], g["k2"], g["k3"]]
+    assert np.allclose(np.mean(ks, axis=0), g["mean_cluster1"])
+    assert abs(np.dot(g["q"], g["k6p"]) - g["dot_k6p"]) < 1e-12
+    W = _attn_tiny([g["q"]], ks, np.eye(3))
+    O, lse = orc.attend(W, np.arange(3, dtype=np.int32)[None])
+    assert np.allclose(O[0, 0], g["weights"], atol=g["weights_tol"])
+    Wv = _attn_tiny([g["q"]], ks, g["v"])
+    Ov, _ = orc.attend(Wv, np.arange(3, dtype=np.int32)[None])
+    assert abs(Ov[0, 0, 0] - np.dot(g["weights"], g["v"])) < 3 * g["weights_tol"] * 4
+
+
+def test_attention_cobs_block_mass_printed():
+    g = golden("cobs_toy_block.txt")
+    keys = g["keys"]
+    for qk, lk, mk in (("q_a", "lnm_a", "m_a"), ("q_b", "lnm_b", "m_b"), ("q_c", "lnm_c", "m_c")):
+        W = _attn_tiny([g[qk]], keys, np.ones(4))
+        O, lse = orc.attend(W, np.arange(4, dtype=np.int32)[None])
+        assert abs(lse[0, 0] - g[lk]) <= g["tol"]
+        assert abs(math.exp(lse[0, 0]) - g[mk]) <= 1e-4 * g[mk]
+        assert abs(O[0, 0, 0] - 1.0) < 1e-12  # softmax weights sum to one
+
+
+def test_attention_linear_recursion_example_causal():
+    # ch. 26 §26.5: logits ln(k_i) turn causal softmax attention into the printed running
+    # weighted average S_i / Z_i: outputs 4, 2, 2.25, then 3.5 after appending (2, 6).
+    g = golden("linear_recursion.txt")
+    kw = list(g["key_weights"]) + [g["append_key"]]
+    vals = list(g["values"]) + [g["append_value"]]
+    n = len(kw)
+    keys = np.log(np.array(kw))[:, None]
+    Q = np.ones((1, 1, n, 1))
+    W = tiny(Q=Q, K=keys[None, None], V=np.array(vals)[None, None, :, None], causal=1, scale=1.0, k=n)
+    O, lse = orc.attend(W, full_idx(W))
+    want = list(g["outputs"]) + [g["append_output"]]
+    assert np.allclose(O[:, 0, 0], want, rtol=0, atol=1e-6)
+
+
+def _torch_sdpa(Q, K, V, scale, mask):
+    q = torch.from_numpy(Q.astype(np.float64)); k = torch.from_numpy(K.astype(np.float64))
+    v = torch.from_numpy(V.astype(np.float64))
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=torch.from_numpy(mask),
+                                                            scale=scale).numpy()
+
+
+def test_attention_degenerate_full_set_equals_dense_causal_sdpa():
+    # Spec invariant and Hashing-and-clustering §5.1 (minimal correctness tests):
+    # when k >= the visible count, sparse attention equals dense causal attention.
+    rng = np.random.default_rng(9)
+    B, H, n, d = 2, 3, 24, 8
+    Q, K, V = (rand_f32(rng, (B, H, n, d)) for _ in range(3))
+    W = tiny(Q=Q, K=K, V=V, causal=1, scale=0.3, k=n)
+    O, lse = orc.attend(W, full_idx(W))
+    mask = np.tril(np.ones((n, n), dtype=bool))
+    ref = _torch_sdpa(Q, K, V, 0.3, mask)  # [B,H,n,d]
+    got = O.reshape(B, n, H, d).transpose(0, 2, 1, 3)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_gqa_sharing_matches_sdpa():
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, n, d = 1, 6, 2, 16, 4
+    Q = rand_f32(rng, (B, Hq, n, d)); K = rand_f32(rng, (B, Hkv, n, d)); V = rand_f32(rng, (B, Hkv, n, d))
+    W = tiny(Q=Q, K=K, V=V, causal=1, scale=0.5, k=n)
+    O, _ = orc.attend(W, full_idx(W))
+    Kx = np.repeat(K, Hq // Hkv, axis=1); Vx = np.repeat(V, Hq // Hkv, axis=1)
+    ref = _torch_sdpa(Q, Kx, Vx, 0.5, np.tril(np.ones((n, n), dtype=bool)))
+    assert np.allclose(O.reshape(B, n, Hq, d).transpose(0, 2, 1, 3), ref, atol=1e-12)
+
+
+def test_attention_local_window_equals_banded_sdpa():
+    # Hashing and clustering §5.1: fixing the candidates to a local window must equal a
+    # regular window implementation.
+    rng = np.random.default_rng(11)
+    n, d, width = 20, 5, 3
+    Q, K, V = (rand_f32(rng, (1, 1, n, d)) for _ in range(3))
+    W = tiny(Q=Q, K=K, V=V, causal=1, scale=0.7, k=width)
+    idx = np.array([[j if j >= 0 else -1 for j in range(i - width + 1, i + 1)] for i in range(n)], np.int32)
+    O, _ = orc.attend(W, idx)
+    ii, jj = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    mask = (jj <= ii) & (jj > ii - width)
+    ref = _torch_sdpa(Q, K, V, 0.7, mask)
+    assert np.allclose(O[:, 0, :], ref[0, 0], atol=1e-12)
+
+
+def test_attention_block_mixture_and_exact_drop_error():
+    # COBS reading note eq. (P3): o* = sum_b P_b v_b^c for any partition of the candidates
+    # into blocks; eq. (2)-(3): renormalising over kept blocks S gives
+    # o* - o_S = 1/(1 - tau) * sum_{b not in S} P_b (v_b^c - o*).
+    rng = np.random.default_rng(12)
+    n, d = 40, 6
+    Q, K, V = (rand_f32(rng, (1, 1, n, d)) for _ in range(3))
+    W = tiny(Q=Q, K=K, V=V, causal=0, scale=0.8, k=n)
+    row = np.array([0], np.int32)
+    o_all, lse_all = orc.attend(W, np.arange(n, dtype=np.int32)[None], rows=row)
+    blocks = [np.arange(s, min(s + 7, n)) for s in range(0, n, 7)]
+    P, vc = [], []
+    for blk in blocks:
+        ix = np.full((1, n), -1, np.int32); ix[0, : blk.size] = blk
+        ob, lb = orc.attend(W, ix, rows=row)
+        P.append(math.exp(lb[0, 0] - lse_all[0, 0])); vc.append(ob[0, 0])
+    P, vc = np.array(P), np.array(vc)
+    assert abs(P.sum() - 1) < 1e-12
+    assert np.allclose((P[:, None] * vc).sum(0), o_all[0, 0], atol=1e-12)
+    keep = [0, 2, 3]
+    drop = [b for b in range(len(blocks)) if b not in keep]
+    ix = np.full((1, n), -1, np.int32)
+    sel = np.concatenate([blocks[b] for b in keep]); ix[0, : sel.size] = sel
+    o_s, _ = orc.attend(W, ix, rows=row)
+    tau = P[drop].sum()
+    pred = (P[drop, None] * (vc[drop] - o_all[0, 0])).sum(0) / (1 - tau)
+    assert np.allclose(o_all[0, 0] - o_s[0, 0], pred, atol=1e-12)
+
+
+def test_attention_permutation_invariance_with_positions():
+    # Hashing and clustering §5.2 (the permuted-order causal-leak test) and the north-star
+    # invariant: permuting history storage together with its positions changes nothing;
+    # causality and the tie-break use positions, not slots.
+    W = sa_synth.make_config(0)
+    rng = np.random.default_rng(13)
+    perm = rng.permutation(W["n_kv"])  # slot s holds position perm[s]
+    inv = np.argsort(perm)
+    Wp = dict(W)
+    Wp["k_idx"] = np.ascontiguousarray(W["k_idx"][:, perm])
+    Wp["K"] = np.ascontiguousarray(W["K"][:, :, perm])
+    Wp["V"] = np.ascontiguousarray(W["V"][:, :, perm])
+    pos = perm[None].astype(np.int32)
+    base = orc.select_attend(W)
+    sc = orc.scores(Wp, pos_of_slot=pos)
+    idx, *_ = orc.select(Wp, sc, pos_of_slot=pos)
+    O, lse = orc.attend(Wp, idx, pos_of_slot=pos)
+    mapped = np.where(idx >= 0, perm[np.maximum(idx, 0)], -1)
+    assert np.array_equal(mapped, base["idx"])
+    assert np.allclose(O, base["O"], atol=1e-12) and np.allclose(lse, base["lse"], atol=1e-12)
+    assert inv.size == W["n_kv"]
+
+
+def test_attention_ignores_invisible_and_invalid_indices():
+    # Supplied indices that are -1, out of range, in the future or in the padding take no
+    # part (Hashing and clustering §1.1: candidates intersect the causal and valid sets).
+    rng = np.random.default_rng(14)
+    n, d = 12, 4
+    Q, K, V = (rand_f32(rng, (1, 1, n, d)) for _ in range(3))
+    W = tiny(Q=Q, K=K, V=V, causal=1, scale=1.0, k=5, kv_len=[10])
+    row = np.array([6], np.int32)
+    clean, lc = orc.attend(W, np.array([[1, 4, 6, -1, -1]], np.int32), rows=row)
+    dirty, ld = orc.attend(W, np.array([[1, 4, 6, 7, 11]], np.int32), rows=row)
+    assert np.array_equal(clean, dirty) and np.array_equal(lc, ld)
+    pad_row = np.array([10], np.int32)  # q_pos 10 >= kv_len: padded query row
+    Op, lp = orc.attend(W, np.array([[0, 1, 2, 3, 4]], np.int32), rows=pad_row)
+    assert (Op == 0).all() and np.isneginf(lp).all()
+
+
+def test_padding_poison_never_leaks():
+    # Padded history (positions >= kv_len) is filled with values that would dominate if read;
+    # replacing them with other values changes nothing.
+    W = sa_synth.make_config(1, n=256)
+    rows = np.array([0, 100, 255, 256, 256 + W["kv_len"][1] - 1, 256 + W["kv_len"][1], 511], np.int32)
+    a = orc.select_attend(W, rows)
+    W2 = dict(W)
+    for key in ("k_idx", "K", "V"):
+        W2[key] = W[key].copy()
+    L = W["kv_len"][1]
+    W2["k_idx"][1, L:] = 0
+    W2["K"][1, :, L:] = 0
+    W2["V"][1, :, L:] = 0
+    b = orc.select_attend(W2, rows)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["O"], b["O"])
+    assert (a["idx"][-2:] == -1).all() and (a["O"][-2:] == 0).all() and np.isneginf(a["lse"][-2:]).all()
+
+
+def test_kv_byte_accounting_example():
+    # ch. 26 §26.2 example 26.1 / Table 26.1 and exercise 1: 2 * Hkv * d * n * bytes.
+    g = golden("kv_bytes.txt")
+    from bench import kv_cache_bytes  # the benchmark's own byte accounting
+    d, n, b = int(g["head_dim"]), int(g["positions"]), int(g["bytes_per"])
+    assert kv_cache_bytes(8, d, n, b) == g["mha_bytes"]
+    assert kv_cache_bytes(2, d, n, b) == g["gqa2_bytes"]
+    assert kv_cache_bytes(1, d, n, b) == g["mqa_bytes"]
+    assert kv_cache_bytes(int(g["exercise_kv_heads"]), d, int(g["exercise_positions"]), b) == g["exercise_bytes"]
