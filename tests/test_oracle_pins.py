@@ -109,6 +109,8 @@ def test_indexer_score_hand_worked_example():
     g, W = _hand_indexer()
     r = orc.scores(W)[0]
     assert np.array_equal(r, np.array(g["scores"]))
+    W["w"] = np.array(g["w_neg"], dtype=np.float32)[None, None]
+    assert np.array_equal(orc.scores(W)[0], np.array(g["scores_wneg"]))
 
 
 def test_indexer_relu_identity_from_resmisa():
@@ -157,17 +159,18 @@ def test_indexer_positive_homogeneity():
     assert np.array_equal(i1, i2)
 
 
-def test_indexer_brute_force_tiny_against_python_loops():
-    # Brute force in pure Python on a tiny problem with causal mask and padding.
+@pytest.mark.parametrize("causal", [1, 0])
+def test_indexer_brute_force_tiny_against_python_loops(causal):
+    # Brute force in pure Python on a tiny problem with padding, causal and not.
     rng = np.random.default_rng(5)
     B, n, H, d = 2, 9, 3, 4
     q = rand_f32(rng, (B, n, H, d)); kk = rand_f32(rng, (B, n, d)); w = rng.random((B, n, H)).astype(np.float32)
-    W = tiny(q_idx=q, k_idx=kk, w=w, causal=1, kv_len=[9, 6])
+    W = tiny(q_idx=q, k_idx=kk, w=w, causal=causal, kv_len=[9, 6])
     r = orc.scores(W).reshape(B, n, n)
     for b in range(B):
         for i in range(n):
             for j in range(n):
-                vis = i < W["kv_len"][b] and j < W["kv_len"][b] and j <= i
+                vis = i < W["kv_len"][b] and j < W["kv_len"][b] and (j <= i or not causal)
                 if not vis:
                     assert r[b, i, j] == -np.inf
                     continue
