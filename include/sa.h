@@ -1,0 +1,175 @@
+/*
+ * sa.h -- C ABI of libsa.so: content-routed token-sparse attention with a
+ * Lightning-Indexer-style selector, for AMD MI355X (gfx950).
+ *
+ * The path has three steps, each with its own entry point, plus one fused call:
+ *   1. sa_indexer_score  proxy score  r[b,i,j] = sum_h w[b,i,h] * ReLU(<q_idx[b,i,h,:], k_idx[b,j,:]>)
+ *                        over the visible history of every query row.
+ *   2. sa_topk           per-row top-k of those scores with a deterministic
+ *                        (score desc, position asc) order; indices in ascending position.
+ *   3. sa_sparse_attn    exact softmax attention over the selected rows only, with one
+ *                        candidate set shared by all main heads of a query.
+ *   sa_select_attend     1 -> 2 -> 3 in one call.
+ * Definitions are those of "PaperTrace 2.2 · Fine-grained indexing" (§1.1 and §3.2 for the
+ * score, §2.1 eq. (4) and the following paragraphs for the selection, §3.1 for the tie
+ * rule and the finiteness check) and "PaperTrace 2.1.1 · Hashing and clustering" (§1.1 for
+ * sparse attention over a candidate set intersected with the causal and padding masks,
+ * §5.1 for one softmax shared by all candidate pieces).
+ *
+ * ---- Conventions shared by every entry point ---------------------------------------
+ * Memory.  Every pointer argument is DEVICE memory on the current HIP device unless
+ *   stated otherwise.  The caller owns every buffer, including the workspace; the library
+ *   never allocates or frees memory and keeps no global state.  All work is enqueued on
+ *   `stream` (a hipStream_t passed as void*; NULL = the default stream) and is
+ *   asynchronous: buffers must stay valid until the stream reaches the work.
+ * Errors.  Argument errors are detected on the host before anything is launched and are
+ *   returned synchronously (SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE).  A
+ *   launch failure returns SA_ERR_HIP.  Non-finite visible scores (from non-finite index
+ *   inputs) are detected on the device and recorded in a status word in the workspace,
+ *   read by sa_device_status(); outputs of such a row are unspecified.
+ * Positions and masks.  Query row i of batch b sits at absolute position
+ *   q_pos(b,i) = q_pos0[b] + i.  History position j is visible to that row iff
+ *   j < kv_len[b] and, when causal, j <= q_pos(b,i) (a query sees itself).  A query row is
+ *   valid iff q_pos(b,i) < kv_len[b]; an invalid (padded) row gets idx all -1, O = 0 and
+ *   LSE = -inf.
+ * Tensors.  An sa_tensor is a strided view whose last dimension is contiguous:
+ *   element (i0, i1, i2, d) lives at data + i0*s0 + i1*s1 + i2*s2 + d (strides in
+ *   ELEMENTS).  The data pointer must be 16-byte aligned and every stride times the element
+ *   size a multiple of 16 bytes.  Dimension order per tensor is given at each argument.
+ * Dtypes.  SA_F32, SA_BF16 (bit pattern of the upper half of an f32) and SA_FP8_E4M3
+ *   (OCP e4m3fn: bias 7, no infinities, 0x7f/0xff are NaN, max 448).
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+typedef enum sa_status {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = 1, /* null pointer, bad size or stride, inconsistent dims */
+    SA_ERR_UNSUPPORTED = 2, /* valid but not implemented: dtype combination or head size */
+    SA_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than sa_workspace_bytes() */
+    SA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+    SA_ERR_NONFINITE = 5    /* device side: a visible score was NaN or infinite */
+} sa_status;
+
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_FP8_E4M3 = 2 } sa_dtype;
+
+typedef enum sa_op {
+    SA_OP_INDEXER_SCORE = 0,
+    SA_OP_TOPK = 1,
+    SA_OP_SPARSE_ATTN = 2,
+    SA_OP_SELECT_ATTEND = 3
+} sa_op;
+
+typedef struct sa_tensor {
+    void* data;       /* device pointer, 16-byte aligned */
+    int32_t dtype;    /* sa_dtype */
+    int64_t s0, s1, s2; /* element strides of the three leading dimensions */
+} sa_tensor;
+
+typedef struct sa_problem {
+    int32_t B;      /* batch */
+    int32_t n_q;    /* query rows per batch */
+    int32_t n_kv;   /* history capacity per batch (rows of k_idx / K / V) */
+    int32_t Hq;     /* main query heads */
+    int32_t Hkv;    /* main key/value heads; Hq % Hkv == 0 (grouped sharing) */
+    int32_t d_qk;   /* main query/key head width */
+    int32_t d_v;    /* main value head width */
+    int32_t Hidx;   /* index heads */
+    int32_t d_idx;  /* index head width */
+    int32_t k;      /* selection budget per query row, >= 1 */
+    int32_t causal; /* 1: j visible only if j <= q_pos(b,i); 0: the whole valid history */
+    const int32_t* kv_len; /* device [B], valid history length per batch, <= n_kv; NULL = n_kv */
+    const int32_t* q_pos0; /* device [B], absolute position of query row 0; NULL = 0 */
+    float scale;    /* softmax logit scale; 0 selects 1/sqrt(d_qk) */
+} sa_problem;
+
+/*
+ * sa_indexer_score -- the proxy score of every (query row, history position).
+ * "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §3.2: per-query index heads, one
+ * index key per token shared by all heads, query-dependent head weights, ReLU matching.
+ *   q_idx  [B, n_q, Hidx, d_idx]  f32 or bf16      (s0 = batch, s1 = row, s2 = head)
+ *   k_idx  [B, n_kv, d_idx]       f32, bf16, e4m3  (s0 = batch, s1 = position; s2 unused)
+ *   w      [B, n_q, Hidx]         f32              (s0 = batch, s1 = row; s2 unused)
+ *   scores [B, n_q, n_kv] f32, contiguous: scores[(b*n_q + i)*n_kv + j]; -inf where j is
+ *          not visible (and on every position of an invalid row).
+ * Accumulation is fp32 over exact bf16 products (e4m3 widens exactly to bf16).  The
+ * reduction order does not depend on j, so byte-identical index keys score bit-identically.
+ */
+sa_status sa_indexer_score(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w,
+                           float* scores, void* stream);
+
+/*
+ * sa_topk -- per-row selection.  "PaperTrace 2.2 · Fine-grained indexing", §2.1 eq. (4),
+ * the causal-prefill paragraph (rows with fewer than k visible positions return all of
+ * them and mark the other slots invalid) and §3.1 (lexicographic (score, index) order).
+ *   scores  f32, row (b,i) at scores + (b*n_q + i)*row_stride; only visible entries are read.
+ *   idx     [B, n_q, k] int32, contiguous: the first min(k, |visible|) positions in
+ *           (score desc, position asc) order, written in ascending position, then -1.
+ *   vals    [B, n_q, k] f32 or NULL: the score of each idx entry (-inf for -1 slots).
+ *   ws      workspace of at least sa_workspace_bytes(p, SA_OP_TOPK) bytes, 256-byte
+ *           aligned, zero-filled by the caller once after allocation (it carries the
+ *           device status word between calls).
+ * A NaN or infinite visible score sets SA_ERR_NONFINITE in the status word.
+ */
+sa_status sa_topk(const sa_problem* p, const float* scores, int64_t row_stride, int32_t* idx, float* vals,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sa_sparse_attn -- exact softmax attention over the selected history rows.
+ * "PaperTrace 2.1.1 · Hashing and clustering", §1.1 eq. (1): logits, mask, softmax and
+ * value aggregation only over the candidate set; §5.1: every piece of the set shares one
+ * row maximum and exp-sum (split pieces are merged by log-sum-exp).
+ *   Q [B, Hq, n_q, d_qk], K [B, Hkv, n_kv, d_qk], V [B, Hkv, n_kv, d_v]   (s0 = batch,
+ *      s1 = head, s2 = row).  Q, K, V and O share one dtype, f32 or bf16.  V may alias K
+ *      (latent layout: V = the first d_v columns of each K row, same strides).
+ *   idx [B, n_q, k] int32, contiguous; entries that are -1, out of range or not visible
+ *      are ignored (never read).  Valid entries must be unique (a duplicate would count
+ *      twice in the softmax); their order does not matter.
+ *   O   [B, Hq, n_q, d_v] output; query head h reads key/value head h / (Hq / Hkv).
+ *   lse [B, Hq, n_q] f32 or NULL: natural-log log-sum-exp of the scaled logits
+ *      (-inf when a row has no valid entry; then O = 0).
+ *   ws  workspace of at least sa_workspace_bytes(p, SA_OP_SPARSE_ATTN) bytes.
+ * Logits and softmax statistics are fp32; probabilities are rounded to the input dtype for
+ * the value product on the matrix-core path.
+ */
+sa_status sa_sparse_attn(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tensor V, const int32_t* idx,
+                         sa_tensor O, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sa_select_attend -- score, select and attend in one call; arguments as in the three
+ * entry points above.  idx_out [B, n_q, k] int32 receives the selection if not NULL.
+ * ws must hold sa_workspace_bytes(p, SA_OP_SELECT_ATTEND) bytes (it includes the score
+ * buffer of the visible part of every row).
+ */
+sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, sa_tensor Q,
+                           sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by operation `op` (an sa_op) for problem p; 0 for a malformed p. */
+size_t sa_workspace_bytes(const sa_problem* p, int op);
+
+/* Synchronises `stream`, returns the status word accumulated in ws by earlier calls
+ * (SA_OK or SA_ERR_NONFINITE) and clears it.  ws is a host-visible pointer to device
+ * memory as passed to the other calls. */
+sa_status sa_device_status(void* ws, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* sa_status_str(sa_status s);
+
+/* SA_ABI_VERSION of the loaded library. */
+int sa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

@@ -1,0 +1,225 @@
+// Host side of libsa.so: argument validation, workspace layout and kernel dispatch.
+// Every argument error is detected here, before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "sa_internal.h"
+
+namespace {
+
+using namespace sa;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int esize(int dtype) {
+    switch (dtype) {
+    case SA_F32: return 4;
+    case SA_BF16: return 2;
+    case SA_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+bool problem_ok(const sa_problem* p) {
+    if (!p) return false;
+    if (p->B < 1 || p->n_q < 1 || p->n_kv < 1 || p->k < 1) return false;
+    if (p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0) return false;
+    if (p->d_qk < 1 || p->d_v < 1 || p->Hidx < 1 || p->d_idx < 1) return false;
+    if (p->causal != 0 && p->causal != 1) return false;
+    if (!(p->scale >= 0.f) || isinf(p->scale)) return false;
+    // flat row counts must stay addressable with 32-bit grid dimensions
+    if ((long long)p->B * p->n_q > 0x7fffffffLL) return false;
+    return true;
+}
+
+// A strided view used with 16-byte vector loads of its contiguous last dimension.
+sa_status tensor_ok(const sa_tensor& t, int last_dim, int ndims_strided) {
+    const int es = esize(t.dtype);
+    if (!t.data) return SA_ERR_INVALID_ARG;
+    if (es == 0) return SA_ERR_UNSUPPORTED;
+    if (((uintptr_t)t.data & 15) != 0) return SA_ERR_INVALID_ARG;
+    const int64_t st[3] = {t.s0, t.s1, t.s2};
+    for (int d = 0; d < ndims_strided; ++d) {
+        if (st[d] < 0) return SA_ERR_INVALID_ARG;
+        if ((st[d] * es) % 16 != 0) return SA_ERR_INVALID_ARG;
+    }
+    if (((int64_t)last_dim * es) % 16 != 0) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+sa_status ws_ok(const void* ws, size_t have, size_t need) {
+    if (!ws) return SA_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255) != 0) return SA_ERR_WORKSPACE;
+    if (have < need) return SA_ERR_WORKSPACE;
+    return SA_OK;
+}
+
+size_t scores_bytes(const sa_problem& p) { return align256((size_t)p.B * p.n_q * p.n_kv * sizeof(float)); }
+size_t idx_bytes(const sa_problem& p) { return align256((size_t)p.B * p.n_q * p.k * sizeof(int32_t)); }
+
+sa_status check_indexer(const sa_problem* p, const sa_tensor& q, const sa_tensor& k, const sa_tensor& w) {
+    sa_status s;
+    if (q.dtype != SA_F32 && q.dtype != SA_BF16) return q.data ? SA_ERR_UNSUPPORTED : SA_ERR_INVALID_ARG;
+    if (k.dtype != SA_F32 && k.dtype != SA_BF16 && k.dtype != SA_FP8_E4M3) return k.data ? SA_ERR_UNSUPPORTED : SA_ERR_INVALID_ARG;
+    if (w.dtype != SA_F32) return w.data ? SA_ERR_UNSUPPORTED : SA_ERR_INVALID_ARG;
+    if ((s = tensor_ok(q, p->d_idx, 3)) != SA_OK) return s;
+    if ((s = tensor_ok(k, p->d_idx, 2)) != SA_OK) return s;
+    if (!w.data || ((uintptr_t)w.data & 3)) return SA_ERR_INVALID_ARG;
+    if (w.s0 < 0 || w.s1 < 0) return SA_ERR_INVALID_ARG;
+    if ((long long)p->Hidx * p->d_idx > 8192) return SA_ERR_UNSUPPORTED;  // LDS staging of the plain path
+    return SA_OK;
+}
+
+sa_status check_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V,
+                     const sa_tensor& O) {
+    sa_status s;
+    if (Q.dtype != K.dtype || Q.dtype != V.dtype || Q.dtype != O.dtype) return SA_ERR_UNSUPPORTED;
+    if (Q.dtype != SA_F32 && Q.dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if ((s = tensor_ok(Q, p->d_qk, 3)) != SA_OK) return s;
+    if ((s = tensor_ok(K, p->d_qk, 3)) != SA_OK) return s;
+    if ((s = tensor_ok(V, p->d_v, 3)) != SA_OK) return s;
+    if ((s = tensor_ok(O, p->d_v, 3)) != SA_OK) return s;
+    const int G = p->Hq / p->Hkv;
+    if (attn_uses_mla(*p, Q.dtype)) return SA_OK;
+    const int lpr = p->d_qk * esize(Q.dtype) / 16;
+    if (p->d_qk != p->d_v) return SA_ERR_UNSUPPORTED;
+    if (lpr != 8 && lpr != 16 && lpr != 32) return SA_ERR_UNSUPPORTED;
+    if (G != 1 && G != 2 && G != 4) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+float eff_scale(const sa_problem* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d_qk); }
+
+sa_status run_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V,
+                   const int32_t* idx, const sa_tensor& O, float* lse, void* partial, hipStream_t st) {
+    AttnArgs a;
+    a.p = *p;
+    a.Q = Q; a.K = K; a.V = V; a.O = O;
+    a.idx = idx;
+    a.lse = lse;
+    a.scale = eff_scale(p);
+    a.splits = attn_uses_mla(*p, Q.dtype) ? attn_splits(*p) : 1;
+    a.partial = partial;
+    return launch_attn(a, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_abi_version(void) { return SA_ABI_VERSION; }
+
+const char* sa_status_str(sa_status s) {
+    switch (s) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARG: return "SA_ERR_INVALID_ARG";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+    case SA_ERR_NONFINITE: return "SA_ERR_NONFINITE";
+    default: return "SA_ERR_UNKNOWN";
+    }
+}
+
+size_t sa_workspace_bytes(const sa_problem* p, int op) {
+    if (!problem_ok(p)) return 0;
+    switch (op) {
+    case SA_OP_INDEXER_SCORE: return 0;
+    case SA_OP_TOPK: return kStatusBytes;
+    case SA_OP_SPARSE_ATTN: return kStatusBytes + align256(attn_partial_bytes(*p));
+    case SA_OP_SELECT_ATTEND:
+        return kStatusBytes + scores_bytes(*p) + idx_bytes(*p) + align256(attn_partial_bytes(*p));
+    default: return 0;
+    }
+}
+
+sa_status sa_indexer_score(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, float* scores,
+                           void* stream) {
+    if (!problem_ok(p) || !scores || ((uintptr_t)scores & 3)) return SA_ERR_INVALID_ARG;
+    sa_status s = check_indexer(p, q_idx, k_idx, w);
+    if (s != SA_OK) return s;
+    IndexerArgs a;
+    a.p = *p;
+    a.q = q_idx; a.k = k_idx; a.w = w;
+    a.scores = scores;
+    a.row_stride = p->n_kv;
+    a.fill_invisible = 1;
+    return launch_indexer(a, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+sa_status sa_topk(const sa_problem* p, const float* scores, int64_t row_stride, int32_t* idx, float* vals, void* ws,
+                  size_t ws_bytes, void* stream) {
+    if (!problem_ok(p) || !scores || !idx || ((uintptr_t)scores & 3)) return SA_ERR_INVALID_ARG;
+    if (row_stride < p->n_kv) return SA_ERR_INVALID_ARG;
+    sa_status s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_TOPK));
+    if (s != SA_OK) return s;
+    TopkArgs a;
+    a.p = *p;
+    a.scores = scores;
+    a.row_stride = row_stride;
+    a.idx = idx;
+    a.vals = vals;
+    a.status = static_cast<Status*>(ws);
+    return launch_topk(a, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+sa_status sa_sparse_attn(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tensor V, const int32_t* idx, sa_tensor O,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (!problem_ok(p) || !idx || ((uintptr_t)idx & 3)) return SA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3)) return SA_ERR_INVALID_ARG;
+    sa_status s = check_attn(p, Q, K, V, O);
+    if (s != SA_OK) return s;
+    if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SPARSE_ATTN))) != SA_OK) return s;
+    void* partial = static_cast<char*>(ws) + kStatusBytes;
+    return run_attn(p, Q, K, V, idx, O, lse, partial, (hipStream_t)stream);
+}
+
+sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, sa_tensor Q,
+                           sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+    if (!problem_ok(p)) return SA_ERR_INVALID_ARG;
+    if (idx_out && ((uintptr_t)idx_out & 3)) return SA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3)) return SA_ERR_INVALID_ARG;
+    sa_status s = check_indexer(p, q_idx, k_idx, w);
+    if (s != SA_OK) return s;
+    if ((s = check_attn(p, Q, K, V, O)) != SA_OK) return s;
+    if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SELECT_ATTEND))) != SA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base + kStatusBytes);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + kStatusBytes + scores_bytes(*p));
+    void* partial = base + kStatusBytes + scores_bytes(*p) + idx_bytes(*p);
+
+    IndexerArgs ia;
+    ia.p = *p;
+    ia.q = q_idx; ia.k = k_idx; ia.w = w;
+    ia.scores = scores;
+    ia.row_stride = p->n_kv;
+    ia.fill_invisible = 0;  // the selection reads only the visible prefix of each row
+    if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
+
+    TopkArgs ta;
+    ta.p = *p;
+    ta.scores = scores;
+    ta.row_stride = p->n_kv;
+    ta.idx = idx;
+    ta.vals = nullptr;
+    ta.status = reinterpret_cast<Status*>(base);
+    if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
+
+    return run_attn(p, Q, K, V, idx, O, lse, partial, st);
+}
+
+sa_status sa_device_status(void* ws, void* stream) {
+    if (!ws || ((uintptr_t)ws & 255)) return SA_ERR_WORKSPACE;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SA_ERR_HIP;
+    Status st;
+    if (hipMemcpy(&st, ws, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return SA_ERR_HIP;
+    Status zero;
+    zero.flags = 0;
+    if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return SA_ERR_HIP;
+    if (st.flags & (1u << SA_ERR_NONFINITE)) return SA_ERR_NONFINITE;
+    return SA_OK;
+}
+
+}  // extern "C"

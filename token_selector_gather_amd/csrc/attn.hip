@@ -1,0 +1,504 @@
+// Sparse gather attention over a selected candidate set.
+//
+// For query row (b,i), main head h (key/value head h / (Hq/Hkv)) and the valid entries
+// j of idx[b,i,:]:  l_j = scale * <Q[b,h,i,:], K[b,hk,j,:]>, one softmax over the whole
+// set (shared row maximum and exp-sum), O = sum_j p_j V[b,hk,j,:], LSE = max + ln(sum)
+// ("PaperTrace 2.1.1 · Hashing and clustering", §1.1 eq. (1) and §5.1; the logit of
+// "PaperTrace 2.2 · Fine-grained indexing", §3.2).  Entries that are -1, out of range or
+// not visible are never read.  Split pieces of one set are merged by log-sum-exp (the
+// block-mixture identity of the COBS reading note, eq. (P3)).
+//
+// Two kernels:
+//  * attn_rows: separate key/value heads (MHA, small GQA groups).  One wave per
+//    (query row, key/value head).  Each history row is fetched by LPR lanes with 16-byte
+//    loads (RPI = 64/LPR rows per load instruction); a dot product finishes with log2(LPR)
+//    xor swaps inside the lane group; every lane group keeps its own online-softmax state
+//    over the rows it fetched and the groups merge once at the end.  Work items are laid
+//    out so that each of the 8 XCDs serves a fixed subset of key/value heads, keeping that
+//    subset's K/V rows in its own L2.
+//  * attn_mla: one latent key/value head shared by many query heads (Hq/Hkv multiple of
+//    16; V = the first d_v columns of K, or a separate tensor).  One workgroup per
+//    (query row, candidate split); wave w owns query heads 16w..16w+15.  A tile of 32
+//    gathered rows is staged in LDS twice: row-major for S^T = K Q^T (v_mfma_f32_16x16x32
+//    _bf16, Q^T fragments stay in registers) and transposed for O^T += V^T P^T.  In the
+//    S^T accumulator layout a lane holds 8 positions of one head, exactly the operand P^T
+//    needs, so probabilities never leave registers; the transposed tile stores positions
+//    in that lane order.
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// 16 bytes -> EPL floats
+template <typename T>
+struct Vec;
+template <>
+struct Vec<float> {
+    static constexpr int EPL = 4;
+    __device__ static void widen(const uint4& u, float* f) {
+        f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+    }
+};
+template <>
+struct Vec<uint16_t> {
+    static constexpr int EPL = 8;
+    __device__ static void widen(const uint4& u, float* f) {
+        f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+        f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+    }
+};
+
+// online-softmax merge of (m, l, o) states in log2 units
+__device__ __forceinline__ void merge_state(float& m, float& l, float* o, int n, float m2, float l2, const float* o2) {
+    const float mn = fmaxf(m, m2);
+    const float a1 = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+    const float a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mn);
+    l = l * a1 + l2 * a2;
+    for (int e = 0; e < n; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+    m = mn;
+}
+
+// ------------------------------------------------------------------ attn_rows
+template <typename T, int LPR, int G>
+__global__ void __launch_bounds__(256) attn_rows(AttnArgs a) {
+    constexpr int EPL = Vec<T>::EPL;
+    constexpr int RPI = 64 / LPR;   // rows per load instruction
+    constexpr int UNROLL = 8;       // load instructions in flight per operand
+    constexpr int ROWS_IT = RPI * UNROLL;
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR, rg = lane / LPR;
+
+    // work item -> (b, i, hk), heads pinned to XCDs when Hkv % 8 == 0
+    const long items = (long)p.B * p.n_q * p.Hkv;
+    const long blk = blockIdx.x;
+    int b, i, hk;
+    {
+        const int nib = (p.n_q + 3) / 4;
+        const int wv = threadIdx.x >> 6;
+        if (p.Hkv % 8 == 0) {
+            const int xcd = (int)(blk % 8);
+            const long local = blk / 8;
+            const int hpx = p.Hkv / 8;
+            hk = xcd + 8 * (int)(local % hpx);
+            const long rest = local / hpx;
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        } else {
+            hk = (int)(blk % p.Hkv);
+            const long rest = blk / p.Hkv;
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        }
+        if (b >= p.B || i >= p.n_q) return;
+        (void)items;
+    }
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const float sl2 = a.scale * kLog2e;
+
+    const T* Qp = static_cast<const T*>(a.Q.data);
+    const T* Kp = static_cast<const T*>(a.K.data);
+    const T* Vp = static_cast<const T*>(a.V.data);
+    float q[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int h = hk * G + g;
+        uint4 u = *reinterpret_cast<const uint4*>(Qp + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2 + sub * EPL);
+        Vec<T>::widen(u, q[g]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) q[g][e] *= sl2;
+    }
+    float m[G], l[G], o[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY; l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+    }
+    const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
+    const int64_t kbase = b * a.K.s0 + hk * a.K.s1 + sub * EPL;
+    const int64_t vbase = b * a.V.s0 + hk * a.V.s1 + sub * EPL;
+
+    if (L > 0) {
+        for (int r0 = 0; r0 < p.k; r0 += ROWS_IT) {
+            int jv[UNROLL];
+            bool ok[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int r = r0 + u * RPI + rg;
+                const int j = r < p.k ? ix[r] : -1;
+                ok[u] = j >= 0 && j < L;
+                jv[u] = ok[u] ? j : 0;
+            }
+            uint4 kr[UNROLL], vr[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                kr[u] = ok[u] ? *reinterpret_cast<const uint4*>(Kp + kbase + (int64_t)jv[u] * a.K.s2) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                vr[u] = ok[u] ? *reinterpret_cast<const uint4*>(Vp + vbase + (int64_t)jv[u] * a.V.s2) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float s[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    float kf[EPL];
+                    Vec<T>::widen(kr[u], kf);
+                    float d = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) d = fmaf(q[g][e], kf[e], d);
+#pragma unroll
+                    for (int o2 = 1; o2 < LPR; o2 <<= 1) d += __shfl_xor(d, o2);
+                    s[u] = ok[u] ? d : -INFINITY;
+                }
+                float mt = m[g];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) mt = fmaxf(mt, s[u]);
+                // mt == -inf only if nothing was valid so far: then l, o are 0 and stay 0
+                const float alpha = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - mt);
+                l[g] *= alpha;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[g][e] *= alpha;
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    const float pu = ok[u] ? exp2f(s[u] - mt) : 0.f;
+                    l[g] += pu;
+                    float vf[EPL];
+                    Vec<T>::widen(vr[u], vf);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pu, vf[e], o[g][e]);
+                }
+                m[g] = mt;
+            }
+        }
+    }
+    // merge the RPI lane groups
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
+            float m2 = __shfl_xor(m[g], off), l2 = __shfl_xor(l[g], off), o2[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o2[e] = __shfl_xor(o[g][e], off);
+            merge_state(m[g], l[g], o[g], EPL, m2, l2, o2);
+        }
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int h = hk * G + g;
+            const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+            T* Op = static_cast<T*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2 + sub * EPL;
+            if constexpr (sizeof(T) == 4) {
+                uint4 w;
+                w.x = __float_as_uint(o[g][0] * inv); w.y = __float_as_uint(o[g][1] * inv);
+                w.z = __float_as_uint(o[g][2] * inv); w.w = __float_as_uint(o[g][3] * inv);
+                *reinterpret_cast<uint4*>(Op) = w;
+            } else {
+                uint32_t pk[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pk[e] = (uint32_t)f32_to_bf16_rne(o[g][2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[g][2 * e + 1] * inv) << 16);
+                *reinterpret_cast<uint4*>(Op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            }
+            if (a.lse && sub == 0)
+                a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = l[g] > 0.f ? (m[g] + log2f(l[g])) * kLn2 : -INFINITY;
+        }
+    }
+}
+
+// ------------------------------------------------------------------- attn_mla
+constexpr int kTile = 32;
+
+__device__ __forceinline__ int vt_slot(int pos) {  // position in tile -> lane-ordered slot
+    const int mt = pos >> 4, g = (pos >> 2) & 3, r = pos & 3;
+    return 8 * g + 4 * mt + r;
+}
+
+template <int DQK, int DV>
+__global__ void __launch_bounds__(512) attn_mla(AttnArgs a) {
+    constexpr int KS = DQK / 32;          // k-steps of S^T
+    constexpr int KPAD = DQK + 8;         // LDS row pitch of the K tile (elements)
+    constexpr int VTP = kTile + 8;        // LDS row pitch of the transposed V tile (elements)
+    constexpr int MTV = DV / 16;          // 16-row tiles of O^T
+    constexpr int CH = DQK / 8;           // 16-byte chunks per K row
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * KPAD];
+    __shared__ __attribute__((aligned(16))) uint16_t VT[DV * VTP];
+    __shared__ int s_j[kTile];
+
+    const sa_problem& p = a.p;
+    const int nw = blockDim.x >> 6;  // waves = heads per kv head / 16
+    const int G = p.Hq / p.Hkv;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = lane & 15, gq = lane >> 4;
+    const int S = a.splits;
+    const long unit = blockIdx.x;  // (b, i, hk, split)
+    const int split = (int)(unit % S);
+    const long rowkv = unit / S;
+    const int hk = (int)(rowkv % p.Hkv);
+    const long row = rowkv / p.Hkv;
+    const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int head = hk * G + 16 * wv + c;  // this lane's query head (column of S^T)
+    const bool v_alias = a.V.data == a.K.data;
+
+    // Q^T fragments: B operand of S^T, lane (gq, c): head c, d = 32 s + 8 gq
+    bf16x8 bq[KS];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + head * a.Q.s1 + (int64_t)i * a.Q.s2;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * gq));
+    }
+    f32x4 oacc[MTV];
+#pragma unroll
+    for (int t = 0; t < MTV; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+    const float sl2 = a.scale * kLog2e;
+
+    const int per = (p.k + S - 1) / S;
+    const int e_begin = split * per, e_end = min(p.k, e_begin + per);
+    const int32_t* ix = a.idx + row * (int64_t)p.k;
+    const uint16_t* Kg = static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1;
+    const uint16_t* Vg = static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1;
+
+    for (int t0 = e_begin; L > 0 && t0 < e_end; t0 += kTile) {
+        if (threadIdx.x < kTile) {
+            const int e = t0 + threadIdx.x;
+            int j = e < e_end ? ix[e] : -1;
+            s_j[threadIdx.x] = (j >= 0 && j < L) ? j : -1;
+        }
+        __syncthreads();
+        // stage K rows (row-major) and V rows (transposed, lane-ordered slots).  A thread
+        // takes one 16-byte chunk of two adjacent positions, which share a 32-bit word in
+        // every transposed row.
+        for (int q = threadIdx.x; q < (kTile / 2) * CH; q += blockDim.x) {
+            const int pp = q % (kTile / 2), ch = q / (kTile / 2);
+            const int p0 = 2 * pp;
+            const int j0 = s_j[p0], j1 = s_j[p0 + 1];
+            const uint4 u0 = j0 >= 0 ? *reinterpret_cast<const uint4*>(Kg + (int64_t)j0 * a.K.s2 + 8 * ch) : make_uint4(0, 0, 0, 0);
+            const uint4 u1 = j1 >= 0 ? *reinterpret_cast<const uint4*>(Kg + (int64_t)j1 * a.K.s2 + 8 * ch) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(&Ks[p0 * KPAD + 8 * ch]) = u0;
+            *reinterpret_cast<uint4*>(&Ks[(p0 + 1) * KPAD + 8 * ch]) = u1;
+            if (ch < DV / 8) {
+                uint4 v0 = u0, v1 = u1;
+                if (!v_alias) {
+                    v0 = j0 >= 0 ? *reinterpret_cast<const uint4*>(Vg + (int64_t)j0 * a.V.s2 + 8 * ch) : make_uint4(0, 0, 0, 0);
+                    v1 = j1 >= 0 ? *reinterpret_cast<const uint4*>(Vg + (int64_t)j1 * a.V.s2 + 8 * ch) : make_uint4(0, 0, 0, 0);
+                }
+                const int sl = vt_slot(p0);  // vt_slot(p0 + 1) == sl + 1 since p0 is even
+                const uint32_t a4[4] = {v0.x, v0.y, v0.z, v0.w}, b4[4] = {v1.x, v1.y, v1.z, v1.w};
+                uint32_t* vt32 = reinterpret_cast<uint32_t*>(VT);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vt32[((8 * ch + 2 * e) * VTP + sl) >> 1] = (a4[e] & 0xffffu) | (b4[e] << 16);
+                    vt32[((8 * ch + 2 * e + 1) * VTP + sl) >> 1] = (a4[e] >> 16) | (b4[e] & 0xffff0000u);
+                }
+            }
+        }
+        __syncthreads();
+        // S^T = K Q^T: two 16-position M-tiles
+        f32x4 sacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint16_t* kr = &Ks[(16 * mt + c) * KPAD + 8 * gq];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 32 * s));
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[s], sacc[mt], 0, 0, 0);
+            }
+        }
+        // lane holds S^T[pos 16 mt + 4 gq + r][head c]
+        float x[8];
+        float mt_max = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pos = 16 * mt + 4 * gq + r;
+                const float v = s_j[pos] >= 0 ? sacc[mt][r] * sl2 : -INFINITY;
+                x[4 * mt + r] = v;
+                mt_max = fmaxf(mt_max, v);
+            }
+        mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16));
+        mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32));
+        const float mn = fmaxf(m, mt_max);
+        if (mn == -INFINITY) {
+            __syncthreads();
+            continue;
+        }
+        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+        m = mn;
+        float pv[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pv[e] = x[e] == -INFINITY ? 0.f : exp2f(x[e] - mn);
+            ps += pv[e];
+        }
+        lsum = lsum * alpha + ps;
+        bf16x8 pb;
+        {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = (uint32_t)f32_to_bf16_rne(pv[2 * e]) | ((uint32_t)f32_to_bf16_rne(pv[2 * e + 1]) << 16);
+            pb = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int t = 0; t < MTV; ++t) {
+            oacc[t][0] *= alpha; oacc[t][1] *= alpha; oacc[t][2] *= alpha; oacc[t][3] *= alpha;
+            bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&VT[(16 * t + c) * VTP + 8 * gq]));
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[t], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    // total exp-sum per head: lanes with the same c hold disjoint positions
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    // lane holds O^T[d = 16 t + 4 gq + r][head c]
+    if (S == 1) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2;
+#pragma unroll
+        for (int t = 0; t < MTV; ++t) {
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(oacc[t][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[t][1] * inv) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_rne(oacc[t][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[t][3] * inv) << 16);
+            *reinterpret_cast<uint2*>(op + 16 * t + 4 * gq) = make_uint2(lo, hi);
+        }
+        if (a.lse && gq == 0)
+            a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
+    } else {
+        // partial: [row, Hq, S] x (m, l) and [row, Hq, S, DV] unnormalised o
+        float* part = static_cast<float*>(a.partial);
+        const int64_t slot = (row * p.Hq + head) * (int64_t)S + split;
+        float* ml = part + slot * 2;
+        float* po = part + (int64_t)p.B * p.n_q * p.Hq * S * 2 + slot * DV;
+#pragma unroll
+        for (int t = 0; t < MTV; ++t)
+            *reinterpret_cast<float4*>(po + 16 * t + 4 * gq) = make_float4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3]);
+        if (gq == 0) {
+            ml[0] = m;
+            ml[1] = lsum;
+        }
+    }
+}
+
+// Merge the S split partials of each (row, head) by log-sum-exp.
+template <int DV>
+__global__ void __launch_bounds__(256) lse_merge(AttnArgs a) {
+    const sa_problem& p = a.p;
+    const int S = a.splits;
+    const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
+    const long total = (long)p.B * p.n_q * p.Hq;
+    if (item >= total) return;
+    const int lane = threadIdx.x & 63;
+    const long row = item / p.Hq;
+    const int head = (int)(item % p.Hq);
+    const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
+    const float* part = static_cast<const float*>(a.partial);
+    const float* ml = part + item * S * 2;
+    const float* po = part + total * S * 2 + item * (int64_t)S * DV;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+    float l = 0.f;
+    constexpr int PER = DV / 64;
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < S; ++s) {
+            const float ms = ml[2 * s];
+            if (ms == -INFINITY) continue;
+            const float w = exp2f(ms - M);
+            l += w * ml[2 * s + 1];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) o[e] = fmaf(w, po[s * DV + lane * PER + e], o[e]);
+        }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2 + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) op[e] = f32_to_bf16_rne(o[e] * inv);
+    if (a.lse && lane == 0) a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int LPR>
+hipError_t launch_rows_g(const AttnArgs& a, int G, unsigned blocks, hipStream_t s) {
+    if (G == 1) hipLaunchKernelGGL((attn_rows<T, LPR, 1>), dim3(blocks), dim3(256), 0, s, a);
+    else if (G == 2) hipLaunchKernelGGL((attn_rows<T, LPR, 2>), dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_rows<T, LPR, 4>), dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_uses_mla(const sa_problem& p, int dtype) {
+    const int G = p.Hq / p.Hkv;
+    return dtype == SA_BF16 && G % 16 == 0 && G <= 128 && p.d_qk == 576 && p.d_v == 512;
+}
+
+int attn_splits(const sa_problem& p) {
+    // enough workgroups to fill 256 CUs twice; at least 4 tiles of candidates per split
+    const long units = (long)p.B * p.n_q * p.Hkv;
+    long s = (512 + units - 1) / units;
+    long cap = p.k / (4 * kTile);
+    if (cap < 1) cap = 1;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+size_t attn_partial_bytes(const sa_problem& p) {
+    const int S = attn_splits(p);
+    if (S <= 1) return 0;
+    return (size_t)p.B * p.n_q * p.Hq * S * (2 + (size_t)p.d_v) * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+    const sa_problem& p = a.p;
+    if (attn_uses_mla(p, a.Q.dtype)) {
+        const int G = p.Hq / p.Hkv;
+        const long units = (long)p.B * p.n_q * p.Hkv * a.splits;
+        hipLaunchKernelGGL((attn_mla<576, 512>), dim3((unsigned)units), dim3(64 * (G / 16)), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.splits == 1) return e;
+        const long items = (long)p.B * p.n_q * p.Hq;
+        hipLaunchKernelGGL((lse_merge<512>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    const int G = p.Hq / p.Hkv;
+    const int esz = a.Q.dtype == SA_F32 ? 4 : 2;
+    const int LPR = p.d_qk * esz / 16;
+    const unsigned blocks = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
+    if (a.Q.dtype == SA_F32) {
+        if (LPR == 8) return launch_rows_g<float, 8>(a, G, blocks, s);
+        if (LPR == 16) return launch_rows_g<float, 16>(a, G, blocks, s);
+        return launch_rows_g<float, 32>(a, G, blocks, s);
+    }
+    if (LPR == 8) return launch_rows_g<uint16_t, 8>(a, G, blocks, s);
+    if (LPR == 16) return launch_rows_g<uint16_t, 16>(a, G, blocks, s);
+    return launch_rows_g<uint16_t, 32>(a, G, blocks, s);
+}
+
+}  // namespace sa

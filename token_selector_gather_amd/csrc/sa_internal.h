@@ -1,0 +1,72 @@
+// Internal declarations shared by the host dispatcher and the kernels of libsa.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa.h"
+
+namespace sa {
+
+// Visible-history description of one batch, read on the device from kv_len / q_pos0.
+struct Rows {
+    const int32_t* kv_len;  // [B] or null (= n_kv)
+    const int32_t* q_pos0;  // [B] or null (= 0)
+    int32_t n_q, n_kv, causal;
+};
+
+// Number of visible history positions of query row (b, i); 0 for an invalid row.  The
+// visible set is always the prefix [0, L) of the history.
+__device__ __forceinline__ int visible_len(const Rows& r, int b, int i) {
+    int kl = r.kv_len ? r.kv_len[b] : r.n_kv;
+    kl = kl < 0 ? 0 : (kl > r.n_kv ? r.n_kv : kl);
+    long qp = (long)(r.q_pos0 ? r.q_pos0[b] : 0) + i;
+    if (qp < 0 || qp >= kl) return 0;
+    if (!r.causal) return kl;
+    long L = qp + 1;
+    return (int)(L < kl ? L : kl);
+}
+
+// Status word layout at the start of every workspace.
+constexpr size_t kStatusBytes = 256;
+struct Status {
+    uint32_t flags;  // bit SA_ERR_NONFINITE set when a visible score was not finite
+};
+
+// --- launchers (each returns hipSuccess or the launch error) ---
+
+struct IndexerArgs {
+    sa_problem p;
+    sa_tensor q, k, w;
+    float* scores;
+    int64_t row_stride;  // floats between consecutive rows of scores
+    int fill_invisible;  // 1: write -inf into every invisible entry of [0, n_kv)
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+
+struct TopkArgs {
+    sa_problem p;
+    const float* scores;
+    int64_t row_stride;
+    int32_t* idx;
+    float* vals;
+    Status* status;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct AttnArgs {
+    sa_problem p;
+    sa_tensor Q, K, V, O;
+    const int32_t* idx;
+    float* lse;
+    float scale;
+    void* partial;  // workspace for split-candidate partial results (may be null if splits == 1)
+    int splits;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// Host-side planning shared by workspace sizing and launches.
+int attn_splits(const sa_problem& p);
+bool attn_uses_mla(const sa_problem& p, int dtype);
+size_t attn_partial_bytes(const sa_problem& p);
+
+}  // namespace sa

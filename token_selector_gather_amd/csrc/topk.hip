@@ -1,0 +1,208 @@
+// Per-row top-k selection.
+//
+// S(b,i) = the first min(k, L) visible positions in (score desc, position asc) order,
+// written in ascending position; the remaining slots are -1 ("PaperTrace 2.2 ·
+// Fine-grained indexing", §2.1: Select over the visible history, rows shorter than k
+// return all their positions and mark the rest invalid; §3.1: lexicographic
+// (score, index) order, NaN handled before the selection).
+//
+// One workgroup of 256 threads per row.  Scores map to order-preserving uint32 keys
+// (sign-flip; -0 is folded onto +0).  A three-digit MSB radix select (11 + 11 + 10 bits,
+// LDS histograms, one suffix scan per digit) finds the k-th largest key T and how many
+// keys equal to T the set needs.  A final ordered pass then keeps every key > T and the
+// first `need` keys == T in position order.  Each thread handles four consecutive
+// positions per tile and a single packed block scan yields, for every position, both the
+// number of greater keys and the number of equal keys before it, so the output is written
+// in ascending position and exact ties go to the lower positions.
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) == 0) u = 0;  // -0 == +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan of one uint32 per thread over the block; returns the prefix, sets total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_tot[wid] = x;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        uint32_t t = wave_tot[w];
+        if (w < wid) before += t;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return before + x - v;
+}
+
+// Find the digit bin holding the `need`-th largest key among the histogram's entries.
+// bins: NB counters.  Returns bin and number of entries in strictly higher bins.
+template <int NB>
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t need, uint32_t* wave_tot, int* out_bin,
+                                         uint32_t* out_above) {
+    constexpr int PER = NB / kThreads;  // bins per thread, highest bins to thread 0
+    const int t = threadIdx.x;
+    uint32_t local = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) local += hist[NB - 1 - (t * PER + e)];
+    uint32_t total;
+    uint32_t above = block_exclusive_scan(local, wave_tot, total);
+    if (above < need && above + local >= need) {
+        uint32_t run = above;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int bin = NB - 1 - (t * PER + e);
+            const uint32_t c = hist[bin];
+            if (run + c >= need) {
+                *out_bin = bin;
+                *out_above = run;
+                break;
+            }
+            run += c;
+        }
+    }
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kThreads) topk_rows(TopkArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t wave_tot[kThreads / 64];
+    __shared__ int s_bin;
+    __shared__ uint32_t s_above;
+    __shared__ int s_bad;
+
+    const sa_problem& p = a.p;
+    const int row = blockIdx.x;
+    const int b = row / p.n_q, i = row % p.n_q;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int K = p.k;
+    const float* sc = a.scores + (int64_t)row * a.row_stride;
+    int32_t* out = a.idx + (int64_t)row * K;
+    float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
+    const int t = threadIdx.x;
+    if (t == 0) {
+        s_bad = 0;
+        s_bin = 0;
+        s_above = 0;
+    }
+    __syncthreads();
+
+    if (L <= K) {
+        int bad = 0;
+        for (int j = t; j < K; j += kThreads) {
+            float v = j < L ? sc[j] : -INFINITY;
+            if (j < L && !isfinite(v)) bad = 1;
+            out[j] = j < L ? j : -1;
+            if (vout) vout[j] = v;
+        }
+        if (bad) s_bad = 1;
+        __syncthreads();
+        if (t == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+        return;
+    }
+
+    // ---- digit 1: bits 31..21
+    for (int e = t; e < 2048; e += kThreads) hist[e] = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int j = t; j < L; j += kThreads) {
+        float v = sc[j];
+        if (!isfinite(v)) bad = 1;
+        atomicAdd(&hist[order_key(v) >> 21], 1u);
+    }
+    if (bad) s_bad = 1;
+    __syncthreads();
+    find_bin<2048>(hist, (uint32_t)K, wave_tot, &s_bin, &s_above);
+    const uint32_t d1 = (uint32_t)s_bin;
+    uint32_t above = s_above;
+
+    // ---- digit 2: bits 20..10 among keys with digit 1 == d1
+    for (int e = t; e < 2048; e += kThreads) hist[e] = 0;
+    __syncthreads();
+    for (int j = t; j < L; j += kThreads) {
+        uint32_t key = order_key(sc[j]);
+        if ((key >> 21) == d1) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
+    }
+    __syncthreads();
+    find_bin<2048>(hist, (uint32_t)K - above, wave_tot, &s_bin, &s_above);
+    const uint32_t d2 = (uint32_t)s_bin;
+    above += s_above;
+
+    // ---- digit 3: bits 9..0 among keys with digits 1,2 == d1,d2
+    for (int e = t; e < 1024; e += kThreads) hist[e] = 0;
+    __syncthreads();
+    const uint32_t pre = (d1 << 11) | d2;
+    for (int j = t; j < L; j += kThreads) {
+        uint32_t key = order_key(sc[j]);
+        if ((key >> 10) == pre) atomicAdd(&hist[key & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin<1024>(hist, (uint32_t)K - above, wave_tot, &s_bin, &s_above);
+    const uint32_t T = (pre << 10) | (uint32_t)s_bin;
+    above += s_above;
+    const uint32_t need_eq = (uint32_t)K - above;  // >= 1 keys equal to T to take
+
+    // ---- ordered compaction
+    uint32_t run_gt = 0, run_eq = 0;
+    for (int base = 0; base < L; base += 4 * kThreads) {
+        const int j0 = base + 4 * t;
+        uint32_t keys[4];
+        uint32_t c_gt = 0, c_eq = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + e;
+            keys[e] = j < L ? order_key(sc[j]) : 0u;
+            if (j < L) {
+                c_gt += keys[e] > T;
+                c_eq += keys[e] == T;
+            }
+        }
+        uint32_t tot;
+        const uint32_t pref = block_exclusive_scan(c_eq | (c_gt << 16), wave_tot, tot);
+        uint32_t G = run_gt + (pref >> 16), E = run_eq + (pref & 0xffffu);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + e;
+            if (j >= L) break;
+            const bool gt = keys[e] > T, eq = keys[e] == T;
+            if (gt || (eq && E < need_eq)) {
+                const uint32_t slot = G + (E < need_eq ? E : need_eq);
+                if (slot < (uint32_t)K) {
+                    out[slot] = j;
+                    if (vout) vout[slot] = sc[j];
+                }
+            }
+            G += gt;
+            E += eq;
+        }
+        run_gt += tot >> 16;
+        run_eq += tot & 0xffffu;
+    }
+    if (t == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+    const long rows = (long)a.p.B * a.p.n_q;
+    hipLaunchKernelGGL(topk_rows, dim3((unsigned)rows), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sa
