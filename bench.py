@@ -1,6 +1,184 @@
-"""Benchmark (placeholder while the library is being built)."""
+"""Benchmark: selected-token attention queries/s on one MI355X.
+
+A step is one sa_select_attend call over the whole batch: indexer score -> per-row top-k
+-> sparse gather attention, inputs resident in HBM.  The default workload is the bf16
+causal prefill B=2, n=4096 (16 heads of width 128, 8 index heads of width 64, k = 512,
+batch 1 padded after 3584 positions).
+
+Prints ONE JSON line.  Besides the headline value it reports per-stage times, the
+indexer TFLOP/s, and a roofline object for the dominant kernel (the gather attention),
+timed live with HIP events on the stream the library launches on, plus the CPU oracle's
+rate on a bounded row sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "selected-token attn queries/sec + indexer TFLOP/s & gather GB/s (% roofline)"
 
 
 def kv_cache_bytes(kv_heads, head_dim, positions, bytes_per):
     """Bytes of one layer's K and V cache for one request: 2 (K and V) x heads x width x positions x bytes."""
     return 2 * kv_heads * head_dim * positions * bytes_per
+
+
+def visible_counts(W):
+    """Visible history length of every query row (0 for padded rows)."""
+    import numpy as np
+
+    B, nq = W["B"], W["n_q"]
+    i = np.arange(nq)[None, :]
+    qp = W["q_pos0"][:, None].astype(np.int64) + i
+    kl = W["kv_len"][:, None].astype(np.int64)
+    valid = qp < kl
+    L = np.minimum(qp + 1, kl) if W["causal"] else np.broadcast_to(kl, (B, nq))
+    return np.where(valid, L, 0)
+
+
+def algorithmic(W):
+    """Algorithmic work of one step (visible pairs, selected pairs, FLOPs, gather bytes)."""
+    import numpy as np
+
+    L = visible_counts(W)
+    pairs = int(L.sum())
+    sel = int(np.minimum(L, W["k"]).sum())
+    rows = int((L > 0).sum())
+    esz = 4 if W["main_dtype"] == 0 else 2
+    idx_flops = 2 * W["d_idx"] * W["Hidx"] * pairs
+    attn_flops = 2 * W["Hq"] * (W["d_qk"] + W["d_v"]) * sel
+    # one gathered history row feeds every head of its key/value group; latent rows carry V inside K
+    row_bytes = W["Hkv"] * (W["d_qk"] + (0 if W["mla"] else W["d_v"])) * esz
+    q_bytes = W["B"] * W["Hq"] * W["n_q"] * W["d_qk"] * esz
+    o_bytes = W["B"] * W["Hq"] * W["n_q"] * W["d_v"] * esz
+    idx_bytes = W["B"] * W["n_q"] * W["k"] * 4
+    gather = sel * row_bytes + q_bytes + o_bytes + idx_bytes
+    return dict(pairs=pairs, selected=sel, rows=rows, idx_flops=idx_flops, attn_flops=attn_flops,
+                gather_bytes=gather, row_bytes=row_bytes)
+
+
+def cpu_baseline(W, budget_rows):
+    """The oracle (unchanged) on a stratified sample of rows: score, select and attend."""
+    import numpy as np
+    from oracle import oracle as orc
+
+    rng = np.random.default_rng(0)
+    L = visible_counts(W).reshape(-1)
+    valid = np.where(L > 0)[0]
+    rows = np.sort(rng.choice(valid, size=min(budget_rows, valid.size), replace=False)).astype(np.int32)
+    threads = orc.threads()
+    t0 = time.perf_counter()
+    orc.select_attend(W, rows)
+    dt = time.perf_counter() - t0
+    return {"value": rows.size / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d valid query rows (uniform random, seed 0), fp64 score+select+attend, %.1f s"
+                      % (rows.size, valid.size, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload id (1 = bf16 prefill B=2 n=4096)")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="rows in the oracle's CPU-baseline sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (--gpus 1); multi-GPU runs are not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sa_synth
+    import token_selector_gather_amd as sa
+    from token_selector_gather_amd.inputs import device_workload, empty_outputs
+
+    os.environ.setdefault("OMP_NUM_THREADS", "16")
+    W = sa_synth.make_config(args.config)
+    alg = algorithmic(W)
+    P, d = device_workload(W)
+    dt = torch.float32 if W["main_dtype"] == sa_synth.F32 else torch.bfloat16
+    O, lse, idx = empty_outputs(W, dt)
+    ws = sa.workspace(P, sa.SA_OP_SELECT_ATTEND)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sa.sa_select_attend(P, d["q_idx"], d["k_idx"], d["w"], d["Q"], d["K"], d["V"], idx, O, lse, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = sa.sa_device_status(ws)
+    if st != sa.SA_OK:
+        raise RuntimeError("device status " + sa.sa_status_str(st))
+    ms_step = 1e3 * elapsed / args.steps
+    value = alg["rows"] / (elapsed / args.steps)
+
+    # per-stage timing with HIP events on the library's stream
+    def timed(fn, reps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            fn()
+        ev1.record(stream)
+        ev1.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    reps = max(3, args.steps)
+    scores = torch.empty((W["B"], W["n_q"], W["n_kv"]), dtype=torch.float32, device="cuda")
+    ws_t = sa.workspace(P, sa.SA_OP_TOPK)
+    ws_a = sa.workspace(P, sa.SA_OP_SPARSE_ATTN)
+    idx2 = idx.clone()
+    O2, lse2 = O.clone(), lse.clone()
+    t_idx = timed(lambda: sa.sa_indexer_score(P, d["q_idx"], d["k_idx"], d["w"], scores, stream), reps)
+    t_topk = timed(lambda: sa.sa_topk(P, scores, W["n_kv"], idx2, None, ws_t, stream), reps)
+    t_attn = timed(lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream), reps)
+    ach_gbs = alg["gather_bytes"] / (t_attn * 1e-3) / 1e9
+    idx_tflops = alg["idx_flops"] / (t_idx * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded generator, seed = workload id)",
+        "config": {"workload": W["name"], "B": W["B"], "n_q": W["n_q"], "n_kv": W["n_kv"], "Hq": W["Hq"],
+                   "Hkv": W["Hkv"], "d_qk": W["d_qk"], "d_v": W["d_v"], "Hidx": W["Hidx"], "d_idx": W["d_idx"],
+                   "k": W["k"], "causal": W["causal"], "valid_rows": alg["rows"]},
+        "stages_ms": {"indexer_score": round(t_idx, 4), "topk": round(t_topk, 4), "sparse_attn": round(t_attn, 4)},
+        "indexer": {"tflops": round(idx_tflops, 3), "frac_bf16_peak": round(idx_tflops / BF16_PEAK_TFLOPS, 5),
+                    "flops_per_call": alg["idx_flops"]},
+        "roofline": {"kernel": "sparse gather attention", "bound": "hbm", "achieved": round(ach_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": alg["gather_bytes"], "ms_per_launch": round(t_attn, 4)},
+    }
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_rows)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
