@@ -57,8 +57,12 @@ class Workload(dict):
             raise AttributeError(k) from e
 
 
-def _fill_rows(arr, dtype, rows_mask_fn):
-    pass
+def custom(seed=100, lens=None, q_pos0=None, with_main=True, **kw):
+    """A workload with explicit sizes and dtypes (defaults: a small bf16 MHA prefill)."""
+    c = dict(name="custom", B=1, n_q=64, n_kv=64, Hq=2, Hkv=2, d_qk=128, d_v=128, Hidx=4, d_idx=64, k=16,
+             causal=1, main_dtype=BF16, qidx_dtype=BF16, kidx_dtype=BF16, main_scale=1.0, mla=False)
+    c.update(kw)
+    return _build(c, cid=-1, seed=seed, lens=lens, q_pos0=q_pos0, with_main=with_main)
 
 
 def make_config(cid, n=None, n_kv=None, n_q=None, B=None, lens=None, k=None, with_main=True, seed=None):
@@ -76,6 +80,12 @@ def make_config(cid, n=None, n_kv=None, n_q=None, B=None, lens=None, k=None, wit
         c["B"] = B
     if k is not None:
         c["k"] = k
+    if n is not None and c.get("pad_last"):
+        c["pad_last"] = min(c["pad_last"], n // 8)
+    return _build(c, cid=cid, seed=seed, lens=lens, q_pos0=None, with_main=with_main)
+
+
+def _build(c, cid, seed, lens, q_pos0, with_main):
     Bn, nq, nkv = c["B"], c["n_q"], c["n_kv"]
     Hq, Hkv, dqk, dv, Hidx, didx = c["Hq"], c["Hkv"], c["d_qk"], c["d_v"], c["Hidx"], c["d_idx"]
     W = Workload(c)
@@ -97,8 +107,8 @@ def make_config(cid, n=None, n_kv=None, n_q=None, B=None, lens=None, k=None, wit
         if lens is not None:
             kv_len = np.asarray(lens, dtype=np.int32)
         elif c.get("pad_last") and Bn > 1:
-            kv_len[1] = nkv - min(c["pad_last"], nkv // 8 if n is not None else c["pad_last"])
-        q_pos0 = np.zeros((Bn,), dtype=np.int32)
+            kv_len[1] = nkv - c["pad_last"]
+        q_pos0 = np.zeros((Bn,), dtype=np.int32) if q_pos0 is None else np.asarray(q_pos0, dtype=np.int32)
     W["kv_len"] = kv_len
     W["q_pos0"] = q_pos0
 
@@ -111,7 +121,7 @@ def make_config(cid, n=None, n_kv=None, n_q=None, B=None, lens=None, k=None, wit
         W["k_idx"] = normal(seed, T_KIDX, (Bn, nkv, didx), c["kidx_dtype"])
     pv_idx = encode(np.array([poison_value(c["kidx_dtype"])]), c["kidx_dtype"])[0]
     for b in range(Bn):
-        W["k_idx"][b, kv_len[b]:, :] = pv_idx
+        W["k_idx"][b, max(int(kv_len[b]), 0):, :] = pv_idx
 
     # main attention tensors
     if with_main:
@@ -121,9 +131,9 @@ def make_config(cid, n=None, n_kv=None, n_q=None, B=None, lens=None, k=None, wit
         W["V"] = None if c["mla"] else normal(seed, T_V, (Bn, Hkv, nkv, dv), md, scale=s)
         pv = encode(np.array([poison_value(md)]), md)[0]
         for b in range(Bn):
-            W["K"][b, :, kv_len[b]:, :] = pv
+            W["K"][b, :, max(int(kv_len[b]), 0):, :] = pv
             if W["V"] is not None:
-                W["V"][b, :, kv_len[b]:, :] = pv
+                W["V"][b, :, max(int(kv_len[b]), 0):, :] = pv
     return W
 
 

@@ -120,3 +120,26 @@ def sample_rows(W, n_each=32, n_rand=64, seed=0):
     rng = np.random.default_rng(seed)
     rows.update(rng.integers(0, B * nq, size=n_rand).tolist())
     return np.array(sorted(rows), dtype=np.int32)
+
+
+def full_check(W, rows=None, tie_groups=None, check_sparse=True):
+    """End-to-end select+attend against the oracle on `rows` (default: all rows), plus the
+    attention kernel alone on the oracle's own candidate sets."""
+    from tests.checker import check_index_rows
+    if rows is None:
+        rows = np.arange(W["B"] * W["n_q"], dtype=np.int32)
+    idx, O, lse, st = gpu_select_attend(W)
+    assert st == sa.SA_OK, sa.sa_status_str(st)
+    idx_r = idx.reshape(-1, W["k"])[rows]
+    ref_sc = orc.scores(W, rows)
+    ref_idx, sk, skp1, nsel = orc.select(W, ref_sc, rows)
+    stats = check_index_rows(W, rows, idx_r, ref_sc, ref_idx, sk, tie_groups=tie_groups)
+    O_or, lse_or = orc.attend(W, idx_r, rows)
+    errs = compare_attention(W, rows, O, lse, O_or, lse_or)
+    if check_sparse:
+        full = np.full((W["B"] * W["n_q"], W["k"]), -1, dtype=np.int32)
+        full[rows] = ref_idx
+        O2, lse2 = gpu_sparse_attn(W, full.reshape(W["B"], W["n_q"], W["k"]))
+        O_or2, lse_or2 = orc.attend(W, ref_idx, rows)
+        compare_attention(W, rows, O2, lse2, O_or2, lse_or2)
+    return dict(stats, err_o=errs[0], err_lse=errs[1], idx=idx, ref_idx=ref_idx, rows=rows)

@@ -1,0 +1,124 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function include/sa.h
+declares, and rejects malformed arguments synchronously (before any launch, so no GPU
+is touched).  Device pointers here are fake aligned addresses that are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_selector_gather_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(sa.LIB_PATH), reason="libsa.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for f in ("sa_indexer_score", "sa_topk", "sa_sparse_attn", "sa_select_attend", "sa_workspace_bytes",
+              "sa_device_status", "sa_status_str", "sa_abi_version"):
+        assert f in names
+
+
+@needs_lib
+def test_library_exports_every_declared_function():
+    L = ctypes.CDLL(sa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+@needs_lib
+def test_abi_version_and_status_strings():
+    assert sa.sa_abi_version() == sa.ABI_VERSION
+    assert sa.sa_status_str(sa.SA_OK) == "SA_OK"
+    assert sa.sa_status_str(sa.SA_ERR_NONFINITE) == "SA_ERR_NONFINITE"
+    assert sa.sa_status_str(99) == "SA_ERR_UNKNOWN"
+
+
+FAKE = 0x10000  # 256-byte aligned, never dereferenced on the error paths below
+
+
+def _prob(**kw):
+    base = dict(B=2, n_q=64, n_kv=64, Hq=4, Hkv=4, d_qk=64, d_v=64, Hidx=4, d_idx=32, k=8, causal=1)
+    base.update(kw)
+    return sa._Problem(*[base[f] for f in sa.Problem.FIELDS], None, None, 0.0)
+
+
+def _t(dtype=sa.SA_BF16, s0=64 * 64 * 4, s1=64 * 64, s2=64, data=FAKE):
+    return sa._Tensor(data, dtype, s0, s1, s2)
+
+
+@needs_lib
+@pytest.mark.parametrize("field,value", [("B", 0), ("n_q", 0), ("n_kv", -1), ("k", 0), ("Hq", 3), ("Hkv", 0),
+                                         ("causal", 2), ("d_idx", 0)])
+def test_malformed_problem_is_rejected(field, value):
+    L = sa.lib()
+    p = _prob(**{field: value})
+    assert L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SELECT_ATTEND) == 0
+    rc = L.sa_topk(ctypes.byref(p), FAKE, 64, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == sa.SA_ERR_INVALID_ARG
+
+
+@needs_lib
+def test_workspace_errors():
+    L = sa.lib()
+    p = _prob()
+    need = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_TOPK)
+    assert need >= 256
+    assert L.sa_topk(ctypes.byref(p), FAKE, 64, FAKE, None, None, need, None) == sa.SA_ERR_WORKSPACE
+    assert L.sa_topk(ctypes.byref(p), FAKE, 64, FAKE, None, FAKE, need - 1, None) == sa.SA_ERR_WORKSPACE
+    assert L.sa_topk(ctypes.byref(p), FAKE, 64, FAKE, None, FAKE + 16, need, None) == sa.SA_ERR_WORKSPACE
+    assert L.sa_topk(ctypes.byref(p), FAKE, 63, FAKE, None, FAKE, need, None) == sa.SA_ERR_INVALID_ARG
+    sel = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SELECT_ATTEND)
+    assert sel >= 256 + 2 * 64 * 64 * 4 + 2 * 64 * 8 * 4  # status + score rows + selection
+
+
+@needs_lib
+def test_attention_argument_errors():
+    L = sa.lib()
+    p = _prob()
+    ws = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SPARSE_ATTN)
+    ok = _t()
+    call = lambda Q=ok, K=ok, V=ok, O=ok, idx=FAKE, lse=None, pp=p: L.sa_sparse_attn(
+        ctypes.byref(pp), Q, K, V, idx, O, lse, FAKE, ws, None)
+    assert call(idx=None) == sa.SA_ERR_INVALID_ARG
+    assert call(Q=_t(data=None)) == sa.SA_ERR_INVALID_ARG
+    assert call(K=_t(data=FAKE + 2)) == sa.SA_ERR_INVALID_ARG          # misaligned
+    assert call(V=_t(s2=60)) == sa.SA_ERR_INVALID_ARG                  # stride not 16-byte multiple
+    assert call(O=_t(dtype=sa.SA_F32)) == sa.SA_ERR_UNSUPPORTED        # mixed dtypes
+    assert call(Q=_t(dtype=7), K=_t(dtype=7), V=_t(dtype=7), O=_t(dtype=7)) == sa.SA_ERR_UNSUPPORTED
+    assert call(lse=FAKE + 1) == sa.SA_ERR_INVALID_ARG
+    odd = _prob(d_qk=48, d_v=48)  # lanes per row not a power of two
+    assert call(pp=odd) == sa.SA_ERR_UNSUPPORTED
+    gqa3 = _prob(Hq=12, Hkv=4)  # group of 3 query heads per key/value head
+    assert call(pp=gqa3) == sa.SA_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_indexer_argument_errors():
+    L = sa.lib()
+    p = _prob()
+    q = _t(s0=64 * 4 * 32, s1=4 * 32, s2=32)
+    k = _t(s0=64 * 32, s1=32, s2=0)
+    w = sa._Tensor(FAKE, sa.SA_F32, 64 * 4, 4, 0)
+    call = lambda q=q, k=k, w=w, out=FAKE: L.sa_indexer_score(ctypes.byref(p), q, k, w, out, None)
+    assert call(out=None) == sa.SA_ERR_INVALID_ARG
+    assert call(q=_t(dtype=sa.SA_FP8_E4M3, s0=64 * 4 * 32, s1=4 * 32, s2=32)) == sa.SA_ERR_UNSUPPORTED
+    assert call(w=sa._Tensor(FAKE, sa.SA_BF16, 64 * 4, 4, 0)) == sa.SA_ERR_UNSUPPORTED
+    assert call(k=_t(data=None, s0=64 * 32, s1=32, s2=0)) == sa.SA_ERR_INVALID_ARG
+    assert call(q=_t(s0=64 * 4 * 32, s1=4 * 32, s2=33)) == sa.SA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(sa, "_lib", None)
+    monkeypatch.setattr(sa, "LIB_PATH", "/nonexistent/libsa.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        sa.lib()

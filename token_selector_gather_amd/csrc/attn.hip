@@ -225,6 +225,179 @@ __global__ void __launch_bounds__(256) attn_rows(AttnArgs a) {
     }
 }
 
+// ------------------------------------------------------------- attn_rows_mfma
+// bf16, one query head per key/value head.  Per 32 gathered rows: QK^T on the matrix
+// cores with the gathered K tile as the A operand (lane (g, c) loads 16 bytes of row c at
+// d = 32 s + 8 g) and the query replicated over the 16 B columns, so every lane receives
+// the scores of rows 4g..4g+3 of each 16-row tile.  Lane (g, c) then loads 16-byte chunk
+// c of exactly those rows of V and accumulates p * V with v_dot2_f32_bf16 on row pairs
+// interleaved by v_perm_b32 (probabilities rounded to bf16, fp32 accumulation).  The four
+// lane groups g hold disjoint rows and merge once at the end.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_rows_mfma(AttnArgs a) {
+    constexpr int KS = D / 32;                 // k-steps of the score MFMA
+    constexpr int NCH = D / 8;                 // 16-byte chunks per row
+    constexpr int CPL = NCH >= 16 ? NCH / 16 : 1;  // V chunks per lane
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+
+    const long blk = blockIdx.x;
+    int b, i, hk;
+    {
+        const int nib = (p.n_q + 3) / 4;
+        const int wv = threadIdx.x >> 6;
+        if (p.Hkv % 8 == 0) {
+            const int xcd = (int)(blk % 8);
+            const long local = blk / 8;
+            const int hpx = p.Hkv / 8;
+            hk = xcd + 8 * (int)(local % hpx);
+            const long rest = local / hpx;
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        } else {
+            hk = (int)(blk % p.Hkv);
+            const long rest = blk / p.Hkv;
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        }
+        if (b >= p.B || i >= p.n_q) return;
+    }
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const float sl2 = a.scale * kLog2e;
+    const int h = hk;  // one query head per key/value head
+
+    const uint16_t* Qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2;
+    const uint16_t* Kp = static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1;
+    const uint16_t* Vp = static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1;
+    bf16x8 qb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Qp + 32 * s + 8 * g));
+
+    float m = -INFINITY, lsum = 0.f;
+    float o[CPL][8];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[cc][e] = 0.f;
+    const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
+    const bool has_chunk = c < NCH;
+
+    for (int r0 = 0; L > 0 && r0 < p.k; r0 += 32) {
+        // A operand rows: positions 16 mt + c
+        uint4 kf[2][KS];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int e = r0 + 16 * mt + c;
+            const int j = e < p.k ? ix[e] : -1;
+            const bool ok = j >= 0 && j < L;
+            const uint16_t* kr = Kp + (int64_t)(ok ? j : 0) * a.K.s2 + 8 * g;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) kf[mt][s] = ok ? *reinterpret_cast<const uint4*>(kr + 32 * s) : make_uint4(0, 0, 0, 0);
+        }
+        // rows whose scores this lane receives: positions 16 mt + 4 g + r
+        bool okv[2][4];
+        uint4 vf[2][4][CPL];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = r0 + 16 * mt + 4 * g + r;
+                const int j = e < p.k ? ix[e] : -1;
+                okv[mt][r] = j >= 0 && j < L;
+                const uint16_t* vr = Vp + (int64_t)(okv[mt][r] ? j : 0) * a.V.s2;
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc)
+                    vf[mt][r][cc] = (okv[mt][r] && has_chunk) ? *reinterpret_cast<const uint4*>(vr + 8 * (c + 16 * cc))
+                                                               : make_uint4(0, 0, 0, 0);
+            }
+        f32x4 acc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[mt][s]), qb[s], acc[mt], 0, 0, 0);
+        }
+        float x[2][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[mt][r] = okv[mt][r] ? acc[mt][r] * sl2 : -INFINITY;
+                mx = fmaxf(mx, x[mt][r]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        if (mn == -INFINITY) continue;  // uniform: nothing valid in this tile or before
+        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+        m = mn;
+        float pr[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[mt][r] = okv[mt][r] ? exp2f(x[mt][r] - mn) : 0.f;
+                ps += pr[mt][r];
+            }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[cc][e] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const bf16x2 pw = {(__bf16)pr[mt][2 * pp], (__bf16)pr[mt][2 * pp + 1]};
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const uint4 va = vf[mt][2 * pp][cc], vb = vf[mt][2 * pp + 1][cc];
+                    const uint32_t A4[4] = {va.x, va.y, va.z, va.w}, B4[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t lo = __builtin_amdgcn_perm(B4[w], A4[w], 0x05040100u);
+                        const uint32_t hi = __builtin_amdgcn_perm(B4[w], A4[w], 0x07060302u);
+                        o[cc][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, lo), o[cc][2 * w], false);
+                        o[cc][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, hi), o[cc][2 * w + 1], false);
+                    }
+                }
+            }
+    }
+    // the four lane groups hold disjoint rows: sum their exp-sums and outputs
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o[cc][e] += __shfl_xor(o[cc][e], 16);
+            o[cc][e] += __shfl_xor(o[cc][e], 32);
+        }
+    if (g == 0) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        uint16_t* Op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2;
+        if (has_chunk) {
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pk[e] = (uint32_t)f32_to_bf16_rne(o[cc][2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[cc][2 * e + 1] * inv) << 16);
+                *reinterpret_cast<uint4*>(Op + 8 * (c + 16 * cc)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            }
+        }
+        if (a.lse && c == 0)
+            a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
+    }
+}
+
 // ------------------------------------------------------------------- attn_mla
 constexpr int kTile = 32;
 
@@ -488,6 +661,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     const int G = p.Hq / p.Hkv;
+    if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
+        const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
+        if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_mfma<64>, dim3(nblk), dim3(256), 0, s, a);
+        else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_mfma<128>, dim3(nblk), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(attn_rows_mfma<256>, dim3(nblk), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     const int esz = a.Q.dtype == SA_F32 ? 4 : 2;
     const int LPR = p.d_qk * esz / 16;
     const unsigned blocks = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
