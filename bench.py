@@ -88,8 +88,20 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload id (1 = bf16 prefill B=2 n=4096)")
-    ap.add_argument("--cpu-rows", type=int, default=768, help="rows in the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=7680, help="rows in the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (--gpus 1); multi-GPU runs are not supported",
               file=sys.stderr)

@@ -398,6 +398,161 @@ __global__ void __launch_bounds__(256) attn_rows_mfma(AttnArgs a) {
     }
 }
 
+// --------------------------------------------------------------- attn_rows_dot
+// bf16, one query head per key/value head, head width D = 8 * LPR.  Loads stay coalesced:
+// each group of LPR lanes reads whole history rows (16 bytes per lane, RPI = 64 / LPR rows
+// per load instruction).  The dot product uses v_dot2_f32_bf16 on the packed operands and
+// finishes with an LPR-lane sum built from DPP moves (quad swaps, half-row and row mirrors),
+// so it stays in the VALU.  p * V runs as v_dot2_f32_bf16 on pairs of rows a lane already
+// holds (interleaved by v_perm_b32; probabilities rounded to bf16, fp32 accumulation).
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror: the other quad of 8
+    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);  // row_mirror: the other half of 16
+    if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_rows_dot(AttnArgs a) {
+    constexpr int LPR = D / 8;
+    constexpr int RPI = 64 / LPR;
+    constexpr int UNROLL = 8;
+    constexpr int ROWS_IT = RPI * UNROLL;
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR, rg = lane / LPR;
+
+    const long blk = blockIdx.x;
+    int b, i, hk;
+    {
+        const int nib = (p.n_q + 3) / 4;
+        const int wv = threadIdx.x >> 6;
+        if (p.Hkv % 8 == 0) {
+#ifndef SA_XCD_MAP
+#define SA_XCD_MAP 2
+#endif
+            const int xcd = (int)(blk % 8);
+            const long local = blk / 8;
+            const int hpx = p.Hkv / 8;
+            long rest;
+            if (SA_XCD_MAP == 2) {  // one head at a time per XCD: its K/V rows stay in that L2
+                hk = xcd + 8 * (int)(local / ((long)p.B * nib));
+                rest = local % ((long)p.B * nib);
+            } else {
+                hk = xcd + 8 * (int)(local % hpx);
+                rest = local / hpx;
+            }
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        } else {
+            hk = (int)(blk % p.Hkv);
+            const long rest = blk / p.Hkv;
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        }
+        if (b >= p.B || i >= p.n_q) return;
+    }
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const float sl2 = a.scale * kLog2e;
+    const int h = hk;
+
+    const uint16_t* Qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2;
+    const uint16_t* Kp = static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1 + 8 * sub;
+    const uint16_t* Vp = static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1 + 8 * sub;
+    const uint4 qv = *reinterpret_cast<const uint4*>(Qp + 8 * sub);
+    const bf16x2 q2[4] = {__builtin_bit_cast(bf16x2, qv.x), __builtin_bit_cast(bf16x2, qv.y),
+                          __builtin_bit_cast(bf16x2, qv.z), __builtin_bit_cast(bf16x2, qv.w)};
+    float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
+
+    for (int r0 = 0; L > 0 && r0 < p.k; r0 += ROWS_IT) {
+        bool ok[UNROLL];
+        int jv[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int r = r0 + u * RPI + rg;
+            const int j = r < p.k ? ix[r] : -1;
+            ok[u] = j >= 0 && j < L;
+            jv[u] = ok[u] ? j : 0;
+        }
+        uint4 kr[UNROLL], vr[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            kr[u] = ok[u] ? *reinterpret_cast<const uint4*>(Kp + (int64_t)jv[u] * a.K.s2) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            vr[u] = ok[u] ? *reinterpret_cast<const uint4*>(Vp + (int64_t)jv[u] * a.V.s2) : make_uint4(0, 0, 0, 0);
+        float s[UNROLL];
+        float mt = m;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            float d = __builtin_amdgcn_fdot2_f32_bf16(q2[0], __builtin_bit_cast(bf16x2, kr[u].x), 0.f, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(q2[1], __builtin_bit_cast(bf16x2, kr[u].y), d, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(q2[2], __builtin_bit_cast(bf16x2, kr[u].z), d, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(q2[3], __builtin_bit_cast(bf16x2, kr[u].w), d, false);
+            d = group_sum<LPR>(d);
+            s[u] = ok[u] ? d * sl2 : -INFINITY;
+            mt = fmaxf(mt, s[u]);
+        }
+        // mt == -inf only if nothing was valid so far: then l, o are 0 and stay 0
+        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mt);
+        float pr[UNROLL];
+        float ps = 0.f;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            pr[u] = ok[u] ? exp2f(s[u] - mt) : 0.f;
+            ps += pr[u];
+        }
+        l = l * alpha + ps;
+        m = mt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < UNROLL; u += 2) {
+            const bf16x2 pw = {(__bf16)pr[u], (__bf16)pr[u + 1]};
+            const uint32_t A4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+            const uint32_t B4[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t lo = __builtin_amdgcn_perm(B4[w], A4[w], 0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(B4[w], A4[w], 0x07060302u);
+                o[2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, lo), o[2 * w], false);
+                o[2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, hi), o[2 * w + 1], false);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+        float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off), o2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[e], off);
+        merge_state(m, l, o, 8, m2, l2, o2);
+    }
+    if (rg == 0) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* Op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2 + 8 * sub;
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = (uint32_t)f32_to_bf16_rne(o[2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * e + 1] * inv) << 16);
+        *reinterpret_cast<uint4*>(Op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        if (a.lse && sub == 0)
+            a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    }
+}
+
 // ------------------------------------------------------------------- attn_mla
 constexpr int kTile = 32;
 
@@ -661,11 +816,21 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     const int G = p.Hq / p.Hkv;
-    if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
+#ifndef SA_ROWS_VARIANT
+#define SA_ROWS_VARIANT 3
+#endif
+    if (SA_ROWS_VARIANT != 1 && a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v &&
+        (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
         const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
-        if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_mfma<64>, dim3(nblk), dim3(256), 0, s, a);
-        else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_mfma<128>, dim3(nblk), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(attn_rows_mfma<256>, dim3(nblk), dim3(256), 0, s, a);
+        if (SA_ROWS_VARIANT == 2) {
+            if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_mfma<64>, dim3(nblk), dim3(256), 0, s, a);
+            else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_mfma<128>, dim3(nblk), dim3(256), 0, s, a);
+            else hipLaunchKernelGGL(attn_rows_mfma<256>, dim3(nblk), dim3(256), 0, s, a);
+        } else {
+            if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_dot<64>, dim3(nblk), dim3(256), 0, s, a);
+            else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_dot<128>, dim3(nblk), dim3(256), 0, s, a);
+            else hipLaunchKernelGGL(attn_rows_dot<256>, dim3(nblk), dim3(256), 0, s, a);
+        }
         return hipGetLastError();
     }
     const int esz = a.Q.dtype == SA_F32 ? 4 : 2;
