@@ -553,6 +553,165 @@ __global__ void __launch_bounds__(256) attn_rows_dot(AttnArgs a) {
     }
 }
 
+// --------------------------------------------------------------- attn_rows_buf
+// The same computation as attn_rows_dot with less instruction overhead per gathered row:
+//  * K and V rows are fetched with raw buffer loads on a per-(batch, head) resource, so a
+//    row address is one 32-bit multiply; an invalid entry gets an offset past the end of
+//    the resource and the hardware returns zeros (no branches, no zero-fill moves);
+//  * each lane covers 32 bytes (16 elements) of a row, LPR = D/16 lanes per row, so the
+//    dot product needs one fewer DPP step per element pair;
+//  * row group rg takes UNROLL consecutive candidate entries, fetched by one 16-byte load;
+//  * exponentials use v_exp_f32 directly on arguments <= 0.
+// Requires k % 4 == 0 and every (batch, head) slice of K and V below 2^31 bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_sum2(float x) {
+    if constexpr (LPR >= 2) x += dpp_mov<0xB1>(x);
+    if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);
+    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);
+    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);
+    return x;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
+    constexpr int LPR = D / 16;      // lanes per row, 32 bytes each
+    constexpr int RPG = 64 / LPR;    // row groups per wave
+    constexpr int UNROLL = 4;        // rows per row group per iteration
+    constexpr int ROWS_IT = RPG * UNROLL;
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR, rg = lane / LPR;
+
+    const long blk = blockIdx.x;
+    int b, i, hk;
+    {
+        const int nib = (p.n_q + 3) / 4;
+        const int wv = threadIdx.x >> 6;
+        if (p.Hkv % 8 == 0) {  // one head at a time per XCD: its K/V rows stay in that L2
+            const int xcd = (int)(blk % 8);
+            const long local = blk / 8;
+            hk = xcd + 8 * (int)(local / ((long)p.B * nib));
+            const long rest = local % ((long)p.B * nib);
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        } else {
+            hk = (int)(blk % p.Hkv);
+            const long rest = blk / p.Hkv;
+            b = (int)(rest / nib);
+            i = (int)(rest % nib) * 4 + wv;
+        }
+        if (b >= p.B || i >= p.n_q) return;
+    }
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const float sl2 = a.scale * kLog2e;
+    const int h = hk;
+
+    const uint16_t* Qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2 + 16 * sub;
+    const uint4 qa = *reinterpret_cast<const uint4*>(Qp), qc = *reinterpret_cast<const uint4*>(Qp + 8);
+    const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qc.x, qc.y, qc.z, qc.w};
+    const uint32_t kstride = (uint32_t)(a.K.s2 * 2), vstride = (uint32_t)(a.V.s2 * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1,
+                                                (uint32_t)p.n_kv * kstride);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1,
+                                                 (uint32_t)p.n_kv * vstride);
+    const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
+    const uint32_t col = 32u * sub;
+
+    float m = -INFINITY, l = 0.f, o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+
+    for (int r0 = 0; L > 0 && r0 < p.k; r0 += ROWS_IT) {
+        const int rb = r0 + UNROLL * rg;
+        int4 jj = rb < p.k ? *reinterpret_cast<const int4*>(ix + rb) : make_int4(-1, -1, -1, -1);
+        const int jv[UNROLL] = {jj.x, jj.y, jj.z, jj.w};
+        uint32_t koff[UNROLL], voff[UNROLL];
+        bool ok[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            ok[u] = (unsigned)jv[u] < (unsigned)L;
+            koff[u] = ok[u] ? __umul24((uint32_t)jv[u], kstride) + col : 0x80000000u;
+            voff[u] = ok[u] ? __umul24((uint32_t)jv[u], vstride) + col : 0x80000000u;
+        }
+        uint32_t kw[UNROLL][8], vw[UNROLL][8];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            auto k0 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[u], 0, 0);
+            auto k1 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[u] + 16, 0, 0);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) { kw[u][w] = k0[w]; kw[u][4 + w] = k1[w]; }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            auto v0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[u], 0, 0);
+            auto v1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[u] + 16, 0, 0);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) { vw[u][w] = v0[w]; vw[u][4 + w] = v1[w]; }
+        }
+        float x[UNROLL];
+        float mt = m;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            float d = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[w]), __builtin_bit_cast(bf16x2, kw[u][w]), d, false);
+            d = group_sum2<LPR>(d);
+            x[u] = ok[u] ? d * sl2 : -INFINITY;
+            mt = fmaxf(mt, x[u]);
+        }
+        // mt == -inf only if nothing was valid so far: then l, o are 0 and stay 0
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mt);
+        float pr[UNROLL];
+        float ps = 0.f;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            pr[u] = __builtin_amdgcn_exp2f(x[u] - mt);  // exp2(-inf) = 0 for invalid rows
+            ps += pr[u];
+        }
+        if (mt == -INFINITY) ps = 0.f;
+        l = l * alpha + ps;
+        m = mt;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < UNROLL; u += 2) {
+            const bf16x2 pw = {(__bf16)pr[u], (__bf16)pr[u + 1]};
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const uint32_t lo = __builtin_amdgcn_perm(vw[u + 1][w], vw[u][w], 0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(vw[u + 1][w], vw[u][w], 0x07060302u);
+                o[2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, lo), o[2 * w], false);
+                o[2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, hi), o[2 * w + 1], false);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+        float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off), o2[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o2[e] = __shfl_xor(o[e], off);
+        merge_state(m, l, o, 16, m2, l2, o2);
+    }
+    if (rg == 0) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* Op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2 + 16 * sub;
+        uint32_t pk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pk[e] = (uint32_t)f32_to_bf16_rne(o[2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * e + 1] * inv) << 16);
+        *reinterpret_cast<uint4*>(Op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        *reinterpret_cast<uint4*>(Op + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        if (a.lse && sub == 0)
+            a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    }
+}
+
 // ------------------------------------------------------------------- attn_mla
 constexpr int kTile = 32;
 
@@ -817,12 +976,20 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     }
     const int G = p.Hq / p.Hkv;
 #ifndef SA_ROWS_VARIANT
-#define SA_ROWS_VARIANT 3
+#define SA_ROWS_VARIANT 4
 #endif
     if (SA_ROWS_VARIANT != 1 && a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v &&
         (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
         const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
-        if (SA_ROWS_VARIANT == 2) {
+        // 32-bit row offsets from 24-bit multiplies: rows < 2^24, row strides < 2^24 bytes
+        const bool buf_ok = (p.k % 4 == 0) && (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) &&
+                            (int64_t)p.n_kv * a.V.s2 * 2 < (1LL << 31) && ((uintptr_t)a.idx & 15) == 0 &&
+                            p.n_kv < (1 << 24) && a.K.s2 * 2 < (1 << 24) && a.V.s2 * 2 < (1 << 24);
+        if (SA_ROWS_VARIANT == 4 && buf_ok) {
+            if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_buf<64>, dim3(nblk), dim3(256), 0, s, a);
+            else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_buf<128>, dim3(nblk), dim3(256), 0, s, a);
+            else hipLaunchKernelGGL(attn_rows_buf<256>, dim3(nblk), dim3(256), 0, s, a);
+        } else if (SA_ROWS_VARIANT == 2) {
             if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_mfma<64>, dim3(nblk), dim3(256), 0, s, a);
             else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_mfma<128>, dim3(nblk), dim3(256), 0, s, a);
             else hipLaunchKernelGGL(attn_rows_mfma<256>, dim3(nblk), dim3(256), 0, s, a);
