@@ -667,14 +667,14 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
         }
         // mt == -inf only if nothing was valid so far: then l, o are 0 and stay 0
         const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mt);
+        const float mref = (mt == -INFINITY) ? 0.f : mt;  // keeps exp2(x - mref) = 0, never NaN
         float pr[UNROLL];
         float ps = 0.f;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            pr[u] = __builtin_amdgcn_exp2f(x[u] - mt);  // exp2(-inf) = 0 for invalid rows
+            pr[u] = __builtin_amdgcn_exp2f(x[u] - mref);  // exp2(-inf) = 0 for invalid rows
             ps += pr[u];
         }
-        if (mt == -INFINITY) ps = 0.f;
         l = l * alpha + ps;
         m = mt;
 #pragma unroll
