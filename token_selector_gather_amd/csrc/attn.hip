@@ -558,8 +558,9 @@ __global__ void __launch_bounds__(256) attn_rows_dot(AttnArgs a) {
 //  * K and V rows are fetched with raw buffer loads on a per-(batch, head) resource, so a
 //    row address is one 32-bit multiply; an invalid entry gets an offset past the end of
 //    the resource and the hardware returns zeros (no branches, no zero-fill moves);
-//  * each lane covers 32 bytes (16 elements) of a row, LPR = D/16 lanes per row, so the
-//    dot product needs one fewer DPP step per element pair;
+//  * each lane covers 32 bytes (16 elements) of a row in two 16-byte pieces, one in each
+//    half-row, so every load instruction reads whole contiguous half-rows; LPR = D/16
+//    lanes per row, one fewer DPP step per element pair;
 //  * row group rg takes UNROLL consecutive candidate entries, fetched by one 16-byte load;
 //  * exponentials use v_exp_f32 directly on arguments <= 0.
 // Requires k % 4 == 0 and every (batch, head) slice of K and V below 2^31 bytes.
@@ -611,8 +612,11 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
     const float sl2 = a.scale * kLog2e;
     const int h = hk;
 
-    const uint16_t* Qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2 + 16 * sub;
-    const uint4 qa = *reinterpret_cast<const uint4*>(Qp), qc = *reinterpret_cast<const uint4*>(Qp + 8);
+    // lane `sub` owns elements [8 sub, 8 sub + 8) and [D/2 + 8 sub, D/2 + 8 sub + 8): each of its
+    // two 16-byte loads is part of one contiguous half-row read by the LPR lanes together
+    constexpr int HALF = D / 2;
+    const uint16_t* Qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2 + 8 * sub;
+    const uint4 qa = *reinterpret_cast<const uint4*>(Qp), qc = *reinterpret_cast<const uint4*>(Qp + HALF);
     const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qc.x, qc.y, qc.z, qc.w};
     const uint32_t kstride = (uint32_t)(a.K.s2 * 2), vstride = (uint32_t)(a.V.s2 * 2);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1,
@@ -620,7 +624,7 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1,
                                                  (uint32_t)p.n_kv * vstride);
     const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
-    const uint32_t col = 32u * sub;
+    const uint32_t col = 16u * sub;
 
     float m = -INFINITY, l = 0.f, o[16];
 #pragma unroll
@@ -642,14 +646,14 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             auto k0 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[u], 0, 0);
-            auto k1 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[u] + 16, 0, 0);
+            auto k1 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[u] + HALF * 2, 0, 0);
 #pragma unroll
             for (int w = 0; w < 4; ++w) { kw[u][w] = k0[w]; kw[u][4 + w] = k1[w]; }
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             auto v0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[u], 0, 0);
-            auto v1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[u] + 16, 0, 0);
+            auto v1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[u] + HALF * 2, 0, 0);
 #pragma unroll
             for (int w = 0; w < 4; ++w) { vw[u][w] = v0[w]; vw[u][4 + w] = v1[w]; }
         }
@@ -700,13 +704,13 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
     }
     if (rg == 0) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* Op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2 + 16 * sub;
+        uint16_t* Op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2 + 8 * sub;
         uint32_t pk[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             pk[e] = (uint32_t)f32_to_bf16_rne(o[2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * e + 1] * inv) << 16);
         *reinterpret_cast<uint4*>(Op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        *reinterpret_cast<uint4*>(Op + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        *reinterpret_cast<uint4*>(Op + HALF) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
         if (a.lse && sub == 0)
             a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
