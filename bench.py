@@ -60,8 +60,65 @@ def algorithmic(W):
     o_bytes = W["B"] * W["Hq"] * W["n_q"] * W["d_v"] * esz
     idx_bytes = W["B"] * W["n_q"] * W["k"] * 4
     gather = sel * row_bytes + q_bytes + o_bytes + idx_bytes
+    # indexer: every visible index key once per query row (decode: the full-history scan), the
+    # index queries and weights once, one fp32 score per visible pair written
+    kb = {0: 4, 1: 2, 2: 1}[W["kidx_dtype"]]
+    qb = {0: 4, 1: 2}[W["qidx_dtype"]]
+    idx_scan_bytes = pairs * W["d_idx"] * kb + W["B"] * W["n_q"] * W["Hidx"] * (W["d_idx"] * qb + 4) + pairs * 4
+    # top-k: every visible score read once, the selection written once
+    topk_bytes = pairs * 4 + idx_bytes
     return dict(pairs=pairs, selected=sel, rows=rows, idx_flops=idx_flops, attn_flops=attn_flops,
-                gather_bytes=gather, row_bytes=row_bytes)
+                gather_bytes=gather, row_bytes=row_bytes, idx_scan_bytes=idx_scan_bytes, topk_bytes=topk_bytes,
+                decode=bool(W.get("decode")) or W["n_q"] <= 8)
+
+
+def stage_rooflines(W, alg, t):
+    """Roofline position of each stage from its algorithmic work and measured time (ms)."""
+    def hbm(nbytes, ms):
+        a = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "bytes_per_launch": int(nbytes), "ms_per_launch": round(ms, 4)}
+
+    def mfma(flops, ms):
+        a = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / BF16_PEAK_TFLOPS, 4), "flops_per_launch": int(flops), "ms_per_launch": round(ms, 4)}
+
+    out = {}
+    out["indexer_score"] = hbm(alg["idx_scan_bytes"], t["indexer_score"]) if alg["decode"] else \
+        mfma(alg["idx_flops"], t["indexer_score"])
+    out["topk"] = hbm(alg["topk_bytes"], t["topk"])
+    if W["mla"] and not alg["decode"]:
+        out["sparse_attn"] = mfma(alg["attn_flops"], t["sparse_attn"])
+    else:
+        out["sparse_attn"] = hbm(alg["gather_bytes"], t["sparse_attn"])
+    for k in out:
+        out[k]["kernel"] = k
+    return out
+
+
+def counted_traffic(workload, stage):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by a
+    plain-copy calibration) as recorded under profiles/, or None when no record exists for this
+    workload and stage or the kernel source has changed since the counters were taken."""
+    import glob
+    import hashlib
+
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_counters.md")):
+        rec = {}
+        for line in open(path):
+            if ":" in line and not line.startswith((" ", "|", "#")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+        if rec.get("workload") != workload or rec.get("stage") != stage:
+            continue
+        src = os.path.join(ROOT, rec.get("source", ""))
+        if not os.path.isfile(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+            return None
+        return int(float(rec["traffic_bytes_per_launch"]))
+    return None
 
 
 def cpu_baseline(W, budget_rows):
@@ -117,6 +174,8 @@ def main():
     os.environ.setdefault("OMP_NUM_THREADS", "16")
     W = sa_synth.make_config(args.config)
     alg = algorithmic(W)
+    if args.config != 1:
+        args.cpu_rows = min(args.cpu_rows, 64)
     P, d = device_workload(W)
     dt = torch.float32 if W["main_dtype"] == sa_synth.F32 else torch.bfloat16
     O, lse, idx = empty_outputs(W, dt)
@@ -161,8 +220,12 @@ def main():
     t_idx = timed(lambda: sa.sa_indexer_score(P, d["q_idx"], d["k_idx"], d["w"], scores, stream), reps)
     t_topk = timed(lambda: sa.sa_topk(P, scores, W["n_kv"], idx2, None, ws_t, stream), reps)
     t_attn = timed(lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream), reps)
-    ach_gbs = alg["gather_bytes"] / (t_attn * 1e-3) / 1e9
     idx_tflops = alg["idx_flops"] / (t_idx * 1e-3) / 1e12
+    times = {"indexer_score": t_idx, "topk": t_topk, "sparse_attn": t_attn}
+    roofs = stage_rooflines(W, alg, times)
+    dominant = max(times, key=times.get)
+    roof = dict(roofs[dominant])
+    roof["traffic"] = counted_traffic(W["name"], dominant)
 
     out = {
         "metric": METRIC,
@@ -183,9 +246,8 @@ def main():
         "stages_ms": {"indexer_score": round(t_idx, 4), "topk": round(t_topk, 4), "sparse_attn": round(t_attn, 4)},
         "indexer": {"tflops": round(idx_tflops, 3), "frac_bf16_peak": round(idx_tflops / BF16_PEAK_TFLOPS, 5),
                     "flops_per_call": alg["idx_flops"]},
-        "roofline": {"kernel": "sparse gather attention", "bound": "hbm", "achieved": round(ach_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": alg["gather_bytes"], "ms_per_launch": round(t_attn, 4)},
+        "roofline": roof,
+        "stage_rooflines": roofs,
     }
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_rows)
