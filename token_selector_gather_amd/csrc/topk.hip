@@ -198,13 +198,13 @@ __global__ void __launch_bounds__(kThreads) topk_rows(TopkArgs a) {
 }
 
 // ------------------------------------------------------------------ register path
-// The same selection with 1024 threads and the row in registers: segments of VPT * 1024
-// positions, thread t holding positions c * 4096 + 4t .. 4t+3 of every chunk c of 4096, all
+// The same selection with NT threads and the row in registers: segments of VPT * NT
+// positions, thread t holding positions c * 4NT + 4t .. 4t+3 of every chunk c of 4NT, all
 // loaded with coalesced 16-byte loads.  A row of one segment is loaded once and every radix
 // pass runs on registers; longer rows stream their segments through once per pass.  The
 // ordered compaction walks the chunks in position order with one block scan each.
-constexpr int kBig = 1024;
 
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan_big(uint32_t v, uint32_t* wave_tot, uint32_t& total) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     uint32_t x = v;
@@ -217,7 +217,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan_big(uint32_t v, uint32_
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kBig / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         uint32_t t = wave_tot[w];
         if (w < wid) before += t;
         tot += t;
@@ -227,16 +227,16 @@ __device__ __forceinline__ uint32_t block_exclusive_scan_big(uint32_t v, uint32_
     return before + x - v;
 }
 
-template <int NB>
+template <int NB, int NT>
 __device__ __forceinline__ void find_bin_big(const uint32_t* hist, uint32_t need, uint32_t* wave_tot, int* out_bin,
                                              uint32_t* out_above) {
-    constexpr int PER = NB / kBig;  // bins per thread, highest bins to thread 0
+    constexpr int PER = NB / NT;  // bins per thread, highest bins to thread 0
     const int t = threadIdx.x;
     uint32_t local = 0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) local += hist[NB - 1 - (t * PER + e)];
     uint32_t total;
-    const uint32_t above = block_exclusive_scan_big(local, wave_tot, total);
+    const uint32_t above = block_exclusive_scan_big<NT>(local, wave_tot, total);
     if (above < need && above + local >= need) {
         uint32_t run = above;
 #pragma unroll
@@ -254,15 +254,34 @@ __device__ __forceinline__ void find_bin_big(const uint32_t* hist, uint32_t need
     __syncthreads();
 }
 
+// LDS histogram increment with lanes of the wave that share a bin combined first (scores
+// of one row often crowd into a few bins of the leading digit, which would serialise plain
+// atomics): up to four rounds pick the bin of the first remaining lane and add the
+// population count of its matches; lanes still left then add individually.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+    const int lane = threadIdx.x & 63;
+    uint64_t rem = __ballot(active);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        if (rem == 0) break;
+        const int leader = __ffsll((unsigned long long)rem) - 1;
+        const uint32_t lb = __shfl(bin, leader);
+        const uint64_t m = __ballot(active && bin == lb) & rem;
+        if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
+        rem &= ~m;
+    }
+    if ((rem >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+}
+
 // keys of segment `seg` (positions >= L get key 0, below every real key); returns 1 on a
 // non-finite visible score
-template <int NCH>
+template <int NCH, int NT>
 __device__ __forceinline__ int load_segment(const float* sc, int L, int seg, bool vec_ok, uint32_t (&key)[NCH][4]) {
     int bad = 0;
     const int t = threadIdx.x;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int j0 = (seg * NCH + c) * 4 * kBig + 4 * t;
+        const int j0 = (seg * NCH + c) * 4 * NT + 4 * t;
         float v[4];
         if (vec_ok && j0 + 3 < L) {
             const float4 f = *reinterpret_cast<const float4*>(sc + j0);
@@ -281,12 +300,12 @@ __device__ __forceinline__ int load_segment(const float* sc, int L, int seg, boo
     return bad;
 }
 
-template <int VPT>
-__global__ void __launch_bounds__(kBig) topk_rows_reg(TopkArgs a) {
-    constexpr int NCH = VPT / 4;       // chunks of 4 * kBig positions per segment
-    constexpr int SEG = VPT * kBig;    // positions per segment
+template <int VPT, int NT>
+__global__ void __launch_bounds__(NT) topk_rows_reg(TopkArgs a) {
+    constexpr int NCH = VPT / 4;       // chunks of 4 * NT positions per segment
+    constexpr int SEG = VPT * NT;    // positions per segment
     __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wave_tot[kBig / 64];
+    __shared__ uint32_t wave_tot[NT / 64];
     __shared__ int s_bin;
     __shared__ uint32_t s_above;
     __shared__ int s_bad;
@@ -310,7 +329,7 @@ __global__ void __launch_bounds__(kBig) topk_rows_reg(TopkArgs a) {
 
     if (L <= K) {
         int bad = 0;
-        for (int j = t; j < K; j += kBig) {
+        for (int j = t; j < K; j += NT) {
             const float v = j < L ? sc[j] : -INFINITY;
             if (j < L && !isfinite(v)) bad = 1;
             out[j] = j < L ? j : -1;
@@ -325,7 +344,7 @@ __global__ void __launch_bounds__(kBig) topk_rows_reg(TopkArgs a) {
     const bool vec_ok = ((a.row_stride & 3) == 0) && (((uintptr_t)a.scores & 15) == 0);
     const int nseg = (L + SEG - 1) / SEG;
     uint32_t key[NCH][4];
-    if (nseg == 1 && load_segment<NCH>(sc, L, 0, vec_ok, key)) s_bad = 1;
+    if (nseg == 1 && load_segment<NCH, NT>(sc, L, 0, vec_ok, key)) s_bad = 1;
 
     // three MSB digits: 11, 11 and 10 bits; `above` counts keys in strictly higher bins
     uint32_t pre = 0, above = 0;
@@ -334,22 +353,22 @@ __global__ void __launch_bounds__(kBig) topk_rows_reg(TopkArgs a) {
         const int shift = dgt == 0 ? 21 : (dgt == 1 ? 10 : 0);
         const uint32_t mask = dgt == 2 ? 1023u : 2047u;
         const int pshift = dgt == 0 ? 32 : shift + (dgt == 1 ? 11 : 10);
-        for (int e = t; e < 2048; e += kBig) hist[e] = 0;
+        for (int e = t; e < 2048; e += NT) hist[e] = 0;
         __syncthreads();
         for (int seg = 0; seg < nseg; ++seg) {
-            if (nseg > 1 && load_segment<NCH>(sc, L, seg, vec_ok, key) && dgt == 0) s_bad = 1;
+            if (nseg > 1 && load_segment<NCH, NT>(sc, L, seg, vec_ok, key) && dgt == 0) s_bad = 1;
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t kk = key[c][e];
-                    const bool in = (seg * NCH + c) * 4 * kBig + 4 * t + e < L;
+                    const bool in = (seg * NCH + c) * 4 * NT + 4 * t + e < L;
                     const bool match = dgt == 0 ? true : ((uint32_t)((uint64_t)kk >> pshift) == pre);
-                    if (in && match) atomicAdd(&hist[(kk >> shift) & mask], 1u);
+                    hist_add(hist, (kk >> shift) & mask, in && match);
                 }
         }
         __syncthreads();
-        find_bin_big<2048>(hist, (uint32_t)K - above, wave_tot, &s_bin, &s_above);
+        find_bin_big<2048, NT>(hist, (uint32_t)K - above, wave_tot, &s_bin, &s_above);
         // append this digit (11, 11 or 10 bits wide) to the prefix of the threshold key
         pre = dgt == 0 ? (uint32_t)s_bin : ((pre << (dgt == 1 ? 11 : 10)) | (uint32_t)s_bin);
         above += s_above;
@@ -360,10 +379,10 @@ __global__ void __launch_bounds__(kBig) topk_rows_reg(TopkArgs a) {
     // ---- ordered compaction, segment by segment, chunk by chunk
     uint32_t run_gt = 0, run_eq = 0;
     for (int seg = 0; seg < nseg; ++seg) {
-        if (nseg > 1) load_segment<NCH>(sc, L, seg, vec_ok, key);
+        if (nseg > 1) load_segment<NCH, NT>(sc, L, seg, vec_ok, key);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int cbase = (seg * NCH + c) * 4 * kBig;
+            const int cbase = (seg * NCH + c) * 4 * NT;
             if (cbase >= L) break;  // uniform
             const int j0 = cbase + 4 * t;
             uint32_t c_gt = 0, c_eq = 0;
@@ -375,7 +394,7 @@ __global__ void __launch_bounds__(kBig) topk_rows_reg(TopkArgs a) {
                 }
             }
             uint32_t tot;
-            const uint32_t pref = block_exclusive_scan_big(c_eq | (c_gt << 16), wave_tot, tot);
+            const uint32_t pref = block_exclusive_scan_big<NT>(c_eq | (c_gt << 16), wave_tot, tot);
             uint32_t G = run_gt + (pref >> 16), E = run_eq + (pref & 0xffffu);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -405,11 +424,14 @@ __global__ void __launch_bounds__(kBig) topk_rows_reg(TopkArgs a) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     const long rows = (long)a.p.B * a.p.n_q;
     const int n = a.p.n_kv;
-    const dim3 g((unsigned)rows), blk(kBig);
-    if (n <= 4 * kBig) hipLaunchKernelGGL(topk_rows_reg<4>, g, blk, 0, s, a);
-    else if (n <= 8 * kBig) hipLaunchKernelGGL(topk_rows_reg<8>, g, blk, 0, s, a);
-    else if (n <= 16 * kBig) hipLaunchKernelGGL(topk_rows_reg<16>, g, blk, 0, s, a);
-    else hipLaunchKernelGGL(topk_rows_reg<32>, g, blk, 0, s, a);
+    const dim3 g((unsigned)rows);
+    // short rows: 256 threads hold a whole row; long rows: 1024 threads, 32768-position segments
+    if (n <= 1024) hipLaunchKernelGGL((topk_rows_reg<4, 256>), g, dim3(256), 0, s, a);
+    else if (n <= 2048) hipLaunchKernelGGL((topk_rows_reg<8, 256>), g, dim3(256), 0, s, a);
+    else if (n <= 4096) hipLaunchKernelGGL((topk_rows_reg<16, 256>), g, dim3(256), 0, s, a);
+    else if (n <= 8192) hipLaunchKernelGGL((topk_rows_reg<32, 256>), g, dim3(256), 0, s, a);
+    else if (n <= 16384) hipLaunchKernelGGL((topk_rows_reg<16, 1024>), g, dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL((topk_rows_reg<32, 1024>), g, dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
