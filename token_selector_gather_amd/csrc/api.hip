@@ -125,10 +125,11 @@ size_t sa_workspace_bytes(const sa_problem* p, int op) {
     if (!problem_ok(p)) return 0;
     switch (op) {
     case SA_OP_INDEXER_SCORE: return 0;
-    case SA_OP_TOPK: return kStatusBytes;
+    case SA_OP_TOPK: return kStatusBytes + align256(topk_ws_bytes(*p));
     case SA_OP_SPARSE_ATTN: return kStatusBytes + align256(attn_partial_bytes(*p));
     case SA_OP_SELECT_ATTEND:
-        return kStatusBytes + scores_bytes(*p) + idx_bytes(*p) + align256(attn_partial_bytes(*p));
+        return kStatusBytes + scores_bytes(*p) + idx_bytes(*p) + align256(attn_partial_bytes(*p)) +
+               align256(topk_ws_bytes(*p));
     default: return 0;
     }
 }
@@ -160,6 +161,7 @@ sa_status sa_topk(const sa_problem* p, const float* scores, int64_t row_stride, 
     a.idx = idx;
     a.vals = vals;
     a.status = static_cast<Status*>(ws);
+    a.scratch = static_cast<char*>(ws) + kStatusBytes;
     return launch_topk(a, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -189,6 +191,7 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     float* scores = reinterpret_cast<float*>(base + kStatusBytes);
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + kStatusBytes + scores_bytes(*p));
     void* partial = base + kStatusBytes + scores_bytes(*p) + idx_bytes(*p);
+    void* tk_scratch = static_cast<char*>(partial) + align256(attn_partial_bytes(*p));
 
     IndexerArgs ia;
     ia.p = *p;
@@ -205,6 +208,7 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     ta.idx = idx;
     ta.vals = nullptr;
     ta.status = reinterpret_cast<Status*>(base);
+    ta.scratch = tk_scratch;
     if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
 
     return run_attn(p, Q, K, V, idx, O, lse, partial, st);

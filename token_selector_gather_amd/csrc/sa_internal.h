@@ -50,8 +50,10 @@ struct TopkArgs {
     int32_t* idx;
     float* vals;
     Status* status;
+    void* scratch;  // topk_ws_bytes(p) bytes of workspace (per-row histograms of the sliced path)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+size_t topk_ws_bytes(const sa_problem& p);
 
 struct AttnArgs {
     sa_problem p;

@@ -19,182 +19,10 @@
 namespace sa {
 namespace {
 
-constexpr int kThreads = 256;
-
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) == 0) u = 0;  // -0 == +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive scan of one uint32 per thread over the block; returns the prefix, sets total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_t& total) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wave_tot[wid] = x;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
-        uint32_t t = wave_tot[w];
-        if (w < wid) before += t;
-        tot += t;
-    }
-    __syncthreads();
-    total = tot;
-    return before + x - v;
-}
-
-// Find the digit bin holding the `need`-th largest key among the histogram's entries.
-// bins: NB counters.  Returns bin and number of entries in strictly higher bins.
-template <int NB>
-__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t need, uint32_t* wave_tot, int* out_bin,
-                                         uint32_t* out_above) {
-    constexpr int PER = NB / kThreads;  // bins per thread, highest bins to thread 0
-    const int t = threadIdx.x;
-    uint32_t local = 0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) local += hist[NB - 1 - (t * PER + e)];
-    uint32_t total;
-    uint32_t above = block_exclusive_scan(local, wave_tot, total);
-    if (above < need && above + local >= need) {
-        uint32_t run = above;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int bin = NB - 1 - (t * PER + e);
-            const uint32_t c = hist[bin];
-            if (run + c >= need) {
-                *out_bin = bin;
-                *out_above = run;
-                break;
-            }
-            run += c;
-        }
-    }
-    __syncthreads();
-}
-
-__global__ void __launch_bounds__(kThreads) topk_rows(TopkArgs a) {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wave_tot[kThreads / 64];
-    __shared__ int s_bin;
-    __shared__ uint32_t s_above;
-    __shared__ int s_bad;
-
-    const sa_problem& p = a.p;
-    const int row = blockIdx.x;
-    const int b = row / p.n_q, i = row % p.n_q;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
-    const int L = visible_len(R, b, i);
-    const int K = p.k;
-    const float* sc = a.scores + (int64_t)row * a.row_stride;
-    int32_t* out = a.idx + (int64_t)row * K;
-    float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
-    const int t = threadIdx.x;
-    if (t == 0) {
-        s_bad = 0;
-        s_bin = 0;
-        s_above = 0;
-    }
-    __syncthreads();
-
-    if (L <= K) {
-        int bad = 0;
-        for (int j = t; j < K; j += kThreads) {
-            float v = j < L ? sc[j] : -INFINITY;
-            if (j < L && !isfinite(v)) bad = 1;
-            out[j] = j < L ? j : -1;
-            if (vout) vout[j] = v;
-        }
-        if (bad) s_bad = 1;
-        __syncthreads();
-        if (t == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
-        return;
-    }
-
-    // ---- digit 1: bits 31..21
-    for (int e = t; e < 2048; e += kThreads) hist[e] = 0;
-    __syncthreads();
-    int bad = 0;
-    for (int j = t; j < L; j += kThreads) {
-        float v = sc[j];
-        if (!isfinite(v)) bad = 1;
-        atomicAdd(&hist[order_key(v) >> 21], 1u);
-    }
-    if (bad) s_bad = 1;
-    __syncthreads();
-    find_bin<2048>(hist, (uint32_t)K, wave_tot, &s_bin, &s_above);
-    const uint32_t d1 = (uint32_t)s_bin;
-    uint32_t above = s_above;
-
-    // ---- digit 2: bits 20..10 among keys with digit 1 == d1
-    for (int e = t; e < 2048; e += kThreads) hist[e] = 0;
-    __syncthreads();
-    for (int j = t; j < L; j += kThreads) {
-        uint32_t key = order_key(sc[j]);
-        if ((key >> 21) == d1) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
-    }
-    __syncthreads();
-    find_bin<2048>(hist, (uint32_t)K - above, wave_tot, &s_bin, &s_above);
-    const uint32_t d2 = (uint32_t)s_bin;
-    above += s_above;
-
-    // ---- digit 3: bits 9..0 among keys with digits 1,2 == d1,d2
-    for (int e = t; e < 1024; e += kThreads) hist[e] = 0;
-    __syncthreads();
-    const uint32_t pre = (d1 << 11) | d2;
-    for (int j = t; j < L; j += kThreads) {
-        uint32_t key = order_key(sc[j]);
-        if ((key >> 10) == pre) atomicAdd(&hist[key & 1023u], 1u);
-    }
-    __syncthreads();
-    find_bin<1024>(hist, (uint32_t)K - above, wave_tot, &s_bin, &s_above);
-    const uint32_t T = (pre << 10) | (uint32_t)s_bin;
-    above += s_above;
-    const uint32_t need_eq = (uint32_t)K - above;  // >= 1 keys equal to T to take
-
-    // ---- ordered compaction
-    uint32_t run_gt = 0, run_eq = 0;
-    for (int base = 0; base < L; base += 4 * kThreads) {
-        const int j0 = base + 4 * t;
-        uint32_t keys[4];
-        uint32_t c_gt = 0, c_eq = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = j0 + e;
-            keys[e] = j < L ? order_key(sc[j]) : 0u;
-            if (j < L) {
-                c_gt += keys[e] > T;
-                c_eq += keys[e] == T;
-            }
-        }
-        uint32_t tot;
-        const uint32_t pref = block_exclusive_scan(c_eq | (c_gt << 16), wave_tot, tot);
-        uint32_t G = run_gt + (pref >> 16), E = run_eq + (pref & 0xffffu);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = j0 + e;
-            if (j >= L) break;
-            const bool gt = keys[e] > T, eq = keys[e] == T;
-            if (gt || (eq && E < need_eq)) {
-                const uint32_t slot = G + (E < need_eq ? E : need_eq);
-                if (slot < (uint32_t)K) {
-                    out[slot] = j;
-                    if (vout) vout[slot] = sc[j];
-                }
-            }
-            G += gt;
-            E += eq;
-        }
-        run_gt += tot >> 16;
-        run_eq += tot & 0xffffu;
-    }
-    if (t == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
 }
 
 // ------------------------------------------------------------------ register path
@@ -252,25 +80,6 @@ __device__ __forceinline__ void find_bin_big(const uint32_t* hist, uint32_t need
         }
     }
     __syncthreads();
-}
-
-// LDS histogram increment with lanes of the wave that share a bin combined first (scores
-// of one row often crowd into a few bins of the leading digit, which would serialise plain
-// atomics): up to four rounds pick the bin of the first remaining lane and add the
-// population count of its matches; lanes still left then add individually.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
-    const int lane = threadIdx.x & 63;
-    uint64_t rem = __ballot(active);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        if (rem == 0) break;
-        const int leader = __ffsll((unsigned long long)rem) - 1;
-        const uint32_t lb = __shfl(bin, leader);
-        const uint64_t m = __ballot(active && bin == lb) & rem;
-        if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
-        rem &= ~m;
-    }
-    if ((rem >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
 // keys of segment `seg` (positions >= L get key 0, below every real key); returns 1 on a
@@ -364,7 +173,7 @@ __global__ void __launch_bounds__(NT) topk_rows_reg(TopkArgs a) {
                     const uint32_t kk = key[c][e];
                     const bool in = (seg * NCH + c) * 4 * NT + 4 * t + e < L;
                     const bool match = dgt == 0 ? true : ((uint32_t)((uint64_t)kk >> pshift) == pre);
-                    hist_add(hist, (kk >> shift) & mask, in && match);
+                    if (in && match) atomicAdd(&hist[(kk >> shift) & mask], 1u);
                 }
         }
         __syncthreads();
@@ -419,12 +228,274 @@ __global__ void __launch_bounds__(NT) topk_rows_reg(TopkArgs a) {
     if (t == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
 }
 
+// -------------------------------------------------------------------- sliced path
+// Few long rows (decode batches): each row is cut into slices of 4096 positions with one
+// 256-thread workgroup per slice, so 8 or 64 rows still occupy the whole GPU.  The radix
+// select above runs as a short chain of kernels with per-row digit histograms in the
+// workspace, accumulated atomically by the row's workgroups; each kernel re-derives the
+// threshold prefix from the finished histograms of the earlier digits.  The last two
+// kernels count keys > T and == T per slice and compact in position order, each slice
+// starting after the counts of the row's earlier slices.
+constexpr int kSlice = 4096, kSliceT = 256;
+
+struct SlicedWs {
+    uint32_t* hist;    // [rows][3][2048]
+    uint32_t* counts;  // [rows][S][2]  (greater, equal)
+    uint32_t* state;   // [rows][4]     (T, need_eq)
+    int S;
+};
+
+__device__ __forceinline__ void load_slice16(const float* sc, int L, int j0, bool vec_ok, uint32_t (&key)[4][4],
+                                             int& bad) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int j = j0 + c * 4 * kSliceT + 4 * t;
+        float v[4];
+        if (vec_ok && j + 3 < L) {
+            const float4 f = *reinterpret_cast<const float4*>(sc + j);
+            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (j + e < L) ? sc[j + e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool in = j + e < L;
+            if (in && !isfinite(v[e])) bad = 1;
+            key[c][e] = in ? order_key(v[e]) : 0u;
+        }
+    }
+}
+
+// prefix of the threshold after `ndig` digits and the count of keys above it
+__device__ __forceinline__ void sliced_prefix(const uint32_t* ghist, int ndig, uint32_t K, uint32_t* lh,
+                                              uint32_t* wave_tot, int* s_bin, uint32_t* s_above, uint32_t& pre,
+                                              uint32_t& above) {
+    pre = 0;
+    above = 0;
+    for (int dgt = 0; dgt < ndig; ++dgt) {
+        for (int e = threadIdx.x; e < 2048; e += kSliceT) lh[e] = ghist[dgt * 2048 + e];
+        __syncthreads();
+        find_bin_big<2048, kSliceT>(lh, K - above, wave_tot, s_bin, s_above);
+        pre = dgt == 0 ? (uint32_t)*s_bin : ((pre << (dgt == 1 ? 11 : 10)) | (uint32_t)*s_bin);
+        above += *s_above;
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(256) topk_sl_zero(SlicedWs w, long words) {
+    for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < words; e += (long)gridDim.x * 256) w.hist[e] = 0;
+}
+
+template <int DIGIT>
+__global__ void __launch_bounds__(kSliceT) topk_sl_hist(TopkArgs a, SlicedWs w) {
+    __shared__ uint32_t lh[2048];
+    __shared__ uint32_t wave_tot[kSliceT / 64];
+    __shared__ int s_bin;
+    __shared__ uint32_t s_above;
+    __shared__ int s_bad;
+    const sa_problem& p = a.p;
+    const int row = blockIdx.x / w.S, slice = blockIdx.x % w.S;
+    const int b = row / p.n_q, i = row % p.n_q;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int K = p.k;
+    const int j0 = slice * kSlice;
+    const float* sc = a.scores + (int64_t)row * a.row_stride;
+    if (threadIdx.x == 0) { s_bad = 0; s_bin = 0; s_above = 0; }
+    __syncthreads();
+    if (L <= K) {
+        if (DIGIT == 0) {  // short row: all visible positions, then -1
+            int32_t* out = a.idx + (int64_t)row * K;
+            float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
+            int bad = 0;
+            for (int j = j0 + threadIdx.x; j < min(K, j0 + kSlice) || (slice == w.S - 1 && j < K); j += kSliceT) {
+                const float v = j < L ? sc[j] : -INFINITY;
+                if (j < L && !isfinite(v)) bad = 1;
+                out[j] = j < L ? j : -1;
+                if (vout) vout[j] = v;
+            }
+            if (bad) s_bad = 1;
+            __syncthreads();
+            if (threadIdx.x == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+        }
+        return;
+    }
+    if (j0 >= L) return;
+    uint32_t* gh = w.hist + (int64_t)row * 3 * 2048;
+    uint32_t pre, above;
+    sliced_prefix(gh, DIGIT, (uint32_t)K, lh, wave_tot, &s_bin, &s_above, pre, above);
+    for (int e = threadIdx.x; e < 2048; e += kSliceT) lh[e] = 0;
+    __syncthreads();
+    uint32_t key[4][4];
+    int bad = 0;
+    const bool vec_ok = ((a.row_stride & 3) == 0) && (((uintptr_t)a.scores & 15) == 0);
+    load_slice16(sc, L, j0, vec_ok, key, bad);
+    const int shift = DIGIT == 0 ? 21 : (DIGIT == 1 ? 10 : 0);
+    const uint32_t mask = DIGIT == 2 ? 1023u : 2047u;
+    const int pshift = DIGIT == 1 ? 21 : 10;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool in = j0 + c * 4 * kSliceT + 4 * threadIdx.x + e < L;
+            const bool match = DIGIT == 0 ? true : ((key[c][e] >> pshift) == pre);
+            if (in && match) atomicAdd(&lh[(key[c][e] >> shift) & mask], 1u);
+        }
+    if (DIGIT == 0 && bad) s_bad = 1;
+    __syncthreads();
+    for (int e = threadIdx.x; e < 2048; e += kSliceT)
+        if (lh[e]) atomicAdd(&gh[DIGIT * 2048 + e], lh[e]);
+    if (DIGIT == 0 && threadIdx.x == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+}
+
+// per-slice counts of keys greater than / equal to the threshold T
+__global__ void __launch_bounds__(kSliceT) topk_sl_count(TopkArgs a, SlicedWs w) {
+    __shared__ uint32_t lh[2048];
+    __shared__ uint32_t wave_tot[kSliceT / 64];
+    __shared__ int s_bin;
+    __shared__ uint32_t s_above;
+    const sa_problem& p = a.p;
+    const int row = blockIdx.x / w.S, slice = blockIdx.x % w.S;
+    const int b = row / p.n_q, i = row % p.n_q;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int K = p.k;
+    const int j0 = slice * kSlice;
+    if (L <= K) return;
+    if (threadIdx.x == 0) { s_bin = 0; s_above = 0; }
+    __syncthreads();
+    uint32_t* gh = w.hist + (int64_t)row * 3 * 2048;
+    uint32_t T, above;
+    sliced_prefix(gh, 3, (uint32_t)K, lh, wave_tot, &s_bin, &s_above, T, above);
+    if (slice == 0 && threadIdx.x == 0) {
+        w.state[row * 4 + 0] = T;
+        w.state[row * 4 + 1] = (uint32_t)K - above;
+    }
+    uint32_t gt = 0, eq = 0;
+    if (j0 < L) {
+        uint32_t key[4][4];
+        int bad = 0;
+        const bool vec_ok = ((a.row_stride & 3) == 0) && (((uintptr_t)a.scores & 15) == 0);
+        load_slice16(a.scores + (int64_t)row * a.row_stride, L, j0, vec_ok, key, bad);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j0 + c * 4 * kSliceT + 4 * threadIdx.x + e < L) {
+                    gt += key[c][e] > T;
+                    eq += key[c][e] == T;
+                }
+    }
+    uint32_t tot;
+    block_exclusive_scan_big<kSliceT>(eq | (gt << 16), wave_tot, tot);
+    if (threadIdx.x == 0) {
+        w.counts[((int64_t)row * w.S + slice) * 2 + 0] = tot >> 16;
+        w.counts[((int64_t)row * w.S + slice) * 2 + 1] = tot & 0xffffu;
+    }
+}
+
+// ordered compaction: slice s writes after the greater/equal counts of slices < s
+__global__ void __launch_bounds__(kSliceT) topk_sl_compact(TopkArgs a, SlicedWs w) {
+    __shared__ uint32_t wave_tot[kSliceT / 64];
+    __shared__ uint32_t s_g0, s_e0;
+    const sa_problem& p = a.p;
+    const int row = blockIdx.x / w.S, slice = blockIdx.x % w.S;
+    const int b = row / p.n_q, i = row % p.n_q;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int K = p.k;
+    const int j0 = slice * kSlice;
+    if (L <= K || j0 >= L) return;
+    const uint32_t T = w.state[row * 4 + 0], need_eq = w.state[row * 4 + 1];
+    if (threadIdx.x < 64) {
+        uint32_t g = 0, e = 0;
+        for (int s2 = threadIdx.x; s2 < slice; s2 += 64) {
+            g += w.counts[((int64_t)row * w.S + s2) * 2 + 0];
+            e += w.counts[((int64_t)row * w.S + s2) * 2 + 1];
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            g += __shfl_xor(g, o);
+            e += __shfl_xor(e, o);
+        }
+        if (threadIdx.x == 0) { s_g0 = g; s_e0 = e; }
+    }
+    __syncthreads();
+    const float* sc = a.scores + (int64_t)row * a.row_stride;
+    int32_t* out = a.idx + (int64_t)row * K;
+    float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
+    uint32_t key[4][4];
+    int bad = 0;
+    const bool vec_ok = ((a.row_stride & 3) == 0) && (((uintptr_t)a.scores & 15) == 0);
+    load_slice16(sc, L, j0, vec_ok, key, bad);
+    uint32_t run_gt = s_g0, run_eq = s_e0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int jc = j0 + c * 4 * kSliceT + 4 * threadIdx.x;
+        uint32_t c_gt = 0, c_eq = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (jc + e < L) {
+                c_gt += key[c][e] > T;
+                c_eq += key[c][e] == T;
+            }
+        uint32_t tot;
+        const uint32_t pref = block_exclusive_scan_big<kSliceT>(c_eq | (c_gt << 16), wave_tot, tot);
+        uint32_t G = run_gt + (pref >> 16), E = run_eq + (pref & 0xffffu);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = jc + e;
+            if (j >= L) break;
+            const bool gt = key[c][e] > T, eq = key[c][e] == T;
+            if (gt || (eq && E < need_eq)) {
+                const uint32_t slot = G + (E < need_eq ? E : need_eq);
+                if (slot < (uint32_t)K) {
+                    out[slot] = j;
+                    if (vout) vout[slot] = sc[j];
+                }
+            }
+            G += gt;
+            E += eq;
+        }
+        run_gt += tot >> 16;
+        run_eq += tot & 0xffffu;
+    }
+}
+
 }  // namespace
+
+bool topk_sliced(const sa_problem& p) { return (long)p.B * p.n_q <= 512 && p.n_kv > 8192; }
+
+size_t topk_ws_bytes(const sa_problem& p) {
+    if (!topk_sliced(p)) return 0;
+    const long rows = (long)p.B * p.n_q;
+    const long S = (p.n_kv + kSlice - 1) / kSlice;
+    return (size_t)rows * (3 * 2048 + 2 * S + 4) * sizeof(uint32_t);
+}
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     const long rows = (long)a.p.B * a.p.n_q;
     const int n = a.p.n_kv;
     const dim3 g((unsigned)rows);
+    if (topk_sliced(a.p)) {
+        SlicedWs w;
+        w.S = (n + kSlice - 1) / kSlice;
+        w.hist = static_cast<uint32_t*>(a.scratch);
+        w.counts = w.hist + rows * 3 * 2048;
+        w.state = w.counts + rows * 2 * w.S;
+        const long words = rows * 3 * 2048;
+        hipLaunchKernelGGL(topk_sl_zero, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                           dim3(256), 0, s, w, words);
+        const dim3 gs((unsigned)(rows * w.S));
+        hipLaunchKernelGGL(topk_sl_hist<0>, gs, dim3(kSliceT), 0, s, a, w);
+        hipLaunchKernelGGL(topk_sl_hist<1>, gs, dim3(kSliceT), 0, s, a, w);
+        hipLaunchKernelGGL(topk_sl_hist<2>, gs, dim3(kSliceT), 0, s, a, w);
+        hipLaunchKernelGGL(topk_sl_count, gs, dim3(kSliceT), 0, s, a, w);
+        hipLaunchKernelGGL(topk_sl_compact, gs, dim3(kSliceT), 0, s, a, w);
+        return hipGetLastError();
+    }
     // short rows: 256 threads hold a whole row; long rows: 1024 threads, 32768-position segments
     if (n <= 1024) hipLaunchKernelGGL((topk_rows_reg<4, 256>), g, dim3(256), 0, s, a);
     else if (n <= 2048) hipLaunchKernelGGL((topk_rows_reg<8, 256>), g, dim3(256), 0, s, a);
