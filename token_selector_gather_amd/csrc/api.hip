@@ -145,6 +145,7 @@ sa_status sa_indexer_score(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     a.scores = scores;
     a.row_stride = p->n_kv;
     a.fill_invisible = 1;
+    a.status = nullptr;
     return launch_indexer(a, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -199,6 +200,7 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     ia.scores = scores;
     ia.row_stride = p->n_kv;
     ia.fill_invisible = 0;  // the selection reads only the visible prefix of each row
+    ia.status = reinterpret_cast<Status*>(base);
     if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
 
     TopkArgs ta;

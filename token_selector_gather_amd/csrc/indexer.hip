@@ -230,6 +230,241 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int n_groups,
     }
 }
 
+// ------------------------------------------------------- matrix-core path, shared keys
+// Four waves of a workgroup read the same history positions: in prefill they own four
+// consecutive query groups (their key fragments then hit the L1), in decode they split
+// one query group's history four ways.  A workgroup covers a long key range, so each
+// wave loads its query fragments once per range, and the next 16-key tile is fetched
+// (raw) while the current one is multiplied.  With FAST_RELU the epilogue clips with one
+// max per element; finiteness of the inputs is then checked by index_finite_check.
+template <int KSTEPS, bool KE4M3>
+struct BRaw;
+template <int KSTEPS>
+struct BRaw<KSTEPS, true> { uint2 v[KSTEPS]; };
+template <int KSTEPS>
+struct BRaw<KSTEPS, false> { uint4 v[KSTEPS]; };
+
+template <int KSTEPS, bool KE4M3>
+__device__ __forceinline__ void braw_load(const uint8_t* kb, bool ok, BRaw<KSTEPS, KE4M3>& r, int lane) {
+    const int dof = 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        if constexpr (KE4M3) r.v[s] = ok ? *reinterpret_cast<const uint2*>(kb + 32 * s + dof) : make_uint2(0, 0);
+        else r.v[s] = ok ? *reinterpret_cast<const uint4*>(kb + 2 * (32 * s + dof)) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int KSTEPS, bool KE4M3>
+__device__ __forceinline__ void braw_widen(const BRaw<KSTEPS, KE4M3>& r, bf16x8 (&bv)[KSTEPS]) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        if constexpr (KE4M3) {
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].x, 1.0f, false);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].x, 1.0f, true);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].y, 1.0f, false);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].y, 1.0f, true);
+            bv[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        } else {
+            bv[s] = __builtin_bit_cast(bf16x8, r.v[s]);
+        }
+    }
+}
+
+template <int KSTEPS, bool KE4M3, int H, bool DECODE, bool FAST_RELU>
+__global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups, int n_qblk, int n_rng, int rng_len) {
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    constexpr int QPG = 64 / H;
+    long wg = blockIdx.x;
+    int b, g, j_begin, j_end;
+    if (DECODE) {
+        const int rng = (int)(wg % n_rng);
+        const long rest = wg / n_rng;
+        g = (int)(rest % n_groups);
+        b = (int)(rest / n_groups);
+        const int sub = rng_len / 4;
+        j_begin = rng * rng_len + wv * sub;
+        j_end = min(j_begin + sub, p.n_kv);
+    } else {
+        const int rng = (int)(wg % n_rng);
+        const long rest = wg / n_rng;
+        const int qb = n_qblk - 1 - (int)(rest % n_qblk);  // longest causal histories first
+        b = (int)(rest / n_qblk);
+        g = qb * 4 + wv;
+        j_begin = rng * rng_len;
+        j_end = min(j_begin + rng_len, p.n_kv);
+    }
+    if (g >= n_groups || j_begin >= p.n_kv) return;
+    const int i0 = g * QPG;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    int Lq = 0;
+    if (lane < QPG && i0 + lane < p.n_q) Lq = visible_len(R, b, i0 + lane);
+    int Lmax = Lq;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Lmax = max(Lmax, __shfl_xor(Lmax, o));
+    const int j_comp_end = min(j_end, Lmax);
+
+    if (j_begin < j_comp_end) {
+        bf16x8 av[kMT][KSTEPS];
+        float wvv[kMT][4];
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+            const int r = 16 * mt + (lane & 15);
+            const int qi = i0 + r / H, h = r % H;
+            const bool ok = qi < p.n_q;
+            const uint16_t* qb = static_cast<const uint16_t*>(a.q.data) + (ok ? (b * a.q.s0 + qi * a.q.s1 + h * a.q.s2) : 0);
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                uint4 u = ok ? *reinterpret_cast<const uint4*>(qb + 32 * s + 8 * (lane >> 4)) : make_uint4(0, 0, 0, 0);
+                av[mt][s] = __builtin_bit_cast(bf16x8, u);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * mt + 4 * (lane >> 4) + e;
+                const int q2 = i0 + rr / H, h2 = rr % H;
+                wvv[mt][e] = q2 < p.n_q ? static_cast<const float*>(a.w.data)[b * a.w.s0 + q2 * a.w.s1 + h2] : 0.f;
+            }
+        }
+        const int64_t kstride_bytes = a.k.s1 * (KE4M3 ? 1 : 2);
+        const uint8_t* kb0 = static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2);
+        BRaw<KSTEPS, KE4M3> cur, nxt;
+        {
+            const int j = j_begin + (lane & 15);
+            braw_load<KSTEPS, KE4M3>(kb0 + (int64_t)j * kstride_bytes, j < j_comp_end, cur, lane);
+        }
+        for (int j0 = j_begin; j0 < j_comp_end; j0 += 16) {
+            const int j = j0 + (lane & 15);
+            {
+                const int jn = j + 16;
+                braw_load<KSTEPS, KE4M3>(kb0 + (int64_t)jn * kstride_bytes, jn < j_comp_end, nxt, lane);
+            }
+            bf16x8 bv[KSTEPS];
+            braw_widen<KSTEPS, KE4M3>(cur, bv);
+            f32x4 acc[kMT];
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][s], bv[s], acc[mt], 0, 0, 0);
+            float part[kMT];
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt) {
+                float t = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float z = acc[mt][e];
+                    t = fmaf(wvv[mt][e], FAST_RELU ? fmaxf(z, 0.f) : relu_keep_nonfinite(z), t);
+                }
+                part[mt] = t;
+            }
+            if constexpr (H >= 16) {
+                constexpr int tpq = H / 16;
+#pragma unroll
+                for (int q = 0; q < QPG; ++q) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int t = 0; t < tpq; ++t) v += part[q * tpq + t];
+                    v += __shfl_xor(v, 16);
+                    v += __shfl_xor(v, 32);
+                    const int qi = i0 + q;
+                    if (lane < 16 && qi < p.n_q) {
+                        const int Lh = __shfl(Lq, q);
+                        const bool vis = j < Lh;
+                        if (j < j_end && (vis || a.fill_invisible))
+                            a.scores[(int64_t)(b * p.n_q + qi) * a.row_stride + j] = vis ? v : -INFINITY;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt) {
+                    float v = part[mt];
+                    int qloc;
+                    if constexpr (H == 8) {
+                        v += __shfl_xor(v, 16);
+                        qloc = 2 * mt + (lane >> 5);
+                    } else {
+                        qloc = 4 * mt + (lane >> 4);
+                    }
+                    const int Lh = __shfl(Lq, qloc);
+                    const int qi = i0 + qloc;
+                    const bool writer = (H == 8) ? ((lane & 16) == 0) : true;
+                    if (writer && qi < p.n_q) {
+                        const bool vis = j < Lh;
+                        if (j < j_end && (vis || a.fill_invisible))
+                            a.scores[(int64_t)(b * p.n_q + qi) * a.row_stride + j] = vis ? v : -INFINITY;
+                    }
+                }
+            }
+            cur = nxt;
+        }
+    }
+    if (a.fill_invisible) {
+        // positions of the range past the computed tiles: beyond every visible history of the
+        // group (invisible positions inside computed tiles were written above)
+        const int start = j_begin < j_comp_end ? j_begin + ((j_comp_end - j_begin + 15) / 16) * 16 : j_begin;
+        for (int q = 0; q < QPG; ++q) {
+            const int qi = i0 + q;
+            if (qi >= p.n_q) break;
+            float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
+            for (int j = start + lane; j < j_end; j += 64) row[j] = -INFINITY;
+        }
+    }
+}
+
+// Non-finite check of the index inputs a query row can see (bf16 index queries with bf16
+// or e4m3 index keys, d_idx a multiple of 16): valid query rows of q_idx and w, and index
+// keys below the longest visible history of each batch.  16-byte chunks; bf16 values are
+// non-finite when their exponent bits are all ones, e4m3 bytes when their low seven bits
+// are (0x7f / 0xff, the format's only non-finite codes).
+__device__ __forceinline__ bool bf16x2_nonfinite(uint32_t w) {
+    return ((w & 0x7f80u) == 0x7f80u) || ((w & 0x7f800000u) == 0x7f800000u);
+}
+__device__ __forceinline__ bool e4m3x4_nan(uint32_t w) {
+    const uint32_t t = w & 0x7f7f7f7fu;            // a byte is 0x7f exactly when adding 1
+    return ((t + 0x01010101u) & 0x80808080u) != 0;  // carries into its top bit
+}
+
+__global__ void __launch_bounds__(256) index_finite_check(IndexerArgs a) {
+    const sa_problem& p = a.p;
+    const int b = blockIdx.y;
+    int kl = p.kv_len ? p.kv_len[b] : p.n_kv;
+    kl = kl < 0 ? 0 : (kl > p.n_kv ? p.n_kv : kl);
+    const long qp0 = p.q_pos0 ? p.q_pos0[b] : 0;
+    if (qp0 >= kl) return;  // no valid query row in this batch
+    const int Lb = p.causal ? (int)min((long)kl, qp0 + p.n_q) : kl;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    bool bad = false;
+    const long tid = (long)blockIdx.x * 256 + threadIdx.x, nth = (long)gridDim.x * 256;
+    const bool e4 = a.k.dtype == SA_FP8_E4M3;
+    const int kch = p.d_idx * (e4 ? 1 : 2) / 16;  // 16-byte chunks per key row
+    const uint8_t* kb = static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (e4 ? 1 : 2);
+    for (long e = tid; e < (long)Lb * kch; e += nth) {
+        const long j = e / kch;
+        const int c = (int)(e % kch);
+        const uint4 u = *reinterpret_cast<const uint4*>(kb + j * a.k.s1 * (e4 ? 1 : 2) + 16 * c);
+        if (e4) bad |= e4m3x4_nan(u.x) | e4m3x4_nan(u.y) | e4m3x4_nan(u.z) | e4m3x4_nan(u.w);
+        else bad |= bf16x2_nonfinite(u.x) | bf16x2_nonfinite(u.y) | bf16x2_nonfinite(u.z) | bf16x2_nonfinite(u.w);
+    }
+    const int qch = p.d_idx / 8;  // 16-byte chunks per index-head vector
+    const long per_row = (long)p.Hidx * qch;
+    for (long e = tid; e < (long)p.n_q * per_row; e += nth) {
+        const int i = (int)(e / per_row);
+        if (visible_len(R, b, i) == 0) continue;
+        const int h = (int)((e % per_row) / qch), c = (int)(e % qch);
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q.data) + b * a.q.s0 +
+                                                         (int64_t)i * a.q.s1 + h * a.q.s2 + 8 * c);
+        bad |= bf16x2_nonfinite(u.x) | bf16x2_nonfinite(u.y) | bf16x2_nonfinite(u.z) | bf16x2_nonfinite(u.w);
+    }
+    for (long e = tid; e < (long)p.n_q * p.Hidx; e += nth) {
+        const int i = (int)(e / p.Hidx), h = (int)(e % p.Hidx);
+        if (visible_len(R, b, i) == 0) continue;
+        if (!isfinite(static_cast<const float*>(a.w.data)[b * a.w.s0 + (int64_t)i * a.w.s1 + h])) bad = true;
+    }
+    if (bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+}
+
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
@@ -239,20 +474,36 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
                          (H == 4 || H == 8 || H == 16 || H == 32 || H == 64) &&
                          (D == 32 || D == 64 || D == 128);
     if (mfma_ok) {
-        const int n_groups = (p.n_q + (64 / H) - 1) / (64 / H);
-        const int n_chunks = (p.n_kv + kChunk - 1) / kChunk;
-        const long waves = (long)p.B * n_groups * n_chunks;
-        const unsigned blocks = (unsigned)((waves + 3) / 4);
+        const int QPG = 64 / H;
+        const int n_groups = (p.n_q + QPG - 1) / QPG;
+        // decode-like: too few query groups for four per workgroup
+        const bool decode = n_groups < 4 || (long)p.B * n_groups < 256;
+        const bool fast = a.status != nullptr && !decode;
+        if (fast) {
+            const dim3 gc((unsigned)max(1L, min(512L, 65536L / p.B)), p.B);
+            hipLaunchKernelGGL(index_finite_check, gc, dim3(256), 0, s, a);
+        }
+        const int rng_len = decode ? 2048 : 1024;
+        const int n_rng = (p.n_kv + rng_len - 1) / rng_len;
+        const int n_qblk = (n_groups + 3) / 4;
+        const long wgs = decode ? (long)p.B * n_groups * n_rng : (long)p.B * n_qblk * n_rng;
         const bool e4 = a.k.dtype == SA_FP8_E4M3;
-#define SA_IDX_H(KS, E4, HH)                                                                               \
-    if (H == HH) hipLaunchKernelGGL((indexer_mfma<KS, E4, HH>), dim3(blocks), dim3(256), 0, s, a, n_groups, n_chunks)
-#define SA_IDX_KS(KS, E4) \
-    do { SA_IDX_H(KS, E4, 4); SA_IDX_H(KS, E4, 8); SA_IDX_H(KS, E4, 16); SA_IDX_H(KS, E4, 32); SA_IDX_H(KS, E4, 64); } while (0)
-        if (D == 32) { if (e4) SA_IDX_KS(1, true); else SA_IDX_KS(1, false); }
-        else if (D == 64) { if (e4) SA_IDX_KS(2, true); else SA_IDX_KS(2, false); }
-        else { if (e4) SA_IDX_KS(4, true); else SA_IDX_KS(4, false); }
-#undef SA_IDX_KS
-#undef SA_IDX_H
+#define SA_IDX2(KS, E4, HH)                                                                                  \
+    if (H == HH) {                                                                                           \
+        if (decode) hipLaunchKernelGGL((indexer_mfma2<KS, E4, HH, true, false>), dim3((unsigned)wgs), dim3(256), 0, s, \
+                                       a, n_groups, n_qblk, n_rng, rng_len);                                 \
+        else if (fast) hipLaunchKernelGGL((indexer_mfma2<KS, E4, HH, false, true>), dim3((unsigned)wgs), dim3(256), 0, \
+                                          s, a, n_groups, n_qblk, n_rng, rng_len);                           \
+        else hipLaunchKernelGGL((indexer_mfma2<KS, E4, HH, false, false>), dim3((unsigned)wgs), dim3(256), 0, s, a, \
+                                n_groups, n_qblk, n_rng, rng_len);                                           \
+    }
+#define SA_IDX2_KS(KS, E4) \
+    do { SA_IDX2(KS, E4, 4) SA_IDX2(KS, E4, 8) SA_IDX2(KS, E4, 16) SA_IDX2(KS, E4, 32) SA_IDX2(KS, E4, 64) } while (0)
+        if (D == 32) { if (e4) SA_IDX2_KS(1, true); else SA_IDX2_KS(1, false); }
+        else if (D == 64) { if (e4) SA_IDX2_KS(2, true); else SA_IDX2_KS(2, false); }
+        else { if (e4) SA_IDX2_KS(4, true); else SA_IDX2_KS(4, false); }
+#undef SA_IDX2_KS
+#undef SA_IDX2
         return hipGetLastError();
     }
     dim3 grid(p.B * p.n_q, (p.n_kv + 255) / 256);

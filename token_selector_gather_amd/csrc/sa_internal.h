@@ -40,6 +40,9 @@ struct IndexerArgs {
     float* scores;
     int64_t row_stride;  // floats between consecutive rows of scores
     int fill_invisible;  // 1: write -inf into every invisible entry of [0, n_kv)
+    Status* status;      // fused call: non-finite index inputs are reported here by a pre-pass,
+                         // and the score kernel may clip NaN with a plain max; null: the score
+                         // kernel keeps NaN / -inf dot products non-finite in the scores
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 
