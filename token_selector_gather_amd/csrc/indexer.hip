@@ -244,13 +244,23 @@ struct BRaw<KSTEPS, true> { uint2 v[KSTEPS]; };
 template <int KSTEPS>
 struct BRaw<KSTEPS, false> { uint4 v[KSTEPS]; };
 
+// Key fragment of one 16-key tile: raw buffer loads on the batch's key rows, so an invalid
+// row (offset past the resource) reads as zeros without a branch and the compiler can count
+// outstanding loads exactly.
 template <int KSTEPS, bool KE4M3>
-__device__ __forceinline__ void braw_load(const uint8_t* kb, bool ok, BRaw<KSTEPS, KE4M3>& r, int lane) {
-    const int dof = 8 * (lane >> 4);
+__device__ __forceinline__ void braw_load(__amdgpu_buffer_rsrc_t rs, uint32_t row_off, BRaw<KSTEPS, KE4M3>& r,
+                                          int lane) {
+    const uint32_t dof = 8u * (lane >> 4) * (KE4M3 ? 1u : 2u);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-        if constexpr (KE4M3) r.v[s] = ok ? *reinterpret_cast<const uint2*>(kb + 32 * s + dof) : make_uint2(0, 0);
-        else r.v[s] = ok ? *reinterpret_cast<const uint4*>(kb + 2 * (32 * s + dof)) : make_uint4(0, 0, 0, 0);
+        const uint32_t off = row_off + (uint32_t)(32 * s) * (KE4M3 ? 1u : 2u) + dof;
+        if constexpr (KE4M3) {
+            auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+            r.v[s] = make_uint2(v[0], v[1]);
+        } else {
+            auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            r.v[s] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
     }
 }
 
@@ -294,6 +304,8 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
         j_begin = rng * rng_len;
         j_end = min(j_begin + rng_len, p.n_kv);
     }
+    g = __builtin_amdgcn_readfirstlane(g);  // wave-uniform (wave index and block index only)
+    b = __builtin_amdgcn_readfirstlane(b);
     if (g >= n_groups || j_begin >= p.n_kv) return;
     const int i0 = g * QPG;
     const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
@@ -302,7 +314,10 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
     int Lmax = Lq;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Lmax = max(Lmax, __shfl_xor(Lmax, o));
-    const int j_comp_end = min(j_end, Lmax);
+    // wave-uniform by construction; say so, so that the key resource below lives in SGPRs
+    j_begin = __builtin_amdgcn_readfirstlane(j_begin);
+    j_end = __builtin_amdgcn_readfirstlane(j_end);
+    const int j_comp_end = __builtin_amdgcn_readfirstlane(min(j_end, Lmax));
 
     if (j_begin < j_comp_end) {
         bf16x8 av[kMT][KSTEPS];
@@ -325,19 +340,24 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
                 wvv[mt][e] = q2 < p.n_q ? static_cast<const float*>(a.w.data)[b * a.w.s0 + q2 * a.w.s1 + h2] : 0.f;
             }
         }
-        const int64_t kstride_bytes = a.k.s1 * (KE4M3 ? 1 : 2);
-        const uint8_t* kb0 = static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2);
-        BRaw<KSTEPS, KE4M3> cur, nxt;
-        {
-            const int j = j_begin + (lane & 15);
-            braw_load<KSTEPS, KE4M3>(kb0 + (int64_t)j * kstride_bytes, j < j_comp_end, cur, lane);
-        }
-        for (int j0 = j_begin; j0 < j_comp_end; j0 += 16) {
+        const uint32_t kstride_bytes = (uint32_t)(a.k.s1 * (KE4M3 ? 1 : 2));
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2)), (short)0,
+            (int)((uint32_t)j_comp_end * kstride_bytes), 0x00020000);
+        // score rows of this wave's query group; lanes that write nothing store out of range
+        const int nrows = min(QPG, p.n_q - i0);
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            a.scores + (int64_t)(b * p.n_q + i0) * a.row_stride, (short)0,
+            (int)((uint32_t)nrows * (uint32_t)a.row_stride * 4u), 0x00020000);
+        // rows at or past j_comp_end lie outside the resource and read as zeros
+        auto row_off = [&](int j) -> uint32_t { return j < j_comp_end ? (uint32_t)j * kstride_bytes : 0x80000000u; };
+        // three key buffers in fixed roles (no register copies of in-flight loads), each
+        // filled two tiles before it is multiplied
+        BRaw<KSTEPS, KE4M3> ba, bb, bc;
+        braw_load<KSTEPS, KE4M3>(krs, row_off(j_begin + (lane & 15)), ba, lane);
+        braw_load<KSTEPS, KE4M3>(krs, row_off(j_begin + 16 + (lane & 15)), bb, lane);
+        auto tile = [&](const BRaw<KSTEPS, KE4M3>& cur, const int j0) {
             const int j = j0 + (lane & 15);
-            {
-                const int jn = j + 16;
-                braw_load<KSTEPS, KE4M3>(kb0 + (int64_t)jn * kstride_bytes, jn < j_comp_end, nxt, lane);
-            }
             bf16x8 bv[KSTEPS];
             braw_widen<KSTEPS, KE4M3>(cur, bv);
             f32x4 acc[kMT];
@@ -368,13 +388,11 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
                     for (int t = 0; t < tpq; ++t) v += part[q * tpq + t];
                     v += __shfl_xor(v, 16);
                     v += __shfl_xor(v, 32);
-                    const int qi = i0 + q;
-                    if (lane < 16 && qi < p.n_q) {
-                        const int Lh = __shfl(Lq, q);
-                        const bool vis = j < Lh;
-                        if (j < j_end && (vis || a.fill_invisible))
-                            a.scores[(int64_t)(b * p.n_q + qi) * a.row_stride + j] = vis ? v : -INFINITY;
-                    }
+                    const int Lh = __shfl(Lq, q);
+                    const bool vis = j < Lh;
+                    const bool wr = lane < 16 && i0 + q < p.n_q && j < j_end && (vis || a.fill_invisible);
+                    __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                                                          wr ? (uint32_t)(q * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
                 }
             } else {
 #pragma unroll
@@ -388,16 +406,23 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
                         qloc = 4 * mt + (lane >> 4);
                     }
                     const int Lh = __shfl(Lq, qloc);
-                    const int qi = i0 + qloc;
                     const bool writer = (H == 8) ? ((lane & 16) == 0) : true;
-                    if (writer && qi < p.n_q) {
-                        const bool vis = j < Lh;
-                        if (j < j_end && (vis || a.fill_invisible))
-                            a.scores[(int64_t)(b * p.n_q + qi) * a.row_stride + j] = vis ? v : -INFINITY;
-                    }
+                    const bool vis = j < Lh;
+                    const bool wr = writer && i0 + qloc < p.n_q && j < j_end && (vis || a.fill_invisible);
+                    __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                                                          wr ? (uint32_t)(qloc * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
                 }
             }
-            cur = nxt;
+        };
+        for (int j0 = j_begin; j0 < j_comp_end; j0 += 48) {
+            braw_load<KSTEPS, KE4M3>(krs, row_off(j0 + 32 + (lane & 15)), bc, lane);
+            tile(ba, j0);
+            if (j0 + 16 >= j_comp_end) break;
+            braw_load<KSTEPS, KE4M3>(krs, row_off(j0 + 48 + (lane & 15)), ba, lane);
+            tile(bb, j0 + 16);
+            if (j0 + 32 >= j_comp_end) break;
+            braw_load<KSTEPS, KE4M3>(krs, row_off(j0 + 64 + (lane & 15)), bb, lane);
+            tile(bc, j0 + 32);
         }
     }
     if (a.fill_invisible) {
@@ -405,6 +430,235 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
         // group (invisible positions inside computed tiles were written above)
         const int start = j_begin < j_comp_end ? j_begin + ((j_comp_end - j_begin + 15) / 16) * 16 : j_begin;
         for (int q = 0; q < QPG; ++q) {
+            const int qi = i0 + q;
+            if (qi >= p.n_q) break;
+            float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
+            for (int j = start + lane; j < j_end; j += 64) row[j] = -INFINITY;
+        }
+    }
+}
+
+// ----------------------------------------------------- matrix-core path, LDS key chunks
+// The workgroup streams its key range through LDS in chunks of 128 keys, double-buffered:
+// all 256 threads fetch the next chunk with 16-byte loads while the waves multiply the
+// current one, so the memory wait is paid once per chunk.  Prefill: wave w owns query
+// group qb*4 + w (all four 16-row M-tiles) and the four groups share every chunk.
+// Decode (64 index heads, one query per group): wave w owns heads 16w..16w+15 of the
+// workgroup's query; the four 16-head partial sums of each position meet in LDS and are
+// added in the fixed order 0+1+2+3.  Key rows are padded in LDS (8 bytes for e4m3, 16 for
+// bf16) so the 16 rows a fragment load touches fall in different banks.
+constexpr int kCK = 128;  // keys per LDS chunk
+
+template <int KSTEPS, bool KE4M3, int H, bool DECODE, bool FAST_RELU>
+__global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups, int n_qblk, int n_rng, int rng_len) {
+    constexpr int D = 32 * KSTEPS;
+    constexpr int RB = D * (KE4M3 ? 1 : 2);      // key row bytes
+    constexpr int RBP = RB + (KE4M3 ? 8 : 16);    // padded LDS row pitch (keeps fragment alignment)
+    constexpr int U16 = kCK * RB / 16;            // 16-byte pieces per chunk
+    constexpr int PPT = U16 / 256;                // pieces per thread
+    constexpr int QPG = 64 / H;
+    constexpr int MW = DECODE ? 1 : kMT;          // M-tiles per wave
+    static_assert(!DECODE || H == 64, "decode layout splits the 64 index heads of one query");
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kCK * RBP];
+    __shared__ float red[DECODE ? 4 * kCK : 1];
+
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long wg = blockIdx.x;
+    const int rng = (int)(wg % n_rng);
+    const long rest = wg / n_rng;
+    int b, g;
+    if (DECODE) {
+        g = (int)(rest % n_groups);
+        b = (int)(rest / n_groups);
+    } else {
+        const int qb = n_qblk - 1 - (int)(rest % n_qblk);  // longest causal histories first
+        b = (int)(rest / n_qblk);
+        g = qb * 4 + wv;
+    }
+    const int j_begin = rng * rng_len;
+    const int j_end = min(j_begin + rng_len, p.n_kv);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    // visible lengths: lane q of a wave holds query q of its group
+    const int i0 = g * QPG;
+    int Lq = 0;
+    if (g < n_groups && lane < QPG && i0 + lane < p.n_q) Lq = visible_len(R, b, i0 + lane);
+    int Lw = Lq;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Lw = max(Lw, __shfl_xor(Lw, o));
+    // workgroup-wide end of the keys worth computing
+    __shared__ int s_L[4];
+    if (lane == 0) s_L[wv] = Lw;
+    __syncthreads();
+    const int Lwg = max(max(s_L[0], s_L[1]), max(s_L[2], s_L[3]));
+    const int j_comp_end = min(j_end, Lwg);
+    const bool wave_live = g < n_groups;
+
+    if (j_begin < j_comp_end) {
+        // this wave's A fragments and head weights
+        bf16x8 av[MW][KSTEPS];
+        float wvv[MW][4];
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            const int mt = DECODE ? wv : m;
+            const int r = 16 * mt + (lane & 15);
+            const int qi = i0 + r / H, h = r % H;
+            const bool ok = wave_live && qi < p.n_q;
+            const uint16_t* qb = static_cast<const uint16_t*>(a.q.data) + (ok ? (b * a.q.s0 + qi * a.q.s1 + h * a.q.s2) : 0);
+#pragma unroll
+            for (int s2 = 0; s2 < KSTEPS; ++s2) {
+                uint4 u = ok ? *reinterpret_cast<const uint4*>(qb + 32 * s2 + 8 * (lane >> 4)) : make_uint4(0, 0, 0, 0);
+                av[m][s2] = __builtin_bit_cast(bf16x8, u);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * mt + 4 * (lane >> 4) + e;
+                const int q2 = i0 + rr / H, h2 = rr % H;
+                wvv[m][e] = (wave_live && q2 < p.n_q) ? static_cast<const float*>(a.w.data)[b * a.w.s0 + q2 * a.w.s1 + h2] : 0.f;
+            }
+        }
+        const uint32_t kstride_bytes = (uint32_t)(a.k.s1 * (KE4M3 ? 1 : 2));
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2)), (short)0,
+            (int)((uint32_t)j_comp_end * kstride_bytes), 0x00020000);
+        const int nrows = wave_live ? min(QPG, p.n_q - i0) : 0;
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            a.scores + (int64_t)(b * p.n_q + (wave_live ? i0 : 0)) * a.row_stride, (short)0,
+            (int)((uint32_t)nrows * (uint32_t)a.row_stride * 4u), 0x00020000);
+
+        uint4 stage[PPT];
+        auto fetch = [&](int c) {
+#pragma unroll
+            for (int e = 0; e < PPT; ++e) {
+                const int u = threadIdx.x + 256 * e;
+                const int r = u / (RB / 16), col = u % (RB / 16);
+                const int j = j_begin + c * kCK + r;
+                const uint32_t off = j < j_comp_end ? (uint32_t)j * kstride_bytes + 16u * col : 0x80000000u;
+                auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+                stage[e] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        };
+        auto commit = [&](int buf) {
+#pragma unroll
+            for (int e = 0; e < PPT; ++e) {
+                const int u = threadIdx.x + 256 * e;
+                const int r = u / (RB / 16), col = u % (RB / 16);
+                if constexpr (RBP % 16 == 0) {
+                    *reinterpret_cast<uint4*>(&kbuf[buf][r * RBP + 16 * col]) = stage[e];
+                } else {
+                    *reinterpret_cast<uint2*>(&kbuf[buf][r * RBP + 16 * col]) = make_uint2(stage[e].x, stage[e].y);
+                    *reinterpret_cast<uint2*>(&kbuf[buf][r * RBP + 16 * col + 8]) = make_uint2(stage[e].z, stage[e].w);
+                }
+            }
+        };
+        const int nch = (j_comp_end - j_begin + kCK - 1) / kCK;
+        fetch(0);
+        commit(0);
+        __syncthreads();
+        for (int c = 0; c < nch; ++c) {
+            const int buf = c & 1;
+            if (c + 1 < nch) fetch(c + 1);
+            const int cbase = j_begin + c * kCK;
+            const int ntile = min(kCK, j_comp_end - cbase + 15) / 16;
+            for (int tI = 0; tI < ntile; ++tI) {
+                const int jl = 16 * tI + (lane & 15);
+                const int j = cbase + jl;
+                bf16x8 bv[KSTEPS];
+                const uint8_t* kr = &kbuf[buf][jl * RBP + 8 * (lane >> 4) * (KE4M3 ? 1 : 2)];
+#pragma unroll
+                for (int s2 = 0; s2 < KSTEPS; ++s2) {
+                    if constexpr (KE4M3) {
+                        const uint2 u = *reinterpret_cast<const uint2*>(kr + 32 * s2);
+                        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.x, 1.0f, false);
+                        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.x, 1.0f, true);
+                        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.y, 1.0f, false);
+                        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.y, 1.0f, true);
+                        bv[s2] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                    } else {
+                        bv[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 64 * s2));
+                    }
+                }
+                f32x4 acc[MW];
+#pragma unroll
+                for (int m = 0; m < MW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KSTEPS; ++s2)
+#pragma unroll
+                    for (int m = 0; m < MW; ++m)
+                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][s2], bv[s2], acc[m], 0, 0, 0);
+                float part[MW];
+#pragma unroll
+                for (int m = 0; m < MW; ++m) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float z = acc[m][e];
+                        t = fmaf(wvv[m][e], FAST_RELU ? fmaxf(z, 0.f) : relu_keep_nonfinite(z), t);
+                    }
+                    part[m] = t;
+                }
+                if constexpr (DECODE) {
+                    float v = part[0];
+                    v += __shfl_xor(v, 16);
+                    v += __shfl_xor(v, 32);
+                    if (lane < 16) red[wv * kCK + jl] = v;
+                } else if constexpr (H >= 16) {
+                    constexpr int tpq = H / 16;
+#pragma unroll
+                    for (int q = 0; q < QPG; ++q) {
+                        float v = 0.f;
+#pragma unroll
+                        for (int t = 0; t < tpq; ++t) v += part[q * tpq + t];
+                        v += __shfl_xor(v, 16);
+                        v += __shfl_xor(v, 32);
+                        const int Lh = __shfl(Lq, q);
+                        const bool vis = j < Lh;
+                        const bool wr = wave_live && lane < 16 && i0 + q < p.n_q && j < j_end && (vis || a.fill_invisible);
+                        __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                                                              wr ? (uint32_t)(q * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt) {
+                        float v = part[mt];
+                        int qloc;
+                        if constexpr (H == 8) {
+                            v += __shfl_xor(v, 16);
+                            qloc = 2 * mt + (lane >> 5);
+                        } else {
+                            qloc = 4 * mt + (lane >> 4);
+                        }
+                        const int Lh = __shfl(Lq, qloc);
+                        const bool writer = (H == 8) ? ((lane & 16) == 0) : true;
+                        const bool vis = j < Lh;
+                        const bool wr = wave_live && writer && i0 + qloc < p.n_q && j < j_end && (vis || a.fill_invisible);
+                        __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                                                              wr ? (uint32_t)(qloc * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
+                    }
+                }
+            }
+            if constexpr (DECODE) {
+                __syncthreads();
+                if (threadIdx.x < kCK) {
+                    const int j = cbase + threadIdx.x;
+                    const float v = ((red[threadIdx.x] + red[kCK + threadIdx.x]) + red[2 * kCK + threadIdx.x]) +
+                                    red[3 * kCK + threadIdx.x];
+                    const int L0 = __shfl(Lq, 0);  // lane 0 of each wave holds the query's length
+                    const bool vis = j < L0;
+                    const bool wr = (int)threadIdx.x < 16 * ntile && j < j_end && (vis || a.fill_invisible) && i0 < p.n_q;
+                    __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs, wr ? (uint32_t)j * 4u : 0x80000000u, 0, 0);
+                }
+            }
+            if (c + 1 < nch) commit(buf ^ 1);
+            __syncthreads();
+        }
+    }
+    if (a.fill_invisible && wave_live) {
+        // positions past the computed chunks (or the whole range when nothing was computed)
+        const int start = j_begin < j_comp_end ? j_begin + ((j_comp_end - j_begin + 15) / 16) * 16 : j_begin;
+        const int qs = DECODE ? (wv == 0 ? 0 : QPG) : 0;  // in decode only wave 0 fills
+        for (int q = qs; q < QPG; ++q) {
             const int qi = i0 + q;
             if (qi >= p.n_q) break;
             float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
@@ -476,8 +730,8 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     if (mfma_ok) {
         const int QPG = 64 / H;
         const int n_groups = (p.n_q + QPG - 1) / QPG;
-        // decode-like: too few query groups for four per workgroup
-        const bool decode = n_groups < 4 || (long)p.B * n_groups < 256;
+        // decode layout (the four waves split one query's 64 index heads) for few query groups
+        const bool decode = H == 64 && (long)p.B * n_groups < 1024;
         const bool fast = a.status != nullptr && !decode;
         if (fast) {
             const dim3 gc((unsigned)max(1L, min(512L, 65536L / p.B)), p.B);
@@ -488,22 +742,25 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
         const int n_qblk = (n_groups + 3) / 4;
         const long wgs = decode ? (long)p.B * n_groups * n_rng : (long)p.B * n_qblk * n_rng;
         const bool e4 = a.k.dtype == SA_FP8_E4M3;
-#define SA_IDX2(KS, E4, HH)                                                                                  \
-    if (H == HH) {                                                                                           \
-        if (decode) hipLaunchKernelGGL((indexer_mfma2<KS, E4, HH, true, false>), dim3((unsigned)wgs), dim3(256), 0, s, \
-                                       a, n_groups, n_qblk, n_rng, rng_len);                                 \
-        else if (fast) hipLaunchKernelGGL((indexer_mfma2<KS, E4, HH, false, true>), dim3((unsigned)wgs), dim3(256), 0, \
-                                          s, a, n_groups, n_qblk, n_rng, rng_len);                           \
-        else hipLaunchKernelGGL((indexer_mfma2<KS, E4, HH, false, false>), dim3((unsigned)wgs), dim3(256), 0, s, a, \
-                                n_groups, n_qblk, n_rng, rng_len);                                           \
+        const dim3 gw((unsigned)wgs), bw(256);
+#define SA_IDX3(KS, E4, HH)                                                                                   \
+    if (H == HH) {                                                                                            \
+        if constexpr (HH == 64) {                                                                             \
+            if (decode) {                                                                                     \
+                hipLaunchKernelGGL((indexer_mfma3<KS, E4, HH, true, false>), gw, bw, 0, s, a, n_groups, n_qblk, n_rng, rng_len); \
+                return hipGetLastError();                                                                     \
+            }                                                                                                 \
+        }                                                                                                     \
+        if (fast) hipLaunchKernelGGL((indexer_mfma3<KS, E4, HH, false, true>), gw, bw, 0, s, a, n_groups, n_qblk, n_rng, rng_len); \
+        else hipLaunchKernelGGL((indexer_mfma3<KS, E4, HH, false, false>), gw, bw, 0, s, a, n_groups, n_qblk, n_rng, rng_len);    \
     }
-#define SA_IDX2_KS(KS, E4) \
-    do { SA_IDX2(KS, E4, 4) SA_IDX2(KS, E4, 8) SA_IDX2(KS, E4, 16) SA_IDX2(KS, E4, 32) SA_IDX2(KS, E4, 64) } while (0)
-        if (D == 32) { if (e4) SA_IDX2_KS(1, true); else SA_IDX2_KS(1, false); }
-        else if (D == 64) { if (e4) SA_IDX2_KS(2, true); else SA_IDX2_KS(2, false); }
-        else { if (e4) SA_IDX2_KS(4, true); else SA_IDX2_KS(4, false); }
-#undef SA_IDX2_KS
-#undef SA_IDX2
+#define SA_IDX3_KS(KS, E4) \
+    do { SA_IDX3(KS, E4, 4) SA_IDX3(KS, E4, 8) SA_IDX3(KS, E4, 16) SA_IDX3(KS, E4, 32) SA_IDX3(KS, E4, 64) } while (0)
+        if (D == 32) { if (e4) SA_IDX3_KS(1, true); else SA_IDX3_KS(1, false); }
+        else if (D == 64) { if (e4) SA_IDX3_KS(2, true); else SA_IDX3_KS(2, false); }
+        else { if (e4) SA_IDX3_KS(4, true); else SA_IDX3_KS(4, false); }
+#undef SA_IDX3_KS
+#undef SA_IDX3
         return hipGetLastError();
     }
     dim3 grid(p.B * p.n_q, (p.n_kv + 255) / 256);
