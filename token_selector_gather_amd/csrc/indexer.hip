@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
                     const int Lh = __shfl(Lq, q);
                     const bool vis = j < Lh;
                     const bool wr = lane < 16 && i0 + q < p.n_q && j < j_end && (vis || a.fill_invisible);
-                    __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vis ? v : -INFINITY), srs,
                                                           wr ? (uint32_t)(q * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
                 }
             } else {
@@ -409,7 +409,7 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
                     const bool writer = (H == 8) ? ((lane & 16) == 0) : true;
                     const bool vis = j < Lh;
                     const bool wr = writer && i0 + qloc < p.n_q && j < j_end && (vis || a.fill_invisible);
-                    __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vis ? v : -INFINITY), srs,
                                                           wr ? (uint32_t)(qloc * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
                 }
             }
@@ -615,7 +615,7 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                         const int Lh = __shfl(Lq, q);
                         const bool vis = j < Lh;
                         const bool wr = wave_live && lane < 16 && i0 + q < p.n_q && j < j_end && (vis || a.fill_invisible);
-                        __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vis ? v : -INFINITY), srs,
                                                               wr ? (uint32_t)(q * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
                     }
                 } else {
@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                         const bool writer = (H == 8) ? ((lane & 16) == 0) : true;
                         const bool vis = j < Lh;
                         const bool wr = wave_live && writer && i0 + qloc < p.n_q && j < j_end && (vis || a.fill_invisible);
-                        __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs,
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vis ? v : -INFINITY), srs,
                                                               wr ? (uint32_t)(qloc * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
                     }
                 }
@@ -647,7 +647,7 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                     const int L0 = __shfl(Lq, 0);  // lane 0 of each wave holds the query's length
                     const bool vis = j < L0;
                     const bool wr = (int)threadIdx.x < 16 * ntile && j < j_end && (vis || a.fill_invisible) && i0 < p.n_q;
-                    __builtin_amdgcn_raw_buffer_store_b32(vis ? v : -INFINITY, srs, wr ? (uint32_t)j * 4u : 0x80000000u, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vis ? v : -INFINITY), srs, wr ? (uint32_t)j * 4u : 0x80000000u, 0, 0);
                 }
             }
             if (c + 1 < nch) commit(buf ^ 1);
