@@ -452,10 +452,9 @@ constexpr int kCK = 128;  // keys per LDS chunk
 template <int KSTEPS, bool KE4M3, int H, bool DECODE, bool FAST_RELU>
 __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups, int n_qblk, int n_rng, int rng_len) {
     constexpr int D = 32 * KSTEPS;
-    constexpr int RB = D * (KE4M3 ? 1 : 2);      // key row bytes in memory
-    constexpr int RBL = 2 * D;                    // key row bytes in LDS (bf16; e4m3 widened at commit)
-    constexpr int RBP = RBL + 16;                 // padded LDS row pitch
-    constexpr int U16 = kCK * RB / 16;            // 16-byte pieces per chunk in memory
+    constexpr int RB = D * (KE4M3 ? 1 : 2);      // key row bytes
+    constexpr int RBP = RB + (KE4M3 ? 8 : 16);    // padded LDS row pitch (keeps fragment alignment)
+    constexpr int U16 = kCK * RB / 16;            // 16-byte pieces per chunk
     constexpr int PPT = U16 / 256;                // pieces per thread
     constexpr int QPG = 64 / H;
     constexpr int MW = DECODE ? 1 : kMT;          // M-tiles per wave
@@ -540,24 +539,16 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                 stage[e] = make_uint4(v[0], v[1], v[2], v[3]);
             }
         };
-        // LDS holds bf16 keys: e4m3 pieces (16 values) widen exactly once here, for all waves
         auto commit = [&](int buf) {
 #pragma unroll
             for (int e = 0; e < PPT; ++e) {
                 const int u = threadIdx.x + 256 * e;
                 const int r = u / (RB / 16), col = u % (RB / 16);
-                if constexpr (KE4M3) {
-                    const uint32_t w4[4] = {stage[e].x, stage[e].y, stage[e].z, stage[e].w};
-                    uint32_t o8[8];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        o8[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[q], 1.0f, false));
-                        o8[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[q], 1.0f, true));
-                    }
-                    *reinterpret_cast<uint4*>(&kbuf[buf][r * RBP + 32 * col]) = make_uint4(o8[0], o8[1], o8[2], o8[3]);
-                    *reinterpret_cast<uint4*>(&kbuf[buf][r * RBP + 32 * col + 16]) = make_uint4(o8[4], o8[5], o8[6], o8[7]);
-                } else {
+                if constexpr (RBP % 16 == 0) {
                     *reinterpret_cast<uint4*>(&kbuf[buf][r * RBP + 16 * col]) = stage[e];
+                } else {
+                    *reinterpret_cast<uint2*>(&kbuf[buf][r * RBP + 16 * col]) = make_uint2(stage[e].x, stage[e].y);
+                    *reinterpret_cast<uint2*>(&kbuf[buf][r * RBP + 16 * col + 8]) = make_uint2(stage[e].z, stage[e].w);
                 }
             }
         };
@@ -574,10 +565,20 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                 const int jl = 16 * tI + (lane & 15);
                 const int j = cbase + jl;
                 bf16x8 bv[KSTEPS];
-                const uint8_t* kr = &kbuf[buf][jl * RBP + 16 * (lane >> 4)];
+                const uint8_t* kr = &kbuf[buf][jl * RBP + 8 * (lane >> 4) * (KE4M3 ? 1 : 2)];
 #pragma unroll
-                for (int s2 = 0; s2 < KSTEPS; ++s2)
-                    bv[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 64 * s2));
+                for (int s2 = 0; s2 < KSTEPS; ++s2) {
+                    if constexpr (KE4M3) {
+                        const uint2 u = *reinterpret_cast<const uint2*>(kr + 32 * s2);
+                        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.x, 1.0f, false);
+                        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.x, 1.0f, true);
+                        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.y, 1.0f, false);
+                        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.y, 1.0f, true);
+                        bv[s2] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                    } else {
+                        bv[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 64 * s2));
+                    }
+                }
                 f32x4 acc[MW];
 #pragma unroll
                 for (int m = 0; m < MW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
