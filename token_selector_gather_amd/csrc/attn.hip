@@ -934,6 +934,293 @@ __global__ void __launch_bounds__(256) lse_merge(AttnArgs a) {
     if (a.lse && lane == 0) a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
+// ------------------------------------------------------------------- attn_mla_lds
+// Latent-head attention for 32-head groups (Hq/Hkv a multiple of 32, V = the first d_v
+// columns of K).  One workgroup per (query row, candidate split); wave w owns query heads
+// 32w..32w+31.  Gathered rows reach LDS through buffer loads that write LDS directly
+// (no staging registers), in a ring of three 32-row tiles so that two tiles are in
+// flight while one is consumed.  Per tile each wave runs S^T = K Q^T (v_mfma_f32_32x32x16
+// _bf16, Q^T fragments in registers) and O^T += V^T P^T, reading V^T out of the same
+// row-major tile with transposing LDS reads (ds_read_b64_tr_b16).  Each head's reference
+// maximum is fixed at its first valid tile, so the accumulators are never rescaled: any
+// reference gives the same softmax, and while no logit exceeds it by more than 64 (exp2
+// units) every probability and sum stays far inside fp32 range.  A set that breaks this
+// margin is run a second time against its true maximum, found during the first run.
+namespace mla {
+constexpr int T = 32;                  // rows per tile
+constexpr int DQK = 576, DV = 512;
+constexpr int CHR = DQK / 8;           // 16-byte chunks per row
+constexpr int ROWB = DQK * 2;          // bytes per row in LDS
+constexpr int TILE_B = T * ROWB;       // bytes per tile
+constexpr int NI_ALL = T * CHR / 64;   // 16-byte LDS-direct loads per tile, 64 lanes each
+constexpr int MAXE = 2048;             // candidates per workgroup
+constexpr float kLazy = 64.f;          // exp2 headroom above the reference maximum
+// Tile layout in LDS: 1 KB block k holds 16-byte chunks 2k and 2k+1 of all 32 rows, chunk
+// 2k + c of row r in slot 32 c + (r ^ 4c ^ 8 (k & 1)).  One LDS-direct load fills one
+// block, every lane keeps one row for a whole tile, and both the row reads of the K
+// operand and the 4-row transposing reads of the V operand are free of bank conflicts.
+__device__ __forceinline__ int slot_row(int r, int c, int k) { return r ^ (4 * c) ^ (8 * (k & 1)); }
+}  // namespace mla
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ v4s lds_tr_read(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 * lane.  Written as asm so
+// that the compiler does not order later LDS reads behind it: the kernel's own vmcnt waits
+// and barriers order every read of the written tile.
+__device__ __forceinline__ void lds_dma16(const v4i& rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "m0");
+}
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
+    using namespace mla;
+    constexpr int NI = NI_ALL / NW;    // loads per wave per tile
+    static_assert(NI * NW == NI_ALL, "tile loads must split evenly over the waves");
+    constexpr int KS = DQK / 16;       // k-steps of S^T
+    constexpr int MT = DV / 32;        // 32-row tiles of O^T
+    constexpr int PD = 4;              // LDS operand reads in flight ahead of the MFMA using them
+    __shared__ __attribute__((aligned(16))) uint8_t ring[3 * TILE_B];
+    __shared__ uint32_t s_off[MAXE];
+    __shared__ uint32_t s_mask[MAXE / T];
+
+    const sa_problem& p = a.p;
+    const int G = p.Hq / p.Hkv;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n32 = lane & 31, h = lane >> 5;
+    const int S = a.splits;
+    const long unit = blockIdx.x;
+    const int split = (int)(unit % S);
+    const long rowkv = unit / S;
+    const int hk = (int)(rowkv % p.Hkv);
+    const long row = rowkv / p.Hkv;
+    const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int head = hk * G + 32 * wv + n32;
+    const uint32_t rowb = (uint32_t)(a.K.s2 * 2);
+
+    const int per = (p.k + S - 1) / S;
+    const int e_begin = split * per;
+    const int ne = max(0, min(p.k, e_begin + per) - e_begin);
+    const int32_t* ix = a.idx + row * (int64_t)p.k + e_begin;
+    // byte offsets of the candidate rows (out-of-range offset for invalid entries, which
+    // the buffer loads turn into zero rows) and one validity bit per candidate
+    const int ne64 = (ne + 63) & ~63;
+    for (int e = threadIdx.x; e < ne64; e += 64 * NW) {
+        const int j = e < ne ? ix[e] : -1;
+        const bool ok = j >= 0 && j < L;
+        s_off[e] = ok ? (uint32_t)j * rowb : 0x80000000u;
+        const uint64_t bal = __ballot(ok);
+        if (lane == 0) {
+            s_mask[e >> 5] = (uint32_t)bal;
+            s_mask[(e >> 5) + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+    // Q^T fragments (B operand of S^T): head n32, d = 16 s + 8 h + 0..7
+    uint4 qf[KS];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + head * a.Q.s1 + (int64_t)i * a.Q.s2;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * h);
+    }
+    wait_vmcnt<0>();  // no vector-memory load of the compiler's own may be pending inside the tile loop
+    __syncthreads();
+    // tiles after the last one holding a valid candidate are never fetched
+    int nt;
+    {
+        const int ntiles = (ne + T - 1) / T;
+        const uint64_t any = __ballot(lane < ntiles && s_mask[lane] != 0u);
+        nt = any ? 64 - __builtin_clzll(any) : 0;
+    }
+
+    const char* kbase = static_cast<const char*>(a.K.data) + (b * a.K.s0 + hk * a.K.s1) * 2;
+    v4i krs;
+    krs[0] = (int)(uint32_t)(uintptr_t)kbase;
+    krs[1] = (int)(uint32_t)((uintptr_t)kbase >> 32);
+    krs[2] = (int)((int64_t)p.n_kv * rowb);
+    krs[3] = 0x00020000;
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+    // this lane's row in even and odd blocks and its chunk within the block
+    const int dcp = lane >> 5;
+    const int drow = slot_row(lane & 31, dcp, 0);
+    auto issue = [&](int tile) {
+        const uint32_t dst = ring_lds + (uint32_t)((tile % 3) * TILE_B);
+        const uint32_t* off = s_off + tile * T;
+        const uint32_t ve = off[drow] + 16u * dcp, vo = off[drow ^ 8] + 16u * dcp;
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+            const int k = wv + NW * ii;
+            lds_dma16(krs, dst + 1024u * (uint32_t)k, (k & 1) ? vo : ve, 32u * (uint32_t)k);
+        }
+    };
+
+    // K operand of k-step s (block s): row n32, chunk 2s + h
+    const int kadr_e = 16 * (32 * h + slot_row(n32, h, 0));
+    const int kadr_o = 16 * (32 * h + slot_row(n32, h, 1));
+    // V operand (transposing reads): this lane supplies row 16 s' + 8 e2 + 4 h + lane%16/4 and
+    // 8 bytes of chunk 4 mt + 2 g2 + c, c = lane%4/2 (block 2 mt + g2)
+    const int sl = lane & 15, g2 = (lane >> 4) & 1, vcp = (sl >> 1) & 1;
+    const int vbase = 1024 * g2 + 512 * vcp + 16 * (sl >> 2) + 64 * (h ^ vcp) + 8 * (sl & 1);
+    const int vadr_e0 = vbase + 128 * g2, vadr_e1 = vbase + 128 * (1 - g2);
+
+    f32x16 oacc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[t][e] = 0.f;
+    float m_ref = -INFINITY, m_all = -INFINITY, lsum = 0.f;
+    const float sl2 = a.scale * kLog2e;
+
+    for (int pass = 0; pass < 2; ++pass) {
+    bool over = false;
+    if (nt > 0) issue(0);
+    if (nt > 1) issue(1);
+    for (int t = 0; t < nt; ++t) {
+        if (t + 1 < nt) wait_vmcnt<NI>();
+        else wait_vmcnt<0>();
+        tile_barrier();
+        if (t + 2 < nt) issue(t + 2);
+        const uint32_t msk = s_mask[t];
+        const uint8_t* tb = ring + (t % 3) * TILE_B;
+        // S^T = K Q^T: lane holds S^T[pos 8 (e/4) + 4 h + e%4][head n32]
+        auto kread = [&](int s) {
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + ((s & 1) ? kadr_o : kadr_e) + 1024 * s));
+        };
+        f32x16 sa0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sa0[e] = 0.f;
+        bf16x8 kb[PD];
+#pragma unroll
+        for (int s = 0; s < PD; ++s) kb[s] = kread(s);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 cur = kb[s % PD];
+            if (s + PD < KS) kb[s % PD] = kread(s + PD);
+            sa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, qf[s]), sa0, 0, 0, 0);
+        }
+        // keep PD operand reads in flight: the scheduler would otherwise sink each read
+        // next to its MFMA to save registers
+        __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (s + PD < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        auto vread = [&](int j) {  // step j = 2 mt + s'
+            const int mt = j >> 1, s2 = j & 1;
+            const uint8_t* vb = tb + 2048 * mt + 256 * s2;
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lds_tr_read(vb + vadr_e0), lds_tr_read(vb + vadr_e1), 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+
+        const uint32_t mh = msk >> (4 * h);
+        float x[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int pr = 8 * (e >> 2) + (e & 3);
+            x[e] = ((mh >> pr) & 1u) ? sa0[e] * sl2 : -INFINITY;
+            tmax = fmaxf(tmax, x[e]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        if (m_ref == -INFINITY) m_ref = tmax;
+        m_all = fmaxf(m_all, tmax);
+        over |= tmax > m_ref + kLazy;
+        float ps = 0.f;
+        uint32_t pw[8];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            const float p0 = x[e] == -INFINITY ? 0.f : exp2f(x[e] - m_ref);
+            const float p1 = x[e + 1] == -INFINITY ? 0.f : exp2f(x[e + 1] - m_ref);
+            ps += p0 + p1;
+            const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+            pw[e >> 1] = __builtin_bit_cast(uint32_t, pk);
+        }
+        lsum += ps;
+        const bf16x8 pb0 = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        const bf16x8 pb1 = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+        bf16x8 vbuf[PD];
+#pragma unroll
+        for (int j = 0; j < PD; ++j) vbuf[j] = vread(j);
+        // O^T += V^T P^T; step j = 2 mt + s' covers positions 16 s' + {4h..4h+3, 8+4h..8+4h+3}
+#pragma unroll
+        for (int j = 0; j < 2 * MT; ++j) {
+            const bf16x8 cur = vbuf[j % PD];
+            if (j + PD < 2 * MT) vbuf[j % PD] = vread(j + PD);
+            oacc[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, (j & 1) ? pb1 : pb0, oacc[j >> 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 1);
+#pragma unroll
+        for (int j = 0; j < 2 * MT; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            if (j + PD < 2 * MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+    }
+    wait_vmcnt<0>();
+    if (!__syncthreads_or(over)) break;
+    // a probability left fp32 headroom: run the set again against the true maximum
+    m_ref = m_all;
+    lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[t][e] = 0.f;
+    }
+    // total exp-sum per head: lanes n32 and n32 + 32 hold disjoint positions
+    lsum += __shfl_xor(lsum, 32);
+    // lane holds O^T[d = 32 mt + 8 (e/4) + 4 h + e%4][head n32]
+    if (S == 1) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bf16x2 v01 = {(__bf16)(oacc[mt][4 * q] * inv), (__bf16)(oacc[mt][4 * q + 1] * inv)};
+                const bf16x2 v23 = {(__bf16)(oacc[mt][4 * q + 2] * inv), (__bf16)(oacc[mt][4 * q + 3] * inv)};
+                *reinterpret_cast<uint2*>(op + 32 * mt + 8 * q + 4 * h) =
+                    make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+            }
+        if (a.lse && h == 0)
+            a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = lsum > 0.f ? (m_ref + log2f(lsum)) * kLn2 : -INFINITY;
+    } else {
+        float* part = static_cast<float*>(a.partial);
+        const int64_t slot = (row * p.Hq + head) * (int64_t)S + split;
+        float* ml = part + slot * 2;
+        float* po = part + (int64_t)p.B * p.n_q * p.Hq * S * 2 + slot * DV;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(po + 32 * mt + 8 * q + 4 * h) =
+                    make_float4(oacc[mt][4 * q], oacc[mt][4 * q + 1], oacc[mt][4 * q + 2], oacc[mt][4 * q + 3]);
+        if (h == 0) {
+            ml[0] = m_ref;
+            ml[1] = lsum;
+        }
+    }
+}
+
 template <typename T, int LPR>
 hipError_t launch_rows_g(const AttnArgs& a, int G, unsigned blocks, hipStream_t s) {
     if (G == 1) hipLaunchKernelGGL((attn_rows<T, LPR, 1>), dim3(blocks), dim3(256), 0, s, a);
@@ -944,18 +1231,32 @@ hipError_t launch_rows_g(const AttnArgs& a, int G, unsigned blocks, hipStream_t 
 
 }  // namespace
 
+// The LDS-direct latent kernel: 32-head groups, V aliasing the first d_v columns of K,
+// 16-byte aligned rows, 32-bit row offsets and at most mla::MAXE candidates per split.
+static bool mla_lds_ok(const AttnArgs& a) {
+    const sa_problem& p = a.p;
+    const int G = p.Hq / p.Hkv;
+    const bool alias = a.V.data == a.K.data && a.V.s0 == a.K.s0 && a.V.s1 == a.K.s1 && a.V.s2 == a.K.s2;
+    const long per = (p.k + a.splits - 1) / a.splits;
+    return G % 32 == 0 && alias && a.K.s2 % 8 == 0 && ((uintptr_t)a.K.data & 15) == 0 &&
+           (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) && per <= mla::MAXE;
+}
+
 bool attn_uses_mla(const sa_problem& p, int dtype) {
     const int G = p.Hq / p.Hkv;
     return dtype == SA_BF16 && G % 16 == 0 && G <= 128 && p.d_qk == 576 && p.d_v == 512;
 }
 
 int attn_splits(const sa_problem& p) {
-    // enough workgroups to fill 256 CUs twice; at least 4 tiles of candidates per split
+    // about one workgroup per CU, at least 4 tiles of candidates per split, and at most
+    // mla::MAXE candidates per workgroup
     const long units = (long)p.B * p.n_q * p.Hkv;
-    long s = (512 + units - 1) / units;
+    long s = (256 + units - 1) / units;
     long cap = p.k / (4 * kTile);
     if (cap < 1) cap = 1;
     if (s > cap) s = cap;
+    const long need = (p.k + mla::MAXE - 1) / mla::MAXE;
+    if (s < need) s = need;
     if (s < 1) s = 1;
     return (int)s;
 }
@@ -971,7 +1272,17 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     if (attn_uses_mla(p, a.Q.dtype)) {
         const int G = p.Hq / p.Hkv;
         const long units = (long)p.B * p.n_q * p.Hkv * a.splits;
-        hipLaunchKernelGGL((attn_mla<576, 512>), dim3((unsigned)units), dim3(64 * (G / 16)), 0, s, a);
+#ifndef SA_MLA_VARIANT
+#define SA_MLA_VARIANT 2
+#endif
+        if (SA_MLA_VARIANT == 2 && mla_lds_ok(a)) {
+            if (G == 128) hipLaunchKernelGGL(attn_mla_lds<4>, dim3((unsigned)units), dim3(256), 0, s, a);
+            else if (G == 96) hipLaunchKernelGGL(attn_mla_lds<3>, dim3((unsigned)units), dim3(192), 0, s, a);
+            else if (G == 64) hipLaunchKernelGGL(attn_mla_lds<2>, dim3((unsigned)units), dim3(128), 0, s, a);
+            else hipLaunchKernelGGL(attn_mla_lds<1>, dim3((unsigned)units), dim3(64), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((attn_mla<576, 512>), dim3((unsigned)units), dim3(64 * (G / 16)), 0, s, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.splits == 1) return e;
         const long items = (long)p.B * p.n_q * p.Hq;
