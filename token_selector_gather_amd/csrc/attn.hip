@@ -955,11 +955,20 @@ constexpr int TILE_B = T * ROWB;       // bytes per tile
 constexpr int NI_ALL = T * CHR / 64;   // 16-byte LDS-direct loads per tile, 64 lanes each
 constexpr int MAXE = 2048;             // candidates per workgroup
 constexpr float kLazy = 64.f;          // exp2 headroom above the reference maximum
-// Tile layout in LDS: 1 KB block k holds 16-byte chunks 2k and 2k+1 of all 32 rows, chunk
-// 2k + c of row r in slot 32 c + (r ^ 4c ^ 8 (k & 1)).  One LDS-direct load fills one
-// block, every lane keeps one row for a whole tile, and both the row reads of the K
-// operand and the 4-row transposing reads of the V operand are free of bank conflicts.
-__device__ __forceinline__ int slot_row(int r, int c, int k) { return r ^ (4 * c) ^ (8 * (k & 1)); }
+// Tile layout in LDS (36 KB): 32 main blocks of 1 KB, block 4 rg + cg holding 16-byte chunks
+// 16 cg .. 16 cg + 15 of rows 4 rg .. 4 rg + 3 (row r at slot 16 (r & 3) + cslot(r, chunk % 16)),
+// then 4 tail blocks at 32 KB, tail block j holding chunks 64..71 of rows 8 j .. 8 j + 7 (row r
+// at slot 8 (r & 7) + ((chunk - 64) ^ tswz(r))).  One LDS-direct load fills one block from 4
+// (or 8) rows, so each load reads whole 128-byte lines; the swizzles make the 16-row reads of
+// the K operand and the 4-row transposing reads of the V operand free of bank conflicts.
+__device__ __forceinline__ int rswz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+__device__ __forceinline__ int cslot(int r, int c) { return c ^ rswz(r) ^ (8 * ((c >> 1) & 1)); }
+// chunk (0..15) of row r stored in slot y (inverse of cslot)
+__device__ __forceinline__ int cslot_inv(int r, int y) {
+    const int x = y ^ rswz(r);
+    return x ^ (8 * ((x >> 1) & 1));
+}
+__device__ __forceinline__ int tswz(int r) { return (r >> 1) & 7; }
 }  // namespace mla
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
@@ -970,6 +979,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
+
+// maximum over the lanes l, l^16, l^32, l^48 (lane swaps between rows, no LDS round trip)
+__device__ __forceinline__ float colmax4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// wait for this wave's LDS and scalar-memory operations only
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __device__ __forceinline__ void tile_barrier() {
     asm volatile("" ::: "memory");
@@ -997,17 +1017,21 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     using namespace mla;
     constexpr int NI = NI_ALL / NW;    // loads per wave per tile
     static_assert(NI * NW == NI_ALL, "tile loads must split evenly over the waves");
-    constexpr int KS = DQK / 16;       // k-steps of S^T
-    constexpr int MT = DV / 32;        // 32-row tiles of O^T
-    constexpr int PD = 4;              // LDS operand reads in flight ahead of the MFMA using them
+    constexpr int KS = DQK / 32;       // k-steps of S^T on 16x16x32 fragments
+    constexpr int MW = DV / 32 / NW;   // 32-row tiles of O^T (rows = d) owned by one wave
+    static_assert(MW * NW * 32 == DV, "the value columns must split evenly over the waves");
+    constexpr int PD = 3;              // k-steps of K operands read ahead of their MFMAs
+    constexpr int PB = 2 * NW * 1024;  // bytes of P^T fragments per tile
     __shared__ __attribute__((aligned(16))) uint8_t ring[3 * TILE_B];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * PB];
     __shared__ uint32_t s_off[MAXE];
     __shared__ uint32_t s_mask[MAXE / T];
+    __shared__ float s_ml[2][32 * NW];
 
     const sa_problem& p = a.p;
     const int G = p.Hq / p.Hkv;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n32 = lane & 31, h = lane >> 5;
+    const int n32 = lane & 31, h = lane >> 5, l15 = lane & 15, g = lane >> 4;
     const int S = a.splits;
     const long unit = blockIdx.x;
     const int split = (int)(unit % S);
@@ -1017,7 +1041,6 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
     const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
     const int L = visible_len(R, b, i);
-    const int head = hk * G + 32 * wv + n32;
     const uint32_t rowb = (uint32_t)(a.K.s2 * 2);
 
     const int per = (p.k + S - 1) / S;
@@ -1037,14 +1060,6 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
             s_mask[(e >> 5) + 1] = (uint32_t)(bal >> 32);
         }
     }
-    // Q^T fragments (B operand of S^T): head n32, d = 16 s + 8 h + 0..7
-    uint4 qf[KS];
-    {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + head * a.Q.s1 + (int64_t)i * a.Q.s2;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * h);
-    }
-    wait_vmcnt<0>();  // no vector-memory load of the compiler's own may be pending inside the tile loop
     __syncthreads();
     // tiles after the last one holding a valid candidate are never fetched
     int nt;
@@ -1054,6 +1069,16 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         nt = any ? 64 - __builtin_clzll(any) : 0;
     }
 
+    // Q^T fragments (B operand of S^T): head 32 wv + 16 nt + lane%16, d = 32 s + 8 (lane/16) + 0..7
+    uint4 qf[KS][2];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + (hk * G + 32 * wv + l15) * a.Q.s1 +
+                             (int64_t)i * a.Q.s2 + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) qf[s][nt] = *reinterpret_cast<const uint4*>(qp + 16 * nt * a.Q.s1 + 32 * s);
+    }
     const char* kbase = static_cast<const char*>(a.K.data) + (b * a.K.s0 + hk * a.K.s1) * 2;
     v4i krs;
     krs[0] = (int)(uint32_t)(uintptr_t)kbase;
@@ -1061,162 +1086,270 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     krs[2] = (int)((int64_t)p.n_kv * rowb);
     krs[3] = 0x00020000;
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
-    // this lane's row in even and odd blocks and its chunk within the block
-    const int dcp = lane >> 5;
-    const int drow = slot_row(lane & 31, dcp, 0);
-    auto issue = [&](int tile) {
-        const uint32_t dst = ring_lds + (uint32_t)((tile % 3) * TILE_B);
-        const uint32_t* off = s_off + tile * T;
-        const uint32_t ve = off[drow] + 16u * dcp, vo = off[drow ^ 8] + 16u * dcp;
+    // Loads of one tile by this wave: main blocks wv NM .. wv NM + NM - 1 (rows 4 (block / 4) +
+    // lane / 16), then tail blocks wv NT .. wv NT + NT - 1 (rows 8 j + lane / 8).
+    constexpr int NM = 32 / NW, NT = 4 / NW, NRG = NM / 4;
+    // Buffer offsets of this lane's rows of tile `tile`.  Tiles at or past nt get an
+    // out-of-range offset: their loads move no data and only write zeros into a free ring
+    // slot, which keeps the count of loads per tile constant.
+    struct TileOff { uint32_t m[NRG], t[NT]; };
+    auto tile_offsets = [&](int tile) {
+        TileOff o;
+        const bool real = tile < nt;
+        const uint32_t* off = s_off + (real ? tile : 0) * T;
 #pragma unroll
-        for (int ii = 0; ii < NI; ++ii) {
-            const int k = wv + NW * ii;
-            lds_dma16(krs, dst + 1024u * (uint32_t)k, (k & 1) ? vo : ve, 32u * (uint32_t)k);
+        for (int q = 0; q < NRG; ++q) {
+            const int r = 4 * (wv * NRG + q) + (lane >> 4);
+            o.m[q] = real ? off[r] + 16u * (uint32_t)cslot_inv(r, lane & 15) : 0x80000000u;
+        }
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const int r = 8 * (wv * NT + q) + (lane >> 3);
+            o.t[q] = real ? off[r] + 16u * (uint32_t)(64 + ((lane & 7) ^ tswz(r))) : 0x80000000u;
+        }
+        return o;
+    };
+    auto dma = [&](int tile, int ii, const TileOff& o) {
+        const uint32_t base = ring_lds + (uint32_t)((tile % 3) * TILE_B);
+        if (ii < NM) {
+            const int blk = wv * NM + ii;
+            lds_dma16(krs, base + 1024u * (uint32_t)blk, o.m[ii >> 2], 256u * (uint32_t)(ii & 3));
+        } else {
+            const int j = wv * NT + (ii - NM);
+            lds_dma16(krs, base + 32768u + 1024u * (uint32_t)j, o.t[ii - NM], 0u);
         }
     };
 
-    // K operand of k-step s (block s): row n32, chunk 2s + h
-    const int kadr_e = 16 * (32 * h + slot_row(n32, h, 0));
-    const int kadr_o = 16 * (32 * h + slot_row(n32, h, 1));
-    // V operand (transposing reads): this lane supplies row 16 s' + 8 e2 + 4 h + lane%16/4 and
-    // 8 bytes of chunk 4 mt + 2 g2 + c, c = lane%4/2 (block 2 mt + g2)
-    const int sl = lane & 15, g2 = (lane >> 4) & 1, vcp = (sl >> 1) & 1;
-    const int vbase = 1024 * g2 + 512 * vcp + 16 * (sl >> 2) + 64 * (h ^ vcp) + 8 * (sl & 1);
-    const int vadr_e0 = vbase + 128 * g2, vadr_e1 = vbase + 128 * (1 - g2);
+    // K operand of S^T k-step s, position tile pt: row r = 16 pt + lane%16, chunk c = 4 s + lane/16;
+    // kadr[pt][s % 4] + 1024 (s / 4) for s < 16, tail blocks for s = 16, 17
+    int kadr[2][4], ktail[2][2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+        const int r = 16 * pt + l15;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) kadr[pt][k4] = 4096 * (r >> 2) + 256 * (r & 3) + 16 * cslot(r, 4 * k4 + g);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+            ktail[pt][k2] = 32768 + 1024 * (r >> 3) + 16 * (8 * (r & 7) + ((4 * k2 + g) ^ tswz(r)));
+    }
+    // V operand of O^T (transposing reads): this lane supplies row r = 16 s' + 8 h + 4 e2 + lane%16/4
+    // and 8 bytes of chunk 4 mt + c2, c2 = 2 (lane/16 % 2) + lane%4/2.  The chunk's slot splits
+    // into bits 0-1 (lane constant) and bits 2-3 = mt % 4 ^ (swizzle bits 2-3): address
+    // vlo[e2] + ((64 (mt % 4)) ^ vx[e2]) + 1024 (mt / 4) + 16384 s'
+    const int g2 = (lane >> 4) & 1, vc2 = 2 * g2 + ((l15 >> 1) & 1);
+    int vlo[2], vx[2];
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+        const int r = 8 * h + 4 * e2 + (l15 >> 2);
+        const int X = rswz(r) ^ (8 * g2);
+        vlo[e2] = 4096 * (r >> 2) + 256 * (r & 3) + 16 * (vc2 ^ (X & 3)) + 8 * (l15 & 1);
+        vx[e2] = 16 * (X & 12);
+    }
+    // P^T fragment of head group grp, k-step s' (positions 16 s' + 8 h + 0..7): 16 bytes at
+    // ((s' NW + grp) 2 + h) 512 + 16 n32 of a tile's P buffer
+    const int pread = 16 * (32 * h + n32);
 
-    f32x16 oacc[MT];
+    f32x16 oacc[MW][NW];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int t2 = 0; t2 < MW; ++t2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[t][e] = 0.f;
-    float m_ref = -INFINITY, m_all = -INFINITY, lsum = 0.f;
+        for (int gr = 0; gr < NW; ++gr)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[t2][gr][e] = 0.f;
+    float m_ref[2] = {-INFINITY, -INFINITY}, m_all[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
     const float sl2 = a.scale * kLog2e;
 
     for (int pass = 0; pass < 2; ++pass) {
     bool over = false;
-    if (nt > 0) issue(0);
-    if (nt > 1) issue(1);
+    if (nt > 0) {
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            const TileOff o = tile_offsets(tile);
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) dma(tile, ii, o);
+        }
+    }
+    // Q fragments and the first two tiles have arrived; no vector-memory load of the
+    // compiler's own may be pending inside the tile loop, whose waits count tile loads only
+    wait_vmcnt<0>();
     for (int t = 0; t < nt; ++t) {
-        if (t + 1 < nt) wait_vmcnt<NI>();
-        else wait_vmcnt<0>();
+        wait_vmcnt<NI>();  // tile t has landed; only tile t + 1 may still be in flight
         tile_barrier();
-        if (t + 2 < nt) issue(t + 2);
+        // tile t + 2 goes into the slot every wave finished reading before the barrier; its
+        // loads are spread over the S^T steps below
+        const TileOff dof = tile_offsets(t + 2);
         const uint32_t msk = s_mask[t];
         const uint8_t* tb = ring + (t % 3) * TILE_B;
-        // S^T = K Q^T: lane holds S^T[pos 8 (e/4) + 4 h + e%4][head n32]
-        auto kread = [&](int s) {
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + ((s & 1) ? kadr_o : kadr_e) + 1024 * s));
+        // S^T = K Q^T: sacc[pt][nt] holds S^T[pos 16 pt + 4 (lane/16) + r][head 16 nt + lane%16]
+        auto kread = [&](int s, int pt) {
+            const int a_ = s < 16 ? kadr[pt][s & 3] + 1024 * (s >> 2) : ktail[pt][s - 16];
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + a_));
         };
-        f32x16 sa0;
+        f32x4 sacc[2][2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sa0[e] = 0.f;
-        bf16x8 kb[PD];
+        for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-        for (int s = 0; s < PD; ++s) kb[s] = kread(s);
+            for (int q = 0; q < 2; ++q) sacc[pt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 kb[PD][2];
+#pragma unroll
+        for (int s = 0; s < PD; ++s)
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) kb[s][pt] = kread(s, pt);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const bf16x8 cur = kb[s % PD];
-            if (s + PD < KS) kb[s % PD] = kread(s + PD);
-            sa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, qf[s]), sa0, 0, 0, 0);
+            const bf16x8 c0 = kb[s % PD][0], c1 = kb[s % PD][1];
+            if (s + PD < KS) {
+                kb[s % PD][0] = kread(s + PD, 0);
+                kb[s % PD][1] = kread(s + PD, 1);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const bf16x8 qb = __builtin_bit_cast(bf16x8, qf[s][q]);
+                sacc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c0, qb, sacc[0][q], 0, 0, 0);
+                sacc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c1, qb, sacc[1][q], 0, 0, 0);
+            }
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii)
+                if ((ii * KS) / NI == s) dma(t + 2, ii, dof);
         }
-        // keep PD operand reads in flight: the scheduler would otherwise sink each read
-        // next to its MFMA to save registers
-        __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+        // keep operand reads in flight: the scheduler would otherwise sink each read next
+        // to its MFMA to save registers
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (s + PD < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            if (s + PD < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        auto vread = [&](int j) {  // step j = 2 mt + s'
-            const int mt = j >> 1, s2 = j & 1;
-            const uint8_t* vb = tb + 2048 * mt + 256 * s2;
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lds_tr_read(vb + vadr_e0), lds_tr_read(vb + vadr_e1), 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-
-        const uint32_t mh = msk >> (4 * h);
-        float x[16];
-        float tmax = -INFINITY;
+        // softmax numerators against the fixed reference; P^T fragments to LDS
+        uint8_t* pw = pbuf + (t & 1) * PB + (size_t)(((g >> 1) * 32) * 16 + 8 * (g & 1));
+        const uint32_t mg = msk >> (4 * g);
+        const bool full = msk == 0xffffffffu;  // no masked position in the tile
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int pr = 8 * (e >> 2) + (e & 3);
-            x[e] = ((mh >> pr) & 1u) ? sa0[e] * sl2 : -INFINITY;
-            tmax = fmaxf(tmax, x[e]);
+        for (int q = 0; q < 2; ++q) {
+            float x[8];
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[4 * pt + r] = sacc[pt][q][r] * sl2;
+            if (!full) {
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (!((mg >> (16 * pt + r)) & 1u)) x[4 * pt + r] = -INFINITY;
+            }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
+            tmax = colmax4(tmax);
+            if (m_ref[q] == -INFINITY) m_ref[q] = tmax;
+            m_all[q] = fmaxf(m_all[q], tmax);
+            over |= tmax > m_ref[q] + kLazy;
+            float ps = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                float pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // v_exp_f32 directly: results below 2^-126 of the reference flush to zero.
+                    // Masked entries are exactly 0 (exp2(-inf - -inf) would be NaN).
+                    const float ev = __builtin_amdgcn_exp2f(x[4 * pt + r] - m_ref[q]);
+                    pv[r] = (full || x[4 * pt + r] != -INFINITY) ? ev : 0.f;
+                    ps += pv[r];
+                }
+                const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
+                *reinterpret_cast<uint2*>(pw + ((pt * NW + wv) * 2) * 512 + 16 * (16 * q + l15)) =
+                    make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+            }
+            lsum[q] += ps;
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        if (m_ref == -INFINITY) m_ref = tmax;
-        m_all = fmaxf(m_all, tmax);
-        over |= tmax > m_ref + kLazy;
-        float ps = 0.f;
-        uint32_t pw[8];
+        wait_lgkmcnt0();
+        tile_barrier();
+        // O^T[d slice of this wave][all heads] += V^T P^T
+        const uint8_t* pr = pbuf + (t & 1) * PB + pread;
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-            const float p0 = x[e] == -INFINITY ? 0.f : exp2f(x[e] - m_ref);
-            const float p1 = x[e + 1] == -INFINITY ? 0.f : exp2f(x[e + 1] - m_ref);
-            ps += p0 + p1;
-            const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
-            pw[e >> 1] = __builtin_bit_cast(uint32_t, pk);
-        }
-        lsum += ps;
-        const bf16x8 pb0 = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-        const bf16x8 pb1 = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
-        bf16x8 vbuf[PD];
+        for (int s2 = 0; s2 < 2; ++s2) {
+            bf16x8 pf[NW];
 #pragma unroll
-        for (int j = 0; j < PD; ++j) vbuf[j] = vread(j);
-        // O^T += V^T P^T; step j = 2 mt + s' covers positions 16 s' + {4h..4h+3, 8+4h..8+4h+3}
+            for (int gr = 0; gr < NW; ++gr)
+                pf[gr] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pr + ((s2 * NW + gr) * 2) * 512));
 #pragma unroll
-        for (int j = 0; j < 2 * MT; ++j) {
-            const bf16x8 cur = vbuf[j % PD];
-            if (j + PD < 2 * MT) vbuf[j % PD] = vread(j + PD);
-            oacc[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, (j & 1) ? pb1 : pb0, oacc[j >> 1], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 1);
+            for (int t2 = 0; t2 < MW; ++t2) {
+                const int mt = MW * wv + t2;
+                const uint8_t* vb = tb + 1024 * (mt >> 2) + 16384 * s2;
+                const bf16x8 va = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lds_tr_read(vb + vlo[0] + ((64 * (mt & 3)) ^ vx[0])),
+                                                    lds_tr_read(vb + vlo[1] + ((64 * (mt & 3)) ^ vx[1])), 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int j = 0; j < 2 * MT; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            if (j + PD < 2 * MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                for (int gr = 0; gr < NW; ++gr)
+                    oacc[t2][gr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[gr], oacc[t2][gr], 0, 0, 0);
+            }
         }
     }
     wait_vmcnt<0>();
     if (!__syncthreads_or(over)) break;
     // a probability left fp32 headroom: run the set again against the true maximum
-    m_ref = m_all;
-    lsum = 0.f;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[t][e] = 0.f;
+    for (int q = 0; q < 2; ++q) {
+        m_ref[q] = m_all[q];
+        lsum[q] = 0.f;
     }
-    // total exp-sum per head: lanes n32 and n32 + 32 hold disjoint positions
-    lsum += __shfl_xor(lsum, 32);
-    // lane holds O^T[d = 32 mt + 8 (e/4) + 4 h + e%4][head n32]
-    if (S == 1) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+    for (int t2 = 0; t2 < MW; ++t2)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bf16x2 v01 = {(__bf16)(oacc[mt][4 * q] * inv), (__bf16)(oacc[mt][4 * q + 1] * inv)};
-                const bf16x2 v23 = {(__bf16)(oacc[mt][4 * q + 2] * inv), (__bf16)(oacc[mt][4 * q + 3] * inv)};
-                *reinterpret_cast<uint2*>(op + 32 * mt + 8 * q + 4 * h) =
-                    make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+        for (int gr = 0; gr < NW; ++gr)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[t2][gr][e] = 0.f;
+    }
+    // per-head reference and exp-sum (lanes with the same lane%16 hold disjoint positions)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        lsum[q] += __shfl_xor(lsum[q], 16);
+        lsum[q] += __shfl_xor(lsum[q], 32);
+        if (g == 0) {
+            s_ml[0][32 * wv + 16 * q + l15] = m_ref[q];
+            s_ml[1][32 * wv + 16 * q + l15] = lsum[q];
+        }
+    }
+    __syncthreads();
+    if (S == 1 && a.lse && g == 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            a.lse[((int64_t)b * p.Hq + hk * G + 32 * wv + 16 * q + l15) * p.n_q + i] =
+                lsum[q] > 0.f ? (m_ref[q] + log2f(lsum[q])) * kLn2 : -INFINITY;
+    }
+    // lane holds O^T[d = 32 (MW wv + t2) + 8 (e/4) + 4 h + e%4][head 32 gr + n32]
+#pragma unroll
+    for (int gr = 0; gr < NW; ++gr) {
+        const int head = hk * G + 32 * gr + n32;
+        if (S == 1) {
+            const float l = s_ml[1][32 * gr + n32];
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2;
+#pragma unroll
+            for (int t2 = 0; t2 < MW; ++t2)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bf16x2 v01 = {(__bf16)(oacc[t2][gr][4 * q] * inv), (__bf16)(oacc[t2][gr][4 * q + 1] * inv)};
+                    const bf16x2 v23 = {(__bf16)(oacc[t2][gr][4 * q + 2] * inv), (__bf16)(oacc[t2][gr][4 * q + 3] * inv)};
+                    *reinterpret_cast<uint2*>(op + 32 * (MW * wv + t2) + 8 * q + 4 * h) =
+                        make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+                }
+        } else {
+            float* part = static_cast<float*>(a.partial);
+            const int64_t slot = (row * p.Hq + head) * (int64_t)S + split;
+            float* po = part + (int64_t)p.B * p.n_q * p.Hq * S * 2 + slot * DV;
+#pragma unroll
+            for (int t2 = 0; t2 < MW; ++t2)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4*>(po + 32 * (MW * wv + t2) + 8 * q + 4 * h) =
+                        make_float4(oacc[t2][gr][4 * q], oacc[t2][gr][4 * q + 1], oacc[t2][gr][4 * q + 2], oacc[t2][gr][4 * q + 3]);
+            if (wv == 0 && h == 0) {
+                float* ml = part + slot * 2;
+                ml[0] = s_ml[0][32 * gr + n32];
+                ml[1] = s_ml[1][32 * gr + n32];
             }
-        if (a.lse && h == 0)
-            a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = lsum > 0.f ? (m_ref + log2f(lsum)) * kLn2 : -INFINITY;
-    } else {
-        float* part = static_cast<float*>(a.partial);
-        const int64_t slot = (row * p.Hq + head) * (int64_t)S + split;
-        float* ml = part + slot * 2;
-        float* po = part + (int64_t)p.B * p.n_q * p.Hq * S * 2 + slot * DV;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<float4*>(po + 32 * mt + 8 * q + 4 * h) =
-                    make_float4(oacc[mt][4 * q], oacc[mt][4 * q + 1], oacc[mt][4 * q + 2], oacc[mt][4 * q + 3]);
-        if (h == 0) {
-            ml[0] = m_ref;
-            ml[1] = lsum;
         }
     }
 }
@@ -1231,14 +1364,14 @@ hipError_t launch_rows_g(const AttnArgs& a, int G, unsigned blocks, hipStream_t 
 
 }  // namespace
 
-// The LDS-direct latent kernel: 32-head groups, V aliasing the first d_v columns of K,
+// The LDS-direct latent kernel: 32, 64 or 128 heads per key/value head, V aliasing the first d_v columns of K,
 // 16-byte aligned rows, 32-bit row offsets and at most mla::MAXE candidates per split.
 static bool mla_lds_ok(const AttnArgs& a) {
     const sa_problem& p = a.p;
     const int G = p.Hq / p.Hkv;
     const bool alias = a.V.data == a.K.data && a.V.s0 == a.K.s0 && a.V.s1 == a.K.s1 && a.V.s2 == a.K.s2;
     const long per = (p.k + a.splits - 1) / a.splits;
-    return G % 32 == 0 && alias && a.K.s2 % 8 == 0 && ((uintptr_t)a.K.data & 15) == 0 &&
+    return (G == 32 || G == 64 || G == 128) && alias && a.K.s2 % 8 == 0 && ((uintptr_t)a.K.data & 15) == 0 &&
            (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) && per <= mla::MAXE;
 }
 
@@ -1277,7 +1410,6 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 #endif
         if (SA_MLA_VARIANT == 2 && mla_lds_ok(a)) {
             if (G == 128) hipLaunchKernelGGL(attn_mla_lds<4>, dim3((unsigned)units), dim3(256), 0, s, a);
-            else if (G == 96) hipLaunchKernelGGL(attn_mla_lds<3>, dim3((unsigned)units), dim3(192), 0, s, a);
             else if (G == 64) hipLaunchKernelGGL(attn_mla_lds<2>, dim3((unsigned)units), dim3(128), 0, s, a);
             else hipLaunchKernelGGL(attn_mla_lds<1>, dim3((unsigned)units), dim3(64), 0, s, a);
         } else {
