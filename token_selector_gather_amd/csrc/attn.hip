@@ -716,6 +716,15 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
     }
 }
 
+// Split partials: (m, l) pairs in fp32 for every (row, head, split), then, from the next
+// 256-byte boundary, o / l in bf16 (d_v values per (row, head, split)).
+__device__ __forceinline__ uint16_t* partial_o(float* part, int64_t slots) {
+    return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(part) + ((slots * 8 + 255) & ~(int64_t)255));
+}
+__device__ __forceinline__ const uint16_t* partial_o(const float* part, int64_t slots) {
+    return partial_o(const_cast<float*>(part), slots);
+}
+
 // ------------------------------------------------------------------- attn_mla
 constexpr int kTile = 32;
 
@@ -880,14 +889,18 @@ __global__ void __launch_bounds__(512) attn_mla(AttnArgs a) {
         if (a.lse && gq == 0)
             a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
     } else {
-        // partial: [row, Hq, S] x (m, l) and [row, Hq, S, DV] unnormalised o
+        // partial: [row, Hq, S] x (m, l) fp32, then [row, Hq, S, DV] o / l in bf16
         float* part = static_cast<float*>(a.partial);
         const int64_t slot = (row * p.Hq + head) * (int64_t)S + split;
         float* ml = part + slot * 2;
-        float* po = part + (int64_t)p.B * p.n_q * p.Hq * S * 2 + slot * DV;
+        uint16_t* po = partial_o(part, (int64_t)p.B * p.n_q * p.Hq * S) + slot * DV;
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-        for (int t = 0; t < MTV; ++t)
-            *reinterpret_cast<float4*>(po + 16 * t + 4 * gq) = make_float4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3]);
+        for (int t = 0; t < MTV; ++t) {
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(oacc[t][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[t][1] * inv) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_rne(oacc[t][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[t][3] * inv) << 16);
+            *reinterpret_cast<uint2*>(po + 16 * t + 4 * gq) = make_uint2(lo, hi);
+        }
         if (gq == 0) {
             ml[0] = m;
             ml[1] = lsum;
@@ -907,13 +920,15 @@ __global__ void __launch_bounds__(256) lse_merge(AttnArgs a) {
     const long row = item / p.Hq;
     const int head = (int)(item % p.Hq);
     const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
+    // partial s holds m_s, l_s and o_s / l_s; weight w_s = l_s 2^(m_s - M)
     const float* part = static_cast<const float*>(a.partial);
     const float* ml = part + item * S * 2;
-    const float* po = part + total * S * 2 + item * (int64_t)S * DV;
+    const uint16_t* po = partial_o(part, total * S) + item * (int64_t)S * DV;
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
     float l = 0.f;
     constexpr int PER = DV / 64;
+    static_assert(PER == 8, "one 16-byte load per lane and split");
     float o[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
@@ -921,10 +936,15 @@ __global__ void __launch_bounds__(256) lse_merge(AttnArgs a) {
         for (int s = 0; s < S; ++s) {
             const float ms = ml[2 * s];
             if (ms == -INFINITY) continue;
-            const float w = exp2f(ms - M);
-            l += w * ml[2 * s + 1];
+            const float w = exp2f(ms - M) * ml[2 * s + 1];
+            l += w;
+            const uint4 u = *reinterpret_cast<const uint4*>(po + s * DV + lane * PER);
+            const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-            for (int e = 0; e < PER; ++e) o[e] = fmaf(w, po[s * DV + lane * PER + e], o[e]);
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = fmaf(w, bf16_lo(uw[e]), o[2 * e]);
+                o[2 * e + 1] = fmaf(w, bf16_hi(uw[e]), o[2 * e + 1]);
+            }
         }
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1319,39 +1339,126 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
                 lsum[q] > 0.f ? (m_ref[q] + log2f(lsum[q])) * kLn2 : -INFINITY;
     }
     // lane holds O^T[d = 32 (MW wv + t2) + 8 (e/4) + 4 h + e%4][head 32 gr + n32]
+    if (S == 1) {
+        // Stage bf16 rows of O in LDS (the ring is free now; each wave owns a region and
+        // handles GR head groups per round) and store them as whole row pieces.
+        constexpr int GR = NW < 2 ? NW : 2;  // head groups per round
+        constexpr int OP = MW * 64 + 8;      // LDS pitch of one staged head row (bytes)
+        constexpr int LPR = MW * 64 / 16;    // lanes per staged row
+        uint8_t* stg = ring + wv * (32 * GR * OP);
 #pragma unroll
-    for (int gr = 0; gr < NW; ++gr) {
-        const int head = hk * G + 32 * gr + n32;
-        if (S == 1) {
+        for (int r0 = 0; r0 < NW; r0 += GR) {
+#pragma unroll
+            for (int gq = 0; gq < GR; ++gq) {
+                const float l = s_ml[1][32 * (r0 + gq) + n32];
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+                for (int t2 = 0; t2 < MW; ++t2)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x16& o = oacc[t2][r0 + gq];
+                        const bf16x2 v01 = {(__bf16)(o[4 * q] * inv), (__bf16)(o[4 * q + 1] * inv)};
+                        const bf16x2 v23 = {(__bf16)(o[4 * q + 2] * inv), (__bf16)(o[4 * q + 3] * inv)};
+                        *reinterpret_cast<uint2*>(stg + (32 * gq + n32) * OP + 2 * (32 * t2 + 8 * q + 4 * h)) =
+                            make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+                    }
+            }
+            wait_lgkmcnt0();  // this wave reads back only what it wrote
+#pragma unroll
+            for (int rr = 0; rr < 32 * GR; rr += 64 / LPR) {
+                const int hr = rr + lane / LPR, j = lane % LPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + hr * OP + 16 * j);
+                uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + (hk * G + 32 * r0 + hr) * a.O.s1 +
+                               (int64_t)i * a.O.s2 + 32 * MW * wv + 8 * j;
+                *reinterpret_cast<uint4*>(op) = v;
+            }
+            wait_lgkmcnt0();
+        }
+    } else {
+        // partial in MFMA fragment order: fragment f = mt NW + gr of (row, hk, split) holds
+        // 64 lanes x 16 values of o / l, 32 contiguous bytes per lane
+        float* part = static_cast<float*>(a.partial);
+        const int64_t slots = (int64_t)p.B * p.n_q * p.Hq * S;
+        uint16_t* pbase = partial_o(part, slots) + ((rowkv * S + split) * (int64_t)G) * DV;
+#pragma unroll
+        for (int gr = 0; gr < NW; ++gr) {
             const float l = s_ml[1][32 * gr + n32];
             const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2;
 #pragma unroll
-            for (int t2 = 0; t2 < MW; ++t2)
+            for (int t2 = 0; t2 < MW; ++t2) {
+                const f32x16& o = oacc[t2][gr];
+                uint32_t w[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const bf16x2 v01 = {(__bf16)(oacc[t2][gr][4 * q] * inv), (__bf16)(oacc[t2][gr][4 * q + 1] * inv)};
-                    const bf16x2 v23 = {(__bf16)(oacc[t2][gr][4 * q + 2] * inv), (__bf16)(oacc[t2][gr][4 * q + 3] * inv)};
-                    *reinterpret_cast<uint2*>(op + 32 * (MW * wv + t2) + 8 * q + 4 * h) =
-                        make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+                for (int e = 0; e < 8; ++e) {
+                    const bf16x2 v = {(__bf16)(o[2 * e] * inv), (__bf16)(o[2 * e + 1] * inv)};
+                    w[e] = __builtin_bit_cast(uint32_t, v);
                 }
-        } else {
-            float* part = static_cast<float*>(a.partial);
-            const int64_t slot = (row * p.Hq + head) * (int64_t)S + split;
-            float* po = part + (int64_t)p.B * p.n_q * p.Hq * S * 2 + slot * DV;
-#pragma unroll
-            for (int t2 = 0; t2 < MW; ++t2)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<float4*>(po + 32 * (MW * wv + t2) + 8 * q + 4 * h) =
-                        make_float4(oacc[t2][gr][4 * q], oacc[t2][gr][4 * q + 1], oacc[t2][gr][4 * q + 2], oacc[t2][gr][4 * q + 3]);
+                uint4* dst = reinterpret_cast<uint4*>(pbase + ((MW * wv + t2) * NW + gr) * 1024 + lane * 16);
+                dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            }
             if (wv == 0 && h == 0) {
-                float* ml = part + slot * 2;
+                float* ml = part + ((row * p.Hq + hk * G + 32 * gr + n32) * (int64_t)S + split) * 2;
                 ml[0] = s_ml[0][32 * gr + n32];
                 ml[1] = s_ml[1][32 * gr + n32];
             }
         }
     }
+}
+
+// Merge the split partials of attn_mla_lds (fragment order, see above): one wave per
+// (row, key/value head, fragment).  Output O[head][d] from o = sum_s w_s o_s / sum_s w_s,
+// w_s = l_s 2^(m_s - M), and the log-sum-exp per head.
+__global__ void __launch_bounds__(256) lse_merge_frag(AttnArgs a) {
+    const sa_problem& p = a.p;
+    const int S = a.splits, G = p.Hq / p.Hkv, NW = G / 32, NF = (512 / 32) * NW;
+    const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, hk, fragment)
+    const long total = (long)p.B * p.n_q * p.Hkv * NF;
+    if (item >= total) return;
+    const int lane = threadIdx.x & 63, n32 = lane & 31, h = lane >> 5;
+    const int f = (int)(item % NF);
+    const long rowkv = item / NF;
+    const int hk = (int)(rowkv % p.Hkv);
+    const long row = rowkv / p.Hkv;
+    const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
+    const int mt = f / NW, gr = f % NW;
+    const int head = hk * G + 32 * gr + n32;
+    const float* part = static_cast<const float*>(a.partial);
+    const int64_t slots = (int64_t)p.B * p.n_q * p.Hq * S;
+    const float* ml = part + (row * p.Hq + head) * (int64_t)S * 2;
+    const uint16_t* pb = partial_o(part, slots) + (rowkv * S) * (int64_t)G * 512 + f * 1024 + lane * 16;
+    // running log-sum-exp over the splits, so that no load waits for a value computed from
+    // another load; a split without valid candidates has m = -inf, l = 0 and zero o
+    float M = -INFINITY, l = 0.f, o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+        const float ms = ml[2 * s], ls = ml[2 * s + 1];
+        const uint4* src = reinterpret_cast<const uint4*>(pb + s * (int64_t)G * 512);
+        const uint4 u0 = src[0], u1 = src[1];
+        const float Mn = fmaxf(M, ms);
+        const float c = M == -INFINITY ? 0.f : exp2f(M - Mn);   // rescale of what is merged so far
+        const float w = ms == -INFINITY ? 0.f : exp2f(ms - Mn) * ls;
+        M = Mn;
+        l = l * c + w;
+        const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o[2 * e] = fmaf(w, bf16_lo(uw[e]), o[2 * e] * c);
+            o[2 * e + 1] = fmaf(w, bf16_hi(uw[e]), o[2 * e + 1] * c);
+        }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2 + 32 * mt + 4 * h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[4 * q] * inv) | ((uint32_t)f32_to_bf16_rne(o[4 * q + 1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16_rne(o[4 * q + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + 8 * q) = make_uint2(lo, hi);
+    }
+    if (a.lse && mt == 0 && h == 0)
+        a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int LPR>
@@ -1397,7 +1504,9 @@ int attn_splits(const sa_problem& p) {
 size_t attn_partial_bytes(const sa_problem& p) {
     const int S = attn_splits(p);
     if (S <= 1) return 0;
-    return (size_t)p.B * p.n_q * p.Hq * S * (2 + (size_t)p.d_v) * sizeof(float);
+    // (m, l) in fp32 and o / l in bf16 per (row, head, split), the o block 256-byte aligned
+    const size_t slots = (size_t)p.B * p.n_q * p.Hq * S;
+    return ((slots * 8 + 255) & ~(size_t)255) + slots * (size_t)p.d_v * sizeof(uint16_t);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
@@ -1408,7 +1517,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 #ifndef SA_MLA_VARIANT
 #define SA_MLA_VARIANT 2
 #endif
-        if (SA_MLA_VARIANT == 2 && mla_lds_ok(a)) {
+        const bool lds_kernel = SA_MLA_VARIANT == 2 && mla_lds_ok(a);
+        if (lds_kernel) {
             if (G == 128) hipLaunchKernelGGL(attn_mla_lds<4>, dim3((unsigned)units), dim3(256), 0, s, a);
             else if (G == 64) hipLaunchKernelGGL(attn_mla_lds<2>, dim3((unsigned)units), dim3(128), 0, s, a);
             else hipLaunchKernelGGL(attn_mla_lds<1>, dim3((unsigned)units), dim3(64), 0, s, a);
@@ -1418,7 +1528,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.splits == 1) return e;
         const long items = (long)p.B * p.n_q * p.Hq;
-        hipLaunchKernelGGL((lse_merge<512>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+        if (lds_kernel) {
+            const long frags = (long)p.B * p.n_q * p.Hkv * (512 / 32) * (G / 32);
+            hipLaunchKernelGGL(lse_merge_frag, dim3((unsigned)((frags + 3) / 4)), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((lse_merge<512>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+        }
         return hipGetLastError();
     }
     const int G = p.Hq / p.Hkv;
