@@ -17,13 +17,18 @@ FLAGS = [
 ]
 
 
+# Per-file code generation options: the indexer keeps its MFMA results in plain VGPRs, which
+# saves a copy per result element ahead of the ReLU / head-weighting arithmetic.
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose=False, jobs=4):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objs = []
     procs = []
     for src in SOURCES:
         obj = os.path.join(CSRC, src.replace(".hip", ".o"))
-        cmd = [hipcc] + [f for f in FLAGS if f != "-shared"] + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc] + [f for f in FLAGS if f != "-shared"] + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(shlex.quote(c) for c in cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -26,6 +26,18 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 __device__ __forceinline__ float relu_keep_nonfinite(float z) { return z > 0.f ? z : 0.f * z; }
+// ReLU of a finite value in one integer max: negative floats are negative int32 patterns
+// (-0 included), non-negative floats keep their pattern
+__device__ __forceinline__ float relu_finite(float z) { return __int_as_float(max(__float_as_int(z), 0)); }
+// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] by lane swaps between rows (no LDS round trip)
+__device__ __forceinline__ float xsum16(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float xsum32(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
 
 __device__ __forceinline__ float load_elem(const void* base, int dtype, int64_t e) {
     if (dtype == SA_F32) return static_cast<const float*>(base)[e];
@@ -230,6 +242,183 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int n_groups,
     }
 }
 
+// ------------------------------------------------------------------ indexer_pf
+// Prefill layout for many query rows: a workgroup takes QB = 4 * 128 / H consecutive query
+// rows of one batch and walks their causal history once, in chunks of 128 keys that are
+// widened to bf16 once per chunk while being written to LDS (double buffered).  Wave w
+// keeps the A fragments of its 128 (query, head) rows (eight 16-row M-tiles) in registers,
+// so each 16-key B fragment read from LDS feeds 8 x KSTEPS MFMAs, and the ReLU /
+// head-weighting / head-sum arithmetic is about 2.5 VALU instructions per MFMA.
+template <int KSTEPS, bool KE4M3, int H, bool FAST_RELU>
+__global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
+    static_assert(H >= 16 && H <= 64, "one query per 16-row M-tile");
+    constexpr int D = 32 * KSTEPS;
+    constexpr int QW = 128 / H;              // queries per wave
+    constexpr int QB = 4 * QW;               // queries per workgroup
+    constexpr int MT = 8;                    // 16-row M-tiles per wave
+    constexpr int TPQ = H / 16;              // M-tiles per query
+    constexpr int CK = 128;                  // keys per chunk
+    constexpr int KP = 2 * D + 16;           // LDS pitch of one widened key row (bytes)
+    constexpr int RB = D * (KE4M3 ? 1 : 2);  // bytes per key row in memory
+    constexpr int PPR = RB / 16;             // 16-byte pieces per key row
+    constexpr int PPT = CK * PPR / 256;      // pieces per thread per chunk
+    static_assert(PPT >= 1 && PPT * 256 == CK * PPR, "chunk pieces must split evenly over the threads");
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][CK * KP];
+    __shared__ int s_L[QB];
+
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63, l15 = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long wg = blockIdx.x;
+    const int qb = p.causal ? n_qb - 1 - (int)(wg % n_qb) : (int)(wg % n_qb);  // longest histories first
+    const int b = (int)(wg / n_qb);
+    const int i0 = qb * QB;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    if (threadIdx.x < QB) s_L[threadIdx.x] = i0 + (int)threadIdx.x < p.n_q ? visible_len(R, b, i0 + threadIdx.x) : 0;
+    __syncthreads();
+    int Lwg = 0;
+#pragma unroll
+    for (int q = 0; q < QB; ++q) Lwg = max(Lwg, s_L[q]);
+    // this wave's queries: i0 + QW wv + q, visible lengths Lq[q]
+    const int iw = i0 + QW * wv;
+    int Lq[QW];
+#pragma unroll
+    for (int q = 0; q < QW; ++q) Lq[q] = s_L[QW * wv + q];
+    const int nch = (Lwg + CK - 1) / CK;
+
+    if (nch > 0) {
+        // A fragments (rows 16 m + lane%16: query m / TPQ, head 16 (m % TPQ) + lane%16) and the
+        // head weights of the accumulator rows (16 m + 4 (lane/16) + e)
+        bf16x8 av[MT][KSTEPS];
+        float wvv[MT][4];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int qi = iw + m / TPQ, h = 16 * (m % TPQ) + l15;
+            const bool ok = qi < p.n_q;
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q.data) + (ok ? (b * a.q.s0 + qi * a.q.s1 + h * a.q.s2) : 0);
+#pragma unroll
+            for (int s2 = 0; s2 < KSTEPS; ++s2)
+                av[m][s2] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const uint4*>(qp + 32 * s2 + 8 * g) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wvv[m][e] = ok ? static_cast<const float*>(a.w.data)[b * a.w.s0 + qi * a.w.s1 + 16 * (m % TPQ) + 4 * g + e] : 0.f;
+        }
+        const uint32_t kstride = (uint32_t)(a.k.s1 * (KE4M3 ? 1 : 2));
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2)), (short)0,
+            (int)((uint32_t)Lwg * kstride), 0x00020000);
+        uint4 stage[PPT];
+        auto fetch = [&](int c) {
+#pragma unroll
+            for (int e = 0; e < PPT; ++e) {
+                const int u = threadIdx.x + 256 * e;
+                const int r = u / PPR, col = u % PPR;
+                const int j = c * CK + r;
+                const uint32_t off = j < Lwg ? (uint32_t)j * kstride + 16u * col : 0x80000000u;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+                stage[e] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        };
+        auto commit = [&](int buf) {
+#pragma unroll
+            for (int e = 0; e < PPT; ++e) {
+                const int u = threadIdx.x + 256 * e;
+                const int r = u / PPR, col = u % PPR;
+                uint8_t* dst = &kbuf[buf][r * KP + (KE4M3 ? 32 : 16) * col];
+                if constexpr (KE4M3) {
+                    const uint32_t w4[4] = {stage[e].x, stage[e].y, stage[e].z, stage[e].w};
+                    uint32_t o[8];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[k], 1.0f, false);
+                        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[k], 1.0f, true);
+                        o[2 * k] = __builtin_bit_cast(uint32_t, lo);
+                        o[2 * k + 1] = __builtin_bit_cast(uint32_t, hi);
+                    }
+                    reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+                    reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+                } else {
+                    *reinterpret_cast<uint4*>(dst) = stage[e];
+                }
+            }
+        };
+        // scores of this wave: lane group g stores query g (and g + 4 when QW = 8)
+        float* srow[QW > 4 ? 2 : 1];
+        int Ls[QW > 4 ? 2 : 1];
+        bool qok[QW > 4 ? 2 : 1];
+#pragma unroll
+        for (int z = 0; z < (QW > 4 ? 2 : 1); ++z) {
+            const int q = g + 4 * z;
+            const int qi = iw + q;
+            qok[z] = q < QW && qi < p.n_q;
+            srow[z] = a.scores + (int64_t)(b * p.n_q + (qok[z] ? qi : 0)) * a.row_stride;
+            int Lz = 0;
+#pragma unroll
+            for (int qq = 0; qq < QW; ++qq)
+                if (qq == q) Lz = Lq[qq];
+            Ls[z] = Lz;
+        }
+        fetch(0);
+        commit(0);
+        __syncthreads();
+        for (int c = 0; c < nch; ++c) {
+            const int buf = c & 1;
+            if (c + 1 < nch) fetch(c + 1);
+            const uint8_t* kb = kbuf[buf] + l15 * KP + 16 * g;
+#pragma unroll 2
+            for (int nt = 0; nt < CK / 16; ++nt) {
+                bf16x8 bv[KSTEPS];
+#pragma unroll
+                for (int s2 = 0; s2 < KSTEPS; ++s2)
+                    bv[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + nt * 16 * KP + 64 * s2));
+                f32x4 acc[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KSTEPS; ++s2)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][s2], bv[s2], acc[m], 0, 0, 0);
+                float sc[QW];
+#pragma unroll
+                for (int q = 0; q < QW; ++q) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int m = q * TPQ; m < (q + 1) * TPQ; ++m)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float zz = acc[m][e];
+                            t = fmaf(wvv[m][e], FAST_RELU ? relu_finite(zz) : relu_keep_nonfinite(zz), t);
+                        }
+                    sc[q] = xsum32(xsum16(t));
+                }
+                const int j = c * CK + nt * 16 + l15;
+#pragma unroll
+                for (int z = 0; z < (QW > 4 ? 2 : 1); ++z) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int q = 0; q < QW; ++q)
+                        if (q == g + 4 * z) v = sc[q];
+                    const bool vis = j < Ls[z];
+                    if (qok[z] && j < p.n_kv && (vis || a.fill_invisible)) srow[z][j] = vis ? v : -INFINITY;
+                }
+            }
+            if (c + 1 < nch) commit(buf ^ 1);
+            __syncthreads();
+        }
+    }
+    if (a.fill_invisible) {
+        // positions past the computed chunks
+        const int start = nch * CK;
+        for (int q = 0; q < QW; ++q) {
+            const int qi = iw + q;
+            if (qi >= p.n_q) break;
+            float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
+            for (int j = start + lane; j < p.n_kv; j += 64) row[j] = -INFINITY;
+        }
+    }
+}
+
 // ------------------------------------------------------- matrix-core path, shared keys
 // Four waves of a workgroup read the same history positions: in prefill they own four
 // consecutive query groups (their key fragments then hit the L1), in decode they split
@@ -375,7 +564,7 @@ __global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float z = acc[mt][e];
-                    t = fmaf(wvv[mt][e], FAST_RELU ? fmaxf(z, 0.f) : relu_keep_nonfinite(z), t);
+                    t = fmaf(wvv[mt][e], FAST_RELU ? __builtin_amdgcn_fmed3f(z, 0.f, INFINITY) : relu_keep_nonfinite(z), t);
                 }
                 part[mt] = t;
             }
@@ -594,14 +783,13 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float z = acc[m][e];
-                        t = fmaf(wvv[m][e], FAST_RELU ? fmaxf(z, 0.f) : relu_keep_nonfinite(z), t);
+                        t = fmaf(wvv[m][e], FAST_RELU ? __builtin_amdgcn_fmed3f(z, 0.f, INFINITY) : relu_keep_nonfinite(z), t);
                     }
                     part[m] = t;
                 }
                 if constexpr (DECODE) {
                     float v = part[0];
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
+                    v = xsum32(xsum16(v));
                     if (lane < 16) red[wv * kCK + jl] = v;
                 } else if constexpr (H >= 16) {
                     constexpr int tpq = H / 16;
@@ -610,8 +798,7 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                         float v = 0.f;
 #pragma unroll
                         for (int t = 0; t < tpq; ++t) v += part[q * tpq + t];
-                        v += __shfl_xor(v, 16);
-                        v += __shfl_xor(v, 32);
+                        v = xsum32(xsum16(v));
                         const int Lh = __shfl(Lq, q);
                         const bool vis = j < Lh;
                         const bool wr = wave_live && lane < 16 && i0 + q < p.n_q && j < j_end && (vis || a.fill_invisible);
@@ -624,7 +811,7 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                         float v = part[mt];
                         int qloc;
                         if constexpr (H == 8) {
-                            v += __shfl_xor(v, 16);
+                            v = xsum16(v);
                             qloc = 2 * mt + (lane >> 5);
                         } else {
                             qloc = 4 * mt + (lane >> 4);
@@ -736,6 +923,26 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
         if (fast) {
             const dim3 gc((unsigned)max(1L, min(512L, 65536L / p.B)), p.B);
             hipLaunchKernelGGL(index_finite_check, gc, dim3(256), 0, s, a);
+        }
+        // prefill with many query rows: one pass over the history per block of query rows
+        if (!decode && H >= 16 && D >= 64) {
+            const int QB = 4 * 128 / H;
+            const int n_qb = (p.n_q + QB - 1) / QB;
+            if ((long)p.B * n_qb >= 512) {
+                const dim3 gp((unsigned)((long)p.B * n_qb)), bp(256);
+                const bool e4 = a.k.dtype == SA_FP8_E4M3;
+#define SA_IDXPF(KS, E4, HH)                                                                                  \
+    if (H == HH) {                                                                                            \
+        if (fast) hipLaunchKernelGGL((indexer_pf<KS, E4, HH, true>), gp, bp, 0, s, a, n_qb);                  \
+        else hipLaunchKernelGGL((indexer_pf<KS, E4, HH, false>), gp, bp, 0, s, a, n_qb);                      \
+        return hipGetLastError();                                                                             \
+    }
+#define SA_IDXPF_H(KS, E4) do { SA_IDXPF(KS, E4, 16) SA_IDXPF(KS, E4, 32) SA_IDXPF(KS, E4, 64) } while (0)
+                if (D == 64) { if (e4) SA_IDXPF_H(2, true); else SA_IDXPF_H(2, false); }
+                else { if (e4) SA_IDXPF_H(4, true); else SA_IDXPF_H(4, false); }
+#undef SA_IDXPF_H
+#undef SA_IDXPF
+            }
         }
         const int rng_len = decode ? 2048 : 1024;
         const int n_rng = (p.n_kv + rng_len - 1) / rng_len;
