@@ -24,6 +24,7 @@
 //    S^T accumulator layout a lane holds 8 positions of one head, exactly the operand P^T
 //    needs, so probabilities never leave registers; the transposed tile stores positions
 //    in that lane order.
+#include "gfx950_mem.h"
 #include "sa_internal.h"
 
 namespace sa {
@@ -994,12 +995,6 @@ __device__ __forceinline__ int tswz(int r) { return (r >> 1) & 7; }
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
 // maximum over the lanes l, l^16, l^32, l^48 (lane swaps between rows, no LDS round trip)
 __device__ __forceinline__ float colmax4(float v) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -1008,28 +1003,8 @@ __device__ __forceinline__ float colmax4(float v) {
     return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// wait for this wave's LDS and scalar-memory operations only
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-__device__ __forceinline__ void tile_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ v4s lds_tr_read(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
-}
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 * lane.  Written as asm so
-// that the compiler does not order later LDS reads behind it: the kernel's own vmcnt waits
-// and barriers order every read of the written tile.
-__device__ __forceinline__ void lds_dma16(const v4i& rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
-                 "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "m0");
 }
 
 template <int NW>

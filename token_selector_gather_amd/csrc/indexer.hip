@@ -16,6 +16,7 @@
 //
 // ReLU is written as (z > 0 ? z : 0*z) so that a NaN or -inf dot product stays non-finite
 // and reaches the selection's finiteness check instead of being clipped to zero.
+#include "gfx950_mem.h"
 #include "sa_internal.h"
 
 namespace sa {
@@ -239,6 +240,136 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int n_groups,
                 }
             }
         }
+    }
+}
+
+// ------------------------------------------------------------------ indexer_dec
+// Few query rows (decode): a workgroup takes one query row and a range of at most 2048 keys;
+// each wave holds all H index heads of that row (H / 16 M-tiles) and walks its own 16-key
+// tiles of the range (tile u of wave w covers keys 16 (w + 4 u)), so every key is widened
+// once and no wave waits for another.  Tiles reach a ring of NB slots in the wave's own LDS
+// region through buffer loads that write LDS directly (NB - 1 tiles in flight per wave, no
+// staging registers, ordered by the wave's own vmcnt waits); scores collect in LDS and are
+// stored once per workgroup.  The contraction index is relabelled so that lane group g owns
+// d in [g D/4, (g+1) D/4): each lane's share of a key row is one contiguous piece (the Q
+// fragments use the same relabelling).
+template <int KSTEPS, bool KE4M3, int H, bool FAST_RELU>
+__global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, int rng_len) {
+    static_assert(H >= 16 && H <= 64, "whole 16-row M-tiles of one query");
+    constexpr int MT = H / 16;
+    constexpr int RB = 32 * KSTEPS * (KE4M3 ? 1 : 2);  // bytes per key row
+    constexpr int KB = RB / 4;                         // bytes of a key row per lane group
+    constexpr int NV = KB / 16;                        // 16-byte pieces per lane per tile
+    constexpr int CPR = RB / 16;                       // 16-byte chunks per key row
+    constexpr int TB = 16 * RB;                        // bytes per 16-key tile
+    constexpr int NI = TB / 1024;                      // LDS-direct loads per tile
+    constexpr int RPI = 1024 / RB;                     // key rows per load
+    constexpr int NB = 8192 / TB < 4 ? 4 : 8192 / TB;  // ring slots per wave (8 KB for 2 KB tiles)
+    static_assert(NI >= 1 && NI * 1024 == TB && NI * (NB - 1) < 64, "tile and ring sizes");
+    constexpr int MAXR = 2048;                         // keys per workgroup range
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4 * NB * TB];
+    __shared__ float s_sc[MAXR];
+
+    const sa_problem& p = a.p;
+    const int lane = threadIdx.x & 63, l15 = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long wg = blockIdx.x;
+    const int rng = (int)(wg % n_rng);
+    const long row = wg / n_rng;  // b * n_q + i
+    const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int j_begin = rng * rng_len, j_end = min(j_begin + rng_len, p.n_kv);
+    const int j_comp = min(j_end, L);  // keys worth computing: [j_begin, j_comp)
+    const int ntl = j_comp > j_begin ? (j_comp - j_begin + 15) / 16 : 0;  // tiles of the range
+    const int nmine = ntl > wv ? (ntl - wv + 3) / 4 : 0;                  // tiles of this wave
+    // within a key row, chunk c sits in slot c ^ cswz(r): conflict-free 16-row fragment reads
+    auto cswz = [](int r) { return (r / (16 / CPR < 1 ? 1 : 16 / CPR)) & (CPR - 1); };
+
+    if (nmine > 0) {
+        // A fragments: row 16 m + lane%16 = head, k-step s holds d = g D/4 + 8 s + 0..7
+        bf16x8 av[MT][KSTEPS];
+        float wvv[MT][4];
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q.data) + b * a.q.s0 + (int64_t)i * a.q.s1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+                av[m][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (16 * m + l15) * a.q.s2 + 8 * KSTEPS * g + 8 * s));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wvv[m][e] = static_cast<const float*>(a.w.data)[b * a.w.s0 + (int64_t)i * a.w.s1 + 16 * m + 4 * g + e];
+        }
+        wait_vmcnt<0>();  // the tile loop's waits count tile loads only
+        const uint32_t kstride = (uint32_t)(a.k.s1 * (KE4M3 ? 1 : 2));
+        const v4i krs = buffer_rsrc(static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2), (uint32_t)j_comp * kstride);
+        const uint32_t ring_w = lds_addr(ring) + (uint32_t)(wv * NB * TB);
+        // this lane's row and chunk in load ii of a tile
+        int lrow[NI];
+        uint32_t loff[NI];
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+            lrow[ii] = ii * RPI + lane / CPR;
+            loff[ii] = (uint32_t)lrow[ii] * kstride + 16u * (uint32_t)((lane % CPR) ^ cswz(lrow[ii]));
+        }
+        auto issue = [&](int u) {
+            const int j0 = j_begin + 16 * (wv + 4 * u);
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) {
+                const bool ok = u < nmine && j0 + lrow[ii] < j_comp;
+                lds_dma16(krs, ring_w + (uint32_t)((u % NB) * TB + 1024 * ii), ok ? (uint32_t)j0 * kstride + loff[ii] : 0x80000000u, 0u);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < NB - 1; ++u) issue(u);
+        const uint8_t* rbase = ring + wv * NB * TB + l15 * RB;
+        for (int u = 0; u < nmine; ++u) {
+            issue(u + NB - 1);       // into the slot of tile u - 1, whose reads fed the MFMAs already
+            wait_vmcnt<NI * (NB - 1)>();  // tile u has landed
+            const uint8_t* tr = rbase + (u % NB) * TB;
+            uint4 rr[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) rr[v] = *reinterpret_cast<const uint4*>(tr + 16 * ((NV * g + v) ^ cswz(l15)));
+            bf16x8 bv[KSTEPS];
+            if constexpr (KE4M3) {
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const uint4 w4 = rr[s / 2];
+                    const uint32_t lo = (s & 1) ? w4.z : w4.x, hi = (s & 1) ? w4.w : w4.y;
+                    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+                    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+                    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+                    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+                    bv[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) bv[s] = __builtin_bit_cast(bf16x8, rr[s]);
+            }
+            f32x4 acc[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][s], bv[s], acc[m], 0, 0, 0);
+            float t = 0.f;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t = fmaf(wvv[m][e], FAST_RELU ? relu_finite(acc[m][e]) : relu_keep_nonfinite(acc[m][e]), t);
+            const float v = xsum32(xsum16(t));
+            if (lane < 16) s_sc[16 * (wv + 4 * u) + l15] = v;
+        }
+        wait_vmcnt<0>();
+    }
+    __syncthreads();
+    // store the range: computed keys that are visible, -inf for the rest when asked to
+    float* srow = a.scores + row * a.row_stride;
+    for (int j = j_begin + (int)threadIdx.x; j < j_end; j += 256) {
+        const bool vis = j < L;
+        if (vis) srow[j] = s_sc[j - j_begin];
+        else if (a.fill_invisible) srow[j] = -INFINITY;
     }
 }
 
@@ -919,10 +1050,28 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
         const int n_groups = (p.n_q + QPG - 1) / QPG;
         // decode layout (the four waves split one query's 64 index heads) for few query groups
         const bool decode = H == 64 && (long)p.B * n_groups < 1024;
-        const bool fast = a.status != nullptr && !decode;
+        const bool few_rows = (long)p.B * p.n_q < 512 && H >= 16 && D >= 64;  // indexer_dec below
+        const bool fast = a.status != nullptr && !decode && !few_rows;
         if (fast) {
             const dim3 gc((unsigned)max(1L, min(512L, 65536L / p.B)), p.B);
             hipLaunchKernelGGL(index_finite_check, gc, dim3(256), 0, s, a);
+        }
+        // few query rows: waves split the keys of one row, keys read straight into registers
+        if (few_rows) {
+            const int rng_len = 2048;
+            const int n_rng = (p.n_kv + rng_len - 1) / rng_len;
+            const dim3 gd((unsigned)((long)p.B * p.n_q * n_rng)), bd(256);
+            const bool e4 = a.k.dtype == SA_FP8_E4M3;
+#define SA_IDXD(KS, E4, HH)                                                                                   \
+    if (H == HH) {                                                                                            \
+        hipLaunchKernelGGL((indexer_dec<KS, E4, HH, false>), gd, bd, 0, s, a, n_rng, rng_len);                \
+        return hipGetLastError();                                                                             \
+    }
+#define SA_IDXD_H(KS, E4) do { SA_IDXD(KS, E4, 16) SA_IDXD(KS, E4, 32) SA_IDXD(KS, E4, 64) } while (0)
+            if (D == 64) { if (e4) SA_IDXD_H(2, true); else SA_IDXD_H(2, false); }
+            else { if (e4) SA_IDXD_H(4, true); else SA_IDXD_H(4, false); }
+#undef SA_IDXD_H
+#undef SA_IDXD
         }
         // prefill with many query rows: one pass over the history per block of query rows
         if (!decode && H >= 16 && D >= 64) {
