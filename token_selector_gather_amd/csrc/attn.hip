@@ -8,22 +8,20 @@
 // not visible are never read.  Split pieces of one set are merged by log-sum-exp (the
 // block-mixture identity of the COBS reading note, eq. (P3)).
 //
-// Two kernels:
-//  * attn_rows: separate key/value heads (MHA, small GQA groups).  One wave per
-//    (query row, key/value head).  Each history row is fetched by LPR lanes with 16-byte
-//    loads (RPI = 64/LPR rows per load instruction); a dot product finishes with log2(LPR)
-//    xor swaps inside the lane group; every lane group keeps its own online-softmax state
-//    over the rows it fetched and the groups merge once at the end.  Work items are laid
-//    out so that each of the 8 XCDs serves a fixed subset of key/value heads, keeping that
+// Kernels:
+//  * attn_rows_buf: bf16 MHA (one query head per key/value head, width 64/128/256).  One wave
+//    per (query row, key/value head); lane groups fetch whole rows with raw buffer loads and
+//    keep their own online-softmax state, merged once at the end.  Work items are laid out
+//    so that each of the 8 XCDs serves a fixed subset of key/value heads, keeping that
 //    subset's K/V rows in its own L2.
-//  * attn_mla: one latent key/value head shared by many query heads (Hq/Hkv multiple of
-//    16; V = the first d_v columns of K, or a separate tensor).  One workgroup per
-//    (query row, candidate split); wave w owns query heads 16w..16w+15.  A tile of 32
-//    gathered rows is staged in LDS twice: row-major for S^T = K Q^T (v_mfma_f32_16x16x32
-//    _bf16, Q^T fragments stay in registers) and transposed for O^T += V^T P^T.  In the
-//    S^T accumulator layout a lane holds 8 positions of one head, exactly the operand P^T
-//    needs, so probabilities never leave registers; the transposed tile stores positions
-//    in that lane order.
+//  * attn_rows: the general fallback (f32, GQA groups of 2 or 4, other widths).
+//  * attn_mla_lds: one latent key/value head shared by 32, 64 or 128 query heads (V = the
+//    first d_v columns of K).  Gathered rows reach LDS through buffer loads that write LDS
+//    directly; S^T on 16x16x32 MFMA chains, P exchanged through LDS, each wave accumulating
+//    O^T for its slice of the value columns (see the kernel's own comment).
+//  * attn_mla: the latent fallback for other multiples of 16 heads or a separate V tensor;
+//    rows staged in LDS row-major for S^T = K Q^T and transposed for O^T += V^T P^T.
+//  * lse_merge_frag / lse_merge: log-sum-exp merge of candidate splits.
 #include "gfx950_mem.h"
 #include "sa_internal.h"
 
@@ -226,342 +224,24 @@ __global__ void __launch_bounds__(256) attn_rows(AttnArgs a) {
     }
 }
 
-// ------------------------------------------------------------- attn_rows_mfma
-// bf16, one query head per key/value head.  Per 32 gathered rows: QK^T on the matrix
-// cores with the gathered K tile as the A operand (lane (g, c) loads 16 bytes of row c at
-// d = 32 s + 8 g) and the query replicated over the 16 B columns, so every lane receives
-// the scores of rows 4g..4g+3 of each 16-row tile.  Lane (g, c) then loads 16-byte chunk
-// c of exactly those rows of V and accumulates p * V with v_dot2_f32_bf16 on row pairs
-// interleaved by v_perm_b32 (probabilities rounded to bf16, fp32 accumulation).  The four
-// lane groups g hold disjoint rows and merge once at the end.
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-
-template <int D>
-__global__ void __launch_bounds__(256) attn_rows_mfma(AttnArgs a) {
-    constexpr int KS = D / 32;                 // k-steps of the score MFMA
-    constexpr int NCH = D / 8;                 // 16-byte chunks per row
-    constexpr int CPL = NCH >= 16 ? NCH / 16 : 1;  // V chunks per lane
-    const sa_problem& p = a.p;
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, c = lane & 15;
-
-    const long blk = blockIdx.x;
-    int b, i, hk;
-    {
-        const int nib = (p.n_q + 3) / 4;
-        const int wv = threadIdx.x >> 6;
-        if (p.Hkv % 8 == 0) {
-            const int xcd = (int)(blk % 8);
-            const long local = blk / 8;
-            const int hpx = p.Hkv / 8;
-            hk = xcd + 8 * (int)(local % hpx);
-            const long rest = local / hpx;
-            b = (int)(rest / nib);
-            i = (int)(rest % nib) * 4 + wv;
-        } else {
-            hk = (int)(blk % p.Hkv);
-            const long rest = blk / p.Hkv;
-            b = (int)(rest / nib);
-            i = (int)(rest % nib) * 4 + wv;
-        }
-        if (b >= p.B || i >= p.n_q) return;
-    }
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
-    const int L = visible_len(R, b, i);
-    const float sl2 = a.scale * kLog2e;
-    const int h = hk;  // one query head per key/value head
-
-    const uint16_t* Qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2;
-    const uint16_t* Kp = static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1;
-    const uint16_t* Vp = static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1;
-    bf16x8 qb[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Qp + 32 * s + 8 * g));
-
-    float m = -INFINITY, lsum = 0.f;
-    float o[CPL][8];
-#pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[cc][e] = 0.f;
-    const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
-    const bool has_chunk = c < NCH;
-
-    for (int r0 = 0; L > 0 && r0 < p.k; r0 += 32) {
-        // A operand rows: positions 16 mt + c
-        uint4 kf[2][KS];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int e = r0 + 16 * mt + c;
-            const int j = e < p.k ? ix[e] : -1;
-            const bool ok = j >= 0 && j < L;
-            const uint16_t* kr = Kp + (int64_t)(ok ? j : 0) * a.K.s2 + 8 * g;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) kf[mt][s] = ok ? *reinterpret_cast<const uint4*>(kr + 32 * s) : make_uint4(0, 0, 0, 0);
-        }
-        // rows whose scores this lane receives: positions 16 mt + 4 g + r
-        bool okv[2][4];
-        uint4 vf[2][4][CPL];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = r0 + 16 * mt + 4 * g + r;
-                const int j = e < p.k ? ix[e] : -1;
-                okv[mt][r] = j >= 0 && j < L;
-                const uint16_t* vr = Vp + (int64_t)(okv[mt][r] ? j : 0) * a.V.s2;
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc)
-                    vf[mt][r][cc] = (okv[mt][r] && has_chunk) ? *reinterpret_cast<const uint4*>(vr + 8 * (c + 16 * cc))
-                                                               : make_uint4(0, 0, 0, 0);
-            }
-        f32x4 acc[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[mt][s]), qb[s], acc[mt], 0, 0, 0);
-        }
-        float x[2][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x[mt][r] = okv[mt][r] ? acc[mt][r] * sl2 : -INFINITY;
-                mx = fmaxf(mx, x[mt][r]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx);
-        if (mn == -INFINITY) continue;  // uniform: nothing valid in this tile or before
-        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-        m = mn;
-        float pr[2][4];
-        float ps = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[mt][r] = okv[mt][r] ? exp2f(x[mt][r] - mn) : 0.f;
-                ps += pr[mt][r];
-            }
-        lsum = lsum * alpha + ps;
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[cc][e] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                const bf16x2 pw = {(__bf16)pr[mt][2 * pp], (__bf16)pr[mt][2 * pp + 1]};
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const uint4 va = vf[mt][2 * pp][cc], vb = vf[mt][2 * pp + 1][cc];
-                    const uint32_t A4[4] = {va.x, va.y, va.z, va.w}, B4[4] = {vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const uint32_t lo = __builtin_amdgcn_perm(B4[w], A4[w], 0x05040100u);
-                        const uint32_t hi = __builtin_amdgcn_perm(B4[w], A4[w], 0x07060302u);
-                        o[cc][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, lo), o[cc][2 * w], false);
-                        o[cc][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, hi), o[cc][2 * w + 1], false);
-                    }
-                }
-            }
-    }
-    // the four lane groups hold disjoint rows: sum their exp-sums and outputs
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-#pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o[cc][e] += __shfl_xor(o[cc][e], 16);
-            o[cc][e] += __shfl_xor(o[cc][e], 32);
-        }
-    if (g == 0) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        uint16_t* Op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2;
-        if (has_chunk) {
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                uint32_t pk[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    pk[e] = (uint32_t)f32_to_bf16_rne(o[cc][2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[cc][2 * e + 1] * inv) << 16);
-                *reinterpret_cast<uint4*>(Op + 8 * (c + 16 * cc)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-            }
-        }
-        if (a.lse && c == 0)
-            a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
-    }
-}
-
-// --------------------------------------------------------------- attn_rows_dot
-// bf16, one query head per key/value head, head width D = 8 * LPR.  Loads stay coalesced:
-// each group of LPR lanes reads whole history rows (16 bytes per lane, RPI = 64 / LPR rows
-// per load instruction).  The dot product uses v_dot2_f32_bf16 on the packed operands and
-// finishes with an LPR-lane sum built from DPP moves (quad swaps, half-row and row mirrors),
-// so it stays in the VALU.  p * V runs as v_dot2_f32_bf16 on pairs of rows a lane already
-// holds (interleaved by v_perm_b32; probabilities rounded to bf16, fp32 accumulation).
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror: the other quad of 8
-    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);  // row_mirror: the other half of 16
-    if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
-    return x;
-}
-
-template <int D>
-__global__ void __launch_bounds__(256) attn_rows_dot(AttnArgs a) {
-    constexpr int LPR = D / 8;
-    constexpr int RPI = 64 / LPR;
-    constexpr int UNROLL = 8;
-    constexpr int ROWS_IT = RPI * UNROLL;
-    const sa_problem& p = a.p;
-    const int lane = threadIdx.x & 63;
-    const int sub = lane % LPR, rg = lane / LPR;
-
-    const long blk = blockIdx.x;
-    int b, i, hk;
-    {
-        const int nib = (p.n_q + 3) / 4;
-        const int wv = threadIdx.x >> 6;
-        if (p.Hkv % 8 == 0) {
-#ifndef SA_XCD_MAP
-#define SA_XCD_MAP 2
-#endif
-            const int xcd = (int)(blk % 8);
-            const long local = blk / 8;
-            const int hpx = p.Hkv / 8;
-            long rest;
-            if (SA_XCD_MAP == 2) {  // one head at a time per XCD: its K/V rows stay in that L2
-                hk = xcd + 8 * (int)(local / ((long)p.B * nib));
-                rest = local % ((long)p.B * nib);
-            } else {
-                hk = xcd + 8 * (int)(local % hpx);
-                rest = local / hpx;
-            }
-            b = (int)(rest / nib);
-            i = (int)(rest % nib) * 4 + wv;
-        } else {
-            hk = (int)(blk % p.Hkv);
-            const long rest = blk / p.Hkv;
-            b = (int)(rest / nib);
-            i = (int)(rest % nib) * 4 + wv;
-        }
-        if (b >= p.B || i >= p.n_q) return;
-    }
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
-    const int L = visible_len(R, b, i);
-    const float sl2 = a.scale * kLog2e;
-    const int h = hk;
-
-    const uint16_t* Qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)i * a.Q.s2;
-    const uint16_t* Kp = static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1 + 8 * sub;
-    const uint16_t* Vp = static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1 + 8 * sub;
-    const uint4 qv = *reinterpret_cast<const uint4*>(Qp + 8 * sub);
-    const bf16x2 q2[4] = {__builtin_bit_cast(bf16x2, qv.x), __builtin_bit_cast(bf16x2, qv.y),
-                          __builtin_bit_cast(bf16x2, qv.z), __builtin_bit_cast(bf16x2, qv.w)};
-    float m = -INFINITY, l = 0.f, o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
-    const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
-
-    for (int r0 = 0; L > 0 && r0 < p.k; r0 += ROWS_IT) {
-        bool ok[UNROLL];
-        int jv[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int r = r0 + u * RPI + rg;
-            const int j = r < p.k ? ix[r] : -1;
-            ok[u] = j >= 0 && j < L;
-            jv[u] = ok[u] ? j : 0;
-        }
-        uint4 kr[UNROLL], vr[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            kr[u] = ok[u] ? *reinterpret_cast<const uint4*>(Kp + (int64_t)jv[u] * a.K.s2) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            vr[u] = ok[u] ? *reinterpret_cast<const uint4*>(Vp + (int64_t)jv[u] * a.V.s2) : make_uint4(0, 0, 0, 0);
-        float s[UNROLL];
-        float mt = m;
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            float d = __builtin_amdgcn_fdot2_f32_bf16(q2[0], __builtin_bit_cast(bf16x2, kr[u].x), 0.f, false);
-            d = __builtin_amdgcn_fdot2_f32_bf16(q2[1], __builtin_bit_cast(bf16x2, kr[u].y), d, false);
-            d = __builtin_amdgcn_fdot2_f32_bf16(q2[2], __builtin_bit_cast(bf16x2, kr[u].z), d, false);
-            d = __builtin_amdgcn_fdot2_f32_bf16(q2[3], __builtin_bit_cast(bf16x2, kr[u].w), d, false);
-            d = group_sum<LPR>(d);
-            s[u] = ok[u] ? d * sl2 : -INFINITY;
-            mt = fmaxf(mt, s[u]);
-        }
-        // mt == -inf only if nothing was valid so far: then l, o are 0 and stay 0
-        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mt);
-        float pr[UNROLL];
-        float ps = 0.f;
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            pr[u] = ok[u] ? exp2f(s[u] - mt) : 0.f;
-            ps += pr[u];
-        }
-        l = l * alpha + ps;
-        m = mt;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= alpha;
-#pragma unroll
-        for (int u = 0; u < UNROLL; u += 2) {
-            const bf16x2 pw = {(__bf16)pr[u], (__bf16)pr[u + 1]};
-            const uint32_t A4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-            const uint32_t B4[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t lo = __builtin_amdgcn_perm(B4[w], A4[w], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(B4[w], A4[w], 0x07060302u);
-                o[2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, lo), o[2 * w], false);
-                o[2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pw, __builtin_bit_cast(bf16x2, hi), o[2 * w + 1], false);
-            }
-        }
-    }
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-        float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off), o2[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[e], off);
-        merge_state(m, l, o, 8, m2, l2, o2);
-    }
-    if (rg == 0) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* Op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2 + 8 * sub;
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            pk[e] = (uint32_t)f32_to_bf16_rne(o[2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * e + 1] * inv) << 16);
-        *reinterpret_cast<uint4*>(Op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        if (a.lse && sub == 0)
-            a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-    }
-}
-
 // --------------------------------------------------------------- attn_rows_buf
-// The same computation as attn_rows_dot with less instruction overhead per gathered row:
+// bf16, one query head per key/value head, head width D.  Loads stay coalesced and the
+// arithmetic stays in the VALU (the contraction is a GEMV per candidate set):
 //  * K and V rows are fetched with raw buffer loads on a per-(batch, head) resource, so a
 //    row address is one 32-bit multiply; an invalid entry gets an offset past the end of
 //    the resource and the hardware returns zeros (no branches, no zero-fill moves);
 //  * each lane covers 32 bytes (16 elements) of a row in two 16-byte pieces, one in each
 //    half-row, so every load instruction reads whole contiguous half-rows; LPR = D/16
-//    lanes per row, one fewer DPP step per element pair;
+//    lanes per row; q.k uses v_dot2_f32_bf16 and an LPR-lane sum of DPP moves (quad swaps,
+//    half-row and row mirrors); p.V runs as v_dot2_f32_bf16 on pairs of rows interleaved by
+//    v_perm_b32 (probabilities rounded to bf16, fp32 accumulation);
 //  * row group rg takes UNROLL consecutive candidate entries, fetched by one 16-byte load;
 //  * exponentials use v_exp_f32 directly on arguments <= 0.
 // Requires k % 4 == 0 and every (batch, head) slice of K and V below 2^31 bytes.
@@ -1489,10 +1169,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     if (attn_uses_mla(p, a.Q.dtype)) {
         const int G = p.Hq / p.Hkv;
         const long units = (long)p.B * p.n_q * p.Hkv * a.splits;
-#ifndef SA_MLA_VARIANT
-#define SA_MLA_VARIANT 2
-#endif
-        const bool lds_kernel = SA_MLA_VARIANT == 2 && mla_lds_ok(a);
+        const bool lds_kernel = mla_lds_ok(a);
         if (lds_kernel) {
             if (G == 128) hipLaunchKernelGGL(attn_mla_lds<4>, dim3((unsigned)units), dim3(256), 0, s, a);
             else if (G == 64) hipLaunchKernelGGL(attn_mla_lds<2>, dim3((unsigned)units), dim3(128), 0, s, a);
@@ -1512,30 +1189,19 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     const int G = p.Hq / p.Hkv;
-#ifndef SA_ROWS_VARIANT
-#define SA_ROWS_VARIANT 4
-#endif
-    if (SA_ROWS_VARIANT != 1 && a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v &&
-        (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
-        const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
-        // 32-bit row offsets from 24-bit multiplies: rows < 2^24, row strides < 2^24 bytes
+    if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
+        // 32-bit row offsets from 24-bit multiplies: rows < 2^24, row strides < 2^24 bytes;
+        // candidate lists read four at a time
         const bool buf_ok = (p.k % 4 == 0) && (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) &&
                             (int64_t)p.n_kv * a.V.s2 * 2 < (1LL << 31) && ((uintptr_t)a.idx & 15) == 0 &&
                             p.n_kv < (1 << 24) && a.K.s2 * 2 < (1 << 24) && a.V.s2 * 2 < (1 << 24);
-        if (SA_ROWS_VARIANT == 4 && buf_ok) {
+        if (buf_ok) {
+            const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
             if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_buf<64>, dim3(nblk), dim3(256), 0, s, a);
             else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_buf<128>, dim3(nblk), dim3(256), 0, s, a);
             else hipLaunchKernelGGL(attn_rows_buf<256>, dim3(nblk), dim3(256), 0, s, a);
-        } else if (SA_ROWS_VARIANT == 2) {
-            if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_mfma<64>, dim3(nblk), dim3(256), 0, s, a);
-            else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_mfma<128>, dim3(nblk), dim3(256), 0, s, a);
-            else hipLaunchKernelGGL(attn_rows_mfma<256>, dim3(nblk), dim3(256), 0, s, a);
-        } else {
-            if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_dot<64>, dim3(nblk), dim3(256), 0, s, a);
-            else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_dot<128>, dim3(nblk), dim3(256), 0, s, a);
-            else hipLaunchKernelGGL(attn_rows_dot<256>, dim3(nblk), dim3(256), 0, s, a);
+            return hipGetLastError();
         }
-        return hipGetLastError();
     }
     const int esz = a.Q.dtype == SA_F32 ? 4 : 2;
     const int LPR = p.d_qk * esz / 16;

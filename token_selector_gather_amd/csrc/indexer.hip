@@ -4,15 +4,18 @@
 // ("PaperTrace 2.2 · Fine-grained indexing", §1.1 and §3.2: per-query index heads, one
 // index key per token shared by all heads, query-dependent head weights).
 //
-// Matrix-core path (bf16 index queries; bf16 or OCP-e4m3 index keys).  The contraction
+// Matrix-core paths (bf16 index queries; bf16 or OCP-e4m3 index keys).  The contraction
 // is a GEMM with M = (query, index head) rows, N = history positions, K = d_idx, on
-// v_mfma_f32_16x16x32_bf16.  One wave owns 64 rows (4 M-tiles: 64/Hidx queries) and a
-// chunk of 256 positions; its index-query fragments stay in registers for the whole
-// chunk.  e4m3 keys widen to bf16 exactly in hardware (v_cvt_scalef32_pk_bf16_fp8, scale
-// 1).  The epilogue applies ReLU and the head weights to the fp32 accumulators and sums
-// the heads inside the accumulator layout (in-lane, then xor-16 / xor-32 lane swaps), so
-// the order of every reduction is the same for every position j: byte-identical keys get
-// bit-identical scores.
+// v_mfma_f32_16x16x32_bf16; e4m3 keys widen to bf16 exactly in hardware
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1).  The epilogue applies ReLU and the head weights to
+// the fp32 accumulators and sums the heads inside the accumulator layout (in-lane, then
+// lane swaps between rows), in the same order for every position j: byte-identical keys
+// get bit-identical scores.  Three layouts:
+//  * indexer_pf: many query rows (prefill); a workgroup walks the causal history of a block
+//    of rows once, keys widened to bf16 once per LDS chunk;
+//  * indexer_dec: few query rows (decode); the waves split the keys of one row;
+//  * indexer_mfma3: the remaining shapes (4 or 8 index heads, moderate row counts).
+// indexer_valu covers f32 inputs and other widths.
 //
 // ReLU is written as (z > 0 ? z : 0*z) so that a NaN or -inf dot product stays non-finite
 // and reaches the selection's finiteness check instead of being clipped to zero.
@@ -95,153 +98,7 @@ __global__ void __launch_bounds__(256) indexer_valu(IndexerArgs a) {
 constexpr int kChunk = 256;  // positions per wave
 constexpr int kMT = 4;       // 16-row M-tiles per wave (64 rows)
 
-template <int KSTEPS, bool KE4M3>
-__device__ __forceinline__ void load_b(const uint8_t* kbase_bytes, bool ok, bf16x8 (&bv)[KSTEPS], int lane) {
-    const int dof = 8 * (lane >> 4);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        if (KE4M3) {
-            uint2 u = ok ? *reinterpret_cast<const uint2*>(kbase_bytes + 32 * s + dof) : make_uint2(0, 0);
-            bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.x, 1.0f, false);
-            bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.x, 1.0f, true);
-            bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.y, 1.0f, false);
-            bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u.y, 1.0f, true);
-            bv[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        } else {
-            uint4 u = ok ? *reinterpret_cast<const uint4*>(kbase_bytes + 2 * (32 * s + dof)) : make_uint4(0, 0, 0, 0);
-            bv[s] = __builtin_bit_cast(bf16x8, u);
-        }
-    }
-}
 
-template <int KSTEPS, bool KE4M3, int H>
-__global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int n_groups, int n_chunks) {
-    const sa_problem& p = a.p;
-    const int lane = threadIdx.x & 63;
-    const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int total = p.B * n_groups * n_chunks;
-    if (wave_id >= total) return;
-    // longest work first: higher query groups see longer causal histories
-    const int chunk = wave_id % n_chunks;
-    const int rest = wave_id / n_chunks;
-    const int g = n_groups - 1 - (rest % n_groups);
-    const int b = rest / n_groups;
-    constexpr int QPG = 64 / H;  // queries per wave group
-    const int i0 = g * QPG;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
-
-    // visible lengths of this group's queries (lane q holds query q's length)
-    int Lq = 0;
-    if (lane < QPG && i0 + lane < p.n_q) Lq = visible_len(R, b, i0 + lane);
-    int Lmax = Lq;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) Lmax = max(Lmax, __shfl_xor(Lmax, o));
-
-    const int j_begin = chunk * kChunk;
-    const int j_end = min(j_begin + kChunk, p.n_kv);
-    const int j_comp_end = min(j_end, Lmax);
-
-    // A fragments: row r = 16*mt + lane%16 -> query r / H, head r % H; d = 32 s + 8 (lane/16)
-    bf16x8 av[kMT][KSTEPS];
-    float wv[kMT][4];
-    if (j_begin < j_comp_end) {
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            const int r = 16 * mt + (lane & 15);
-            const int qi = i0 + r / H, h = r % H;
-            const bool ok = qi < p.n_q;
-            const uint16_t* qb = static_cast<const uint16_t*>(a.q.data) + (ok ? (b * a.q.s0 + qi * a.q.s1 + h * a.q.s2) : 0);
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                uint4 u = ok ? *reinterpret_cast<const uint4*>(qb + 32 * s + 8 * (lane >> 4)) : make_uint4(0, 0, 0, 0);
-                av[mt][s] = __builtin_bit_cast(bf16x8, u);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * mt + 4 * (lane >> 4) + e;
-                const int q2 = i0 + rr / H, h2 = rr % H;
-                wv[mt][e] = q2 < p.n_q ? static_cast<const float*>(a.w.data)[b * a.w.s0 + q2 * a.w.s1 + h2] : 0.f;
-            }
-        }
-    }
-
-    const int64_t kstride_bytes = a.k.s1 * (KE4M3 ? 1 : 2);
-    const uint8_t* kb0 = static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2);
-
-    for (int j0 = j_begin; j0 < j_end; j0 += 16) {
-        const int j = j0 + (lane & 15);
-        if (j0 >= j_comp_end) {
-            // nothing visible for any query of the group from here on
-            if (a.fill_invisible && j < j_end) {
-                for (int q = (lane >> 4); q < QPG; q += 4)
-                    if (i0 + q < p.n_q) a.scores[(int64_t)(b * p.n_q + i0 + q) * a.row_stride + j] = -INFINITY;
-            }
-            continue;
-        }
-        bf16x8 bv[KSTEPS];
-        load_b<KSTEPS, KE4M3>(kb0 + (int64_t)j * kstride_bytes, j < j_end, bv, lane);
-        f32x4 acc[kMT];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][s], bv[s], acc[mt], 0, 0, 0);
-
-        // epilogue: w * ReLU, summed over the heads of each query inside the C layout
-        float part[kMT];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            float t = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t = fmaf(wv[mt][e], relu_keep_nonfinite(acc[mt][e]), t);
-            part[mt] = t;
-        }
-        // Lane (g = lane/16) holds rows 4g..4g+3 of every M-tile.
-        // H >= 16: an M-tile belongs to one query; sum tiles of the same query, then over g.
-        // H == 8: rows 0-7 (g 0,1) and 8-15 (g 2,3) are two queries; sum over g pairs.
-        // H == 4: each g is its own query.
-        if constexpr (H >= 16) {
-            constexpr int tpq = H / 16;  // tiles per query
-#pragma unroll
-            for (int q = 0; q < QPG; ++q) {
-                float v = 0.f;
-#pragma unroll
-                for (int t = 0; t < tpq; ++t) v += part[q * tpq + t];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                const int qi = i0 + q;
-                if (lane < 16 && qi < p.n_q) {
-                    const int Lh = __shfl(Lq, q);
-                    const bool vis = j < Lh;
-                    if (j < j_end && (vis || a.fill_invisible))
-                        a.scores[(int64_t)(b * p.n_q + qi) * a.row_stride + j] = vis ? v : -INFINITY;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) {
-                float v = part[mt];
-                int qloc;
-                if constexpr (H == 8) {
-                    v += __shfl_xor(v, 16);
-                    qloc = 2 * mt + (lane >> 5);
-                } else {  // H == 4
-                    qloc = 4 * mt + (lane >> 4);
-                }
-                const int Lh = __shfl(Lq, qloc);
-                const int qi = i0 + qloc;
-                const bool writer = (H == 8) ? ((lane & 16) == 0) : true;
-                if (writer && qi < p.n_q) {
-                    const bool vis = j < Lh;
-                    if (j < j_end && (vis || a.fill_invisible))
-                        a.scores[(int64_t)(b * p.n_q + qi) * a.row_stride + j] = vis ? v : -INFINITY;
-                }
-            }
-        }
-    }
-}
 
 // ------------------------------------------------------------------ indexer_dec
 // Few query rows (decode): a workgroup takes one query row and a range of at most 2048 keys;
@@ -546,214 +403,6 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
             if (qi >= p.n_q) break;
             float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
             for (int j = start + lane; j < p.n_kv; j += 64) row[j] = -INFINITY;
-        }
-    }
-}
-
-// ------------------------------------------------------- matrix-core path, shared keys
-// Four waves of a workgroup read the same history positions: in prefill they own four
-// consecutive query groups (their key fragments then hit the L1), in decode they split
-// one query group's history four ways.  A workgroup covers a long key range, so each
-// wave loads its query fragments once per range, and the next 16-key tile is fetched
-// (raw) while the current one is multiplied.  With FAST_RELU the epilogue clips with one
-// max per element; finiteness of the inputs is then checked by index_finite_check.
-template <int KSTEPS, bool KE4M3>
-struct BRaw;
-template <int KSTEPS>
-struct BRaw<KSTEPS, true> { uint2 v[KSTEPS]; };
-template <int KSTEPS>
-struct BRaw<KSTEPS, false> { uint4 v[KSTEPS]; };
-
-// Key fragment of one 16-key tile: raw buffer loads on the batch's key rows, so an invalid
-// row (offset past the resource) reads as zeros without a branch and the compiler can count
-// outstanding loads exactly.
-template <int KSTEPS, bool KE4M3>
-__device__ __forceinline__ void braw_load(__amdgpu_buffer_rsrc_t rs, uint32_t row_off, BRaw<KSTEPS, KE4M3>& r,
-                                          int lane) {
-    const uint32_t dof = 8u * (lane >> 4) * (KE4M3 ? 1u : 2u);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        const uint32_t off = row_off + (uint32_t)(32 * s) * (KE4M3 ? 1u : 2u) + dof;
-        if constexpr (KE4M3) {
-            auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-            r.v[s] = make_uint2(v[0], v[1]);
-        } else {
-            auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-            r.v[s] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
-    }
-}
-
-template <int KSTEPS, bool KE4M3>
-__device__ __forceinline__ void braw_widen(const BRaw<KSTEPS, KE4M3>& r, bf16x8 (&bv)[KSTEPS]) {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        if constexpr (KE4M3) {
-            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].x, 1.0f, false);
-            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].x, 1.0f, true);
-            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].y, 1.0f, false);
-            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[s].y, 1.0f, true);
-            bv[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        } else {
-            bv[s] = __builtin_bit_cast(bf16x8, r.v[s]);
-        }
-    }
-}
-
-template <int KSTEPS, bool KE4M3, int H, bool DECODE, bool FAST_RELU>
-__global__ void __launch_bounds__(256) indexer_mfma2(IndexerArgs a, int n_groups, int n_qblk, int n_rng, int rng_len) {
-    const sa_problem& p = a.p;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    constexpr int QPG = 64 / H;
-    long wg = blockIdx.x;
-    int b, g, j_begin, j_end;
-    if (DECODE) {
-        const int rng = (int)(wg % n_rng);
-        const long rest = wg / n_rng;
-        g = (int)(rest % n_groups);
-        b = (int)(rest / n_groups);
-        const int sub = rng_len / 4;
-        j_begin = rng * rng_len + wv * sub;
-        j_end = min(j_begin + sub, p.n_kv);
-    } else {
-        const int rng = (int)(wg % n_rng);
-        const long rest = wg / n_rng;
-        const int qb = n_qblk - 1 - (int)(rest % n_qblk);  // longest causal histories first
-        b = (int)(rest / n_qblk);
-        g = qb * 4 + wv;
-        j_begin = rng * rng_len;
-        j_end = min(j_begin + rng_len, p.n_kv);
-    }
-    g = __builtin_amdgcn_readfirstlane(g);  // wave-uniform (wave index and block index only)
-    b = __builtin_amdgcn_readfirstlane(b);
-    if (g >= n_groups || j_begin >= p.n_kv) return;
-    const int i0 = g * QPG;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
-    int Lq = 0;
-    if (lane < QPG && i0 + lane < p.n_q) Lq = visible_len(R, b, i0 + lane);
-    int Lmax = Lq;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) Lmax = max(Lmax, __shfl_xor(Lmax, o));
-    // wave-uniform by construction; say so, so that the key resource below lives in SGPRs
-    j_begin = __builtin_amdgcn_readfirstlane(j_begin);
-    j_end = __builtin_amdgcn_readfirstlane(j_end);
-    const int j_comp_end = __builtin_amdgcn_readfirstlane(min(j_end, Lmax));
-
-    if (j_begin < j_comp_end) {
-        bf16x8 av[kMT][KSTEPS];
-        float wvv[kMT][4];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            const int r = 16 * mt + (lane & 15);
-            const int qi = i0 + r / H, h = r % H;
-            const bool ok = qi < p.n_q;
-            const uint16_t* qb = static_cast<const uint16_t*>(a.q.data) + (ok ? (b * a.q.s0 + qi * a.q.s1 + h * a.q.s2) : 0);
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                uint4 u = ok ? *reinterpret_cast<const uint4*>(qb + 32 * s + 8 * (lane >> 4)) : make_uint4(0, 0, 0, 0);
-                av[mt][s] = __builtin_bit_cast(bf16x8, u);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * mt + 4 * (lane >> 4) + e;
-                const int q2 = i0 + rr / H, h2 = rr % H;
-                wvv[mt][e] = q2 < p.n_q ? static_cast<const float*>(a.w.data)[b * a.w.s0 + q2 * a.w.s1 + h2] : 0.f;
-            }
-        }
-        const uint32_t kstride_bytes = (uint32_t)(a.k.s1 * (KE4M3 ? 1 : 2));
-        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (KE4M3 ? 1 : 2)), (short)0,
-            (int)((uint32_t)j_comp_end * kstride_bytes), 0x00020000);
-        // score rows of this wave's query group; lanes that write nothing store out of range
-        const int nrows = min(QPG, p.n_q - i0);
-        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-            a.scores + (int64_t)(b * p.n_q + i0) * a.row_stride, (short)0,
-            (int)((uint32_t)nrows * (uint32_t)a.row_stride * 4u), 0x00020000);
-        // rows at or past j_comp_end lie outside the resource and read as zeros
-        auto row_off = [&](int j) -> uint32_t { return j < j_comp_end ? (uint32_t)j * kstride_bytes : 0x80000000u; };
-        // three key buffers in fixed roles (no register copies of in-flight loads), each
-        // filled two tiles before it is multiplied
-        BRaw<KSTEPS, KE4M3> ba, bb, bc;
-        braw_load<KSTEPS, KE4M3>(krs, row_off(j_begin + (lane & 15)), ba, lane);
-        braw_load<KSTEPS, KE4M3>(krs, row_off(j_begin + 16 + (lane & 15)), bb, lane);
-        auto tile = [&](const BRaw<KSTEPS, KE4M3>& cur, const int j0) {
-            const int j = j0 + (lane & 15);
-            bf16x8 bv[KSTEPS];
-            braw_widen<KSTEPS, KE4M3>(cur, bv);
-            f32x4 acc[kMT];
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt][s], bv[s], acc[mt], 0, 0, 0);
-            float part[kMT];
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) {
-                float t = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float z = acc[mt][e];
-                    t = fmaf(wvv[mt][e], FAST_RELU ? __builtin_amdgcn_fmed3f(z, 0.f, INFINITY) : relu_keep_nonfinite(z), t);
-                }
-                part[mt] = t;
-            }
-            if constexpr (H >= 16) {
-                constexpr int tpq = H / 16;
-#pragma unroll
-                for (int q = 0; q < QPG; ++q) {
-                    float v = 0.f;
-#pragma unroll
-                    for (int t = 0; t < tpq; ++t) v += part[q * tpq + t];
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
-                    const int Lh = __shfl(Lq, q);
-                    const bool vis = j < Lh;
-                    const bool wr = lane < 16 && i0 + q < p.n_q && j < j_end && (vis || a.fill_invisible);
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vis ? v : -INFINITY), srs,
-                                                          wr ? (uint32_t)(q * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) {
-                    float v = part[mt];
-                    int qloc;
-                    if constexpr (H == 8) {
-                        v += __shfl_xor(v, 16);
-                        qloc = 2 * mt + (lane >> 5);
-                    } else {
-                        qloc = 4 * mt + (lane >> 4);
-                    }
-                    const int Lh = __shfl(Lq, qloc);
-                    const bool writer = (H == 8) ? ((lane & 16) == 0) : true;
-                    const bool vis = j < Lh;
-                    const bool wr = writer && i0 + qloc < p.n_q && j < j_end && (vis || a.fill_invisible);
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vis ? v : -INFINITY), srs,
-                                                          wr ? (uint32_t)(qloc * a.row_stride + j) * 4u : 0x80000000u, 0, 0);
-                }
-            }
-        };
-        for (int j0 = j_begin; j0 < j_comp_end; j0 += 48) {
-            braw_load<KSTEPS, KE4M3>(krs, row_off(j0 + 32 + (lane & 15)), bc, lane);
-            tile(ba, j0);
-            if (j0 + 16 >= j_comp_end) break;
-            braw_load<KSTEPS, KE4M3>(krs, row_off(j0 + 48 + (lane & 15)), ba, lane);
-            tile(bb, j0 + 16);
-            if (j0 + 32 >= j_comp_end) break;
-            braw_load<KSTEPS, KE4M3>(krs, row_off(j0 + 64 + (lane & 15)), bb, lane);
-            tile(bc, j0 + 32);
-        }
-    }
-    if (a.fill_invisible) {
-        // positions of the range past the computed tiles: beyond every visible history of the
-        // group (invisible positions inside computed tiles were written above)
-        const int start = j_begin < j_comp_end ? j_begin + ((j_comp_end - j_begin + 15) / 16) * 16 : j_begin;
-        for (int q = 0; q < QPG; ++q) {
-            const int qi = i0 + q;
-            if (qi >= p.n_q) break;
-            float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
-            for (int j = start + lane; j < j_end; j += 64) row[j] = -INFINITY;
         }
     }
 }
