@@ -40,6 +40,10 @@ def _print(x):
                                 q_pos0=[494], lens=[500])),
     ("mla_two_kv_heads", dict(n_q=30, n_kv=130, Hq=32, Hkv=2, d_qk=576, d_v=512, k=45, mla=False,
                               q_pos0=[100], lens=[130])),
+    ("mla_g32_aliased_v", dict(n_q=12, n_kv=900, Hq=32, Hkv=1, d_qk=576, d_v=512, k=230, mla=True,
+                               q_pos0=[888], lens=[900])),
+    ("mla_g64_aliased_v_two_rows", dict(B=2, n_q=10, n_kv=700, Hq=64, Hkv=1, d_qk=576, d_v=512, k=150, mla=True,
+                                        q_pos0=[650, 90], lens=[660, 100])),
 ])
 def test_edge_case_end_to_end(name, kw):
     _print("edge " + name)
@@ -106,3 +110,26 @@ def test_sparse_attn_empty_candidate_rows_give_zero_and_neg_inf():
     idx = np.full((1, 8, 4), -1, np.int32)
     O, lse = gc.gpu_sparse_attn(W, idx)
     assert (O == 0).all() and np.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("Hq", [32, 64, 128])
+def test_mla_logits_far_above_the_first_tile_rerun_the_set(Hq):
+    """The latent kernel fixes each head's reference maximum at its first tile of
+    candidates; a later logit more than 64 (log2 units) above it makes the kernel run the
+    set again against the true maximum.  Low positions get small keys and the queries are
+    scaled up, so every head takes that second run."""
+    _print("mla second run Hq=%d" % Hq)
+    W = sa_synth.custom(B=1, n_q=4, n_kv=400, k=160, Hq=Hq, Hkv=1, d_qk=576, d_v=512, mla=True,
+                        q_pos0=[396], lens=[400])
+    K = sa_synth.bf16_to_f32(W["K"]).astype(np.float64)
+    K[:, :, :200, :] *= 0.01
+    W["K"] = sa_synth.encode(K, BF16)
+    W["Q"] = sa_synth.encode(sa_synth.bf16_to_f32(W["Q"]).astype(np.float64) * 100.0, BF16)
+    rows = np.arange(4, dtype=np.int32)
+    # every set starts below position 200 and reaches past it, where logits are far above
+    # the first tile's
+    idx = np.stack([np.arange(100 + 20 * i, 260 + 20 * i, dtype=np.int32) for i in range(4)])
+    O, lse = gc.gpu_sparse_attn(W, idx.reshape(1, 4, 160))
+    O_or, lse_or = orc.attend(W, idx, rows)
+    assert lse_or.min() > 50
+    gc.compare_attention(W, rows, O, lse, O_or, lse_or)

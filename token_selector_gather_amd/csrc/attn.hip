@@ -639,10 +639,12 @@ __global__ void __launch_bounds__(256) lse_merge(AttnArgs a) {
 // Latent-head attention for 32-head groups (Hq/Hkv a multiple of 32, V = the first d_v
 // columns of K).  One workgroup per (query row, candidate split); wave w owns query heads
 // 32w..32w+31.  Gathered rows reach LDS through buffer loads that write LDS directly
-// (no staging registers), in a ring of three 32-row tiles so that two tiles are in
-// flight while one is consumed.  Per tile each wave runs S^T = K Q^T (v_mfma_f32_32x32x16
-// _bf16, Q^T fragments in registers) and O^T += V^T P^T, reading V^T out of the same
-// row-major tile with transposing LDS reads (ds_read_b64_tr_b16).  Each head's reference
+// (no staging registers), in a ring of four 32-row tiles: while tiles t and t + 1 are read,
+// t + 2 and t + 3 are in flight.  Iteration t runs the softmax of tile t, S^T = K Q^T of tile
+// t + 1 (v_mfma_f32_16x16x32_bf16, Q^T fragments in registers), then O^T += V^T P^T of tile t
+// (v_mfma_f32_32x32x16_bf16), reading V^T out of the same row-major tile with transposing LDS
+// reads (ds_read_b64_tr_b16); each wave accumulates O^T for its slice of the value columns
+// over all heads, so P goes through LDS.  Each head's reference
 // maximum is fixed at its first valid tile, so the accumulators are never rescaled: any
 // reference gives the same softmax, and while no logit exceeds it by more than 64 (exp2
 // units) every probability and sum stays far inside fp32 range.  A set that breaks this
@@ -655,6 +657,7 @@ constexpr int ROWB = DQK * 2;          // bytes per row in LDS
 constexpr int TILE_B = T * ROWB;       // bytes per tile
 constexpr int NI_ALL = T * CHR / 64;   // 16-byte LDS-direct loads per tile, 64 lanes each
 constexpr int MAXE = 2048;             // candidates per workgroup
+constexpr int RING = 4;                // tile slots in LDS
 constexpr float kLazy = 64.f;          // exp2 headroom above the reference maximum
 // Tile layout in LDS (36 KB): 32 main blocks of 1 KB, block 4 rg + cg holding 16-byte chunks
 // 16 cg .. 16 cg + 15 of rows 4 rg .. 4 rg + 3 (row r at slot 16 (r & 3) + cslot(r, chunk % 16)),
@@ -662,13 +665,16 @@ constexpr float kLazy = 64.f;          // exp2 headroom above the reference maxi
 // at slot 8 (r & 7) + ((chunk - 64) ^ tswz(r))).  One LDS-direct load fills one block from 4
 // (or 8) rows, so each load reads whole 128-byte lines; the swizzles make the 16-row reads of
 // the K operand and the 4-row transposing reads of the V operand free of bank conflicts.
-__device__ __forceinline__ int rswz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
-__device__ __forceinline__ int cslot(int r, int c) { return c ^ rswz(r) ^ (8 * ((c >> 1) & 1)); }
-// chunk (0..15) of row r stored in slot y (inverse of cslot)
-__device__ __forceinline__ int cslot_inv(int r, int y) {
-    const int x = y ^ rswz(r);
-    return x ^ (8 * ((x >> 1) & 1));
+// Row swizzle: a linear map of the row's low four bits (bit0 = r0, bit1 = r1, bit2 = r0^r1^r2,
+// bit3 = r0^r3).  A 128-bit read serves half a wave at a time: the K-operand reads (16 rows x
+// two adjacent chunks per half wave) and the 4-row transposing V reads then touch every bank
+// once per pass.
+__device__ __forceinline__ int rswz(int r) {
+    return (r & 3) | (((r ^ (r >> 1) ^ (r >> 2)) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
 }
+__device__ __forceinline__ int cslot(int r, int c) { return c ^ rswz(r); }
+// chunk (0..15) of row r stored in slot y (inverse of cslot)
+__device__ __forceinline__ int cslot_inv(int r, int y) { return y ^ rswz(r); }
 __device__ __forceinline__ int tswz(int r) { return (r >> 1) & 7; }
 }  // namespace mla
 
@@ -695,20 +701,25 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     constexpr int KS = DQK / 32;       // k-steps of S^T on 16x16x32 fragments
     constexpr int MW = DV / 32 / NW;   // 32-row tiles of O^T (rows = d) owned by one wave
     static_assert(MW * NW * 32 == DV, "the value columns must split evenly over the waves");
-    constexpr int PD = 3;              // k-steps of K operands read ahead of their MFMAs
+    constexpr int PD = 2;              // k-steps of K operands read ahead of their MFMAs
     constexpr int PB = 2 * NW * 1024;  // bytes of P^T fragments per tile
-    __shared__ __attribute__((aligned(16))) uint8_t ring[3 * TILE_B];
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * PB];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[RING * TILE_B];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[PB];
     __shared__ uint32_t s_off[MAXE];
-    __shared__ uint32_t s_mask[MAXE / T];
-    __shared__ float s_ml[2][32 * NW];
 
     const sa_problem& p = a.p;
     const int G = p.Hq / p.Hkv;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n32 = lane & 31, h = lane >> 5, l15 = lane & 15, g = lane >> 4;
     const int S = a.splits;
-    const long unit = blockIdx.x;
+    // Split sets: the splits of one row run on one XCD (workgroups go round-robin over the
+    // eight XCDs), so that row's query fragments come from HBM once and from L2 after
+    long unit = blockIdx.x;
+    if (S > 1) {
+        const long units = (long)p.B * p.n_q * p.Hkv * S;
+        unit = (long)(blockIdx.x % 8) * ((units + 7) / 8) + blockIdx.x / 8;
+        if (unit >= units) return;
+    }
     const int split = (int)(unit % S);
     const long rowkv = unit / S;
     const int hk = (int)(rowkv % p.Hkv);
@@ -723,37 +734,22 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     const int ne = max(0, min(p.k, e_begin + per) - e_begin);
     const int32_t* ix = a.idx + row * (int64_t)p.k + e_begin;
     // byte offsets of the candidate rows (out-of-range offset for invalid entries, which
-    // the buffer loads turn into zero rows) and one validity bit per candidate
+    // the buffer loads turn into zero rows); the number of tiles up to the last one holding
+    // a valid candidate goes through the P buffer, which is first written inside the loop
+    int* s_nt = reinterpret_cast<int*>(pbuf);
+    if (threadIdx.x == 0) *s_nt = 0;
+    __syncthreads();
     const int ne64 = (ne + 63) & ~63;
     for (int e = threadIdx.x; e < ne64; e += 64 * NW) {
         const int j = e < ne ? ix[e] : -1;
         const bool ok = j >= 0 && j < L;
         s_off[e] = ok ? (uint32_t)j * rowb : 0x80000000u;
         const uint64_t bal = __ballot(ok);
-        if (lane == 0) {
-            s_mask[e >> 5] = (uint32_t)bal;
-            s_mask[(e >> 5) + 1] = (uint32_t)(bal >> 32);
-        }
+        if (lane == 0 && bal != 0) atomicMax(s_nt, (e >> 5) + ((bal >> 32) != 0 ? 2 : 1));
     }
     __syncthreads();
-    // tiles after the last one holding a valid candidate are never fetched
-    int nt;
-    {
-        const int ntiles = (ne + T - 1) / T;
-        const uint64_t any = __ballot(lane < ntiles && s_mask[lane] != 0u);
-        nt = any ? 64 - __builtin_clzll(any) : 0;
-    }
+    const int nt = __builtin_amdgcn_readfirstlane(*s_nt);
 
-    // Q^T fragments (B operand of S^T): head 32 wv + 16 nt + lane%16, d = 32 s + 8 (lane/16) + 0..7
-    uint4 qf[KS][2];
-    {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + (hk * G + 32 * wv + l15) * a.Q.s1 +
-                             (int64_t)i * a.Q.s2 + 8 * g;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) qf[s][nt] = *reinterpret_cast<const uint4*>(qp + 16 * nt * a.Q.s1 + 32 * s);
-    }
     const char* kbase = static_cast<const char*>(a.K.data) + (b * a.K.s0 + hk * a.K.s1) * 2;
     v4i krs;
     krs[0] = (int)(uint32_t)(uintptr_t)kbase;
@@ -771,21 +767,23 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     auto tile_offsets = [&](int tile) {
         TileOff o;
         const bool real = tile < nt;
-        const uint32_t* off = s_off + (real ? tile : 0) * T;
+        const uint32_t* off = s_off + min(tile, nt - 1) * T;  // read unconditionally (no branch)
 #pragma unroll
         for (int q = 0; q < NRG; ++q) {
             const int r = 4 * (wv * NRG + q) + (lane >> 4);
-            o.m[q] = real ? off[r] + 16u * (uint32_t)cslot_inv(r, lane & 15) : 0x80000000u;
+            const uint32_t v = off[r];
+            o.m[q] = real ? v + 16u * (uint32_t)cslot_inv(r, lane & 15) : 0x80000000u;
         }
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
             const int r = 8 * (wv * NT + q) + (lane >> 3);
-            o.t[q] = real ? off[r] + 16u * (uint32_t)(64 + ((lane & 7) ^ tswz(r))) : 0x80000000u;
+            const uint32_t v = off[r];
+            o.t[q] = real ? v + 16u * (uint32_t)(64 + ((lane & 7) ^ tswz(r))) : 0x80000000u;
         }
         return o;
     };
     auto dma = [&](int tile, int ii, const TileOff& o) {
-        const uint32_t base = ring_lds + (uint32_t)((tile % 3) * TILE_B);
+        const uint32_t base = ring_lds + (uint32_t)((tile % RING) * TILE_B);
         if (ii < NM) {
             const int blk = wv * NM + ii;
             lds_dma16(krs, base + 1024u * (uint32_t)blk, o.m[ii >> 2], 256u * (uint32_t)(ii & 3));
@@ -797,16 +795,14 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
 
     // K operand of S^T k-step s, position tile pt: row r = 16 pt + lane%16, chunk c = 4 s + lane/16;
     // kadr[pt][s % 4] + 1024 (s / 4) for s < 16, tail blocks for s = 16, 17
-    int kadr[2][4], ktail[2][2];
+    // (row 16 + r has the swizzles of row r, so position tile 1 sits at a fixed offset:
+    // 16 KB in the main blocks, 2 KB in the tail blocks)
+    int kadr[4], ktail[2];
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-        const int r = 16 * pt + l15;
+    for (int k4 = 0; k4 < 4; ++k4) kadr[k4] = 4096 * (l15 >> 2) + 256 * (l15 & 3) + 16 * cslot(l15, 4 * k4 + g);
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) kadr[pt][k4] = 4096 * (r >> 2) + 256 * (r & 3) + 16 * cslot(r, 4 * k4 + g);
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-            ktail[pt][k2] = 32768 + 1024 * (r >> 3) + 16 * (8 * (r & 7) + ((4 * k2 + g) ^ tswz(r)));
-    }
+    for (int k2 = 0; k2 < 2; ++k2)
+        ktail[k2] = 32768 + 1024 * (l15 >> 3) + 16 * (8 * (l15 & 7) + ((4 * k2 + g) ^ tswz(l15)));
     // V operand of O^T (transposing reads): this lane supplies row r = 16 s' + 8 h + 4 e2 + lane%16/4
     // and 8 bytes of chunk 4 mt + c2, c2 = 2 (lane/16 % 2) + lane%4/2.  The chunk's slot splits
     // into bits 0-1 (lane constant) and bits 2-3 = mt % 4 ^ (swizzle bits 2-3): address
@@ -816,13 +812,14 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
         const int r = 8 * h + 4 * e2 + (l15 >> 2);
-        const int X = rswz(r) ^ (8 * g2);
+        const int X = rswz(r);
         vlo[e2] = 4096 * (r >> 2) + 256 * (r & 3) + 16 * (vc2 ^ (X & 3)) + 8 * (l15 & 1);
         vx[e2] = 16 * (X & 12);
     }
     // P^T fragment of head group grp, k-step s' (positions 16 s' + 8 h + 0..7): 16 bytes at
-    // ((s' NW + grp) 2 + h) 512 + 16 n32 of a tile's P buffer
+    // ((s' NW + grp) 2 + h) 512 + 16 n32 of the P buffer
     const int pread = 16 * (32 * h + n32);
+    uint8_t* const pw = pbuf + (size_t)(((g >> 1) * 32) * 16 + 8 * (g & 1));
 
     f32x16 oacc[MW][NW];
 #pragma unroll
@@ -831,45 +828,35 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         for (int gr = 0; gr < NW; ++gr)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[t2][gr][e] = 0.f;
-    float m_ref[2] = {-INFINITY, -INFINITY}, m_all[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+    // softmax state per head group q: fixed reference (log2 units; 0 until the first tile
+    // with a valid candidate), the raw-logit level above which a probability would leave the
+    // fp32 headroom, this lane's largest raw logit and exp-sum
+    float m_ref[2] = {0.f, 0.f}, thr[2], m_lane[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+    bool ref_set = false;
     const float sl2 = a.scale * kLog2e;
+    thr[0] = thr[1] = kLazy / sl2;
 
-    for (int pass = 0; pass < 2; ++pass) {
-    bool over = false;
-    if (nt > 0) {
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile) {
-            const TileOff o = tile_offsets(tile);
-#pragma unroll
-            for (int ii = 0; ii < NI; ++ii) dma(tile, ii, o);
-        }
-    }
-    // Q fragments and the first two tiles have arrived; no vector-memory load of the
-    // compiler's own may be pending inside the tile loop, whose waits count tile loads only
-    wait_vmcnt<0>();
-    for (int t = 0; t < nt; ++t) {
-        wait_vmcnt<NI>();  // tile t has landed; only tile t + 1 may still be in flight
-        tile_barrier();
-        // tile t + 2 goes into the slot every wave finished reading before the barrier; its
-        // loads are spread over the S^T steps below
-        const TileOff dof = tile_offsets(t + 2);
-        const uint32_t msk = s_mask[t];
-        const uint8_t* tb = ring + (t % 3) * TILE_B;
-        // S^T = K Q^T: sacc[pt][nt] holds S^T[pos 16 pt + 4 (lane/16) + r][head 16 nt + lane%16]
+    // S^T = K Q^T of the tile in ring slot kt: acc[pt][q] holds S^T[pos 16 pt + 4 (lane/16) + r]
+    // [head 16 q + lane%16]; step(s) runs once after the MFMAs of k-step s (loads of a later
+    // tile, softmax work of the previous tile)
+    uint4 qf[KS][2];
+    constexpr int VPM = 1;  // vector-ALU instructions placed after each MFMA of S^T
+    auto s_tile = [&](const uint8_t* kt, f32x4 (&acc)[2][2], auto step) {
         auto kread = [&](int s, int pt) {
-            const int a_ = s < 16 ? kadr[pt][s & 3] + 1024 * (s >> 2) : ktail[pt][s - 16];
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + a_));
+            const int a_ = s < 16 ? kadr[s & 3] + 1024 * (s >> 2) + 16384 * pt : ktail[s - 16] + 2048 * pt;
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kt + a_));
         };
-        f32x4 sacc[2][2];
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) sacc[pt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < 2; ++q) acc[pt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
         bf16x8 kb[PD][2];
 #pragma unroll
         for (int s = 0; s < PD; ++s)
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) kb[s][pt] = kread(s, pt);
+        // Each k-step is its own scheduling region (sched_barrier), so the reads for k-step
+        // s + PD stay ahead of the MFMAs of k-step s instead of sinking next to their use.
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const bf16x8 c0 = kb[s % PD][0], c1 = kb[s % PD][1];
@@ -880,93 +867,171 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const bf16x8 qb = __builtin_bit_cast(bf16x8, qf[s][q]);
-                sacc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c0, qb, sacc[0][q], 0, 0, 0);
-                sacc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c1, qb, sacc[1][q], 0, 0, 0);
+                acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c0, qb, acc[0][q], 0, 0, 0);
+                acc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c1, qb, acc[1][q], 0, 0, 0);
             }
-#pragma unroll
-            for (int ii = 0; ii < NI; ++ii)
-                if ((ii * KS) / NI == s) dma(t + 2, ii, dof);
-        }
-        // keep operand reads in flight: the scheduler would otherwise sink each read next
-        // to its MFMA to save registers
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            step(s);
             if (s + PD < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        // softmax numerators against the fixed reference; P^T fragments to LDS
-        uint8_t* pw = pbuf + (t & 1) * PB + (size_t)(((g >> 1) * 32) * 16 + 8 * (g & 1));
-        const uint32_t mg = msk >> (4 * g);
-        const bool full = msk == 0xffffffffu;  // no masked position in the tile
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            float x[8];
+            for (int m = 0; m < 4; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // softmax numerators of S^T tile `acc` (raw logits; masked positions already -inf)
+    // against the fixed reference, per head group q in three stages: largest raw logit and the
+    // headroom check, then the exponentials and P^T fragments of position tile 0 and of 1
+    float ps[2];
+    bool over = false;
+    auto soft_stage = [&](const f32x4 (&acc)[2][2], int q, int stage) {
+        if (stage == 0) {
+            const f32x4 &u = acc[0][q], &v = acc[1][q];
+            const float mx = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+            m_lane[q] = fmaxf(m_lane[q], mx);
+            over |= mx > thr[q];
+            ps[q] = 0.f;
+        } else {
+            const int pt = stage - 1;
+            // v_exp_f32 directly: results below 2^-126 of the reference flush to zero, masked
+            // positions (-inf) give exactly 0
+            float pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[pt][q][r], sl2, -m_ref[q]));
+                ps[q] += pv[r];
+            }
+            const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
+            *reinterpret_cast<uint2*>(pw + ((pt * NW + wv) * 2) * 512 + 16 * (16 * q + l15)) =
+                make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+            if (pt == 1) lsum[q] += ps[q];
+        }
+    };
+    // O^T[d slice of this wave][all heads] += V^T P^T for the tile in ring slot tb
+    auto o_tile = [&](const uint8_t* tb) {
+        const uint8_t* pr = pbuf + pread;
+        auto vread = [&](int s2, int t2) {
+            const int mt = MW * wv + t2;
+            const uint8_t* vb = tb + 1024 * (mt >> 2) + 16384 * s2;
+            return __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lds_tr_read(vb + vlo[0] + ((64 * (mt & 3)) ^ vx[0])),
+                                                lds_tr_read(vb + vlo[1] + ((64 * (mt & 3)) ^ vx[1])), 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 pf[NW];
+#pragma unroll
+        for (int gr = 0; gr < NW; ++gr)
+            pf[gr] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pr + (gr * 2) * 512));
+        bf16x8 va = vread(0, 0);
+#pragma unroll
+        for (int st = 0; st < 2 * MW; ++st) {
+            const int t2 = st % MW;
+            const bf16x8 vc = va;
+            if (st + 1 < 2 * MW) va = vread((st + 1) / MW, (st + 1) % MW);
+#pragma unroll
+            for (int gr = 0; gr < NW; ++gr) {
+                oacc[t2][gr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, pf[gr], oacc[t2][gr], 0, 0, 0);
+                // P^T of the second k-step replaces each fragment right after its last use
+                if (st == MW - 1)
+                    pf[gr] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pr + ((NW + gr) * 2) * 512));
+            }
+        }
+    };
+
+    f32x4 sacc[2][2];
+    for (int pass = 0; pass < 2; ++pass) {
+    over = false;
+    if (nt > 0) {
+        const TileOff o0 = tile_offsets(0);
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) dma(0, ii, o0);
+    }
+    if (pass == 0) {
+        asm volatile("" ::: "memory");
+        // Q^T fragments (B operand of S^T): head 32 wv + 16 q + lane%16, d = 32 s + 8 (lane/16) + 0..7
+        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + (hk * G + 32 * wv + l15) * a.Q.s1 +
+                             (int64_t)i * a.Q.s2 + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) qf[s][q] = *reinterpret_cast<const uint4*>(qp + 16 * q * a.Q.s1 + 32 * s);
+    }
+    // Q fragments and tile 0 have arrived; no vector-memory load of the compiler's own may be
+    // pending inside the tile loop, whose waits count tile loads only
+    wait_vmcnt<0>();
+    if (nt > 0) {
+#pragma unroll
+        for (int tile = 1; tile < RING - 1; ++tile) {
+            const TileOff o = tile_offsets(tile);
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) dma(tile, ii, o);
+        }
+        tile_barrier();
+        s_tile(ring, sacc, [&](int) {});
+    }
+    // Iteration t: softmax of tile t, S^T of tile t + 1, O^T of tile t.  Ring slots: t (V of
+    // O^T), t + 1 (K of S^T), t + 2 and t + 3 in flight.
+    for (int t = 0; t < nt; ++t) {
+        wait_vmcnt<(RING - 3) * NI>();  // tile t + 1 has landed; only tile t + 2 may still be in flight
+        tile_barrier();                 // every wave is past O^T of tile t - 1: its slot and P are free
+        const uint32_t msk = (uint32_t)__ballot(s_off[T * t + n32] != 0x80000000u);
+        if (msk != 0xffffffffu) {
+            // invalid positions of this tile (zero rows) get -inf logits
+            const uint32_t mg = msk >> (4 * g);
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[4 * pt + r] = sacc[pt][q][r] * sl2;
-            if (!full) {
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt)
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (!((mg >> (16 * pt + r)) & 1u)) x[4 * pt + r] = -INFINITY;
-            }
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-            tmax = colmax4(tmax);
-            if (m_ref[q] == -INFINITY) m_ref[q] = tmax;
-            m_all[q] = fmaxf(m_all[q], tmax);
-            over |= tmax > m_ref[q] + kLazy;
-            float ps = 0.f;
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                float pv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // v_exp_f32 directly: results below 2^-126 of the reference flush to zero.
-                    // Masked entries are exactly 0 (exp2(-inf - -inf) would be NaN).
-                    const float ev = __builtin_amdgcn_exp2f(x[4 * pt + r] - m_ref[q]);
-                    pv[r] = (full || x[4 * pt + r] != -INFINITY) ? ev : 0.f;
-                    ps += pv[r];
-                }
-                const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
-                *reinterpret_cast<uint2*>(pw + ((pt * NW + wv) * 2) * 512 + 16 * (16 * q + l15)) =
-                    make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
-            }
-            lsum[q] += ps;
+                        if (!((mg >> (16 * pt + r)) & 1u)) sacc[pt][q][r] = -INFINITY;
         }
+        if (!ref_set && msk != 0u) {
+            // first tile with a valid candidate: it fixes each head's reference maximum
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const f32x4 &u = sacc[0][q], &v = sacc[1][q];
+                const float mx = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+                m_ref[q] = colmax4(mx) * sl2;
+                thr[q] = (m_ref[q] + kLazy) / sl2;
+            }
+            ref_set = true;
+        }
+        // S^T of tile t + 1 (zero rows when t + 1 = nt: computed and discarded, which keeps the
+        // loop body free of branches)
+        // softmax of tile t, then S^T of tile t + 1 into the same registers
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int stage = 0; stage < 3; ++stage) soft_stage(sacc, q, stage);
+        __builtin_amdgcn_sched_barrier(0);
+        const TileOff dof = tile_offsets(t + RING - 1);
+        s_tile(ring + ((t + 1) % RING) * TILE_B, sacc, [&](int s) {
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii)
+                if ((ii * KS) / NI == s) dma(t + RING - 1, ii, dof);
+        });
         wait_lgkmcnt0();
         tile_barrier();
-        // O^T[d slice of this wave][all heads] += V^T P^T
-        const uint8_t* pr = pbuf + (t & 1) * PB + pread;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 pf[NW];
-#pragma unroll
-            for (int gr = 0; gr < NW; ++gr)
-                pf[gr] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pr + ((s2 * NW + gr) * 2) * 512));
-#pragma unroll
-            for (int t2 = 0; t2 < MW; ++t2) {
-                const int mt = MW * wv + t2;
-                const uint8_t* vb = tb + 1024 * (mt >> 2) + 16384 * s2;
-                const bf16x8 va = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lds_tr_read(vb + vlo[0] + ((64 * (mt & 3)) ^ vx[0])),
-                                                    lds_tr_read(vb + vlo[1] + ((64 * (mt & 3)) ^ vx[1])), 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int gr = 0; gr < NW; ++gr)
-                    oacc[t2][gr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[gr], oacc[t2][gr], 0, 0, 0);
-            }
-        }
+        o_tile(ring + (t % RING) * TILE_B);
     }
+    // the last tiles' loads (zero rows past nt) land before the ring is reused
     wait_vmcnt<0>();
-    if (!__syncthreads_or(over)) break;
+    __syncthreads();
+    int* s_over = reinterpret_cast<int*>(ring);
+    if (threadIdx.x == 0) *s_over = 0;
+    __syncthreads();
+    if (over) *s_over = 1;
+    __syncthreads();
+    const bool again = *s_over != 0;
+    __syncthreads();
+    if (!again) break;
     // a probability left fp32 headroom: run the set again against the true maximum
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        m_ref[q] = m_all[q];
+        m_ref[q] = colmax4(m_lane[q]) * sl2;
+        thr[q] = (m_ref[q] + kLazy) / sl2;
         lsum[q] = 0.f;
     }
 #pragma unroll
@@ -976,14 +1041,16 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[t2][gr][e] = 0.f;
     }
-    // per-head reference and exp-sum (lanes with the same lane%16 hold disjoint positions)
+    // per-head reference and exp-sum (lanes with the same lane%16 hold disjoint positions),
+    // kept in the last ring slot, which the output staging below does not reach
+    float* s_ml = reinterpret_cast<float*>(ring + (RING - 1) * TILE_B);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         lsum[q] += __shfl_xor(lsum[q], 16);
         lsum[q] += __shfl_xor(lsum[q], 32);
         if (g == 0) {
-            s_ml[0][32 * wv + 16 * q + l15] = m_ref[q];
-            s_ml[1][32 * wv + 16 * q + l15] = lsum[q];
+            s_ml[32 * wv + 16 * q + l15] = lsum[q] > 0.f ? m_ref[q] : -INFINITY;
+            s_ml[32 * NW + 32 * wv + 16 * q + l15] = lsum[q];
         }
     }
     __syncthreads();
@@ -1005,7 +1072,7 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         for (int r0 = 0; r0 < NW; r0 += GR) {
 #pragma unroll
             for (int gq = 0; gq < GR; ++gq) {
-                const float l = s_ml[1][32 * (r0 + gq) + n32];
+                const float l = s_ml[32 * NW + 32 * (r0 + gq) + n32];
                 const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
                 for (int t2 = 0; t2 < MW; ++t2)
@@ -1037,7 +1104,7 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         uint16_t* pbase = partial_o(part, slots) + ((rowkv * S + split) * (int64_t)G) * DV;
 #pragma unroll
         for (int gr = 0; gr < NW; ++gr) {
-            const float l = s_ml[1][32 * gr + n32];
+            const float l = s_ml[32 * NW + 32 * gr + n32];
             const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
             for (int t2 = 0; t2 < MW; ++t2) {
@@ -1054,8 +1121,8 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
             }
             if (wv == 0 && h == 0) {
                 float* ml = part + ((row * p.Hq + hk * G + 32 * gr + n32) * (int64_t)S + split) * 2;
-                ml[0] = s_ml[0][32 * gr + n32];
-                ml[1] = s_ml[1][32 * gr + n32];
+                ml[0] = s_ml[32 * gr + n32];
+                ml[1] = s_ml[32 * NW + 32 * gr + n32];
             }
         }
     }
@@ -1171,9 +1238,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         const long units = (long)p.B * p.n_q * p.Hkv * a.splits;
         const bool lds_kernel = mla_lds_ok(a);
         if (lds_kernel) {
-            if (G == 128) hipLaunchKernelGGL(attn_mla_lds<4>, dim3((unsigned)units), dim3(256), 0, s, a);
-            else if (G == 64) hipLaunchKernelGGL(attn_mla_lds<2>, dim3((unsigned)units), dim3(128), 0, s, a);
-            else hipLaunchKernelGGL(attn_mla_lds<1>, dim3((unsigned)units), dim3(64), 0, s, a);
+            const dim3 grid((unsigned)(a.splits > 1 ? 8 * ((units + 7) / 8) : units));
+            if (G == 128) hipLaunchKernelGGL(attn_mla_lds<4>, grid, dim3(256), 0, s, a);
+            else if (G == 64) hipLaunchKernelGGL(attn_mla_lds<2>, grid, dim3(128), 0, s, a);
+            else hipLaunchKernelGGL(attn_mla_lds<1>, grid, dim3(64), 0, s, a);
         } else {
             hipLaunchKernelGGL((attn_mla<576, 512>), dim3((unsigned)units), dim3(64 * (G / 16)), 0, s, a);
         }
