@@ -6,6 +6,11 @@
 // return all their positions and mark the rest invalid; §3.1: lexicographic
 // (score, index) order, NaN handled before the selection).
 //
+// Three layouts: one workgroup per row with the row in registers (up to 8192 positions:
+// 256 threads; 8193 to 32768: 1024 threads, first digit relative to the row's own key range
+// and the threshold bin resolved from an LDS list), and several workgroups per row for a few
+// long rows (decode batches).  The description below is the register path.
+//
 // One workgroup of 256 threads per row.  Scores map to order-preserving uint32 keys
 // (sign-flip; -0 is folded onto +0).  A three-digit MSB radix select (11 + 11 + 10 bits,
 // LDS histograms, one suffix scan per digit) finds the k-th largest key T and how many
@@ -222,6 +227,247 @@ __global__ void __launch_bounds__(NT) topk_rows_reg(TopkArgs a) {
             }
             run_gt += tot >> 16;
             run_eq += tot & 0xffffu;
+        }
+    }
+    __syncthreads();
+    if (t == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+}
+
+// ---------------------------------------------------------------- long-row path
+// Rows of 8193 to 32768 positions, one workgroup of NT threads per row, the row in registers
+// (thread t holds positions 4 NT c + 4t .. 4t + 3 of every chunk c).  The first digit is taken
+// relative to the row's own key range: bin = (key - kmin) >> s with s chosen so that
+// (kmax - kmin) >> s < 2048, which spreads concentrated scores over the histogram.  The keys
+// of the threshold bin are then gathered into LDS and the remaining s bits are resolved there
+// (at most two more 11-bit digits); a bin too large for the list is resolved over the
+// registers instead.  The ordered write uses per-(chunk, wave) counts, one scan over them and
+// ballots inside each wave, so a chunk costs no block-wide scan.
+template <int NT, int NCH>
+__global__ void __launch_bounds__(NT) topk_rows_long(TopkArgs a) {
+    constexpr int NW = NT / 64, CAP = 4096;
+    static_assert(NCH * NW <= 128, "the (chunk, wave) scan takes two entries per lane");
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t cand[CAP];
+    __shared__ uint32_t wave_tot[NW];
+    __shared__ uint32_t cnt[NCH * NW][2];  // per (chunk, wave): keys > T, keys == T; then exclusive prefixes
+    __shared__ uint32_t s_min[NW], s_max[NW];
+    __shared__ int s_bin;
+    __shared__ uint32_t s_above, s_ncand;
+    __shared__ int s_bad;
+
+    const sa_problem& p = a.p;
+    const int row = blockIdx.x;
+    const int b = row / p.n_q, i = row % p.n_q;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int K = p.k;
+    const float* sc = a.scores + (int64_t)row * a.row_stride;
+    int32_t* out = a.idx + (int64_t)row * K;
+    float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    if (t == 0) {
+        s_bad = 0;
+        s_bin = 0;
+        s_above = 0;
+        s_ncand = 0;
+    }
+    __syncthreads();
+
+    if (L <= K) {
+        int bad = 0;
+        for (int j = t; j < K; j += NT) {
+            const float v = j < L ? sc[j] : -INFINITY;
+            if (j < L && !isfinite(v)) bad = 1;
+            out[j] = j < L ? j : -1;
+            if (vout) vout[j] = v;
+        }
+        if (bad) s_bad = 1;
+        __syncthreads();
+        if (t == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+        return;
+    }
+
+    // keys (0 past L, below every real key: a visible key is never 0, the bit pattern that
+    // would map to 0 is a NaN, which is reported) and the row's key range
+    const bool vec_ok = ((a.row_stride & 3) == 0) && (((uintptr_t)a.scores & 15) == 0);
+    const int nch = min(NCH, (L + 4 * NT - 1) / (4 * NT));  // chunks holding visible positions
+    uint32_t key[NCH][4];
+    int bad = 0;
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int j0 = c * 4 * NT + 4 * t;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (c < nch) {
+            if (vec_ok && j0 + 3 < L) {
+                const float4 f = *reinterpret_cast<const float4*>(sc + j0);
+                v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (j0 + e < L) ? sc[j0 + e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool in = j0 + e < L;
+            if (in && !isfinite(v[e])) bad = 1;
+            key[c][e] = in ? order_key(v[e]) : 0u;
+            kmin = min(kmin, key[c][e] != 0u ? key[c][e] : 0xffffffffu);
+            kmax = max(kmax, key[c][e]);
+        }
+    }
+    if (bad) s_bad = 1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    if (lane == 0) {
+        s_min[wv] = kmin;
+        s_max[wv] = kmax;
+    }
+    for (int e = t; e < 2048; e += NT) hist[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        kmin = min(kmin, s_min[w]);
+        kmax = max(kmax, s_max[w]);
+    }
+    const uint32_t range = kmax - kmin;
+    const int sh = range == 0 ? 0 : max(0, 32 - __clz((int)range) - 11);  // (key - kmin) >> sh < 2048
+
+    // first digit
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (c >= nch) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (key[c][e] != 0u) atomicAdd(&hist[(key[c][e] - kmin) >> sh], 1u);
+    }
+    __syncthreads();
+    find_bin_big<2048, NT>(hist, (uint32_t)K, wave_tot, &s_bin, &s_above);
+    const uint32_t B = (uint32_t)s_bin;
+    uint32_t above = s_above;
+    const uint32_t nB = hist[B];
+    uint32_t tu = B << sh;  // threshold relative to kmin, refined below
+    if (sh > 0) {
+        // gather the keys of bin B (relative to kmin) when they fit the list
+        const bool listed = nB <= (uint32_t)CAP;
+        if (listed) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                if (c >= nch) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t u = key[c][e] - kmin;
+                    const bool hit = key[c][e] != 0u && (u >> sh) == B;
+                    const uint64_t m = __ballot(hit);
+                    if (m == 0) continue;
+                    uint32_t base = 0;
+                    if (lane == 0) base = atomicAdd(&s_ncand, (uint32_t)__popcll(m));
+                    base = __shfl(base, 0);
+                    if (hit) cand[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = u;
+                }
+            }
+        }
+        // at most two more digits over the low sh bits
+        int done = 0;  // low bits still open: sh - done
+        while (done < sh) {
+            const int wdt = min(11, sh - done);
+            const int dsh = sh - done - wdt;
+            const uint32_t pmask_shift = (uint32_t)(sh - done);  // bits above the digit already fixed
+            const uint32_t prefix = tu >> pmask_shift;
+            __syncthreads();  // list complete / previous histogram read
+            for (int e = t; e < 2048; e += NT) hist[e] = 0;
+            __syncthreads();
+            if (listed) {
+                for (uint32_t q = t; q < nB; q += NT) {
+                    const uint32_t u = cand[q];
+                    if ((u >> pmask_shift) == prefix) atomicAdd(&hist[(u >> dsh) & ((1u << wdt) - 1u)], 1u);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    if (c >= nch) break;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t u = key[c][e] - kmin;
+                        if (key[c][e] != 0u && (u >> pmask_shift) == prefix)
+                            atomicAdd(&hist[(u >> dsh) & ((1u << wdt) - 1u)], 1u);
+                    }
+                }
+            }
+            __syncthreads();
+            if (t == 0) s_bin = 0, s_above = 0;
+            __syncthreads();
+            find_bin_big<2048, NT>(hist, (uint32_t)K - above, wave_tot, &s_bin, &s_above);
+            tu |= (uint32_t)s_bin << dsh;
+            above += s_above;
+            done += wdt;
+        }
+    }
+    const uint32_t T = kmin + tu;
+    const uint32_t need_eq = (uint32_t)K - above;
+
+    // ordered write: counts per (chunk, wave), one exclusive scan in (chunk, wave) order, then
+    // ballot prefixes inside each wave
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        uint32_t g = 0, q = 0;
+        if (c < nch) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // T is a visible key, so neither test holds for a position past L (key 0)
+                g += (uint32_t)__popcll(__ballot(key[c][e] > T));
+                q += (uint32_t)__popcll(__ballot(key[c][e] == T));
+            }
+        }
+        if (lane == 0) {
+            cnt[c * NW + wv][0] = g;
+            cnt[c * NW + wv][1] = q;
+        }
+    }
+    __syncthreads();
+    if (wv == 0) {
+        // NCH * NW <= 128 entries, two per lane
+        uint32_t g0 = 0, q0 = 0, g1 = 0, q1 = 0;
+        const int e0 = 2 * lane, e1 = 2 * lane + 1;
+        if (e0 < NCH * NW) { g0 = cnt[e0][0]; q0 = cnt[e0][1]; }
+        if (e1 < NCH * NW) { g1 = cnt[e1][0]; q1 = cnt[e1][1]; }
+        uint32_t gs = g0 + g1, qs = q0 + q1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t gy = __shfl_up(gs, o), qy = __shfl_up(qs, o);
+            if (lane >= o) { gs += gy; qs += qy; }
+        }
+        const uint32_t gb = gs - g0 - g1, qb = qs - q0 - q1;  // exclusive
+        if (e0 < NCH * NW) { cnt[e0][0] = gb; cnt[e0][1] = qb; }
+        if (e1 < NCH * NW) { cnt[e1][0] = gb + g0; cnt[e1][1] = qb + q0; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (c >= nch) break;
+        const int j0 = c * 4 * NT + 4 * t;
+        uint32_t G = cnt[c * NW + wv][0], E = cnt[c * NW + wv][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            G += (uint32_t)__popcll(__ballot(key[c][e] > T) & below);
+            E += (uint32_t)__popcll(__ballot(key[c][e] == T) & below);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool gt = key[c][e] > T, eq = key[c][e] == T;
+            if (gt || (eq && E < need_eq)) {
+                const uint32_t slot = G + (E < need_eq ? E : need_eq);
+                if (slot < (uint32_t)K) {
+                    out[slot] = j0 + e;
+                    if (vout) vout[slot] = sc[j0 + e];
+                }
+            }
+            G += gt;
+            E += eq;
         }
     }
     __syncthreads();
@@ -501,7 +747,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     else if (n <= 2048) hipLaunchKernelGGL((topk_rows_reg<8, 256>), g, dim3(256), 0, s, a);
     else if (n <= 4096) hipLaunchKernelGGL((topk_rows_reg<16, 256>), g, dim3(256), 0, s, a);
     else if (n <= 8192) hipLaunchKernelGGL((topk_rows_reg<32, 256>), g, dim3(256), 0, s, a);
-    else if (n <= 16384) hipLaunchKernelGGL((topk_rows_reg<16, 1024>), g, dim3(1024), 0, s, a);
+    else if (n <= 16384) hipLaunchKernelGGL((topk_rows_long<1024, 4>), g, dim3(1024), 0, s, a);
+    else if (n <= 32768) hipLaunchKernelGGL((topk_rows_long<1024, 8>), g, dim3(1024), 0, s, a);
     else hipLaunchKernelGGL((topk_rows_reg<32, 1024>), g, dim3(1024), 0, s, a);
     return hipGetLastError();
 }
