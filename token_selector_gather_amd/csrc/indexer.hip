@@ -30,8 +30,10 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 __device__ __forceinline__ float relu_keep_nonfinite(float z) { return z > 0.f ? z : 0.f * z; }
-// ReLU of a finite value in one integer max: negative floats are negative int32 patterns
-// (-0 included), non-negative floats keep their pattern
+// ReLU in one integer max: negative floats are negative int32 patterns (-0 included),
+// non-negative floats keep their pattern.  Exact for finite values; +inf and positive NaN
+// pass, -inf and negative NaN give 0, so a kernel that may see non-finite dot products also
+// adds z * 0 (0, or NaN for a non-finite z) to the score.
 __device__ __forceinline__ float relu_finite(float z) { return __int_as_float(max(__float_as_int(z), 0)); }
 // v[l] + v[l ^ 16] and v[l] + v[l ^ 32] by lane swaps between rows (no LDS round trip)
 __device__ __forceinline__ float xsum16(float v) {
@@ -210,12 +212,17 @@ __global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, 
             for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
                 for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][s], bv[s], acc[m], 0, 0, 0);
-            float t = 0.f;
+            // four partial sums; z * 0 keeps every non-finite dot product visible in the score
+            float t[4] = {0.f, 0.f, 0.f, 0.f}, chk = 0.f;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t = fmaf(wvv[m][e], FAST_RELU ? relu_finite(acc[m][e]) : relu_keep_nonfinite(acc[m][e]), t);
-            const float v = xsum32(xsum16(t));
+                for (int e = 0; e < 4; ++e) {
+                    t[e] = fmaf(wvv[m][e], relu_finite(acc[m][e]), t[e]);
+                    if (!FAST_RELU) chk = fmaf(acc[m][e], 0.f, chk);
+                }
+            const float tt = (t[0] + t[1]) + (t[2] + t[3]);
+            const float v = xsum32(xsum16(FAST_RELU ? tt : tt + chk));
             if (lane < 16) s_sc[16 * (wv + 4 * u) + l15] = v;
         }
         wait_vmcnt<0>();
@@ -273,6 +280,24 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
 #pragma unroll
     for (int q = 0; q < QW; ++q) Lq[q] = s_L[QW * wv + q];
     const int nch = (Lwg + CK - 1) / CK;
+
+    if (a.fill_invisible) {
+        // -inf for the positions past the computed chunks, issued first so that the stores
+        // drain while the chunks are computed; 16-byte stores where the rows allow it
+        const int start = min(nch * CK, p.n_kv);
+        const bool vec = ((a.row_stride & 3) == 0) && (((uintptr_t)a.scores & 15) == 0);
+        const int head = vec ? min(p.n_kv, (start + 3) & ~3) : p.n_kv;
+        const int body = vec ? head + ((p.n_kv - head) & ~3) : p.n_kv;
+        const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        for (int q = 0; q < QW; ++q) {
+            const int qi = iw + q;
+            if (qi >= p.n_q) break;
+            float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
+            for (int j = start + lane; j < head; j += 64) row[j] = -INFINITY;
+            for (int j = head + 4 * lane; j < body; j += 256) *reinterpret_cast<float4*>(row + j) = ninf;
+            for (int j = body + lane; j < p.n_kv; j += 64) row[j] = -INFINITY;
+        }
+    }
 
     if (nch > 0) {
         // A fragments (rows 16 m + lane%16: query m / TPQ, head 16 (m % TPQ) + lane%16) and the
@@ -370,15 +395,20 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
                 float sc[QW];
 #pragma unroll
                 for (int q = 0; q < QW; ++q) {
-                    float t = 0.f;
+                    // four partial sums (short dependency chains); without the finiteness
+                    // pre-pass, z * 0 collects a NaN for every non-finite dot product so the
+                    // score stays non-finite (the ReLU itself is the one-instruction integer max)
+                    float t[4] = {0.f, 0.f, 0.f, 0.f}, chk = 0.f;
 #pragma unroll
                     for (int m = q * TPQ; m < (q + 1) * TPQ; ++m)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float zz = acc[m][e];
-                            t = fmaf(wvv[m][e], FAST_RELU ? relu_finite(zz) : relu_keep_nonfinite(zz), t);
+                            t[e] = fmaf(wvv[m][e], relu_finite(zz), t[e]);
+                            if (!FAST_RELU) chk = fmaf(zz, 0.f, chk);
                         }
-                    sc[q] = xsum32(xsum16(t));
+                    const float tt = (t[0] + t[1]) + (t[2] + t[3]);
+                    sc[q] = xsum32(xsum16(FAST_RELU ? tt : tt + chk));
                 }
                 const int j = c * CK + nt * 16 + l15;
 #pragma unroll
@@ -393,16 +423,6 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
             }
             if (c + 1 < nch) commit(buf ^ 1);
             __syncthreads();
-        }
-    }
-    if (a.fill_invisible) {
-        // positions past the computed chunks
-        const int start = nch * CK;
-        for (int q = 0; q < QW; ++q) {
-            const int qi = iw + q;
-            if (qi >= p.n_q) break;
-            float* row = a.scores + (int64_t)(b * p.n_q + qi) * a.row_stride;
-            for (int j = start + lane; j < p.n_kv; j += 64) row[j] = -INFINITY;
         }
     }
 }
@@ -559,13 +579,14 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
                 float part[MW];
 #pragma unroll
                 for (int m = 0; m < MW; ++m) {
-                    float t = 0.f;
+                    float t = 0.f, chk = 0.f;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float z = acc[m][e];
-                        t = fmaf(wvv[m][e], FAST_RELU ? __builtin_amdgcn_fmed3f(z, 0.f, INFINITY) : relu_keep_nonfinite(z), t);
+                        t = fmaf(wvv[m][e], relu_finite(z), t);
+                        if (!FAST_RELU) chk = fmaf(z, 0.f, chk);  // NaN for a non-finite dot product
                     }
-                    part[m] = t;
+                    part[m] = FAST_RELU ? t : t + chk;
                 }
                 if constexpr (DECODE) {
                     float v = part[0];
