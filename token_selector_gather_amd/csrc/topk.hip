@@ -370,8 +370,35 @@ __global__ void __launch_bounds__(NT) topk_rows_long(TopkArgs a) {
                 }
             }
         }
-        // at most two more digits over the low sh bits
+        // A short list (the usual case: tens of keys) is ranked by one wave: candidate c is the
+        // threshold when fewer than `need` candidates exceed it and at least `need` are >= it.
+        // Longer lists and unlisted bins take at most two more digits over the low sh bits.
         int done = 0;  // low bits still open: sh - done
+        if (listed && nB <= 64u) {
+            __syncthreads();  // list complete
+            if (wv == 0) {
+                const uint32_t need = (uint32_t)K - above;
+                const uint32_t c = lane < (int)nB ? cand[lane] : 0u;
+                uint32_t g = 0, q = 0;
+                for (uint32_t j = 0; j < nB; ++j) {
+                    const uint32_t cj = cand[j];
+                    g += cj > c;
+                    q += cj == c;
+                }
+                const bool hit = lane < (int)nB && g < need && need <= g + q;
+                const uint64_t m = __ballot(hit);
+                const int src = __builtin_ctzll(m);  // a threshold always exists; equal values agree
+                const uint32_t cu = __shfl(c, src), gu = __shfl(g, src);
+                if (lane == 0) {
+                    s_bin = (int)cu;
+                    s_above = gu;
+                }
+            }
+            __syncthreads();
+            tu = (uint32_t)s_bin;  // the full key relative to kmin
+            above += s_above;
+            done = sh;
+        }
         while (done < sh) {
             const int wdt = min(11, sh - done);
             const int dsh = sh - done - wdt;
