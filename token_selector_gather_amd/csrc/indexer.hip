@@ -35,6 +35,14 @@ __device__ __forceinline__ float relu_keep_nonfinite(float z) { return z > 0.f ?
 // pass, -inf and negative NaN give 0, so a kernel that may see non-finite dot products also
 // adds z * 0 (0, or NaN for a non-finite z) to the score.
 __device__ __forceinline__ float relu_finite(float z) { return __int_as_float(max(__float_as_int(z), 0)); }
+__device__ __forceinline__ bool bf16x2_nonfinite(uint32_t w) {
+    return ((w & 0x7f80u) == 0x7f80u) || ((w & 0x7f800000u) == 0x7f800000u);
+}
+__device__ __forceinline__ bool e4m3x4_nan(uint32_t w) {
+    const uint32_t t = w & 0x7f7f7f7fu;            // a byte is 0x7f exactly when adding 1
+    return ((t + 0x01010101u) & 0x80808080u) != 0;  // carries into its top bit
+}
+
 // v[l] + v[l ^ 16] and v[l] + v[l ^ 32] by lane swaps between rows (no LDS round trip)
 __device__ __forceinline__ float xsum16(float v) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -244,7 +252,7 @@ __global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, 
 // keeps the A fragments of its 128 (query, head) rows (eight 16-row M-tiles) in registers,
 // so each 16-key B fragment read from LDS feeds 8 x KSTEPS MFMAs, and the ReLU /
 // head-weighting / head-sum arithmetic is about 2.5 VALU instructions per MFMA.
-template <int KSTEPS, bool KE4M3, int H, bool FAST_RELU>
+template <int KSTEPS, bool KE4M3, int H>
 __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
     static_assert(H >= 16 && H <= 64, "one query per 16-row M-tile");
     constexpr int D = 32 * KSTEPS;
@@ -315,6 +323,23 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 wvv[m][e] = ok ? static_cast<const float*>(a.w.data)[b * a.w.s0 + qi * a.w.s1 + 16 * (m % TPQ) + 4 * g + e] : 0.f;
+        }
+        // a query row with a non-finite index-query element scores NaN on every visible key
+        // (the plain-max ReLU alone could turn a negative NaN dot product into 0)
+        bool qbad[QW];
+#pragma unroll
+        for (int q = 0; q < QW; ++q) qbad[q] = false;
+        if (a.fix_nonfinite) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                bool bad = false;
+#pragma unroll
+                for (int s2 = 0; s2 < KSTEPS; ++s2) {
+                    const uint4 u = __builtin_bit_cast(uint4, av[m][s2]);
+                    bad |= bf16x2_nonfinite(u.x) | bf16x2_nonfinite(u.y) | bf16x2_nonfinite(u.z) | bf16x2_nonfinite(u.w);
+                }
+                if (__ballot(bad) != 0) qbad[m / TPQ] = true;
+            }
         }
         const uint32_t kstride = (uint32_t)(a.k.s1 * (KE4M3 ? 1 : 2));
         const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -395,20 +420,14 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
                 float sc[QW];
 #pragma unroll
                 for (int q = 0; q < QW; ++q) {
-                    // four partial sums (short dependency chains); without the finiteness
-                    // pre-pass, z * 0 collects a NaN for every non-finite dot product so the
-                    // score stays non-finite (the ReLU itself is the one-instruction integer max)
-                    float t[4] = {0.f, 0.f, 0.f, 0.f}, chk = 0.f;
+                    // four partial sums (short dependency chains); the ReLU is the
+                    // one-instruction integer max (non-finite inputs are handled apart)
+                    float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int m = q * TPQ; m < (q + 1) * TPQ; ++m)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float zz = acc[m][e];
-                            t[e] = fmaf(wvv[m][e], relu_finite(zz), t[e]);
-                            if (!FAST_RELU) chk = fmaf(zz, 0.f, chk);
-                        }
-                    const float tt = (t[0] + t[1]) + (t[2] + t[3]);
-                    sc[q] = xsum32(xsum16(FAST_RELU ? tt : tt + chk));
+                        for (int e = 0; e < 4; ++e) t[e] = fmaf(wvv[m][e], relu_finite(acc[m][e]), t[e]);
+                    sc[q] = xsum32(xsum16((t[0] + t[1]) + (t[2] + t[3])));
                 }
                 const int j = c * CK + nt * 16 + l15;
 #pragma unroll
@@ -418,7 +437,11 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
                     for (int q = 0; q < QW; ++q)
                         if (q == g + 4 * z) v = sc[q];
                     const bool vis = j < Ls[z];
-                    if (qok[z] && j < p.n_kv && (vis || a.fill_invisible)) srow[z][j] = vis ? v : -INFINITY;
+                    bool qb = false;
+#pragma unroll
+                    for (int q = 0; q < QW; ++q)
+                        if (q == g + 4 * z) qb = qbad[q];
+                    if (qok[z] && j < p.n_kv && (vis || a.fill_invisible)) srow[z][j] = vis ? (qb ? __builtin_nanf("") : v) : -INFINITY;
                 }
             }
             if (c + 1 < nch) commit(buf ^ 1);
@@ -660,14 +683,6 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
 // keys below the longest visible history of each batch.  16-byte chunks; bf16 values are
 // non-finite when their exponent bits are all ones, e4m3 bytes when their low seven bits
 // are (0x7f / 0xff, the format's only non-finite codes).
-__device__ __forceinline__ bool bf16x2_nonfinite(uint32_t w) {
-    return ((w & 0x7f80u) == 0x7f80u) || ((w & 0x7f800000u) == 0x7f800000u);
-}
-__device__ __forceinline__ bool e4m3x4_nan(uint32_t w) {
-    const uint32_t t = w & 0x7f7f7f7fu;            // a byte is 0x7f exactly when adding 1
-    return ((t + 0x01010101u) & 0x80808080u) != 0;  // carries into its top bit
-}
-
 __global__ void __launch_bounds__(256) index_finite_check(IndexerArgs a) {
     const sa_problem& p = a.p;
     const int b = blockIdx.y;
@@ -705,6 +720,30 @@ __global__ void __launch_bounds__(256) index_finite_check(IndexerArgs a) {
         if (!isfinite(static_cast<const float*>(a.w.data)[b * a.w.s0 + (int64_t)i * a.w.s1 + h])) bad = true;
     }
     if (bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+}
+
+// Keys with a non-finite index-key element score NaN for every query row that sees them
+// (the plain-max ReLU alone could turn a negative NaN dot product into 0).  Runs after the
+// score kernel; each thread checks one 16-byte chunk of one key row.
+__global__ void __launch_bounds__(256) index_key_fix(IndexerArgs a) {
+    const sa_problem& p = a.p;
+    const int b = blockIdx.y;
+    int kl = p.kv_len ? p.kv_len[b] : p.n_kv;
+    kl = kl < 0 ? 0 : (kl > p.n_kv ? p.n_kv : kl);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const bool e4 = a.k.dtype == SA_FP8_E4M3;
+    const int kch = p.d_idx * (e4 ? 1 : 2) / 16;
+    const uint8_t* kb = static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (e4 ? 1 : 2);
+    for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < (long)kl * kch; e += (long)gridDim.x * 256) {
+        const long j = e / kch;
+        const int c = (int)(e % kch);
+        const uint4 u = *reinterpret_cast<const uint4*>(kb + j * a.k.s1 * (e4 ? 1 : 2) + 16 * c);
+        const bool bad = e4 ? (e4m3x4_nan(u.x) | e4m3x4_nan(u.y) | e4m3x4_nan(u.z) | e4m3x4_nan(u.w))
+                            : (bf16x2_nonfinite(u.x) | bf16x2_nonfinite(u.y) | bf16x2_nonfinite(u.z) | bf16x2_nonfinite(u.w));
+        if (!bad) continue;
+        for (int i = 0; i < p.n_q; ++i)
+            if (j < visible_len(R, b, i)) a.scores[(int64_t)(b * p.n_q + i) * a.row_stride + j] = __builtin_nanf("");
+    }
 }
 
 }  // namespace
@@ -750,10 +789,15 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
             if ((long)p.B * n_qb >= 512) {
                 const dim3 gp((unsigned)((long)p.B * n_qb)), bp(256);
                 const bool e4 = a.k.dtype == SA_FP8_E4M3;
+                // without the pre-pass (standalone scores): the plain-max kernel with NaN for
+                // non-finite query rows, then NaN for non-finite keys
+                IndexerArgs af = a;
+                af.fix_nonfinite = fast ? 0 : 1;
+                const dim3 gk((unsigned)max(1L, min(512L, 65536L / p.B)), p.B);
 #define SA_IDXPF(KS, E4, HH)                                                                                  \
     if (H == HH) {                                                                                            \
-        if (fast) hipLaunchKernelGGL((indexer_pf<KS, E4, HH, true>), gp, bp, 0, s, a, n_qb);                  \
-        else hipLaunchKernelGGL((indexer_pf<KS, E4, HH, false>), gp, bp, 0, s, a, n_qb);                      \
+        hipLaunchKernelGGL((indexer_pf<KS, E4, HH>), gp, bp, 0, s, af, n_qb);                                 \
+        if (!fast) hipLaunchKernelGGL(index_key_fix, gk, dim3(256), 0, s, af);                                \
         return hipGetLastError();                                                                             \
     }
 #define SA_IDXPF_H(KS, E4) do { SA_IDXPF(KS, E4, 16) SA_IDXPF(KS, E4, 32) SA_IDXPF(KS, E4, 64) } while (0)

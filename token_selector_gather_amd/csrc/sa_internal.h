@@ -43,6 +43,8 @@ struct IndexerArgs {
     Status* status;      // fused call: non-finite index inputs are reported here by a pre-pass,
                          // and the score kernel may clip NaN with a plain max; null: the score
                          // kernel keeps NaN / -inf dot products non-finite in the scores
+    int fix_nonfinite = 0;  // set by the launcher: the plain-max kernel writes NaN for query rows
+                            // with non-finite inputs, and a later pass for such keys
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 
