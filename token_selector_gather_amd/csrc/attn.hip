@@ -698,7 +698,6 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     using namespace mla;
     constexpr int NI = NI_ALL / NW;    // loads per wave per tile
     static_assert(NI * NW == NI_ALL, "tile loads must split evenly over the waves");
-    constexpr int KS = DQK / 32;       // k-steps of S^T on 16x16x32 fragments
     constexpr int MW = DV / 32 / NW;   // 32-row tiles of O^T (rows = d) owned by one wave
     static_assert(MW * NW * 32 == DV, "the value columns must split evenly over the waves");
     constexpr int PD = 2;              // k-steps of K operands read ahead of their MFMAs
@@ -738,17 +737,42 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     // a valid candidate goes through the P buffer, which is first written inside the loop
     int* s_nt = reinterpret_cast<int*>(pbuf);
     if (threadIdx.x == 0) *s_nt = 0;
+    // Q^T fragments (B operand of S^T): head 32 wv + 16 q + lane%16, d = 32 s + 8 (lane/16) + 0..7.
+    // Issued first, then every candidate index of this thread, so that the row's input
+    // latencies overlap instead of adding up.
+    constexpr int KS = DQK / 32;       // k-steps of S^T on 16x16x32 fragments
+    uint4 qf[KS][2];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + (hk * G + 32 * wv + l15) * a.Q.s1 +
+                             (int64_t)i * a.Q.s2 + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) qf[s][q] = *reinterpret_cast<const uint4*>(qp + 16 * q * a.Q.s1 + 32 * s);
+    }
+    constexpr int EPT = MAXE / (64 * NW);  // candidate entries per thread
+    int jv[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = (int)threadIdx.x + 64 * NW * k;
+        jv[k] = e < ne ? ix[e] : -1;
+    }
     __syncthreads();
     const int ne64 = (ne + 63) & ~63;
-    for (int e = threadIdx.x; e < ne64; e += 64 * NW) {
-        const int j = e < ne ? ix[e] : -1;
-        const bool ok = j >= 0 && j < L;
-        s_off[e] = ok ? (uint32_t)j * rowb : 0x80000000u;
-        const uint64_t bal = __ballot(ok);
-        if (lane == 0 && bal != 0) atomicMax(s_nt, (e >> 5) + ((bal >> 32) != 0 ? 2 : 1));
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = (int)threadIdx.x + 64 * NW * k;
+        if (e < ne64) {  // uniform per wave (ne64 is a multiple of 64)
+            const int j = jv[k];
+            const bool ok = j >= 0 && j < L;
+            s_off[e] = ok ? (uint32_t)j * rowb : 0x80000000u;
+            const uint64_t bal = __ballot(ok);
+            if (lane == 0 && bal != 0) atomicMax(s_nt, (e >> 5) + ((bal >> 32) != 0 ? 2 : 1));
+        }
     }
     __syncthreads();
     const int nt = __builtin_amdgcn_readfirstlane(*s_nt);
+    wait_vmcnt<0>();  // (already true: the loaded values were used) no load of the compiler's own is pending
 
     const char* kbase = static_cast<const char*>(a.K.data) + (b * a.K.s0 + hk * a.K.s1) * 2;
     v4i krs;
@@ -839,7 +863,6 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     // S^T = K Q^T of the tile in ring slot kt: acc[pt][q] holds S^T[pos 16 pt + 4 (lane/16) + r]
     // [head 16 q + lane%16]; step(s) runs once after the MFMAs of k-step s (loads of a later
     // tile, softmax work of the previous tile)
-    uint4 qf[KS][2];
     constexpr int VPM = 1;  // vector-ALU instructions placed after each MFMA of S^T
     auto s_tile = [&](const uint8_t* kt, f32x4 (&acc)[2][2], auto step) {
         auto kread = [&](int s, int pt) {
@@ -881,36 +904,80 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         }
     };
 
-    // softmax numerators of S^T tile `acc` (raw logits; masked positions already -inf)
-    // against the fixed reference, per head group q in three stages: largest raw logit and the
-    // headroom check, then the exponentials and P^T fragments of position tile 0 and of 1
-    float ps[2];
+    f32x4 sacc[2][2];
+    // Softmax numerators of the S^T tile in sacc (raw logits; masked positions already -inf)
+    // against the fixed reference, in parts that the O^T MFMAs of the previous tile cover:
+    // parts 0-1 the largest raw logit of head group q and the headroom check, parts 2-5 the
+    // exponentials of one (position tile, head group) each.  The bf16 P^T fragments stay in
+    // registers (pk) until the next iteration writes them to the P buffer.
     bool over = false;
-    auto soft_stage = [&](const f32x4 (&acc)[2][2], int q, int stage) {
-        if (stage == 0) {
-            const f32x4 &u = acc[0][q], &v = acc[1][q];
+    uint32_t pk[2][2][2];
+    auto soft_part = [&](int part) {
+        if (part < 2) {
+            const int q = part;
+            const f32x4 &u = sacc[0][q], &v = sacc[1][q];
             const float mx = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
             m_lane[q] = fmaxf(m_lane[q], mx);
             over |= mx > thr[q];
-            ps[q] = 0.f;
-        } else {
-            const int pt = stage - 1;
+        } else if (part < 6) {
+            const int pt = (part - 2) >> 1, q = (part - 2) & 1;
             // v_exp_f32 directly: results below 2^-126 of the reference flush to zero, masked
             // positions (-inf) give exactly 0
             float pv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[pt][q][r], sl2, -m_ref[q]));
-                ps[q] += pv[r];
-            }
+            for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(sacc[pt][q][r], sl2, -m_ref[q]));
+            lsum[q] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
             const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
-            *reinterpret_cast<uint2*>(pw + ((pt * NW + wv) * 2) * 512 + 16 * (16 * q + l15)) =
-                make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
-            if (pt == 1) lsum[q] += ps[q];
+            pk[pt][q][0] = __builtin_bit_cast(uint32_t, p01);
+            pk[pt][q][1] = __builtin_bit_cast(uint32_t, p23);
         }
     };
+    // invalid positions of the S^T tile in sacc (zero rows) get -inf logits; the first tile
+    // with a valid candidate fixes each head's reference maximum (both rare: uniform branches)
+    auto prep = [&](uint32_t msk) {
+        if (msk != 0xffffffffu) {
+            const uint32_t mg = msk >> (4 * g);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (!((mg >> (16 * pt + r)) & 1u)) sacc[pt][q][r] = -INFINITY;
+        }
+        if (!ref_set && msk != 0u) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const f32x4 &u = sacc[0][q], &v = sacc[1][q];
+                const float mx = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+                m_ref[q] = colmax4(mx) * sl2;
+                thr[q] = (m_ref[q] + kLazy) / sl2;
+            }
+            ref_set = true;
+        }
+    };
+    // validity of tile u: tile_off(u) reads position 32 u + lane % 32 of the offset list and
+    // valid_mask turns it into bit n = position 32 u + n holds a valid candidate.  Lane % 32
+    // comes from the lane mask, recomputed here (volatile: kept at its place) so that no
+    // long-lived register holds this address (a spilled one would be reloaded before the tile
+    // loop, and the wait for it would stall every iteration on the tile loads).
+    auto tile_off = [&](int u) {
+        uint32_t l32;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(l32));
+        return s_off[T * u + (l32 & 31u)];
+    };
+    auto valid_mask = [](uint32_t off) { return (uint32_t)__ballot(off != 0x80000000u); };
+    // P^T fragments of the last softmax into the P buffer
+    auto put_p = [&]() {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                *reinterpret_cast<uint2*>(pw + ((pt * NW + wv) * 2) * 512 + 16 * (16 * q + l15)) = make_uint2(pk[pt][q][0], pk[pt][q][1]);
+    };
     // O^T[d slice of this wave][all heads] += V^T P^T for the tile in ring slot tb
-    auto o_tile = [&](const uint8_t* tb) {
+    constexpr int VPO = 4;  // vector-ALU instructions placed after each MFMA of O^T
+    auto o_tile = [&](const uint8_t* tb, auto step) {
         const uint8_t* pr = pbuf + pread;
         auto vread = [&](int s2, int t2) {
             const int mt = MW * wv + t2;
@@ -936,85 +1003,57 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
                 if (st == MW - 1)
                     pf[gr] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pr + ((NW + gr) * 2) * 512));
             }
+            step(st);
+            // each step its own scheduling region: the reads first, then every MFMA followed
+            // by a few of the step's vector-ALU instructions
+            if (st + 1 < 2 * MW) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int gr = 0; gr < NW; ++gr) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, VPO, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    f32x4 sacc[2][2];
     for (int pass = 0; pass < 2; ++pass) {
     over = false;
-    if (nt > 0) {
-        const TileOff o0 = tile_offsets(0);
-#pragma unroll
-        for (int ii = 0; ii < NI; ++ii) dma(0, ii, o0);
-    }
-    if (pass == 0) {
-        asm volatile("" ::: "memory");
-        // Q^T fragments (B operand of S^T): head 32 wv + 16 q + lane%16, d = 32 s + 8 (lane/16) + 0..7
-        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + (hk * G + 32 * wv + l15) * a.Q.s1 +
-                             (int64_t)i * a.Q.s2 + 8 * g;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) qf[s][q] = *reinterpret_cast<const uint4*>(qp + 16 * q * a.Q.s1 + 32 * s);
-    }
-    // Q fragments and tile 0 have arrived; no vector-memory load of the compiler's own may be
-    // pending inside the tile loop, whose waits count tile loads only
-    wait_vmcnt<0>();
+    // from here on the waits count tile loads only
     if (nt > 0) {
 #pragma unroll
-        for (int tile = 1; tile < RING - 1; ++tile) {
+        for (int tile = 0; tile < RING - 1; ++tile) {
             const TileOff o = tile_offsets(tile);
 #pragma unroll
             for (int ii = 0; ii < NI; ++ii) dma(tile, ii, o);
         }
+        wait_vmcnt<((RING - 2) * NI < 63 ? (RING - 2) * NI : 63)>();  // (at least) tile 0 has landed
         tile_barrier();
         s_tile(ring, sacc, [&](int) {});
+        prep(valid_mask(tile_off(0)));
+#pragma unroll
+        for (int part = 0; part < 6; ++part) soft_part(part);
     }
-    // Iteration t: softmax of tile t, S^T of tile t + 1, O^T of tile t.  Ring slots: t (V of
-    // O^T), t + 1 (K of S^T), t + 2 and t + 3 in flight.
+    // Iteration t: P^T of tile t (computed in the previous iteration) to the P buffer, S^T of
+    // tile t + 1, then O^T of tile t with the softmax of tile t + 1 between its MFMAs.  Ring
+    // slots: t (V of O^T), t + 1 (K of S^T), t + 2 and t + 3 in flight.
     for (int t = 0; t < nt; ++t) {
         wait_vmcnt<(RING - 3) * NI>();  // tile t + 1 has landed; only tile t + 2 may still be in flight
         tile_barrier();                 // every wave is past O^T of tile t - 1: its slot and P are free
-        const uint32_t msk = (uint32_t)__ballot(s_off[T * t + n32] != 0x80000000u);
-        if (msk != 0xffffffffu) {
-            // invalid positions of this tile (zero rows) get -inf logits
-            const uint32_t mg = msk >> (4 * g);
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (!((mg >> (16 * pt + r)) & 1u)) sacc[pt][q][r] = -INFINITY;
-        }
-        if (!ref_set && msk != 0u) {
-            // first tile with a valid candidate: it fixes each head's reference maximum
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const f32x4 &u = sacc[0][q], &v = sacc[1][q];
-                const float mx = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-                m_ref[q] = colmax4(mx) * sl2;
-                thr[q] = (m_ref[q] + kLazy) / sl2;
-            }
-            ref_set = true;
-        }
+        put_p();
+        // validity of tile t + 1 (past the last tile: nothing valid, its softmax is discarded)
+        const uint32_t offn = tile_off(min(t + 1, nt - 1));
+        const TileOff dof = tile_offsets(t + RING - 1);
         // S^T of tile t + 1 (zero rows when t + 1 = nt: computed and discarded, which keeps the
         // loop body free of branches)
-        // softmax of tile t, then S^T of tile t + 1 into the same registers
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int stage = 0; stage < 3; ++stage) soft_stage(sacc, q, stage);
-        __builtin_amdgcn_sched_barrier(0);
-        const TileOff dof = tile_offsets(t + RING - 1);
         s_tile(ring + ((t + 1) % RING) * TILE_B, sacc, [&](int s) {
 #pragma unroll
             for (int ii = 0; ii < NI; ++ii)
                 if ((ii * KS) / NI == s) dma(t + RING - 1, ii, dof);
         });
+        prep(t + 1 < nt ? valid_mask(offn) : 0u);
         wait_lgkmcnt0();
         tile_barrier();
-        o_tile(ring + (t % RING) * TILE_B);
+        o_tile(ring + (t % RING) * TILE_B, [&](int st) { soft_part(st); });
     }
     // the last tiles' loads (zero rows past nt) land before the ring is reused
     wait_vmcnt<0>();
