@@ -1,9 +1,9 @@
 """GPU parity of the indexer's many-row prefill layout (one pass over the history per block
 of query rows, keys widened to bf16 once per chunk), which serves workloads with thousands
-of query rows.  Sampled rows of the standalone score call (NaN-preserving ReLU, invisible
-entries filled) and of the fused call (finite inputs, plain ReLU) against the oracle
-("PaperTrace 2.2 · Fine-grained indexing", §2.1 eq. (1); the score definition of the
-Lightning indexer)."""
+of query rows.  Sampled rows of the standalone score call (invisible entries filled; NaN
+for the rows and keys with non-finite index inputs) and of the fused call (finite inputs,
+plain ReLU) against the oracle ("PaperTrace 2.2 · Fine-grained indexing", §2.1 eq. (1);
+the score definition of the Lightning indexer)."""
 import numpy as np
 import pytest
 import torch

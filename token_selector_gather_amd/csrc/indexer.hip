@@ -32,8 +32,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 __device__ __forceinline__ float relu_keep_nonfinite(float z) { return z > 0.f ? z : 0.f * z; }
 // ReLU in one integer max: negative floats are negative int32 patterns (-0 included),
 // non-negative floats keep their pattern.  Exact for finite values; +inf and positive NaN
-// pass, -inf and negative NaN give 0, so a kernel that may see non-finite dot products also
-// adds z * 0 (0, or NaN for a non-finite z) to the score.
+// pass, -inf and negative NaN give 0.  A kernel that may see non-finite dot products either
+// adds z * 0 (0, or NaN for a non-finite z) to the score, or its launcher marks the rows and
+// keys with non-finite inputs separately (indexer_pf without the pre-pass).
 __device__ __forceinline__ float relu_finite(float z) { return __int_as_float(max(__float_as_int(z), 0)); }
 __device__ __forceinline__ bool bf16x2_nonfinite(uint32_t w) {
     return ((w & 0x7f80u) == 0x7f80u) || ((w & 0x7f800000u) == 0x7f800000u);

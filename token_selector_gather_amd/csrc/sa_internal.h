@@ -41,8 +41,8 @@ struct IndexerArgs {
     int64_t row_stride;  // floats between consecutive rows of scores
     int fill_invisible;  // 1: write -inf into every invisible entry of [0, n_kv)
     Status* status;      // fused call: non-finite index inputs are reported here by a pre-pass,
-                         // and the score kernel may clip NaN with a plain max; null: the score
-                         // kernel keeps NaN / -inf dot products non-finite in the scores
+                         // and the score kernel may clip NaN with a plain max; null: the visible
+                         // scores of rows and keys with non-finite inputs come out non-finite
     int fix_nonfinite = 0;  // set by the launcher: the plain-max kernel writes NaN for query rows
                             // with non-finite inputs, and a later pass for such keys
 };
