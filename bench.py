@@ -8,7 +8,9 @@ batch 1 padded after 3584 positions).
 Prints ONE JSON line.  Besides the headline value it reports per-stage times, the
 indexer TFLOP/s, and a roofline object for the dominant kernel (the gather attention),
 timed live with HIP events on the stream the library launches on, plus the CPU oracle's
-rate on a bounded row sample of the same workload.
+rate on a bounded row sample of the same workload.  It also reports the p10 / median / p90
+of single-step times and each stage timed with cold caches (a 512 MiB write between calls
+evicts L2 and the MALL), the numbers to use for claims against the HBM roofline.
 """
 import argparse
 import json
@@ -222,6 +224,39 @@ def main():
     t_attn = timed(lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream), reps)
     idx_tflops = alg["idx_flops"] / (t_idx * 1e-3) / 1e12
     times = {"indexer_score": t_idx, "topk": t_topk, "sparse_attn": t_attn}
+
+    # distribution of single-step times (HIP events around each step, after the timed region)
+    nrep = max(20, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nrep)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+
+    # cold caches: a 512 MiB write between calls evicts L2 and the MALL, so HBM-bound stages
+    # are measured without reuse from an earlier call
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def cold(fn, reps=5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for r in range(reps):
+            flush.fill_(r & 1)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    cold_times = {
+        "indexer_score": cold(lambda: sa.sa_indexer_score(P, d["q_idx"], d["k_idx"], d["w"], scores, stream)),
+        "topk": cold(lambda: sa.sa_topk(P, scores, W["n_kv"], idx2, None, ws_t, stream)),
+        "sparse_attn": cold(lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream)),
+    }
+    del flush
     roofs = stage_rooflines(W, alg, times)
     dominant = max(times, key=times.get)
     roof = dict(roofs[dominant])
@@ -244,10 +279,14 @@ def main():
                    "Hkv": W["Hkv"], "d_qk": W["d_qk"], "d_v": W["d_v"], "Hidx": W["Hidx"], "d_idx": W["d_idx"],
                    "k": W["k"], "causal": W["causal"], "valid_rows": alg["rows"]},
         "stages_ms": {"indexer_score": round(t_idx, 4), "topk": round(t_topk, 4), "sparse_attn": round(t_attn, 4)},
+        "step_ms_dist": {"p10": round(float(np.percentile(step_ms, 10)), 4), "p50": round(float(np.median(step_ms)), 4),
+                         "p90": round(float(np.percentile(step_ms, 90)), 4), "reps": nrep},
+        "stages_ms_cold": {k: round(v, 4) for k, v in cold_times.items()},
         "indexer": {"tflops": round(idx_tflops, 3), "frac_bf16_peak": round(idx_tflops / BF16_PEAK_TFLOPS, 5),
                     "flops_per_call": alg["idx_flops"]},
         "roofline": roof,
         "stage_rooflines": roofs,
+        "stage_rooflines_cold": stage_rooflines(W, alg, cold_times),
     }
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_rows)

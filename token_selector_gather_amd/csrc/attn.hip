@@ -640,11 +640,12 @@ __global__ void __launch_bounds__(256) lse_merge(AttnArgs a) {
 // columns of K).  One workgroup per (query row, candidate split); wave w owns query heads
 // 32w..32w+31.  Gathered rows reach LDS through buffer loads that write LDS directly
 // (no staging registers), in a ring of four 32-row tiles: while tiles t and t + 1 are read,
-// t + 2 and t + 3 are in flight.  Iteration t runs the softmax of tile t, S^T = K Q^T of tile
-// t + 1 (v_mfma_f32_16x16x32_bf16, Q^T fragments in registers), then O^T += V^T P^T of tile t
-// (v_mfma_f32_32x32x16_bf16), reading V^T out of the same row-major tile with transposing LDS
-// reads (ds_read_b64_tr_b16); each wave accumulates O^T for its slice of the value columns
-// over all heads, so P goes through LDS.  Each head's reference
+// t + 2 and t + 3 are in flight.  Iteration t writes the P^T fragments of tile t (computed in
+// the previous iteration) to LDS, runs S^T = K Q^T of tile t + 1 (v_mfma_f32_16x16x32_bf16,
+// Q^T fragments in registers), then O^T += V^T P^T of tile t (v_mfma_f32_32x32x16_bf16) with
+// the softmax of tile t + 1 between those MFMAs, reading V^T out of the same row-major tile
+// with transposing LDS reads (ds_read_b64_tr_b16); each wave accumulates O^T for its slice of
+// the value columns over all heads, so P goes through LDS.  Each head's reference
 // maximum is fixed at its first valid tile, so the accumulators are never rescaled: any
 // reference gives the same softmax, and while no logit exceeds it by more than 64 (exp2
 // units) every probability and sum stays far inside fp32 range.  A set that breaks this
