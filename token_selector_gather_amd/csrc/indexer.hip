@@ -17,8 +17,10 @@
 //  * indexer_mfma3: the remaining shapes (4 or 8 index heads, moderate row counts).
 // indexer_valu covers f32 inputs and other widths.
 //
-// ReLU is written as (z > 0 ? z : 0*z) so that a NaN or -inf dot product stays non-finite
-// and reaches the selection's finiteness check instead of being clipped to zero.
+// Non-finite index inputs must reach the selection's finiteness check instead of being
+// clipped to zero by the ReLU: the VALU path uses (z > 0 ? z : 0*z); the matrix-core paths
+// use a one-instruction integer-max ReLU and either add z * 0 to each score, check the
+// inputs in a pre-pass (fused call), or mark rows and keys with non-finite inputs apart.
 #include "gfx950_mem.h"
 #include "sa_internal.h"
 
