@@ -168,3 +168,92 @@ def select_attend(W, rows=None):
     idx, sk, skp1, nsel = select(W, sc, rows)
     O, lse = attend(W, idx, rows)
     return dict(scores=sc, idx=idx, sk=sk, skp1=skp1, nsel=nsel, O=O, lse=lse)
+
+
+# ------------------------------------------------------------------ hierarchical selection
+# "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs (coarse-to-fine search
+# domain): the history is cut into blocks of b positions, each block is scored through a
+# representative, the k_b best blocks are kept, and the token indexer runs only inside
+# them; the output keeps the token top-k interface.  Readings (the pages leave these open):
+#  * representative of a block = the mean of its b index keys, rounded to bf16 (the
+#    precision the kernels score it in), scored with the same weighted-ReLU formula;
+#  * only complete blocks inside a row's visible prefix compete (block B of row (b, i) is
+#    visible iff (B + 1) b <= L(b, i)); the open block [P b, L), P = floor(L / b), is always
+#    a candidate (the pages hand unfinished blocks to a local path);
+#  * blocks and tokens are both ranked by (score desc, position asc).
+
+_DEC = {}
+
+
+def _decode_table(dtype):
+    """Value of every bit pattern of a storage dtype, from this oracle's own decoder."""
+    if dtype not in _DEC:
+        n = 256 if dtype == E4M3 else 65536
+        _DEC[dtype] = np.array([decode(dtype, c) for c in range(n)], dtype=np.float64)
+    return _DEC[dtype]
+
+
+def decode_array(a):
+    a = np.asarray(a)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    return _decode_table(_dtype_code(a))[a.astype(np.int64)]
+
+
+def f64_to_bf16_bits(x):
+    """Round-to-nearest-even of fp64 values to bf16 bit patterns (normal range)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    y = np.ldexp(np.rint(m * 256.0), e - 8)  # 8 significant bits, ties to even
+    return (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def block_means(W, blk):
+    """Block representatives [B, n_kv // blk, d_idx] as bf16 bit patterns: the mean of each
+    complete block of blk index keys (fp64 sum of the decoded keys, rounded once)."""
+    k = decode_array(W["k_idx"])
+    nb = W["n_kv"] // blk
+    m = k[:, : nb * blk].reshape(W["B"], nb, blk, W["d_idx"]).sum(axis=2) / blk
+    return np.ascontiguousarray(f64_to_bf16_bits(m))
+
+
+def _block_problem(W, blk):
+    """The block-level problem: slot B of batch b holds the block's last position, so the
+    oracle's visibility test admits exactly the complete blocks inside the visible prefix."""
+    nb = W["n_kv"] // blk
+    Wb = dict(W)
+    Wb["n_kv"] = nb
+    ends = np.broadcast_to((np.arange(nb, dtype=np.int32) + 1) * blk - 1, (W["B"], nb))
+    return Wb, np.ascontiguousarray(ends, dtype=np.int32)
+
+
+def hisa_select(W, blk, k_blocks, rows=None, kbar=None):
+    """Hierarchical selection of the listed rows.  Returns dict(idx [n, k] positions in
+    ascending order, -1 padded; blocks [n, k_blocks] selected block indices ascending, -1
+    padded; block_scores [n, n_kv // blk]; bsk / bskp1 the k_b-th and (k_b+1)-th visible
+    block scores; ncand candidates per row)."""
+    rows = _rows(W, rows)
+    if kbar is None:
+        kbar = block_means(W, blk)
+    Wb, ends = _block_problem(W, blk)
+    bsc = scores(Wb, rows, pos_of_slot=ends, k_idx=kbar)
+    bidx, bsk, bskp1, _ = select(Wb, bsc, rows, pos_of_slot=ends, k=k_blocks)
+    tsc = scores(W, rows)
+    L = np.isfinite(tsc).sum(axis=1)  # the visible positions form the prefix [0, L)
+    K = W["k"]
+    idx = np.full((rows.size, K), -1, dtype=np.int32)
+    ncand = np.zeros(rows.size, dtype=np.int64)
+    for r in range(rows.size):
+        P = L[r] // blk
+        cand = [np.arange(B * blk, (B + 1) * blk) for B in bidx[r] if B >= 0]
+        cand.append(np.arange(P * blk, L[r]))
+        pos = np.concatenate(cand).astype(np.int64)
+        ncand[r] = pos.size
+        if pos.size == 0:
+            continue
+        s = tsc[r, pos]
+        order = np.lexsort((pos, -s))[:K]  # score descending, then position ascending
+        sel = np.sort(pos[order])
+        idx[r, : sel.size] = sel
+    return dict(idx=idx, blocks=bidx, block_scores=bsc, bsk=bsk, bskp1=bskp1, token_scores=tsc, ncand=ncand)
+

@@ -489,3 +489,104 @@ def test_kv_byte_accounting_example():
     assert kv_cache_bytes(2, d, n, b) == g["gqa2_bytes"]
     assert kv_cache_bytes(1, d, n, b) == g["mqa_bytes"]
     assert kv_cache_bytes(int(g["exercise_kv_heads"]), d, int(g["exercise_positions"]), b) == g["exercise_bytes"]
+
+
+# ------------------------------------------------------------------ hierarchical selection
+# "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs: score block
+# representatives, keep k_b blocks, run the token indexer inside them, same top-k output.
+
+HISA_CASES = {
+    "causal_padded": dict(B=2, n_q=48, n_kv=64, Hidx=4, d_idx=64, k=8, lens=[64, 45]),
+    "noncausal": dict(B=1, n_q=6, n_kv=96, Hidx=8, d_idx=32, k=12, causal=0, lens=[90]),
+    "chunked": dict(B=2, n_q=20, n_kv=80, Hidx=4, d_idx=32, k=6, q_pos0=[40, 55], lens=[80, 80],
+                    kidx_dtype=sa_synth.E4M3),
+}
+
+
+@pytest.mark.parametrize("case", list(HISA_CASES))
+def test_hisa_keeping_every_block_is_the_flat_selection(case):
+    # with k_b >= the number of blocks every visible position is a candidate, so the
+    # hierarchical selection must be the flat token top-k
+    kw = dict(HISA_CASES[case])
+    lens, q_pos0 = kw.pop("lens", None), kw.pop("q_pos0", None)
+    W = sa_synth.custom(seed=3, lens=lens, q_pos0=q_pos0, with_main=False, **kw)
+    rows = all_rows(W)
+    flat, _, _, _ = orc.select(W, orc.scores(W, rows), rows)
+    for blk in (4, 8, 16):
+        h = orc.hisa_select(W, blk, W["n_kv"] // blk + 2, rows)
+        np.testing.assert_array_equal(h["idx"], flat)
+
+
+def test_hisa_unit_blocks_reduce_to_the_flat_selection():
+    # b = 1: a block is one key (bf16 keys round-trip exactly), so the block top-k_b with
+    # k_b >= k already holds the token top-k and the second stage returns it
+    W = sa_synth.custom(seed=5, B=2, n_q=40, n_kv=64, Hidx=4, d_idx=64, k=8, lens=[64, 33], with_main=False)
+    rows = all_rows(W)
+    flat, _, _, _ = orc.select(W, orc.scores(W, rows), rows)
+    for kb in (8, 11):
+        np.testing.assert_array_equal(orc.hisa_select(W, 1, kb, rows)["idx"], flat)
+
+
+def test_bf16_rounding_of_block_means_matches_torch():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-3, 4, 4000),
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0]])
+    ref = torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(orc.f64_to_bf16_bits(x), ref)
+
+
+def _brute_hisa(q, kk, w, L, blk, kb, K):
+    """Tiny-input brute force of the hierarchical selection for one query row, in plain
+    Python floats with torch's bf16 rounding for the block means."""
+    H, D = len(q), len(q[0])
+
+    def score(key):
+        return sum(w[h] * max(0.0, sum(q[h][d] * key[d] for d in range(D))) for h in range(H))
+
+    P = L // blk
+    blocks = []
+    for B in range(P):
+        mean = [sum(kk[B * blk + t][d] for t in range(blk)) / blk for d in range(D)]
+        mean = torch.tensor(mean, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).tolist()
+        blocks.append((-score(mean), B))
+    keep = sorted(sorted(blocks)[:kb], key=lambda x: x[1])
+    cand = [B * blk + t for _, B in keep for t in range(blk)] + list(range(P * blk, L))
+    ranked = sorted((-score(kk[j]), j) for j in cand)
+    return sorted(j for _, j in ranked[:K])
+
+
+def test_hisa_matches_brute_force_on_tiny_rows():
+    rng = np.random.default_rng(11)
+    B, n_q, n_kv, H, D = 1, 10, 22, 3, 5
+    q = rand_f32(rng, (B, n_q, H, D))
+    kk = rand_f32(rng, (B, n_kv, D))
+    w = rng.uniform(0, 1, (B, n_q, H)).astype(np.float32)
+    for causal, q0 in ((1, 12), (0, 0)):
+        W = tiny(q_idx=q, k_idx=kk, w=w, k=4, causal=causal, q_pos0=[q0], kv_len=[20])
+        for blk, kb in ((3, 2), (4, 1), (2, 3)):
+            got = orc.hisa_select(W, blk, kb)["idx"]
+            for i in range(n_q):
+                L = 0 if q0 + i >= 20 else (q0 + i + 1 if causal else 20)  # a row at or past kv_len sees nothing
+                ref = _brute_hisa(q[0, i].astype(np.float64).tolist(), kk[0].astype(np.float64).tolist(),
+                                  w[0, i].astype(np.float64).tolist(), L, blk, kb, 4)
+                assert got[i, : len(ref)].tolist() == ref and (got[i, len(ref):] == -1).all(), (causal, blk, kb, i)
+
+
+def test_hisa_misses_a_strong_token_inside_a_weak_block():
+    # a coarse miss cannot be recovered by the token stage: position 9 scores highest, but
+    # its block's mean is low, so with one block kept (and no open block) it is not selected
+    D = 2
+    kk = np.zeros((1, 12, D))
+    kk[0, 0:4] = [1.0, 0.0]          # block 0: uniformly good keys, mean score 1
+    kk[0, 4:8] = [0.25, 0.0]         # block 1: weak
+    kk[0, 8:12] = [-3.0, 0.0]        # block 2: very negative keys ...
+    kk[0, 9] = [5.0, 0.0]            # ... and one strong token (block mean still negative)
+    q = np.array([[[[1.0, 0.0]]]])
+    w = np.ones((1, 1, 1))
+    W = tiny(q_idx=q, k_idx=kk, w=w, k=2, causal=0)
+    flat, _, _, _ = orc.select(W, orc.scores(W))
+    assert flat[0].tolist() == [0, 9]  # ties among block 0 go to the lowest position
+    h = orc.hisa_select(W, 4, 1)
+    assert h["blocks"][0].tolist() == [0]
+    assert h["idx"][0].tolist() == [0, 1]
+    assert orc.hisa_select(W, 4, 3)["idx"][0].tolist() == [0, 9]
