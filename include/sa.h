@@ -157,6 +157,51 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
 /* Workspace bytes needed by operation `op` (an sa_op) for problem p; 0 for a malformed p. */
 size_t sa_workspace_bytes(const sa_problem* p, int op);
 
+/*
+ * Hierarchical selection.  "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs
+ * (coarse-to-fine search domain, cost O(B d_c + k_b b d_r), conditional recall eq. (7)):
+ * the history is cut into blocks of `blk` positions, each block is scored through a
+ * representative key, the k_blocks best blocks are kept and the token scores run only
+ * inside them.  Readings where the pages leave the step open: a block's representative is
+ * the mean of its blk index keys rounded to bf16 and is scored with the indexer's own
+ * formula (d_c = d_idx); only complete blocks inside a row's visible prefix compete (block
+ * B is a candidate of row (b, i) iff (B + 1) blk <= L(b, i)); the open block
+ * [floor(L / blk) blk, L) is always a token candidate; blocks and tokens are both ranked
+ * by (score desc, position asc).
+ *
+ * sa_block_means -- the representatives, kept with the index keys (a coarse index built
+ * once per completed block, not per selection).
+ *   k_idx  [B, n_kv, d_idx]  f32, bf16 or e4m3 (as for sa_indexer_score)
+ *   blk    16, 32, 64, 128 or 256
+ *   kbar   [B, n_kv / blk, d_idx] bf16 bit patterns, contiguous, caller-owned device memory;
+ *          block B of batch b = positions [B blk, (B + 1) blk).  Blocks past kv_len hold
+ *          means of padding and are never candidates.
+ */
+sa_status sa_block_means(const sa_problem* p, sa_tensor k_idx, int blk, uint16_t* kbar, void* stream);
+
+/* Workspace bytes of sa_hisa_select; 0 for malformed arguments. */
+size_t sa_hisa_workspace_bytes(const sa_problem* p, int blk, int k_blocks);
+
+/*
+ * sa_hisa_select -- block top-k_blocks over the representatives, then token top-k over
+ * the kept blocks and the open block.
+ *   q_idx, k_idx, w   as for sa_indexer_score; q_idx and w must have s0 = n_q * s1 (rows of
+ *                     all batches equally spaced)
+ *   kbar              from sa_block_means with the same k_idx and blk
+ *   k_blocks          >= 1, (k_blocks + 1) * blk <= 32768
+ *   idx               [B, n_q, k] int32, contiguous: like sa_topk, the selected positions in
+ *                     ascending order, then -1
+ *   blocks            [B, n_q, k_blocks] int32, contiguous, or NULL: the kept blocks of each
+ *                     row in ascending order, then -1 (the coarse candidates, so that a miss
+ *                     can be traced to the block or the token stage)
+ *   ws                sa_hisa_workspace_bytes(p, blk, k_blocks) bytes, 256-byte aligned,
+ *                     zero-filled once after allocation (its first word is the status word
+ *                     read by sa_device_status: non-finite scores set SA_ERR_NONFINITE).
+ */
+sa_status sa_hisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, const uint16_t* kbar,
+                         int blk, int k_blocks, int32_t* idx, int32_t* blocks, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Synchronises `stream`, returns the status word accumulated in ws by earlier calls
  * (SA_OK or SA_ERR_NONFINITE) and clears it.  ws is a host-visible pointer to device
  * memory as passed to the other calls. */

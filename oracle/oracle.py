@@ -208,13 +208,17 @@ def f64_to_bf16_bits(x):
     return (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def block_means(W, blk):
-    """Block representatives [B, n_kv // blk, d_idx] as bf16 bit patterns: the mean of each
-    complete block of blk index keys (fp64 sum of the decoded keys, rounded once)."""
-    k = decode_array(W["k_idx"])
+def block_means(W, blk, batches=None):
+    """Block representatives [B, n_kv // blk, d_idx] (or [len(batches), ...]) as bf16 bit
+    patterns: the mean of each complete block of blk index keys (fp64 sum of the decoded
+    keys, rounded once)."""
+    batches = np.arange(W["B"]) if batches is None else np.asarray(batches)
     nb = W["n_kv"] // blk
-    m = k[:, : nb * blk].reshape(W["B"], nb, blk, W["d_idx"]).sum(axis=2) / blk
-    return np.ascontiguousarray(f64_to_bf16_bits(m))
+    out = np.empty((batches.size, nb, W["d_idx"]), dtype=np.uint16)
+    for n, b in enumerate(batches):
+        k = decode_array(W["k_idx"][b, : nb * blk])
+        out[n] = f64_to_bf16_bits(k.reshape(nb, blk, W["d_idx"]).sum(axis=1) / blk)
+    return out
 
 
 def _block_problem(W, blk):
@@ -231,7 +235,8 @@ def hisa_select(W, blk, k_blocks, rows=None, kbar=None):
     """Hierarchical selection of the listed rows.  Returns dict(idx [n, k] positions in
     ascending order, -1 padded; blocks [n, k_blocks] selected block indices ascending, -1
     padded; block_scores [n, n_kv // blk]; bsk / bskp1 the k_b-th and (k_b+1)-th visible
-    block scores; ncand candidates per row)."""
+    block scores; ncand candidates per row; csk / cskp1 the k-th and (k+1)-th candidate
+    token scores, -inf where they do not exist)."""
     rows = _rows(W, rows)
     if kbar is None:
         kbar = block_means(W, blk)
@@ -243,6 +248,7 @@ def hisa_select(W, blk, k_blocks, rows=None, kbar=None):
     K = W["k"]
     idx = np.full((rows.size, K), -1, dtype=np.int32)
     ncand = np.zeros(rows.size, dtype=np.int64)
+    csk, cskp1 = np.full(rows.size, -np.inf), np.full(rows.size, -np.inf)
     for r in range(rows.size):
         P = L[r] // blk
         cand = [np.arange(B * blk, (B + 1) * blk) for B in bidx[r] if B >= 0]
@@ -252,8 +258,14 @@ def hisa_select(W, blk, k_blocks, rows=None, kbar=None):
         if pos.size == 0:
             continue
         s = tsc[r, pos]
+        ranked = np.sort(s)[::-1]
+        if ranked.size >= K:
+            csk[r] = ranked[K - 1]
+        if ranked.size > K:
+            cskp1[r] = ranked[K]
         order = np.lexsort((pos, -s))[:K]  # score descending, then position ascending
         sel = np.sort(pos[order])
         idx[r, : sel.size] = sel
-    return dict(idx=idx, blocks=bidx, block_scores=bsc, bsk=bsk, bskp1=bskp1, token_scores=tsc, ncand=ncand)
+    return dict(idx=idx, blocks=bidx, block_scores=bsc, bsk=bsk, bskp1=bskp1, token_scores=tsc, ncand=ncand,
+                csk=csk, cskp1=cskp1)
 

@@ -117,6 +117,35 @@ def test_indexer_argument_errors():
     assert call(q=_t(s0=64 * 4 * 32, s1=4 * 32, s2=33)) == sa.SA_ERR_INVALID_ARG
 
 
+@needs_lib
+def test_hierarchical_selection_argument_errors():
+    L = sa.lib()
+    p = _prob()
+    q = _t(s0=64 * 4 * 32, s1=4 * 32, s2=32)
+    k = _t(s0=64 * 32, s1=32, s2=0)
+    w = sa._Tensor(FAKE, sa.SA_F32, 64 * 4, 4, 0)
+    ws_need = L.sa_hisa_workspace_bytes(ctypes.byref(p), 16, 2)
+    assert ws_need > 0
+    assert L.sa_hisa_workspace_bytes(ctypes.byref(p), 24, 2) == 0      # block size not supported
+    assert L.sa_hisa_workspace_bytes(ctypes.byref(p), 16, 0) == 0      # no block kept
+    assert L.sa_hisa_workspace_bytes(ctypes.byref(p), 128, 2) == 0     # no complete block in the history
+    call = lambda blk=16, kb=2, q=q, w=w, kbar=FAKE, idx=FAKE, blocks=None, ws=FAKE, n=ws_need: L.sa_hisa_select(
+        ctypes.byref(p), q, k, w, kbar, blk, kb, idx, blocks, ws, n, None)
+    assert call(blk=48) == sa.SA_ERR_INVALID_ARG
+    assert call(kbar=None) == sa.SA_ERR_INVALID_ARG
+    assert call(idx=FAKE + 2) == sa.SA_ERR_INVALID_ARG
+    assert call(blocks=FAKE + 2) == sa.SA_ERR_INVALID_ARG
+    assert call(n=ws_need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == sa.SA_ERR_WORKSPACE
+    # rows of different batches not equally spaced: a row cannot stand as its own batch
+    assert call(q=_t(s0=64 * 4 * 32 + 32, s1=4 * 32, s2=32)) == sa.SA_ERR_UNSUPPORTED
+    assert call(w=sa._Tensor(FAKE, sa.SA_BF16, 64 * 4, 4, 0)) == sa.SA_ERR_UNSUPPORTED
+    bm = lambda blk=16, kb_=k, out=FAKE: L.sa_block_means(ctypes.byref(p), kb_, blk, out, None)
+    assert bm(blk=12) == sa.SA_ERR_INVALID_ARG
+    assert bm(out=None) == sa.SA_ERR_INVALID_ARG
+    assert bm(kb_=_t(data=None, s0=64 * 32, s1=32, s2=0)) == sa.SA_ERR_INVALID_ARG
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(sa, "_lib", None)
     monkeypatch.setattr(sa, "LIB_PATH", "/nonexistent/libsa.so")

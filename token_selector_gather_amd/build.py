@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "hisa.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep hipcc from emitting packed fp32 instructions

@@ -88,6 +88,52 @@ sa_status check_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K
     return SA_OK;
 }
 
+// Workspace of the hierarchical selection: status word, per-row block and candidate counts,
+// block scores, kept-block lists, compact candidate keys, candidate scores and slots, top-k
+// scratch.  R = B n_q rows, nb = n_kv / blk blocks, nc = (k_blocks + 1) blk candidates.
+struct HisaLayout {
+    size_t row_blk, row_tok, bscores, bidx, ckeys, cscores, cidx, scratch, total;
+};
+bool hisa_args_ok(const sa_problem* p, int blk, int k_blocks) {
+    if (!problem_ok(p)) return false;
+    if (blk != 16 && blk != 32 && blk != 64 && blk != 128 && blk != 256) return false;
+    if (k_blocks < 1 || (long long)(k_blocks + 1) * blk > 32768) return false;
+    return p->n_kv / blk >= 1;
+}
+sa_problem hisa_block_problem(const sa_problem& p, int blk, int k_blocks) {
+    sa_problem q = p;
+    q.n_kv = p.n_kv / blk;
+    q.k = k_blocks;
+    return q;
+}
+sa_problem hisa_token_problem(const sa_problem& p, int blk, int k_blocks) {
+    sa_problem q = p;
+    q.B = p.B * p.n_q;  // every row is its own batch over its own compact candidates
+    q.n_q = 1;
+    q.n_kv = (k_blocks + 1) * blk;
+    q.causal = 0;
+    q.kv_len = nullptr;
+    q.q_pos0 = nullptr;
+    return q;
+}
+HisaLayout hisa_layout(const sa_problem& p, int blk, int k_blocks, int k_es) {
+    const size_t R = (size_t)p.B * p.n_q, nb = (size_t)(p.n_kv / blk), nc = (size_t)(k_blocks + 1) * blk;
+    HisaLayout l;
+    size_t o = kStatusBytes;
+    l.row_blk = o; o += align256(R * 4);
+    l.row_tok = o; o += align256(R * 4);
+    l.bscores = o; o += align256(R * nb * 4);
+    l.bidx = o; o += align256(R * (size_t)k_blocks * 4);
+    l.ckeys = o; o += align256(R * nc * (size_t)p.d_idx * (size_t)k_es);
+    l.cscores = o; o += align256(R * nc * 4);
+    l.cidx = o; o += align256(R * (size_t)p.k * 4);
+    const size_t t1 = topk_ws_bytes(hisa_block_problem(p, blk, k_blocks));
+    const size_t t2 = topk_ws_bytes(hisa_token_problem(p, blk, k_blocks));
+    l.scratch = o; o += align256(t1 > t2 ? t1 : t2);
+    l.total = o;
+    return l;
+}
+
 float eff_scale(const sa_problem* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d_qk); }
 
 sa_status run_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V,
@@ -214,6 +260,95 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
 
     return run_attn(p, Q, K, V, idx, O, lse, partial, st);
+}
+
+sa_status sa_block_means(const sa_problem* p, sa_tensor k_idx, int blk, uint16_t* kbar, void* stream) {
+    if (!problem_ok(p) || !kbar || ((uintptr_t)kbar & 15)) return SA_ERR_INVALID_ARG;
+    if (blk != 16 && blk != 32 && blk != 64 && blk != 128 && blk != 256) return SA_ERR_INVALID_ARG;
+    if (k_idx.dtype != SA_F32 && k_idx.dtype != SA_BF16 && k_idx.dtype != SA_FP8_E4M3)
+        return k_idx.data ? SA_ERR_UNSUPPORTED : SA_ERR_INVALID_ARG;
+    sa_status s = tensor_ok(k_idx, p->d_idx, 2);
+    if (s != SA_OK) return s;
+    return launch_block_means(*p, k_idx, blk, kbar, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+size_t sa_hisa_workspace_bytes(const sa_problem* p, int blk, int k_blocks) {
+    if (!hisa_args_ok(p, blk, k_blocks)) return 0;
+    return hisa_layout(*p, blk, k_blocks, 4).total;  // sized for the widest key dtype
+}
+
+sa_status sa_hisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, const uint16_t* kbar,
+                         int blk, int k_blocks, int32_t* idx, int32_t* blocks, void* ws, size_t ws_bytes,
+                         void* stream) {
+    if (!hisa_args_ok(p, blk, k_blocks)) return SA_ERR_INVALID_ARG;
+    if (!kbar || ((uintptr_t)kbar & 15) || !idx || ((uintptr_t)idx & 3)) return SA_ERR_INVALID_ARG;
+    if (blocks && ((uintptr_t)blocks & 3)) return SA_ERR_INVALID_ARG;
+    sa_status s = check_indexer(p, q_idx, k_idx, w);
+    if (s != SA_OK) return s;
+    // rows of all batches equally spaced: each row can stand as its own batch
+    if (q_idx.s0 != (int64_t)p->n_q * q_idx.s1 || w.s0 != (int64_t)p->n_q * w.s1) return SA_ERR_UNSUPPORTED;
+    if ((s = ws_ok(ws, ws_bytes, sa_hisa_workspace_bytes(p, blk, k_blocks))) != SA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    const int es = esize(k_idx.dtype);
+    const HisaLayout l = hisa_layout(*p, blk, k_blocks, es);
+    int32_t* row_blk = reinterpret_cast<int32_t*>(base + l.row_blk);
+    int32_t* row_tok = reinterpret_cast<int32_t*>(base + l.row_tok);
+    float* bscores = reinterpret_cast<float*>(base + l.bscores);
+    int32_t* bidx = blocks ? blocks : reinterpret_cast<int32_t*>(base + l.bidx);
+    uint8_t* ckeys = reinterpret_cast<uint8_t*>(base + l.ckeys);
+    float* cscores = reinterpret_cast<float*>(base + l.cscores);
+    int32_t* cidx = reinterpret_cast<int32_t*>(base + l.cidx);
+    Status* status = reinterpret_cast<Status*>(base);
+    const sa_problem pb = hisa_block_problem(*p, blk, k_blocks);
+    const sa_problem pt = hisa_token_problem(*p, blk, k_blocks);
+
+    if (launch_hisa_rows(*p, blk, row_blk, st) != hipSuccess) return SA_ERR_HIP;
+    // block scores over the representatives; visible blocks = complete blocks of the prefix
+    IndexerArgs ia;
+    ia.p = pb;
+    ia.q = q_idx; ia.w = w;
+    ia.k = sa_tensor{const_cast<uint16_t*>(kbar), SA_BF16, (int64_t)pb.n_kv * p->d_idx, p->d_idx, 0};
+    ia.scores = bscores;
+    ia.row_stride = pb.n_kv;
+    ia.fill_invisible = 0;
+    ia.status = nullptr;  // non-finite scores stay visible and are reported by the selection
+    ia.row_len = row_blk;
+    if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
+    TopkArgs ta;
+    ta.p = pb;
+    ta.scores = bscores;
+    ta.row_stride = pb.n_kv;
+    ta.idx = bidx;
+    ta.vals = nullptr;
+    ta.status = status;
+    ta.scratch = base + l.scratch;
+    ta.row_len = row_blk;
+    if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
+    // the kept blocks and the open block of every row as compact candidate keys
+    if (launch_hisa_gather(*p, k_idx, blk, k_blocks, bidx, row_blk, ckeys, row_tok, st) != hipSuccess) return SA_ERR_HIP;
+    IndexerArgs ib;
+    ib.p = pt;
+    ib.q = sa_tensor{q_idx.data, q_idx.dtype, q_idx.s1, q_idx.s1, q_idx.s2};
+    ib.w = sa_tensor{w.data, w.dtype, w.s1, w.s1, 0};
+    ib.k = sa_tensor{ckeys, k_idx.dtype, (int64_t)pt.n_kv * p->d_idx, p->d_idx, 0};
+    ib.scores = cscores;
+    ib.row_stride = pt.n_kv;
+    ib.fill_invisible = 0;
+    ib.status = nullptr;
+    ib.row_len = row_tok;
+    if (launch_indexer(ib, st) != hipSuccess) return SA_ERR_HIP;
+    TopkArgs tb;
+    tb.p = pt;
+    tb.scores = cscores;
+    tb.row_stride = pt.n_kv;
+    tb.idx = cidx;
+    tb.vals = nullptr;
+    tb.status = status;
+    tb.scratch = base + l.scratch;
+    tb.row_len = row_tok;
+    if (launch_topk(tb, st) != hipSuccess) return SA_ERR_HIP;
+    return launch_hisa_map(*p, blk, k_blocks, bidx, row_blk, cidx, idx, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
 sa_status sa_device_status(void* ws, void* stream) {

@@ -1,0 +1,136 @@
+// Hierarchical (coarse-to-fine) selection: the small kernels around the indexer and top-k.
+//
+// "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs: the history is cut into
+// blocks of b positions, every block is scored through a representative index key, the
+// k_b best blocks are kept, and the token indexer runs only inside them, so the output is
+// the same token top-k.  The scoring and the two selections reuse the indexer and top-k
+// kernels on derived problems; the kernels here build those problems:
+//  * block_means: representative of each complete block = the mean of its b index keys
+//    (fp32 sum of the exactly decoded keys, divided by b, rounded once to bf16);
+//  * hisa_rows: number of complete blocks inside each row's visible prefix;
+//  * hisa_gather: each row's candidate keys copied to a compact array, kept blocks in
+//    ascending block order and then the open block [P b, L) (always a candidate), so that
+//    candidate slot order is position order and the top-k tie rule carries over;
+//  * hisa_map: candidate slots back to history positions.
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    // OCP e4m3fn: sign, 4 exponent bits (bias 7), 3 mantissa bits; 0x7f / 0xff are NaN
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float v = e ? ldexpf(1.f + 0.125f * (float)m, (int)e - 7) : ldexpf((float)m, -9);
+    if (e == 15u && m == 7u) v = __builtin_nanf("");
+    return (c & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// one workgroup per (block, batch); thread d sums dimension d over the block's rows
+__global__ void __launch_bounds__(256) block_means(sa_problem p, sa_tensor k, int blk, uint16_t* kbar) {
+    const int B = blockIdx.x, b = blockIdx.y, nb = p.n_kv / blk;
+    for (int d = threadIdx.x; d < p.d_idx; d += blockDim.x) {
+        float s = 0.f;
+        for (int t = 0; t < blk; ++t) {
+            const int64_t e = b * k.s0 + (int64_t)(B * blk + t) * k.s1 + d;
+            float v;
+            if (k.dtype == SA_FP8_E4M3) v = e4m3_value(static_cast<const uint8_t*>(k.data)[e]);
+            else if (k.dtype == SA_BF16) v = __uint_as_float((uint32_t)static_cast<const uint16_t*>(k.data)[e] << 16);
+            else v = static_cast<const float*>(k.data)[e];
+            s += v;
+        }
+        kbar[((int64_t)b * nb + B) * p.d_idx + d] = bf16_rne(s / (float)blk);
+    }
+}
+
+__global__ void __launch_bounds__(256) hisa_rows(sa_problem p, int blk, int32_t* row_blk) {
+    const long r = (long)blockIdx.x * 256 + threadIdx.x;
+    if (r >= (long)p.B * p.n_q) return;
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    row_blk[r] = visible_len(R, (int)(r / p.n_q), (int)(r % p.n_q)) / blk;
+}
+
+// workgroup (r, s): slot s < k_blocks copies kept block s of row r, slot k_blocks the open
+// block; rows are copied in 16-byte pieces
+__global__ void __launch_bounds__(256) hisa_gather(sa_problem p, sa_tensor k, int blk, int k_blocks, const int32_t* bidx,
+                                                   const int32_t* row_blk, uint8_t* ck, int32_t* row_tok, int es) {
+    const int s = blockIdx.y;
+    const long r = blockIdx.x;
+    const int b = (int)(r / p.n_q), i = (int)(r % p.n_q);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int P = row_blk[r];
+    const int nb = min(k_blocks, P);  // kept blocks: the first nb entries of the row's block list
+    int src0, dst0, nrow;
+    if (s < k_blocks) {
+        if (s >= nb) return;
+        src0 = bidx[r * k_blocks + s] * blk;
+        dst0 = s * blk;
+        nrow = blk;
+    } else {
+        src0 = P * blk;
+        dst0 = nb * blk;
+        nrow = L - P * blk;
+        if (threadIdx.x == 0) row_tok[r] = nb * blk + nrow;
+    }
+    const int rb = p.d_idx * es, pieces = rb / 16;
+    const int nc = (k_blocks + 1) * blk;
+    const uint8_t* kb = static_cast<const uint8_t*>(k.data) + (int64_t)b * k.s0 * es;
+    uint8_t* out = ck + (r * nc + dst0) * (int64_t)rb;
+    for (int e = threadIdx.x; e < nrow * pieces; e += 256) {
+        const int t = e / pieces, c = e % pieces;
+        *reinterpret_cast<uint4*>(out + (int64_t)t * rb + 16 * c) =
+            *reinterpret_cast<const uint4*>(kb + (int64_t)(src0 + t) * k.s1 * es + 16 * c);
+    }
+}
+
+__global__ void __launch_bounds__(256) hisa_map(sa_problem p, int blk, int k_blocks, const int32_t* bidx,
+                                                const int32_t* row_blk, const int32_t* cidx, int32_t* idx) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long)p.B * p.n_q * p.k) return;
+    const long r = e / p.k;
+    const int c = cidx[e];
+    if (c < 0) { idx[e] = -1; return; }
+    const int P = row_blk[r], nb = min(k_blocks, P);
+    idx[e] = c < nb * blk ? bidx[r * k_blocks + c / blk] * blk + c % blk : P * blk + (c - nb * blk);
+}
+
+}  // namespace
+
+hipError_t launch_block_means(const sa_problem& p, const sa_tensor& k, int blk, uint16_t* kbar, hipStream_t s) {
+    const int nb = p.n_kv / blk;
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(block_means, dim3((unsigned)nb, (unsigned)p.B), dim3(p.d_idx < 256 ? p.d_idx : 256), 0, s, p, k,
+                       blk, kbar);
+    return hipGetLastError();
+}
+
+hipError_t launch_hisa_rows(const sa_problem& p, int blk, int32_t* row_blk, hipStream_t s) {
+    const long rows = (long)p.B * p.n_q;
+    hipLaunchKernelGGL(hisa_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p, blk, row_blk);
+    return hipGetLastError();
+}
+
+hipError_t launch_hisa_gather(const sa_problem& p, const sa_tensor& k, int blk, int k_blocks, const int32_t* bidx,
+                              const int32_t* row_blk, uint8_t* ck, int32_t* row_tok, hipStream_t s) {
+    const int es = k.dtype == SA_F32 ? 4 : (k.dtype == SA_BF16 ? 2 : 1);
+    hipLaunchKernelGGL(hisa_gather, dim3((unsigned)((long)p.B * p.n_q), (unsigned)(k_blocks + 1)), dim3(256), 0, s, p, k,
+                       blk, k_blocks, bidx, row_blk, ck, row_tok, es);
+    return hipGetLastError();
+}
+
+hipError_t launch_hisa_map(const sa_problem& p, int blk, int k_blocks, const int32_t* bidx, const int32_t* row_blk,
+                           const int32_t* cidx, int32_t* idx, hipStream_t s) {
+    const long n = (long)p.B * p.n_q * p.k;
+    hipLaunchKernelGGL(hisa_map, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, blk, k_blocks, bidx, row_blk, cidx,
+                       idx);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) indexer_valu(IndexerArgs a) {
     const sa_problem& p = a.p;
     const int row = blockIdx.x;
     const int b = row / p.n_q, i = row % p.n_q;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int j = blockIdx.y * 256 + threadIdx.x;
     float* out = a.scores + (int64_t)row * a.row_stride;
@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, 
     const int rng = (int)(wg % n_rng);
     const long row = wg / n_rng;  // b * n_q + i
     const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int j_begin = rng * rng_len, j_end = min(j_begin + rng_len, p.n_kv);
     const int j_comp = min(j_end, L);  // keys worth computing: [j_begin, j_comp)
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
     const int qb = p.causal ? n_qb - 1 - (int)(wg % n_qb) : (int)(wg % n_qb);  // longest histories first
     const int b = (int)(wg / n_qb);
     const int i0 = qb * QB;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     if (threadIdx.x < QB) s_L[threadIdx.x] = i0 + (int)threadIdx.x < p.n_q ? visible_len(R, b, i0 + threadIdx.x) : 0;
     __syncthreads();
     int Lwg = 0;
@@ -494,7 +494,7 @@ __global__ void __launch_bounds__(256) indexer_mfma3(IndexerArgs a, int n_groups
     }
     const int j_begin = rng * rng_len;
     const int j_end = min(j_begin + rng_len, p.n_kv);
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     // visible lengths: lane q of a wave holds query q of its group
     const int i0 = g * QPG;
     int Lq = 0;
@@ -694,7 +694,7 @@ __global__ void __launch_bounds__(256) index_finite_check(IndexerArgs a) {
     const long qp0 = p.q_pos0 ? p.q_pos0[b] : 0;
     if (qp0 >= kl) return;  // no valid query row in this batch
     const int Lb = p.causal ? (int)min((long)kl, qp0 + p.n_q) : kl;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     bool bad = false;
     const long tid = (long)blockIdx.x * 256 + threadIdx.x, nth = (long)gridDim.x * 256;
     const bool e4 = a.k.dtype == SA_FP8_E4M3;
@@ -733,7 +733,7 @@ __global__ void __launch_bounds__(256) index_key_fix(IndexerArgs a) {
     const int b = blockIdx.y;
     int kl = p.kv_len ? p.kv_len[b] : p.n_kv;
     kl = kl < 0 ? 0 : (kl > p.n_kv ? p.n_kv : kl);
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const bool e4 = a.k.dtype == SA_FP8_E4M3;
     const int kch = p.d_idx * (e4 ? 1 : 2) / 16;
     const uint8_t* kb = static_cast<const uint8_t*>(a.k.data) + b * a.k.s0 * (e4 ? 1 : 2);

@@ -12,11 +12,14 @@ struct Rows {
     const int32_t* kv_len;  // [B] or null (= n_kv)
     const int32_t* q_pos0;  // [B] or null (= 0)
     int32_t n_q, n_kv, causal;
+    const int32_t* row_len = nullptr;  // [B * n_q] or null: explicit visible lengths (derived
+                                       // problems of the hierarchical selection)
 };
 
 // Number of visible history positions of query row (b, i); 0 for an invalid row.  The
 // visible set is always the prefix [0, L) of the history.
 __device__ __forceinline__ int visible_len(const Rows& r, int b, int i) {
+    if (r.row_len) return r.row_len[(long)b * r.n_q + i];
     int kl = r.kv_len ? r.kv_len[b] : r.n_kv;
     kl = kl < 0 ? 0 : (kl > r.n_kv ? r.n_kv : kl);
     long qp = (long)(r.q_pos0 ? r.q_pos0[b] : 0) + i;
@@ -45,6 +48,7 @@ struct IndexerArgs {
                          // scores of rows and keys with non-finite inputs come out non-finite
     int fix_nonfinite = 0;  // set by the launcher: the plain-max kernel writes NaN for query rows
                             // with non-finite inputs, and a later pass for such keys
+    const int32_t* row_len = nullptr;  // explicit visible length per row (see Rows)
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 
@@ -56,6 +60,7 @@ struct TopkArgs {
     float* vals;
     Status* status;
     void* scratch;  // topk_ws_bytes(p) bytes of workspace (per-row histograms of the sliced path)
+    const int32_t* row_len = nullptr;  // explicit visible length per row (see Rows)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 size_t topk_ws_bytes(const sa_problem& p);
@@ -70,6 +75,18 @@ struct AttnArgs {
     int splits;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// Hierarchical selection (block representatives, then tokens inside the kept blocks).
+hipError_t launch_block_means(const sa_problem& p, const sa_tensor& k, int blk, uint16_t* kbar, hipStream_t s);
+// row_blk[r] = complete visible blocks of row r
+hipError_t launch_hisa_rows(const sa_problem& p, int blk, int32_t* row_blk, hipStream_t s);
+// compact candidate keys of every row (kept blocks in ascending order, then the open block),
+// their count in row_tok
+hipError_t launch_hisa_gather(const sa_problem& p, const sa_tensor& k, int blk, int k_blocks, const int32_t* bidx,
+                              const int32_t* row_blk, uint8_t* ck, int32_t* row_tok, hipStream_t s);
+// candidate slots -> history positions
+hipError_t launch_hisa_map(const sa_problem& p, int blk, int k_blocks, const int32_t* bidx, const int32_t* row_blk,
+                           const int32_t* cidx, int32_t* idx, hipStream_t s);
 
 // Host-side planning shared by workspace sizing and launches.
 int attn_splits(const sa_problem& p);

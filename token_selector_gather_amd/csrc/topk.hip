@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(NT) topk_rows_reg(TopkArgs a) {
     const sa_problem& p = a.p;
     const int row = blockIdx.x;
     const int b = row / p.n_q, i = row % p.n_q;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int K = p.k;
     const float* sc = a.scores + (int64_t)row * a.row_stride;
@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(NT) topk_rows_long(TopkArgs a) {
     const sa_problem& p = a.p;
     const int row = blockIdx.x;
     const int b = row / p.n_q, i = row % p.n_q;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int K = p.k;
     const float* sc = a.scores + (int64_t)row * a.row_stride;
@@ -571,7 +571,7 @@ __global__ void __launch_bounds__(kSliceT) topk_sl_hist(TopkArgs a, SlicedWs w) 
     const sa_problem& p = a.p;
     const int row = blockIdx.x / w.S, slice = blockIdx.x % w.S;
     const int b = row / p.n_q, i = row % p.n_q;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int K = p.k;
     const int j0 = slice * kSlice;
@@ -632,7 +632,7 @@ __global__ void __launch_bounds__(kSliceT) topk_sl_count(TopkArgs a, SlicedWs w)
     const sa_problem& p = a.p;
     const int row = blockIdx.x / w.S, slice = blockIdx.x % w.S;
     const int b = row / p.n_q, i = row % p.n_q;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int K = p.k;
     const int j0 = slice * kSlice;
@@ -676,7 +676,7 @@ __global__ void __launch_bounds__(kSliceT) topk_sl_compact(TopkArgs a, SlicedWs 
     const sa_problem& p = a.p;
     const int row = blockIdx.x / w.S, slice = blockIdx.x % w.S;
     const int b = row / p.n_q, i = row % p.n_q;
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int K = p.k;
     const int j0 = slice * kSlice;
