@@ -123,6 +123,48 @@ def counted_traffic(workload, stage):
     return None
 
 
+def hisa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat):
+    """Hierarchical selection (block representatives, k_b blocks, token top-k inside them)
+    timed beside the flat score + select, with the overlap of the two selections.  Block size
+    64 and k_b = ceil(2k / 64) kept blocks (candidates about twice the budget).  The
+    representatives are index state built once per completed block; their build is timed
+    separately and is not part of the selection."""
+    import numpy as np
+    import torch
+
+    import token_selector_gather_amd as sa
+
+    blk = 64
+    kb = -(-2 * W["k"] // blk)
+    nb = W["n_kv"] // blk
+    if nb < 1 or (kb + 1) * blk > 32768:
+        return None
+    kbar = torch.empty((W["B"], nb, W["d_idx"]), dtype=torch.bfloat16, device="cuda")
+    t_bm = timed(lambda: sa.sa_block_means(P, d["k_idx"], blk, kbar, stream), reps)
+    ws_h = sa.hisa_workspace(P, blk, kb)
+    idx_h = torch.empty((W["B"], W["n_q"], W["k"]), dtype=torch.int32, device="cuda")
+    t_h = timed(lambda: sa.sa_hisa_select(P, d["q_idx"], d["k_idx"], d["w"], kbar, blk, kb, idx_h, ws_h,
+                                          stream=stream), reps)
+    st = sa.sa_device_status(ws_h)
+    if st != sa.SA_OK:
+        raise RuntimeError("hierarchical selection: device status " + sa.sa_status_str(st))
+    a = idx_h.reshape(-1, W["k"]).cpu().numpy()
+    f = flat_idx.reshape(-1, W["k"]).cpu().numpy()
+    L = visible_counts(W).reshape(-1)
+    iou = [np.intersect1d(x[x >= 0], y[y >= 0]).size / max(1, np.union1d(x[x >= 0], y[y >= 0]).size)
+           for x, y, n in zip(a, f, L) if n > 0]
+    # algorithmic bytes: every visible complete block's representative (bf16) and every
+    # candidate's index key once per row, the selection written once
+    kbytes = {0: 4, 1: 2, 2: 1}[W["kidx_dtype"]]
+    Pb = L // blk
+    ncand = np.minimum(kb, Pb) * blk + (L - Pb * blk)
+    nbytes = int((Pb * W["d_idx"] * 2 + ncand * W["d_idx"] * kbytes).sum() + W["B"] * W["n_q"] * W["k"] * 4)
+    return {"blk": blk, "k_blocks": kb, "select_ms": round(t_h, 4), "flat_score_select_ms": round(t_flat, 4),
+            "speedup_vs_flat": round(t_flat / t_h, 3), "block_means_ms": round(t_bm, 4),
+            "iou_vs_flat": round(float(np.mean(iou)), 4) if iou else None,
+            "bytes_per_call": nbytes, "achieved_gbs": round(nbytes / (t_h * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(W, budget_rows):
     """The oracle (unchanged) on a stratified sample of rows: score, select and attend."""
     import numpy as np
@@ -148,6 +190,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload id (1 = bf16 prefill B=2 n=4096)")
     ap.add_argument("--cpu-rows", type=int, default=7680, help="rows in the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--hisa", type=int, default=-1,
+                    help="time the hierarchical selection beside the flat one (default: decode workloads only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
@@ -288,6 +332,8 @@ def main():
         "stage_rooflines": roofs,
         "stage_rooflines_cold": stage_rooflines(W, alg, cold_times),
     }
+    if args.hisa == 1 or (args.hisa == -1 and alg["decode"]):
+        out["hisa"] = hisa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_rows)
     print(json.dumps(out))

@@ -171,7 +171,7 @@ size_t sa_workspace_bytes(const sa_problem* p, int op);
  *
  * sa_block_means -- the representatives, kept with the index keys (a coarse index built
  * once per completed block, not per selection).
- *   k_idx  [B, n_kv, d_idx]  f32, bf16 or e4m3 (as for sa_indexer_score)
+ *   k_idx  [B, n_kv, d_idx]  f32, bf16 or e4m3 (as for sa_indexer_score), d_idx <= 256
  *   blk    16, 32, 64, 128 or 256
  *   kbar   [B, n_kv / blk, d_idx] bf16 bit patterns, contiguous, caller-owned device memory;
  *          block B of batch b = positions [B blk, (B + 1) blk).  Blocks past kv_len hold

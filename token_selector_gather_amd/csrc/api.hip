@@ -269,6 +269,7 @@ sa_status sa_block_means(const sa_problem* p, sa_tensor k_idx, int blk, uint16_t
         return k_idx.data ? SA_ERR_UNSUPPORTED : SA_ERR_INVALID_ARG;
     sa_status s = tensor_ok(k_idx, p->d_idx, 2);
     if (s != SA_OK) return s;
+    if (p->d_idx > 256) return SA_ERR_UNSUPPORTED;
     return launch_block_means(*p, k_idx, blk, kbar, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

@@ -6,7 +6,8 @@
 // the same token top-k.  The scoring and the two selections reuse the indexer and top-k
 // kernels on derived problems; the kernels here build those problems:
 //  * block_means: representative of each complete block = the mean of its b index keys
-//    (fp32 sum of the exactly decoded keys, divided by b, rounded once to bf16);
+//    (fp32 sums of the exactly decoded keys in a fixed order, divided by b, rounded once
+//    to bf16);
 //  * hisa_rows: number of complete blocks inside each row's visible prefix;
 //  * hisa_gather: each row's candidate keys copied to a compact array, kept blocks in
 //    ascending block order and then the open block [P b, L) (always a candidate), so that
@@ -32,19 +33,41 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// one workgroup per (block, batch); thread d sums dimension d over the block's rows
-__global__ void __launch_bounds__(256) block_means(sa_problem p, sa_tensor k, int blk, uint16_t* kbar) {
+// One workgroup per (block, batch).  A key row splits into 16-byte pieces; thread (g, c)
+// sums piece c over rows g, g + G, g + 2G, ... (G row groups), then the G partial sums of
+// each dimension are added in group order through LDS.
+constexpr int kMeanMaxD = 256;  // widest index key handled (elements)
+__global__ void __launch_bounds__(256) block_means(sa_problem p, sa_tensor k, int blk, uint16_t* kbar, int es) {
+    __shared__ float part[4096];  // [row group][dimension] partial sums: G * d_idx = 4096 / es
     const int B = blockIdx.x, b = blockIdx.y, nb = p.n_kv / blk;
-    for (int d = threadIdx.x; d < p.d_idx; d += blockDim.x) {
-        float s = 0.f;
-        for (int t = 0; t < blk; ++t) {
-            const int64_t e = b * k.s0 + (int64_t)(B * blk + t) * k.s1 + d;
-            float v;
-            if (k.dtype == SA_FP8_E4M3) v = e4m3_value(static_cast<const uint8_t*>(k.data)[e]);
-            else if (k.dtype == SA_BF16) v = __uint_as_float((uint32_t)static_cast<const uint16_t*>(k.data)[e] << 16);
-            else v = static_cast<const float*>(k.data)[e];
-            s += v;
+    const int ppr = p.d_idx * es / 16, epp = 16 / es;  // pieces per row, elements per piece
+    const int G = 256 / ppr;                           // row groups
+    const int g = threadIdx.x / ppr, c = threadIdx.x % ppr;
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    if (g < G) {
+        const uint8_t* base = static_cast<const uint8_t*>(k.data) + ((int64_t)b * k.s0 + (int64_t)B * blk * k.s1) * es + 16 * c;
+        for (int t = g; t < blk; t += G) {
+            const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)t * k.s1 * es);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            if (es == 1) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[e] += e4m3_value((w[e / 4] >> (8 * (e % 4))) & 0xffu);
+            } else if (es == 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += __uint_as_float(((w[e / 2] >> (16 * (e % 2))) & 0xffffu) << 16);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
+            }
         }
+        for (int e = 0; e < epp; ++e) part[g * p.d_idx + c * epp + e] = acc[e];
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < p.d_idx; d += 256) {
+        float s = 0.f;
+        for (int gg = 0; gg < G; ++gg) s += part[gg * p.d_idx + d];
         kbar[((int64_t)b * nb + B) * p.d_idx + d] = bf16_rne(s / (float)blk);
     }
 }
@@ -106,8 +129,9 @@ __global__ void __launch_bounds__(256) hisa_map(sa_problem p, int blk, int k_blo
 hipError_t launch_block_means(const sa_problem& p, const sa_tensor& k, int blk, uint16_t* kbar, hipStream_t s) {
     const int nb = p.n_kv / blk;
     if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(block_means, dim3((unsigned)nb, (unsigned)p.B), dim3(p.d_idx < 256 ? p.d_idx : 256), 0, s, p, k,
-                       blk, kbar);
+    const int es = k.dtype == SA_F32 ? 4 : (k.dtype == SA_BF16 ? 2 : 1);
+    if (p.d_idx > kMeanMaxD || p.d_idx * es / 16 > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(block_means, dim3((unsigned)nb, (unsigned)p.B), dim3(256), 0, s, p, k, blk, kbar, es);
     return hipGetLastError();
 }
 
