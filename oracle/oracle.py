@@ -269,3 +269,62 @@ def hisa_select(W, blk, k_blocks, rows=None, kbar=None):
     return dict(idx=idx, blocks=bidx, block_scores=bsc, bsk=bsk, bskp1=bskp1, token_scores=tsc, ncand=ncand,
                 csk=csk, cskp1=cskp1)
 
+
+
+# ------------------------------------------------------------------ active index heads
+# "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: each query keeps g of its
+# G index heads, chosen from the block-averaged index keys (the absolute value of each
+# head's weighted ReLU response, averaged over the blocks of the current prefix), and the
+# score sums only those heads.  Readings: the blocks are the complete blocks of the visible
+# prefix with the bf16 representatives of the hierarchical selection; heads are ranked by
+# (routing score desc, head index asc); a row without a complete visible block has all
+# routing scores 0 and so keeps heads 0 .. g-1.
+
+def misa_route(W, blk, rows=None, kbar=None):
+    """Routing score [n, Hidx] of the listed rows (fp64)."""
+    rows = _rows(W, rows)
+    if kbar is None:
+        kbar = block_means(W, blk)
+    kb = decode_array(kbar)
+    L = np.isfinite(scores(W, rows)).sum(axis=1)
+    out = np.zeros((rows.size, W["Hidx"]))
+    for r, row in enumerate(rows):
+        b, i = divmod(int(row), W["n_q"])
+        P = int(L[r]) // blk
+        if P == 0:
+            continue
+        q = decode_array(W["q_idx"][b, i])                # [Hidx, d_idx]
+        z = np.maximum(q @ kb[b, :P].T, 0.0)              # [Hidx, P]
+        out[r] = np.abs(W["w"][b, i].astype(np.float64)) * z.mean(axis=1)
+    return out
+
+
+def misa_heads(route, g):
+    """Active heads per row: the g best by (routing score desc, head asc), ascending."""
+    H = route.shape[1]
+    out = np.empty((route.shape[0], g), dtype=np.int32)
+    for r in range(route.shape[0]):
+        order = np.lexsort((np.arange(H), -route[r]))[:g]
+        out[r] = np.sort(order)
+    return out
+
+
+def misa_select(W, blk, g, rows=None, kbar=None, heads=None):
+    """Selection of the listed rows with g active index heads.  Returns dict(idx, heads,
+    route, scores, sk, skp1).  `heads` overrides the routing (the GPU's choice, for
+    checking the token stage on the same heads)."""
+    rows = _rows(W, rows)
+    route = misa_route(W, blk, rows, kbar)
+    if heads is None:
+        heads = misa_heads(route, g)
+    b, i = rows // W["n_q"], rows % W["n_q"]
+    Wa = dict(W)
+    qa = np.stack([W["q_idx"][bb, ii, h] for bb, ii, h in zip(b, i, heads)])  # [n, g, d]
+    wa = np.stack([W["w"][bb, ii, h] for bb, ii, h in zip(b, i, heads)])      # [n, g]
+    # each listed row as its own batch of one query over its batch's history
+    Wa.update(B=rows.size, n_q=1, Hidx=g, q_idx=np.ascontiguousarray(qa[:, None]), w=np.ascontiguousarray(wa[:, None]),
+              k_idx=np.ascontiguousarray(W["k_idx"][b]), kv_len=np.asarray(W["kv_len"], np.int32)[b],
+              q_pos0=(np.asarray(W["q_pos0"], np.int32)[b] + i).astype(np.int32))
+    sc = scores(Wa)
+    idx, sk, skp1, _ = select(Wa, sc)
+    return dict(idx=idx, heads=heads, route=route, scores=sc, sk=sk, skp1=skp1)

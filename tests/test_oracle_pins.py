@@ -590,3 +590,68 @@ def test_hisa_misses_a_strong_token_inside_a_weak_block():
     assert h["blocks"][0].tolist() == [0]
     assert h["idx"][0].tolist() == [0, 1]
     assert orc.hisa_select(W, 4, 3)["idx"][0].tolist() == [0, 9]
+
+
+# ------------------------------------------------------------------ active index heads
+# "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: route each query to g of
+# its G index heads by the block-averaged |weighted ReLU| response, score with those only.
+
+@pytest.mark.parametrize("case", list(HISA_CASES))
+def test_misa_with_every_head_active_is_the_flat_selection(case):
+    kw = dict(HISA_CASES[case])
+    lens, q_pos0 = kw.pop("lens", None), kw.pop("q_pos0", None)
+    W = sa_synth.custom(seed=8, lens=lens, q_pos0=q_pos0, with_main=False, **kw)
+    rows = all_rows(W)
+    flat, _, _, _ = orc.select(W, orc.scores(W, rows), rows)
+    np.testing.assert_array_equal(orc.misa_select(W, 8, W["Hidx"], rows)["idx"], flat)
+
+
+def _brute_misa(q, kk, w, L, blk, g, K):
+    """Tiny-input brute force of the active-head selection for one query row."""
+    H, D = len(q), len(q[0])
+    dot = lambda a, b: sum(x * y for x, y in zip(a, b))
+    P = L // blk
+    means = []
+    for B in range(P):
+        m = [sum(kk[B * blk + t][d] for t in range(blk)) / blk for d in range(D)]
+        means.append(torch.tensor(m, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).tolist())
+    route = [abs(w[h]) * (sum(max(0.0, dot(q[h], mb)) for mb in means) / P if P else 0.0) for h in range(H)]
+    heads = sorted(h for _, h in sorted((-route[h], h) for h in range(H))[:g])
+    sc = [(-sum(w[h] * max(0.0, dot(q[h], kk[j])) for h in heads), j) for j in range(L)]
+    return heads, sorted(j for _, j in sorted(sc)[:K])
+
+
+def test_misa_matches_brute_force_on_tiny_rows():
+    rng = np.random.default_rng(17)
+    B, n_q, n_kv, H, D = 1, 9, 20, 5, 4
+    q = rand_f32(rng, (B, n_q, H, D))
+    kk = rand_f32(rng, (B, n_kv, D))
+    w = rng.uniform(-1, 1, (B, n_q, H)).astype(np.float32)  # a negative weight routes by |w|
+    for causal, q0 in ((1, 2), (0, 0)):
+        W = tiny(q_idx=q, k_idx=kk, w=w, k=3, causal=causal, q_pos0=[q0], kv_len=[18])
+        for blk, g in ((3, 2), (4, 1), (2, 3)):
+            got = orc.misa_select(W, blk, g)
+            for i in range(n_q):
+                L = 0 if q0 + i >= 18 else (q0 + i + 1 if causal else 18)
+                heads, ref = _brute_misa(q[0, i].astype(np.float64).tolist(), kk[0].astype(np.float64).tolist(),
+                                         w[0, i].astype(np.float64).tolist(), L, blk, g, 3)
+                if L == 0:
+                    assert (got["idx"][i] == -1).all()
+                    continue
+                assert got["heads"][i].tolist() == heads, (causal, blk, g, i)
+                assert got["idx"][i, : len(ref)].tolist() == ref and (got["idx"][i, len(ref):] == -1).all()
+
+
+def test_misa_routes_to_the_head_with_the_larger_weighted_block_response():
+    # head 0 matches block 0 only, head 1 matches both blocks, head 2 never fires; with the
+    # same weights head 1 wins; a 3x weight on head 0 makes it win (mean 3 * 0.5 > 1)
+    kk = np.array([[[1.0, 0.0]] * 4 + [[0.0, 1.0]] * 4])
+    q = np.array([[[[1.0, 0.0], [1.0, 1.0], [-1.0, -1.0]]]])
+    W = tiny(q_idx=q, k_idx=kk, w=np.ones((1, 1, 3)), k=2, causal=0)
+    r = orc.misa_select(W, 4, 1)
+    np.testing.assert_allclose(r["route"][0], [0.5, 1.0, 0.0])
+    assert r["heads"][0].tolist() == [1]
+    W2 = tiny(q_idx=q, k_idx=kk, w=np.array([[[3.0, 1.0, 1.0]]]), k=2, causal=0)
+    r2 = orc.misa_select(W2, 4, 1)
+    assert r2["heads"][0].tolist() == [0]
+    assert r2["idx"][0].tolist() == [0, 1]  # head 0 scores block 0's keys 3, the rest 0: lowest positions
