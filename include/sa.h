@@ -202,6 +202,31 @@ sa_status sa_hisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, 
                          int blk, int k_blocks, int32_t* idx, int32_t* blocks, void* ws, size_t ws_bytes,
                          void* stream);
 
+/*
+ * Active index heads.  "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: each
+ * query row keeps g of its Hidx index heads and its score sums only those heads.  The heads
+ * are chosen from the block representatives of sa_block_means: routing score of head h =
+ * |w_h| times the mean over the row's complete visible blocks B of ReLU(<q_h, kbar_B>)
+ * (0 for a row without a complete visible block); the g best by (routing score desc, head
+ * asc) are kept.  Then the token scores sum the kept heads only and the top-k is taken as
+ * by sa_topk.
+ *
+ * sa_misa_select
+ *   q_idx, k_idx, w   as for sa_indexer_score; q_idx bf16, Hidx 16, 32 or 64, d_idx 64 or 128
+ *   kbar, blk         from sa_block_means with the same k_idx
+ *   g                 active heads per row, 1 <= g <= Hidx
+ *   idx               [B, n_q, k] int32, contiguous, as for sa_topk
+ *   heads             [B, n_q, g] int32, contiguous, or NULL: the active heads, ascending
+ *   ws                sa_misa_workspace_bytes(p, blk, g) bytes, 256-byte aligned,
+ *                     zero-filled once after allocation (status word as for sa_topk; it
+ *                     includes a score row of n_kv floats per query row).
+ */
+sa_status sa_misa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, const uint16_t* kbar,
+                         int blk, int g, int32_t* idx, int32_t* heads, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sa_misa_select; 0 for malformed or unsupported arguments. */
+size_t sa_misa_workspace_bytes(const sa_problem* p, int blk, int g);
+
 /* Synchronises `stream`, returns the status word accumulated in ws by earlier calls
  * (SA_OK or SA_ERR_NONFINITE) and clears it.  ws is a host-visible pointer to device
  * memory as passed to the other calls. */

@@ -7,7 +7,7 @@ library and raises if it is missing.
 
 The functions mirror the C ABI in include/sa.h and keep its names:
     sa_indexer_score, sa_topk, sa_sparse_attn, sa_select_attend,
-    sa_block_means, sa_hisa_select, sa_hisa_workspace_bytes,
+    sa_block_means, sa_hisa_select, sa_hisa_workspace_bytes, sa_misa_select, sa_misa_workspace_bytes,
     sa_workspace_bytes, sa_device_status, sa_status_str, sa_abi_version
 Tensors are torch tensors on the GPU whose last dimension is contiguous: float32,
 bfloat16 or float8_e4m3fn (index keys only).
@@ -63,9 +63,12 @@ def lib():
         L.sa_select_attend.argtypes = [P, T, T, T, T, T, T, vp, T, vp, vp, sz, vp]
         L.sa_block_means.argtypes = [P, T, ctypes.c_int, vp, vp]
         L.sa_hisa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
+        L.sa_misa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         for f in (L.sa_indexer_score, L.sa_topk, L.sa_sparse_attn, L.sa_select_attend, L.sa_block_means,
-                  L.sa_hisa_select):
+                  L.sa_hisa_select, L.sa_misa_select):
             f.restype = st
+        L.sa_misa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
+        L.sa_misa_workspace_bytes.restype = sz
         L.sa_hisa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
         L.sa_hisa_workspace_bytes.restype = sz
         L.sa_workspace_bytes.argtypes = [P, ctypes.c_int]
@@ -197,6 +200,23 @@ def sa_hisa_select(p, q_idx, k_idx, w, kbar, blk, k_blocks, idx, ws, blocks=None
                                 int(blk), int(k_blocks), _ptr(idx), _ptr(blocks), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "sa_hisa_select")
+
+
+def sa_misa_workspace_bytes(p, blk, g):
+    return lib().sa_misa_workspace_bytes(p.ref, int(blk), int(g))
+
+
+def misa_workspace(p, blk, g, device="cuda"):
+    """A zero-filled workspace for sa_misa_select."""
+    n = max(256, sa_misa_workspace_bytes(p, blk, g))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def sa_misa_select(p, q_idx, k_idx, w, kbar, blk, g, idx, ws, heads=None, stream=None):
+    _check(lib().sa_misa_select(p.ref, _tensor(q_idx, "q_idx"), _tensor(k_idx, "k_idx"), _tensor(w, "w"), _ptr(kbar),
+                                int(blk), int(g), _ptr(idx), _ptr(heads), _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "sa_misa_select")
 
 
 def sa_device_status(ws, stream=None):

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "hisa.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "hisa.hip", "misa.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep hipcc from emitting packed fp32 instructions
@@ -19,7 +19,7 @@ FLAGS = [
 
 # Per-file code generation options: the indexer keeps its MFMA results in plain VGPRs, which
 # saves a copy per result element ahead of the ReLU / head-weighting arithmetic.
-FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "misa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose=False, jobs=4):

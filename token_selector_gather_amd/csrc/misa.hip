@@ -1,0 +1,134 @@
+// Active index heads: routing scores and the gather of each query's active heads.
+//
+// "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: every query keeps g of its
+// G index heads, chosen from the block-averaged index keys (the absolute value of each
+// head's weighted ReLU response, averaged over the blocks of the current prefix), and the
+// score then sums only those heads.  The head choice and the scores reuse the top-k and
+// indexer kernels; the kernels here compute the routing scores and gather the chosen heads:
+//  * misa_route: route[r][h] = |w_h| * mean over the complete visible blocks B of
+//    ReLU(<q_h, kbar_B>), with kbar the bf16 block representatives of the hierarchical
+//    selection; 0 for a row without a complete visible block.  One workgroup per query
+//    row: the G x d_idx query in MFMA A fragments (rows = heads), 16 representatives per
+//    B fragment read straight from memory (a batch's representatives stay in L2), the
+//    ReLU'd products summed per head in registers, then across the 16 lanes of a head and
+//    the four waves in a fixed order;
+//  * misa_gather: the active heads' index queries and weights, in ascending head order.
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+template <int KSTEPS, int H>
+__global__ void __launch_bounds__(256) misa_route(sa_problem p, sa_tensor q, sa_tensor w, const uint16_t* kbar, int nb,
+                                                  const int32_t* row_blk, float* route) {
+    constexpr int MT = H / 16;
+    constexpr int D = 32 * KSTEPS;
+    __shared__ float s_part[4][H];
+    const int lane = threadIdx.x & 63, l15 = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long r = blockIdx.x;
+    const int b = (int)(r / p.n_q), i = (int)(r % p.n_q);
+    const int P = row_blk[r];
+    float rs[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rs[m][e] = 0.f;
+    if (P > 0) {
+        // A fragments: row 16 m + lane%16 = head, k-step s holds d = 32 s + 8 (lane/16) + 0..7
+        bf16x8 av[MT][KSTEPS];
+        const uint16_t* qp = static_cast<const uint16_t*>(q.data) + b * q.s0 + (int64_t)i * q.s1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+                av[m][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (16 * m + l15) * q.s2 + 32 * s + 8 * g));
+        const uint16_t* kb = kbar + (int64_t)b * nb * D;
+        const int ntl = (P + 15) / 16;
+        for (int u = wv; u < ntl; u += 4) {
+            const int blk_id = 16 * u + l15;  // this lane's column: representative blk_id
+            const bool ok = blk_id < P;
+            const uint16_t* kr = kb + (int64_t)(ok ? blk_id : 0) * D + 8 * g;
+            f32x4 acc[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 32 * s));
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][s], bv, acc[m], 0, 0, 0);
+            }
+            // acc[m][e]: head 16 m + 4 (lane/16) + e against representative blk_id
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rs[m][e] += ok ? fmaxf(acc[m][e], 0.f) : 0.f;
+        }
+    }
+    // sum over the 16 representatives of a lane row, then over the waves
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = rs[m][e];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+            if (l15 == 0) s_part[wv][16 * m + 4 * g + e] = v;
+        }
+    __syncthreads();
+    if (threadIdx.x < H) {
+        const int h = threadIdx.x;
+        const float sum = ((s_part[0][h] + s_part[1][h]) + s_part[2][h]) + s_part[3][h];
+        const float wh = fabsf(static_cast<const float*>(w.data)[b * w.s0 + (int64_t)i * w.s1 + h]);
+        route[r * H + h] = P > 0 ? wh * (sum / (float)P) : 0.f;
+    }
+}
+
+// thread (r, j, piece): piece of active head j of row r (16 bytes of its bf16 query)
+__global__ void __launch_bounds__(256) misa_gather(sa_problem p, sa_tensor q, sa_tensor w, int g, const int32_t* heads,
+                                                   uint16_t* qa, float* wa) {
+    const int pieces = p.d_idx / 8;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long)p.B * p.n_q * g * pieces) return;
+    const int c = (int)(e % pieces);
+    const long rj = e / pieces;
+    const long r = rj / g;
+    const int b = (int)(r / p.n_q), i = (int)(r % p.n_q);
+    const int h = heads[rj];
+    const uint16_t* src = static_cast<const uint16_t*>(q.data) + b * q.s0 + (int64_t)i * q.s1 + (int64_t)h * q.s2 + 8 * c;
+    *reinterpret_cast<uint4*>(qa + rj * p.d_idx + 8 * c) = *reinterpret_cast<const uint4*>(src);
+    if (c == 0) wa[rj] = static_cast<const float*>(w.data)[b * w.s0 + (int64_t)i * w.s1 + h];
+}
+
+}  // namespace
+
+bool misa_route_supported(const sa_problem& p) {
+    return (p.Hidx == 16 || p.Hidx == 32 || p.Hidx == 64) && (p.d_idx == 64 || p.d_idx == 128);
+}
+
+hipError_t launch_misa_route(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, const uint16_t* kbar, int blk,
+                             const int32_t* row_blk, float* route, hipStream_t s) {
+    const int nb = p.n_kv / blk;
+    const dim3 grid((unsigned)((long)p.B * p.n_q)), block(256);
+#define SA_ROUTE(KS, HH)                                                                         \
+    if (p.Hidx == HH) {                                                                          \
+        hipLaunchKernelGGL((misa_route<KS, HH>), grid, block, 0, s, p, q, w, kbar, nb, row_blk, route); \
+        return hipGetLastError();                                                                \
+    }
+    if (p.d_idx == 64) { SA_ROUTE(2, 16) SA_ROUTE(2, 32) SA_ROUTE(2, 64) }
+    else { SA_ROUTE(4, 16) SA_ROUTE(4, 32) SA_ROUTE(4, 64) }
+#undef SA_ROUTE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_misa_gather(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, int g, const int32_t* heads,
+                              uint16_t* qa, float* wa, hipStream_t s) {
+    const long n = (long)p.B * p.n_q * g * (p.d_idx / 8);
+    hipLaunchKernelGGL(misa_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, q, w, g, heads, qa, wa);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -88,6 +88,14 @@ hipError_t launch_hisa_gather(const sa_problem& p, const sa_tensor& k, int blk, 
 hipError_t launch_hisa_map(const sa_problem& p, int blk, int k_blocks, const int32_t* bidx, const int32_t* row_blk,
                            const int32_t* cidx, int32_t* idx, hipStream_t s);
 
+// Active index heads: routing scores over the block representatives, and the gather of the
+// chosen heads' queries and weights.
+bool misa_route_supported(const sa_problem& p);
+hipError_t launch_misa_route(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, const uint16_t* kbar, int blk,
+                             const int32_t* row_blk, float* route, hipStream_t s);
+hipError_t launch_misa_gather(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, int g, const int32_t* heads,
+                              uint16_t* qa, float* wa, hipStream_t s);
+
 // Host-side planning shared by workspace sizing and launches.
 int attn_splits(const sa_problem& p);
 bool attn_uses_mla(const sa_problem& p, int dtype);
