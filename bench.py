@@ -165,6 +165,42 @@ def hisa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat):
             "bytes_per_call": nbytes, "achieved_gbs": round(nbytes / (t_h * 1e-3) / 1e9, 1)}
 
 
+def misa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat):
+    """Active index heads (g = Hidx / 4 of the heads per query, routed by the block
+    representatives, b = 128) timed beside the flat score + select, with the overlap of
+    the two selections; the representatives are prebuilt index state."""
+    import numpy as np
+    import torch
+
+    import token_selector_gather_amd as sa
+
+    blk, g = 128, W["Hidx"] // 4
+    nb = W["n_kv"] // blk
+    if nb < 1 or g < 1 or sa.sa_misa_workspace_bytes(P, blk, g) == 0:
+        return None
+    kbar = torch.empty((W["B"], nb, W["d_idx"]), dtype=torch.bfloat16, device="cuda")
+    sa.sa_block_means(P, d["k_idx"], blk, kbar, stream)
+    ws_m = sa.misa_workspace(P, blk, g)
+    idx_m = torch.empty((W["B"], W["n_q"], W["k"]), dtype=torch.int32, device="cuda")
+    t_m = timed(lambda: sa.sa_misa_select(P, d["q_idx"], d["k_idx"], d["w"], kbar, blk, g, idx_m, ws_m, stream=stream),
+                reps)
+    st = sa.sa_device_status(ws_m)
+    if st != sa.SA_OK:
+        raise RuntimeError("active-head selection: device status " + sa.sa_status_str(st))
+    a = idx_m.reshape(-1, W["k"]).cpu().numpy()
+    f = flat_idx.reshape(-1, W["k"]).cpu().numpy()
+    L = visible_counts(W).reshape(-1)
+    rng = np.random.default_rng(0)
+    rows = rng.choice(np.where(L > 0)[0], size=min(2048, int((L > 0).sum())), replace=False)
+    iou = [np.intersect1d(a[r][a[r] >= 0], f[r][f[r] >= 0]).size /
+           max(1, np.union1d(a[r][a[r] >= 0], f[r][f[r] >= 0]).size) for r in rows]
+    pairs = int(L.sum())
+    flops = 2 * W["d_idx"] * g * pairs + 2 * W["d_idx"] * W["Hidx"] * int((L // blk).sum())
+    return {"blk": blk, "g": g, "select_ms": round(t_m, 4), "flat_score_select_ms": round(t_flat, 4),
+            "speedup_vs_flat": round(t_flat / t_m, 3), "iou_vs_flat": round(float(np.mean(iou)), 4),
+            "iou_rows": int(len(rows)), "flops_per_call": flops, "tflops": round(flops / (t_m * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(W, budget_rows):
     """The oracle (unchanged) on a stratified sample of rows: score, select and attend."""
     import numpy as np
@@ -192,6 +228,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=7680, help="rows in the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--hisa", type=int, default=-1,
                     help="time the hierarchical selection beside the flat one (default: decode workloads only)")
+    ap.add_argument("--misa", type=int, default=-1,
+                    help="time the active-head selection beside the flat one (default: prefill workloads with 64 index heads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
@@ -334,6 +372,8 @@ def main():
     }
     if args.hisa == 1 or (args.hisa == -1 and alg["decode"]):
         out["hisa"] = hisa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
+    if args.misa == 1 or (args.misa == -1 and not alg["decode"] and W["Hidx"] == 64):
+        out["misa"] = misa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_rows)
     print(json.dumps(out))
