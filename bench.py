@@ -201,6 +201,38 @@ def misa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat):
             "iou_rows": int(len(rows)), "flops_per_call": flops, "tflops": round(flops / (t_m * 1e-3) / 1e12, 2)}
 
 
+def paged_stage(W, P, d, stream, timed, cold, reps, idx, t_attn, t_attn_cold, O_ref, lse_ref):
+    """The sparse attention over paged K/V (pages of 64 rows at seeded random places in one
+    pool, block-table translation in the gather) timed beside the contiguous call on the same
+    candidates, warm and with cold caches; the two outputs must agree bit for bit."""
+    import numpy as np
+    import torch
+
+    import sa_synth
+    import token_selector_gather_amd as sa
+    from token_selector_gather_amd.inputs import device_pool, empty_outputs
+
+    ps = 64
+    bt, pool_rows = sa_synth.paged_layout(W["seed"] + 7, W["B"], W["n_kv"], ps, 3)
+    Kp = device_pool(d["K"], bt, ps, pool_rows)
+    Vp = Kp[..., : W["d_v"]] if W.get("V") is None else device_pool(d["V"], bt, ps, pool_rows)
+    btd = torch.from_numpy(bt).cuda()
+    O, lse, _ = empty_outputs(W, O_ref.dtype)
+    ws = sa.workspace(P, sa.SA_OP_SPARSE_ATTN_PAGED)
+
+    def call():
+        sa.sa_sparse_attn_paged(P, d["Q"], Kp, Vp, btd, ps, idx, O, lse, ws, stream)
+
+    t = timed(call, reps)
+    tc = cold(call)
+    same = bool(torch.equal(O, O_ref) and torch.equal(lse, lse_ref))
+    del Kp, Vp
+    return {"page_size": ps, "pool_pages": pool_rows // ps, "sparse_attn_paged_ms": round(t, 4),
+            "sparse_attn_ms": round(t_attn, 4), "paged_over_contiguous": round(t / t_attn, 4),
+            "sparse_attn_paged_ms_cold": round(tc, 4), "sparse_attn_ms_cold": round(t_attn_cold, 4),
+            "bit_identical_to_contiguous": same}
+
+
 def cpu_baseline(W, budget_rows):
     """The oracle (unchanged) on a stratified sample of rows: score, select and attend."""
     import numpy as np
@@ -230,6 +262,8 @@ def main():
                     help="time the hierarchical selection beside the flat one (default: decode workloads only)")
     ap.add_argument("--misa", type=int, default=-1,
                     help="time the active-head selection beside the flat one (default: prefill workloads with 64 index heads)")
+    ap.add_argument("--paged", type=int, default=1,
+                    help="time the sparse attention over paged K/V beside the contiguous call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
@@ -338,7 +372,6 @@ def main():
         "topk": cold(lambda: sa.sa_topk(P, scores, W["n_kv"], idx2, None, ws_t, stream)),
         "sparse_attn": cold(lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream)),
     }
-    del flush
     roofs = stage_rooflines(W, alg, times)
     dominant = max(times, key=times.get)
     roof = dict(roofs[dominant])
@@ -374,6 +407,8 @@ def main():
         out["hisa"] = hisa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
     if args.misa == 1 or (args.misa == -1 and not alg["decode"] and W["Hidx"] == 64):
         out["misa"] = misa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
+    if args.paged == 1:
+        out["paged"] = paged_stage(W, P, d, stream, timed, cold, reps, idx, t_attn, cold_times["sparse_attn"], O2, lse2)
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_rows)
     print(json.dumps(out))

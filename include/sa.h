@@ -66,7 +66,8 @@ typedef enum sa_op {
     SA_OP_INDEXER_SCORE = 0,
     SA_OP_TOPK = 1,
     SA_OP_SPARSE_ATTN = 2,
-    SA_OP_SELECT_ATTEND = 3
+    SA_OP_SELECT_ATTEND = 3,
+    SA_OP_SPARSE_ATTN_PAGED = 4
 } sa_op;
 
 typedef struct sa_tensor {
@@ -143,6 +144,34 @@ sa_status sa_topk(const sa_problem* p, const float* scores, int64_t row_stride, 
  */
 sa_status sa_sparse_attn(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tensor V, const int32_t* idx,
                          sa_tensor O, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sa_sparse_attn_paged -- sa_sparse_attn over K/V held in fixed-size pages.
+ * "PaperTrace 2.2 · Fine-grained indexing", §2.1 (the gather of the main KV: the selected
+ * logical positions go through the block table to physical rows before the attention
+ * reads them) and §3.1 (the block table among the objects of the sparse-attention call).
+ * The result is that of sa_sparse_attn on the logical K/V in which position j of batch b
+ * is physical row  block_table[b*bt_stride + j/page_size]*page_size + j%page_size  of the pools.
+ *   K, V        page pools: element (head h, physical row r, column c) at data + h*s1 +
+ *               r*s2 + c (s0 is not used); pool_rows rows per head; V may alias K as above.
+ *   pool_rows   rows in the pools (a whole number of pages is expected; a page that does
+ *               not fit entirely is never read).
+ *   block_table int32, device; row b holds the page numbers of batch b's logical pages
+ *               0 .. ceil(n_kv/page_size) - 1; bt_stride >= that count.  Only pages that
+ *               hold a visible selected position are read.  A page number outside
+ *               [0, pool_rows/page_size) skips the candidate (as an idx entry of -1 would).
+ *   page_size   a power of two, 1 .. 65536.
+ *   ws          workspace of at least sa_workspace_bytes(p, SA_OP_SPARSE_ATTN_PAGED) bytes
+ *               (it holds the translated candidate rows of the multi-head kernel).
+ * Q, idx, O, lse and the dtypes are as for sa_sparse_attn.  The call is supported on
+ * the two matrix-core/vector kernels: bf16 latent (d_qk 576, d_v 512, V aliasing K,
+ * 32/64/128 query heads per key head, pool_rows * row stride below 2^31 bytes) and bf16
+ * multi-head with Hq == Hkv and d_qk == d_v in {64, 128, 256} (k a multiple of 4, fewer
+ * than 2^24 pool rows); other shapes return SA_ERR_UNSUPPORTED.
+ */
+sa_status sa_sparse_attn_paged(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tensor V, int64_t pool_rows,
+                               const int32_t* block_table, int64_t bt_stride, int page_size, const int32_t* idx,
+                               sa_tensor O, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sa_select_attend -- score, select and attend in one call; arguments as in the three

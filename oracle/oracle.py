@@ -152,6 +152,34 @@ def attend(W, idx, rows=None, pos_of_slot=None, Q=None, K=None, V=None, scale=No
     return O, lse
 
 
+def attend_paged(W, idx, K_pool, V_pool, block_table, page_size, rows=None):
+    """attend() over K/V held in pages.  "PaperTrace 2.2 · Fine-grained indexing", §2.1 (the
+    gather of the main KV: selected logical positions pass through the block table before
+    the attention reads physical rows) and §3.1 (block_table maps logical positions to
+    physical pages).  Logical row j of batch b is pool row
+    block_table[b, j // page_size] * page_size + j % page_size; K_pool, V_pool are
+    [Hkv, pool_rows, d] (V_pool None: the latent layout, V = the first d_v columns of K).
+    Reading: a candidate whose page number lies outside the pool is skipped, as a -1 slot.
+    The pools are un-paged into the contiguous layout, then attend() runs on it."""
+    K_pool = np.asarray(K_pool)
+    bt = np.asarray(block_table, dtype=np.int64)
+    B, n_kv = W["B"], W["n_kv"]
+    pool_pages = K_pool.shape[1] // page_size
+    j = np.arange(n_kv)
+    page = bt[:, j // page_size]                                   # [B, n_kv]
+    ok = (page >= 0) & (page < pool_pages)
+    phys = np.where(ok, page * page_size + j % page_size, 0)       # [B, n_kv]
+    K = np.ascontiguousarray(K_pool[:, phys].transpose(1, 0, 2, 3))  # [B, Hkv, n_kv, d]
+    V = None if V_pool is None else np.ascontiguousarray(np.asarray(V_pool)[:, phys].transpose(1, 0, 2, 3))
+    rows_ = _rows(W, rows)
+    idx = np.array(idx, dtype=np.int32, copy=True)
+    b_of = rows_ // W["n_q"]
+    inr = (idx >= 0) & (idx < n_kv)
+    bad = inr & ~ok[b_of[:, None], np.clip(idx, 0, n_kv - 1)]
+    idx[bad] = -1
+    return attend(W, idx, rows_, K=K, V=V)
+
+
 def count_visible(W, causal=None):
     P = Problem(W, causal=causal)
     return lib().or_count_visible(ctypes.byref(P.p))

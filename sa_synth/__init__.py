@@ -74,4 +74,4 @@ def bf16_to_f32(a):
     return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-from .configs import CONFIGS, custom, make_config, poison_value  # noqa: E402,F401
+from .configs import CONFIGS, custom, make_config, paged_layout, poison_value, to_pool  # noqa: E402,F401

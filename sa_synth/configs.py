@@ -175,3 +175,29 @@ def _clustered_keys(W, seed):
                 keys[b, needle_pos[b, i, m]] = (6.0 + 0.25 * m) * u * math.sqrt(didx) / 4.0
     W["needle_pos"] = needle_pos
     return encode(keys, W.kidx_dtype)
+
+
+def paged_layout(seed, B, n_kv, page_size, spare_pages=3):
+    """Block table of a paged KV cache: each batch's ceil(n_kv / page_size) logical pages sit
+    on distinct pages of one shared pool, chosen by a seeded random permutation, with
+    `spare_pages` pages left unused.  Returns (block_table [B, pages] int32, pool_rows)."""
+    npg = -(-n_kv // page_size)
+    total = B * npg + spare_pages
+    perm = np.random.default_rng(seed).permutation(total)[: B * npg].reshape(B, npg)
+    return np.ascontiguousarray(perm, dtype=np.int32), total * page_size
+
+
+def to_pool(X, block_table, page_size, pool_rows, fill):
+    """Scatter per-batch rows X [B, H, n_kv, d] into a pool [H, pool_rows, d] along the
+    block table; rows no batch uses hold `fill` (a storage value of X's dtype)."""
+    B, H, n_kv, d = X.shape
+    pool = np.full((H, pool_rows, d), fill, dtype=X.dtype)
+    for b in range(B):
+        for pg in range(block_table.shape[1]):
+            lo = pg * page_size
+            if lo >= n_kv:
+                break
+            hi = min(lo + page_size, n_kv)
+            dst = int(block_table[b, pg]) * page_size
+            pool[:, dst:dst + hi - lo] = X[b, :, lo:hi]
+    return pool

@@ -103,6 +103,37 @@ def test_attention_argument_errors():
 
 
 @needs_lib
+def test_paged_attention_argument_errors():
+    L = sa.lib()
+    p = _prob()
+    ws = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SPARSE_ATTN_PAGED)
+    assert ws >= 256 + 2 * 64 * 8 * 4  # status + translated candidate rows
+    ok = _t(s0=0)
+
+    def call(pool_rows=4096, bt=FAKE, bt_stride=4, page=16, pp=p, K=ok, Q=ok):
+        return L.sa_sparse_attn_paged(ctypes.byref(pp), Q, K, ok, pool_rows, bt, bt_stride, page, FAKE, ok,
+                                      None, FAKE, ws, None)
+    assert call(bt=None) == sa.SA_ERR_INVALID_ARG
+    assert call(bt=FAKE + 2) == sa.SA_ERR_INVALID_ARG
+    assert call(page=24) == sa.SA_ERR_INVALID_ARG       # not a power of two
+    assert call(page=0) == sa.SA_ERR_INVALID_ARG
+    assert call(page=1 << 17) == sa.SA_ERR_INVALID_ARG
+    assert call(bt_stride=3) == sa.SA_ERR_INVALID_ARG   # 64 positions need 4 pages of 16
+    assert call(pool_rows=0) == sa.SA_ERR_INVALID_ARG
+    assert call(K=_t(s0=0, data=FAKE + 2)) == sa.SA_ERR_INVALID_ARG
+    f32 = _t(dtype=sa.SA_F32, s0=0)
+    assert L.sa_sparse_attn_paged(ctypes.byref(p), f32, f32, f32, 4096, FAKE, 4, 16, FAKE, f32, None, FAKE, ws,
+                                  None) == sa.SA_ERR_UNSUPPORTED  # only the bf16 kernels translate pages
+    gqa = _prob(Hq=8, Hkv=4)
+    ws2 = L.sa_workspace_bytes(ctypes.byref(gqa), sa.SA_OP_SPARSE_ATTN_PAGED)
+    assert L.sa_sparse_attn_paged(ctypes.byref(gqa), ok, ok, ok, 4096, FAKE, 4, 16, FAKE, ok, None, FAKE, ws2,
+                                  None) == sa.SA_ERR_UNSUPPORTED
+    assert call(pool_rows=1 << 24) == sa.SA_ERR_UNSUPPORTED  # 24-bit row products of the MHA kernel
+    big = _prob(k=6)
+    assert call(pp=big) == sa.SA_ERR_UNSUPPORTED             # MHA kernel reads candidates four at a time
+
+
+@needs_lib
 def test_indexer_argument_errors():
     L = sa.lib()
     p = _prob()

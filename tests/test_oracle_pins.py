@@ -655,3 +655,68 @@ def test_misa_routes_to_the_head_with_the_larger_weighted_block_response():
     r2 = orc.misa_select(W2, 4, 1)
     assert r2["heads"][0].tolist() == [0]
     assert r2["idx"][0].tolist() == [0, 1]  # head 0 scores block 0's keys 3, the rest 0: lowest positions
+
+
+# ------------------------------------------------------------------ paged K/V
+# "PaperTrace 2.2 · Fine-grained indexing", §2.1 (the main-KV gather reaches physical rows
+# through the block table) and §3.1 (block_table maps logical positions to physical pages).
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 64])
+def test_paged_attention_on_a_shuffled_pool_equals_the_contiguous_layout(page_size):
+    # Paging is a storage layout: scattering every batch's rows to random pages of a pool
+    # (unused rows poisoned) and attending through the table must give exactly the result on
+    # the contiguous tensors.  A wrong page or offset formula reads another row or a poison row.
+    W = sa_synth.custom(seed=21, B=2, n_q=40, n_kv=150, Hq=2, Hkv=2, d_qk=64, d_v=64, k=24, lens=[150, 97])
+    rows = all_rows(W)
+    ref = orc.select_attend(W, rows)
+    bt, pool_rows = sa_synth.paged_layout(5, W["B"], W["n_kv"], page_size)
+    fill = sa_synth.encode(np.array([sa_synth.poison_value(W["main_dtype"])]), W["main_dtype"])[0]
+    Kp = sa_synth.to_pool(W["K"], bt, page_size, pool_rows, fill)
+    Vp = sa_synth.to_pool(W["V"], bt, page_size, pool_rows, fill)
+    O, lse = orc.attend_paged(W, ref["idx"], Kp, Vp, bt, page_size, rows)
+    assert np.array_equal(O, ref["O"]) and np.array_equal(lse, ref["lse"])
+
+
+def test_paged_attention_latent_layout_and_page_order():
+    # Latent layout (V = the first d_v columns of each K row) through pages; a table whose
+    # pages are listed in reverse order for batch 0 is followed, not the pool order.
+    W = sa_synth.make_config(3, B=2, n_kv=300, k=64)
+    rows = all_rows(W)
+    ref = orc.select_attend(W, rows)
+    ps = 32
+    npg = -(-W["n_kv"] // ps)
+    bt = np.stack([np.arange(npg)[::-1], npg + np.arange(npg)]).astype(np.int32)
+    Kp = sa_synth.to_pool(W["K"], bt, ps, 2 * npg * ps, 0)
+    O, lse = orc.attend_paged(W, ref["idx"], Kp, None, bt, ps, rows)
+    assert np.array_equal(O, ref["O"]) and np.array_equal(lse, ref["lse"])
+    # reading the pool as if it were contiguous (identity table) is a different, wrong answer
+    ident = np.stack([np.arange(npg), npg + np.arange(npg)]).astype(np.int32)
+    O2, _ = orc.attend_paged(W, ref["idx"], Kp, None, ident, ps, rows)
+    assert not np.allclose(O2[0], ref["O"][0])
+
+
+def test_paged_attention_hand_case_page_outside_the_pool_is_skipped():
+    # Six positions in pages of two; the pool holds three pages, stored in the order
+    # (page 1, page 2, page 0).  Position 3 lives on logical page 1 = pool page 0, row 1.
+    rng = np.random.default_rng(22)
+    Q, K, V = (rand_f32(rng, (1, 1, 6, 4)) for _ in range(3))
+    W = tiny(Q=Q, K=K, V=V, causal=0, scale=0.5, k=4)
+    bt = np.array([[2, 0, 1]], np.int32)
+    Kp = np.empty((1, 6, 4), np.float32)
+    Vp = np.empty((1, 6, 4), np.float32)
+    for j in range(6):
+        r = bt[0, j // 2] * 2 + j % 2
+        Kp[0, r], Vp[0, r] = K[0, 0, j], V[0, 0, j]
+    assert np.array_equal(Kp[0, 1], K[0, 0, 3])
+    row = np.array([4], np.int32)
+    idx = np.array([[0, 3, 4, 5]], np.int32)
+    O, lse = orc.attend_paged(W, idx, Kp, Vp, bt, 2, rows=row)
+    Oc, lc = orc.attend(W, idx, rows=row)
+    assert np.array_equal(O, Oc) and np.array_equal(lse, lc)
+    # page 2 (positions 4, 5) pointed outside the pool: those candidates drop out
+    bad = bt.copy()
+    bad[0, 2] = 3
+    Ob, lb = orc.attend_paged(W, idx, Kp, Vp, bad, 2, rows=row)
+    Oe, le = orc.attend(W, np.array([[0, 3, -1, -1]], np.int32), rows=row)
+    assert np.array_equal(Ob, Oe) and np.array_equal(lb, le)

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libsa.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_NONFINITE = range(6)
 SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
-SA_OP_INDEXER_SCORE, SA_OP_TOPK, SA_OP_SPARSE_ATTN, SA_OP_SELECT_ATTEND = range(4)
+SA_OP_INDEXER_SCORE, SA_OP_TOPK, SA_OP_SPARSE_ATTN, SA_OP_SELECT_ATTEND, SA_OP_SPARSE_ATTN_PAGED = range(5)
 ABI_VERSION = 1
 
 _TORCH_DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
@@ -61,11 +61,12 @@ def lib():
         L.sa_topk.argtypes = [P, vp, i64, vp, vp, vp, sz, vp]
         L.sa_sparse_attn.argtypes = [P, T, T, T, vp, T, vp, vp, sz, vp]
         L.sa_select_attend.argtypes = [P, T, T, T, T, T, T, vp, T, vp, vp, sz, vp]
+        L.sa_sparse_attn_paged.argtypes = [P, T, T, T, i64, vp, i64, ctypes.c_int, vp, T, vp, vp, sz, vp]
         L.sa_block_means.argtypes = [P, T, ctypes.c_int, vp, vp]
         L.sa_hisa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         L.sa_misa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         for f in (L.sa_indexer_score, L.sa_topk, L.sa_sparse_attn, L.sa_select_attend, L.sa_block_means,
-                  L.sa_hisa_select, L.sa_misa_select):
+                  L.sa_hisa_select, L.sa_misa_select, L.sa_sparse_attn_paged):
             f.restype = st
         L.sa_misa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
         L.sa_misa_workspace_bytes.restype = sz
@@ -167,6 +168,21 @@ def sa_sparse_attn(p, Q, K, V, idx, O, lse, ws, stream=None):
                                 _tensor(O, "O"), _ptr(lse), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "sa_sparse_attn")
+
+
+def sa_sparse_attn_paged(p, Q, K_pool, V_pool, block_table, page_size, idx, O, lse, ws, stream=None):
+    """sa_sparse_attn over paged pools K_pool / V_pool [1, Hkv, pool_rows, d] (one unit leading
+    dimension, so that the head and row strides land where the C call reads them) and an int32
+    block_table [B, pages per batch]."""
+    if K_pool.dim() != 4 or K_pool.shape[0] != 1 or V_pool.dim() != 4 or V_pool.shape[0] != 1:
+        raise ValueError("K_pool and V_pool must be [1, Hkv, pool_rows, d]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be an int32 [B, pages] tensor with contiguous rows")
+    _check(lib().sa_sparse_attn_paged(p.ref, _tensor(Q, "Q"), _tensor(K_pool, "K_pool"), _tensor(V_pool, "V_pool"),
+                                      int(K_pool.shape[2]), _ptr(block_table), int(block_table.stride(0)),
+                                      int(page_size), _ptr(idx), _tensor(O, "O"), _ptr(lse), _ptr(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "sa_sparse_attn_paged")
 
 
 def sa_select_attend(p, q_idx, k_idx, w, Q, K, V, idx_out, O, lse, ws, stream=None):

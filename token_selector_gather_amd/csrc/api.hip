@@ -177,8 +177,15 @@ MisaLayout misa_layout(const sa_problem& p, int g) {
 
 float eff_scale(const sa_problem* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d_qk); }
 
-sa_status run_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V,
-                   const int32_t* idx, const sa_tensor& O, float* lse, void* partial, hipStream_t st) {
+// Block-table view of paged K/V pools (table null: K and V hold each batch's rows).
+struct Pages {
+    const int32_t* table = nullptr;
+    int64_t stride = 0, pool_rows = 0;
+    int shift = 0;
+};
+
+AttnArgs attn_args(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V, const int32_t* idx,
+                   const sa_tensor& O, float* lse, void* partial, const Pages& pg) {
     AttnArgs a;
     a.p = *p;
     a.Q = Q; a.K = K; a.V = V; a.O = O;
@@ -187,7 +194,17 @@ sa_status run_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, 
     a.scale = eff_scale(p);
     a.splits = attn_uses_mla(*p, Q.dtype) ? attn_splits(*p) : 1;
     a.partial = partial;
-    return launch_attn(a, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
+    a.block_table = pg.table;
+    a.bt_stride = pg.stride;
+    a.page_shift = pg.shift;
+    a.pool_rows = pg.pool_rows;
+    return a;
+}
+
+sa_status run_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V,
+                   const int32_t* idx, const sa_tensor& O, float* lse, void* partial, hipStream_t st,
+                   const Pages& pg = Pages()) {
+    return launch_attn(attn_args(p, Q, K, V, idx, O, lse, partial, pg), st) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
 }  // namespace
@@ -214,6 +231,11 @@ size_t sa_workspace_bytes(const sa_problem* p, int op) {
     case SA_OP_INDEXER_SCORE: return 0;
     case SA_OP_TOPK: return kStatusBytes + align256(topk_ws_bytes(*p));
     case SA_OP_SPARSE_ATTN: return kStatusBytes + align256(attn_partial_bytes(*p));
+    case SA_OP_SPARSE_ATTN_PAGED: {
+        // the latent kernel's split partials, or the multi-head kernel's translated rows
+        const size_t part = align256(attn_partial_bytes(*p)), rows = idx_bytes(*p);
+        return kStatusBytes + (part > rows ? part : rows);
+    }
     case SA_OP_SELECT_ATTEND:
         return kStatusBytes + scores_bytes(*p) + idx_bytes(*p) + align256(attn_partial_bytes(*p)) +
                align256(topk_ws_bytes(*p));
@@ -262,6 +284,27 @@ sa_status sa_sparse_attn(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tenso
     if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SPARSE_ATTN))) != SA_OK) return s;
     void* partial = static_cast<char*>(ws) + kStatusBytes;
     return run_attn(p, Q, K, V, idx, O, lse, partial, (hipStream_t)stream);
+}
+
+sa_status sa_sparse_attn_paged(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tensor V, int64_t pool_rows,
+                               const int32_t* block_table, int64_t bt_stride, int page_size, const int32_t* idx,
+                               sa_tensor O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (!problem_ok(p) || !idx || ((uintptr_t)idx & 3)) return SA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3)) return SA_ERR_INVALID_ARG;
+    if (!block_table || ((uintptr_t)block_table & 3)) return SA_ERR_INVALID_ARG;
+    if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0) return SA_ERR_INVALID_ARG;
+    if (pool_rows < 1 || bt_stride < ((int64_t)p->n_kv + page_size - 1) / page_size) return SA_ERR_INVALID_ARG;
+    sa_status s = check_attn(p, Q, K, V, O);
+    if (s != SA_OK) return s;
+    if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SPARSE_ATTN_PAGED))) != SA_OK) return s;
+    Pages pg;
+    pg.table = block_table;
+    pg.stride = bt_stride;
+    pg.pool_rows = pool_rows;
+    while ((1 << pg.shift) < page_size) ++pg.shift;
+    void* partial = static_cast<char*>(ws) + kStatusBytes;
+    if (!attn_paged_ok(attn_args(p, Q, K, V, idx, O, lse, partial, pg))) return SA_ERR_UNSUPPORTED;
+    return run_attn(p, Q, K, V, idx, O, lse, partial, (hipStream_t)stream, pg);
 }
 
 sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, sa_tensor Q,

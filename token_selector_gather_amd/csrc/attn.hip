@@ -65,6 +65,32 @@ struct Vec<uint16_t> {
 };
 
 // online-softmax merge of (m, l, o) states in log2 units
+// Row of logical history position j of batch b in the K/V tensors: j itself (rows of the
+// batch's own slice), or its physical row in the page pools when a block table is given;
+// -1 when the table names a page outside the pools (the candidate is then skipped).
+__device__ __forceinline__ int64_t kv_row(const AttnArgs& a, int b, int j) {
+    if (!a.block_table) return j;
+    const int64_t page = a.block_table[b * a.bt_stride + (j >> a.page_shift)];
+    if (page < 0 || page >= (a.pool_rows >> a.page_shift)) return -1;
+    return (page << a.page_shift) | (int64_t)(j & ((1 << a.page_shift) - 1));
+}
+
+// Pool rows of a candidate list: out[e] = the pool row of candidate e (kv_row), or -1 when
+// the candidate is -1, out of range, not visible or on a page outside the pools.  One pass
+// per call, so the multi-head kernel's workgroups (one per key/value head) read pool rows
+// directly instead of each repeating the table lookups.
+__global__ void __launch_bounds__(256) page_rows(AttnArgs a, int32_t* out) {
+    const sa_problem& p = a.p;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long)p.B * p.n_q * p.k) return;
+    const long r = e / p.k;
+    const int b = (int)(r / p.n_q), i = (int)(r % p.n_q);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    const int j = a.idx[e];
+    out[e] = (unsigned)j < (unsigned)L ? (int32_t)kv_row(a, b, j) : -1;
+}
+
 __device__ __forceinline__ void merge_state(float& m, float& l, float* o, int n, float m2, float l2, const float* o2) {
     const float mn = fmaxf(m, m2);
     const float a1 = (m == -INFINITY) ? 0.f : exp2f(m - mn);
@@ -258,7 +284,8 @@ __device__ __forceinline__ float group_sum2(float x) {
     return x;
 }
 
-template <int D>
+// PAGED: the candidate list holds pool rows already (page_rows below), -1 for a skipped slot.
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
     constexpr int LPR = D / 16;      // lanes per row, 32 bytes each
     constexpr int RPG = 64 / LPR;    // row groups per wave
@@ -300,10 +327,10 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
     const uint4 qa = *reinterpret_cast<const uint4*>(Qp), qc = *reinterpret_cast<const uint4*>(Qp + HALF);
     const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qc.x, qc.y, qc.z, qc.w};
     const uint32_t kstride = (uint32_t)(a.K.s2 * 2), vstride = (uint32_t)(a.V.s2 * 2);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const uint16_t*>(a.K.data) + b * a.K.s0 + hk * a.K.s1,
-                                                (uint32_t)p.n_kv * kstride);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.V.data) + b * a.V.s0 + hk * a.V.s1,
-                                                 (uint32_t)p.n_kv * vstride);
+    const int64_t kb0 = PAGED ? 0 : b * a.K.s0, vb0 = PAGED ? 0 : b * a.V.s0;
+    const uint32_t nrows = (uint32_t)(PAGED ? a.pool_rows : p.n_kv);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const uint16_t*>(a.K.data) + kb0 + hk * a.K.s1, nrows * kstride);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.V.data) + vb0 + hk * a.V.s1, nrows * vstride);
     const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
     const uint32_t col = 16u * sub;
 
@@ -319,7 +346,7 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
         bool ok[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            ok[u] = (unsigned)jv[u] < (unsigned)L;
+            ok[u] = PAGED ? jv[u] >= 0 : (unsigned)jv[u] < (unsigned)L;
             koff[u] = ok[u] ? __umul24((uint32_t)jv[u], kstride) + col : 0x80000000u;
             voff[u] = ok[u] ? __umul24((uint32_t)jv[u], vstride) + col : 0x80000000u;
         }
@@ -694,7 +721,13 @@ __device__ __forceinline__ v4s lds_tr_read(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
 }
 
-template <int NW>
+// IDX: paged pools.  The offset list holds pool row indices, and every lane of a tile load
+// forms its own 64-bit address (pool base + row * row stride + column), since a pool may
+// exceed the 4 GiB a buffer resource reaches; an empty slot reads the zero row instead.
+constexpr int kZeroRowBytes = 4096;
+__device__ __align__(16) const uint8_t kZeroRow[kZeroRowBytes] = {};
+
+template <int NW, bool IDX>
 __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     using namespace mla;
     constexpr int NI = NI_ALL / NW;    // loads per wave per tile
@@ -728,6 +761,7 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
     const int L = visible_len(R, b, i);
     const uint32_t rowb = (uint32_t)(a.K.s2 * 2);
+    const uint32_t SENT = IDX ? (uint32_t)a.pool_rows : 0x80000000u;  // offset-list value of an empty slot
 
     const int per = (p.k + S - 1) / S;
     const int e_begin = split * per;
@@ -765,8 +799,9 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         const int e = (int)threadIdx.x + 64 * NW * k;
         if (e < ne64) {  // uniform per wave (ne64 is a multiple of 64)
             const int j = jv[k];
-            const bool ok = j >= 0 && j < L;
-            s_off[e] = ok ? (uint32_t)j * rowb : 0x80000000u;
+            const int64_t row = j >= 0 && j < L ? (IDX ? kv_row(a, b, j) : (int64_t)j) : -1;
+            const bool ok = row >= 0;
+            s_off[e] = ok ? (IDX ? (uint32_t)row : (uint32_t)row * rowb) : SENT;
             const uint64_t bal = __ballot(ok);
             if (lane == 0 && bal != 0) atomicMax(s_nt, (e >> 5) + ((bal >> 32) != 0 ? 2 : 1));
         }
@@ -775,11 +810,11 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     const int nt = __builtin_amdgcn_readfirstlane(*s_nt);
     wait_vmcnt<0>();  // (already true: the loaded values were used) no load of the compiler's own is pending
 
-    const char* kbase = static_cast<const char*>(a.K.data) + (b * a.K.s0 + hk * a.K.s1) * 2;
+    const char* kbase = static_cast<const char*>(a.K.data) + ((IDX ? 0 : b * a.K.s0) + hk * a.K.s1) * 2;
     v4i krs;
     krs[0] = (int)(uint32_t)(uintptr_t)kbase;
     krs[1] = (int)(uint32_t)((uintptr_t)kbase >> 32);
-    krs[2] = (int)((int64_t)p.n_kv * rowb);
+    krs[2] = (int)((int64_t)p.n_kv * rowb);  // (unused by the paged variant)
     krs[3] = 0x00020000;
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
     // Loads of one tile by this wave: main blocks wv NM .. wv NM + NM - 1 (rows 4 (block / 4) +
@@ -797,13 +832,13 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         for (int q = 0; q < NRG; ++q) {
             const int r = 4 * (wv * NRG + q) + (lane >> 4);
             const uint32_t v = off[r];
-            o.m[q] = real ? v + 16u * (uint32_t)cslot_inv(r, lane & 15) : 0x80000000u;
+            o.m[q] = real ? (IDX ? v : v + 16u * (uint32_t)cslot_inv(r, lane & 15)) : SENT;
         }
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
             const int r = 8 * (wv * NT + q) + (lane >> 3);
             const uint32_t v = off[r];
-            o.t[q] = real ? v + 16u * (uint32_t)(64 + ((lane & 7) ^ tswz(r))) : 0x80000000u;
+            o.t[q] = real ? (IDX ? v : v + 16u * (uint32_t)(64 + ((lane & 7) ^ tswz(r)))) : SENT;
         }
         return o;
     };
@@ -811,10 +846,26 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         const uint32_t base = ring_lds + (uint32_t)((tile % RING) * TILE_B);
         if (ii < NM) {
             const int blk = wv * NM + ii;
-            lds_dma16(krs, base + 1024u * (uint32_t)blk, o.m[ii >> 2], 256u * (uint32_t)(ii & 3));
+            if (IDX) {
+                const int r = 4 * (wv * NRG + (ii >> 2)) + (lane >> 4);
+                const uint32_t col = 16u * (uint32_t)cslot_inv(r, lane & 15) + 256u * (uint32_t)(ii & 3);
+                const uint32_t row = o.m[ii >> 2];
+                lds_dma16_g(base + 1024u * (uint32_t)blk,
+                            (row == SENT ? reinterpret_cast<const char*>(kZeroRow) : kbase + (uint64_t)row * rowb) + col);
+            } else {
+                lds_dma16(krs, base + 1024u * (uint32_t)blk, o.m[ii >> 2], 256u * (uint32_t)(ii & 3));
+            }
         } else {
             const int j = wv * NT + (ii - NM);
-            lds_dma16(krs, base + 32768u + 1024u * (uint32_t)j, o.t[ii - NM], 0u);
+            if (IDX) {
+                const int r = 8 * j + (lane >> 3);
+                const uint32_t col = 16u * (uint32_t)(64 + ((lane & 7) ^ tswz(r)));
+                const uint32_t row = o.t[ii - NM];
+                lds_dma16_g(base + 32768u + 1024u * (uint32_t)j,
+                            (row == SENT ? reinterpret_cast<const char*>(kZeroRow) : kbase + (uint64_t)row * rowb) + col);
+            } else {
+                lds_dma16(krs, base + 32768u + 1024u * (uint32_t)j, o.t[ii - NM], 0u);
+            }
         }
     };
 
@@ -967,7 +1018,7 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(l32));
         return s_off[T * u + (l32 & 31u)];
     };
-    auto valid_mask = [](uint32_t off) { return (uint32_t)__ballot(off != 0x80000000u); };
+    auto valid_mask = [SENT](uint32_t off) { return (uint32_t)__ballot(off != SENT); };
     // P^T fragments of the last softmax into the P buffer
     auto put_p = [&]() {
 #pragma unroll
@@ -1240,8 +1291,26 @@ static bool mla_lds_ok(const AttnArgs& a) {
     const int G = p.Hq / p.Hkv;
     const bool alias = a.V.data == a.K.data && a.V.s0 == a.K.s0 && a.V.s1 == a.K.s1 && a.V.s2 == a.K.s2;
     const long per = (p.k + a.splits - 1) / a.splits;
-    return (G == 32 || G == 64 || G == 128) && alias && a.K.s2 % 8 == 0 && ((uintptr_t)a.K.data & 15) == 0 &&
-           (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) && per <= mla::MAXE;
+    // contiguous: 32-bit byte offsets into one batch's rows; paged: 32-bit row indices (the
+    // value pool_rows marks an empty slot) and rows no longer than the zero row
+    const bool addr = a.block_table ? (a.pool_rows < 0xffffffffLL && a.K.s2 * 2 <= kZeroRowBytes)
+                                    : (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31);
+    return (G == 32 || G == 64 || G == 128) && alias && a.K.s2 % 8 == 0 && ((uintptr_t)a.K.data & 15) == 0 && addr &&
+           per <= mla::MAXE;
+}
+
+// The bf16 MHA kernel: rows below 2^24 and row strides below 2^24 bytes (24-bit multiplies),
+// every head's slice of K and V below 2^31 bytes, candidate lists read four at a time.
+static bool rows_buf_ok(const AttnArgs& a) {
+    const sa_problem& p = a.p;
+    const int64_t rows = a.block_table ? a.pool_rows : (int64_t)p.n_kv;
+    return a.Q.dtype == SA_BF16 && p.Hq == p.Hkv && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256) &&
+           (p.k % 4 == 0) && rows * a.K.s2 * 2 < (1LL << 31) && rows * a.V.s2 * 2 < (1LL << 31) &&
+           ((uintptr_t)a.idx & 15) == 0 && rows < (1 << 24) && a.K.s2 * 2 < (1 << 24) && a.V.s2 * 2 < (1 << 24);
+}
+
+bool attn_paged_ok(const AttnArgs& a) {
+    return attn_uses_mla(a.p, a.Q.dtype) ? mla_lds_ok(a) : rows_buf_ok(a);
 }
 
 bool attn_uses_mla(const sa_problem& p, int dtype) {
@@ -1273,15 +1342,22 @@ size_t attn_partial_bytes(const sa_problem& p) {
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     const sa_problem& p = a.p;
+    if (a.block_table && !attn_paged_ok(a)) return hipErrorInvalidValue;  // only the two kernels above translate pages
     if (attn_uses_mla(p, a.Q.dtype)) {
         const int G = p.Hq / p.Hkv;
         const long units = (long)p.B * p.n_q * p.Hkv * a.splits;
         const bool lds_kernel = mla_lds_ok(a);
         if (lds_kernel) {
             const dim3 grid((unsigned)(a.splits > 1 ? 8 * ((units + 7) / 8) : units));
-            if (G == 128) hipLaunchKernelGGL(attn_mla_lds<4>, grid, dim3(256), 0, s, a);
-            else if (G == 64) hipLaunchKernelGGL(attn_mla_lds<2>, grid, dim3(128), 0, s, a);
-            else hipLaunchKernelGGL(attn_mla_lds<1>, grid, dim3(64), 0, s, a);
+            if (a.block_table) {
+                if (G == 128) hipLaunchKernelGGL((attn_mla_lds<4, true>), grid, dim3(256), 0, s, a);
+                else if (G == 64) hipLaunchKernelGGL((attn_mla_lds<2, true>), grid, dim3(128), 0, s, a);
+                else hipLaunchKernelGGL((attn_mla_lds<1, true>), grid, dim3(64), 0, s, a);
+            } else {
+                if (G == 128) hipLaunchKernelGGL((attn_mla_lds<4, false>), grid, dim3(256), 0, s, a);
+                else if (G == 64) hipLaunchKernelGGL((attn_mla_lds<2, false>), grid, dim3(128), 0, s, a);
+                else hipLaunchKernelGGL((attn_mla_lds<1, false>), grid, dim3(64), 0, s, a);
+            }
         } else {
             hipLaunchKernelGGL((attn_mla<576, 512>), dim3((unsigned)units), dim3(64 * (G / 16)), 0, s, a);
         }
@@ -1298,16 +1374,23 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     }
     const int G = p.Hq / p.Hkv;
     if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
-        // 32-bit row offsets from 24-bit multiplies: rows < 2^24, row strides < 2^24 bytes;
-        // candidate lists read four at a time
-        const bool buf_ok = (p.k % 4 == 0) && (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) &&
-                            (int64_t)p.n_kv * a.V.s2 * 2 < (1LL << 31) && ((uintptr_t)a.idx & 15) == 0 &&
-                            p.n_kv < (1 << 24) && a.K.s2 * 2 < (1 << 24) && a.V.s2 * 2 < (1 << 24);
-        if (buf_ok) {
+        if (rows_buf_ok(a)) {
             const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
-            if (p.d_qk == 64) hipLaunchKernelGGL(attn_rows_buf<64>, dim3(nblk), dim3(256), 0, s, a);
-            else if (p.d_qk == 128) hipLaunchKernelGGL(attn_rows_buf<128>, dim3(nblk), dim3(256), 0, s, a);
-            else hipLaunchKernelGGL(attn_rows_buf<256>, dim3(nblk), dim3(256), 0, s, a);
+            if (a.block_table) {
+                // translate once into the workspace, then read pool rows
+                int32_t* rows = static_cast<int32_t*>(a.partial);
+                const long n = (long)p.B * p.n_q * p.k;
+                hipLaunchKernelGGL(page_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, rows);
+                AttnArgs t = a;
+                t.idx = rows;
+                if (p.d_qk == 64) hipLaunchKernelGGL((attn_rows_buf<64, true>), dim3(nblk), dim3(256), 0, s, t);
+                else if (p.d_qk == 128) hipLaunchKernelGGL((attn_rows_buf<128, true>), dim3(nblk), dim3(256), 0, s, t);
+                else hipLaunchKernelGGL((attn_rows_buf<256, true>), dim3(nblk), dim3(256), 0, s, t);
+            } else {
+                if (p.d_qk == 64) hipLaunchKernelGGL((attn_rows_buf<64, false>), dim3(nblk), dim3(256), 0, s, a);
+                else if (p.d_qk == 128) hipLaunchKernelGGL((attn_rows_buf<128, false>), dim3(nblk), dim3(256), 0, s, a);
+                else hipLaunchKernelGGL((attn_rows_buf<256, false>), dim3(nblk), dim3(256), 0, s, a);
+            }
             return hipGetLastError();
         }
     }

@@ -45,6 +45,13 @@ static __device__ __forceinline__ void lds_dma16(const v4i& rs, uint32_t lds, ui
                  : "m0");
 }
 
+// The same transfer from a full 64-bit address per lane (no buffer resource, so no 4 GiB
+// window and no range check: every lane must point at readable memory).
+static __device__ __forceinline__ void lds_dma16_g(uint32_t lds, const void* src) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+                 : "m0");
+}
+
 // LDS byte address of a __shared__ object
 static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

@@ -73,6 +73,13 @@ struct AttnArgs {
     float scale;
     void* partial;  // workspace for split-candidate partial results (may be null if splits == 1)
     int splits;
+    // paged K/V: logical position j of batch b lives in physical row
+    // block_table[b * bt_stride + (j >> page_shift)] << page_shift | j % page size of page
+    // pools indexed (head, physical row) without a batch offset; null: contiguous per batch
+    const int32_t* block_table = nullptr;
+    int64_t bt_stride = 0;
+    int page_shift = 0;
+    int64_t pool_rows = 0;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
@@ -99,6 +106,7 @@ hipError_t launch_misa_gather(const sa_problem& p, const sa_tensor& q, const sa_
 // Host-side planning shared by workspace sizing and launches.
 int attn_splits(const sa_problem& p);
 bool attn_uses_mla(const sa_problem& p, int dtype);
+bool attn_paged_ok(const AttnArgs& a);  // a paged call runs on the LDS latent or the bf16 MHA kernel
 size_t attn_partial_bytes(const sa_problem& p);
 
 }  // namespace sa
