@@ -233,6 +233,34 @@ def paged_stage(W, P, d, stream, timed, cold, reps, idx, t_attn, t_attn_cold, O_
             "bit_identical_to_contiguous": same}
 
 
+def grouped_stage(W, P, d, stream, timed, reps, G, t_step):
+    """Grouped candidate sets (G groups of query heads, each selecting with its own Hidx / G
+    index heads) timed as one call, beside the shared fused step; the overlap (IoU) of the
+    first two groups' sets says how far the groups' selections differ."""
+    import numpy as np
+    import torch
+
+    import token_selector_gather_amd as sa
+    from token_selector_gather_amd.inputs import empty_outputs
+
+    if sa.sa_grouped_workspace_bytes(P, G) == 0:
+        return None
+    O, lse, _ = empty_outputs(W, torch.bfloat16 if W["main_dtype"] != 0 else torch.float32)
+    idx = torch.empty((G, W["B"], W["n_q"], W["k"]), dtype=torch.int32, device="cuda")
+    ws = sa.grouped_workspace(P, G)
+    t = timed(lambda: sa.sa_select_attend_grouped(P, G, d["q_idx"], d["k_idx"], d["w"], d["Q"], d["K"], d["V"], idx,
+                                                   O, lse, ws, stream), reps)
+    st = sa.sa_device_status(ws)
+    if st != sa.SA_OK:
+        raise RuntimeError("grouped selection: device status " + sa.sa_status_str(st))
+    a = idx[0].reshape(-1, W["k"])[:4096].cpu().numpy()
+    b = idx[1].reshape(-1, W["k"])[:4096].cpu().numpy()
+    iou = [np.intersect1d(x[x >= 0], y[y >= 0]).size / max(1, np.union1d(x[x >= 0], y[y >= 0]).size)
+           for x, y in zip(a, b) if (x >= 0).any()]
+    return {"groups": G, "step_ms": round(t, 4), "shared_step_ms": round(t_step, 4),
+            "over_shared": round(t / t_step, 3), "iou_group0_group1": round(float(np.mean(iou)), 4) if iou else None}
+
+
 def cpu_baseline(W, budget_rows):
     """The oracle (unchanged) on a stratified sample of rows: score, select and attend."""
     import numpy as np
@@ -264,6 +292,8 @@ def main():
                     help="time the active-head selection beside the flat one (default: prefill workloads with 64 index heads)")
     ap.add_argument("--paged", type=int, default=1,
                     help="time the sparse attention over paged K/V beside the contiguous call")
+    ap.add_argument("--groups", type=int, default=2,
+                    help="time grouped candidate sets with this many groups beside the shared step (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
@@ -407,6 +437,8 @@ def main():
         out["hisa"] = hisa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
     if args.misa == 1 or (args.misa == -1 and not alg["decode"] and W["Hidx"] == 64):
         out["misa"] = misa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
+    if args.groups > 1:
+        out["grouped"] = grouped_stage(W, P, d, stream, timed, reps, args.groups, float(np.median(step_ms)))
     if args.paged == 1:
         out["paged"] = paged_stage(W, P, d, stream, timed, cold, reps, idx, t_attn, cold_times["sparse_attn"], O2, lse2)
     if args.cpu_rows > 0:

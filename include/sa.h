@@ -183,6 +183,30 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
                            sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O, float* lse, void* ws,
                            size_t ws_bytes, void* stream);
 
+/*
+ * sa_select_attend_grouped -- grouped candidate sets.  "PaperTrace 2.2 · Fine-grained
+ * indexing", §2 eq. (5) and the paragraphs around it (shared versus per-head candidates):
+ * the Hq main heads form G groups, each with its own selector, S_{t,g} = TopK(Agg over the
+ * group's heads of r, k_g); G = 1 is the shared set of sa_select_attend.  Reading where the
+ * pages leave the step open: heads are grouped contiguously and in equal numbers, the
+ * index heads are grouped the same way (Hidx / G per group, a multiple of 4 when G > 1),
+ * Agg is the indexer's own weighted ReLU sum over the group's index heads, k_g = k for
+ * every group, and group g's Hq / G query heads attend over S_{t,g} with the same tie rule.
+ * The key/value heads split into G groups as well (Hkv a multiple of G), or all groups
+ * share the single key/value head (Hkv = 1, the latent layout).
+ *   arguments as for sa_select_attend, the group problem (Hq / G, Hkv / G or 1, Hidx / G)
+ *   supported by sa_sparse_attn;
+ *   idx_out [G, B, n_q, k] int32 (16-byte aligned) or NULL: group g's selection at
+ *           idx_out + g*B*n_q*k;
+ *   ws      sa_grouped_workspace_bytes(p, groups) bytes, zero-filled once (status word).
+ * The groups run one after another on the stream, each as score, select and attend.
+ */
+sa_status sa_select_attend_grouped(const sa_problem* p, int groups, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w,
+                                   sa_tensor Q, sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream);
+/* Workspace bytes of sa_select_attend_grouped; 0 when p or groups is not accepted. */
+size_t sa_grouped_workspace_bytes(const sa_problem* p, int groups);
+
 /* Workspace bytes needed by operation `op` (an sa_op) for problem p; 0 for a malformed p. */
 size_t sa_workspace_bytes(const sa_problem* p, int op);
 

@@ -180,6 +180,41 @@ def attend_paged(W, idx, K_pool, V_pool, block_table, page_size, rows=None):
     return attend(W, idx, rows_, K=K, V=V)
 
 
+def group_workload(W, G, g):
+    """The problem of group g of G: index heads and query heads [g H/G, (g+1) H/G), the
+    key/value heads of the group (or the one shared key/value head)."""
+    Hig, Hg = W["Hidx"] // G, W["Hq"] // G
+    Wg = dict(W)
+    Wg["Hidx"], Wg["Hq"] = Hig, Hg
+    Wg["q_idx"] = np.ascontiguousarray(W["q_idx"][:, :, g * Hig:(g + 1) * Hig])
+    Wg["w"] = np.ascontiguousarray(W["w"][:, :, g * Hig:(g + 1) * Hig])
+    Wg["Q"] = np.ascontiguousarray(W["Q"][:, g * Hg:(g + 1) * Hg])
+    if W["Hkv"] > 1:
+        Hkg = W["Hkv"] // G
+        Wg["Hkv"] = Hkg
+        Wg["K"] = np.ascontiguousarray(W["K"][:, g * Hkg:(g + 1) * Hkg])
+        if W.get("V") is not None:
+            Wg["V"] = np.ascontiguousarray(W["V"][:, g * Hkg:(g + 1) * Hkg])
+    return Wg
+
+
+def select_attend_grouped(W, G, rows=None):
+    """Grouped candidate sets, "PaperTrace 2.2 · Fine-grained indexing", §2 eq. (5): the main
+    heads form G groups, each with its own selector; S_{t,g} = TopK over the group's
+    aggregated scores.  Reading: equal contiguous groups of query heads and of index heads,
+    Agg = the indexer's weighted ReLU sum over the group's index heads, k_g = k, and group
+    g's query heads attend over S_{t,g}.  Returns idx [G, rows, k], O [rows, Hq, d_v],
+    lse [rows, Hq] (query heads in their original order)."""
+    rows = _rows(W, rows)
+    idx, O, lse = [], [], []
+    for g in range(G):
+        r = select_attend(group_workload(W, G, g), rows)
+        idx.append(r["idx"])
+        O.append(r["O"])
+        lse.append(r["lse"])
+    return np.stack(idx), np.concatenate(O, axis=1), np.concatenate(lse, axis=1)
+
+
 def count_visible(W, causal=None):
     P = Problem(W, causal=causal)
     return lib().or_count_visible(ctypes.byref(P.p))

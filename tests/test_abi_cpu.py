@@ -134,6 +134,28 @@ def test_paged_attention_argument_errors():
 
 
 @needs_lib
+def test_grouped_selection_argument_errors():
+    L = sa.lib()
+    p = _prob(Hidx=8)
+    wsz = lambda pp, g: L.sa_grouped_workspace_bytes(ctypes.byref(pp), g)
+    assert wsz(p, 2) > 256 and wsz(p, 1) > 256
+    assert wsz(p, 0) == 0                    # no groups
+    assert wsz(p, 3) == 0                    # 4 query heads do not split in 3
+    assert wsz(_prob(Hidx=4), 2) == 0        # 2 index heads per group (w groups 16-byte aligned)
+    assert wsz(_prob(Hq=8, Hkv=2, Hidx=16), 4) == 0  # 2 key/value heads neither split in 4 nor shared
+    assert wsz(_prob(Hq=8, Hkv=1, Hidx=16), 4) > 0   # one shared key/value head
+    ok, f32 = _t(), _t(dtype=sa.SA_F32)
+    need = wsz(p, 2)
+
+    def call(g=2, idx=None, ws=FAKE, n=need, pp=p):
+        return L.sa_select_attend_grouped(ctypes.byref(pp), g, ok, ok, f32, ok, ok, ok, idx, ok, None, ws, n, None)
+    assert call(g=3) == sa.SA_ERR_INVALID_ARG
+    assert call(idx=FAKE + 4) == sa.SA_ERR_INVALID_ARG
+    assert call(n=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ws=None) == sa.SA_ERR_WORKSPACE
+
+
+@needs_lib
 def test_indexer_argument_errors():
     L = sa.lib()
     p = _prob()

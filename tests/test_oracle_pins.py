@@ -720,3 +720,91 @@ def test_paged_attention_hand_case_page_outside_the_pool_is_skipped():
     Ob, lb = orc.attend_paged(W, idx, Kp, Vp, bad, 2, rows=row)
     Oe, le = orc.attend(W, np.array([[0, 3, -1, -1]], np.int32), rows=row)
     assert np.array_equal(Ob, Oe) and np.array_equal(lb, le)
+
+
+# ------------------------------------------------------------------ grouped candidate sets
+# "PaperTrace 2.2 · Fine-grained indexing", §2 eq. (5): G groups of main heads, one selector
+# per group; G = 1 is the shared set, G = Hq gives every head its own set.
+
+
+def _per_head_brute(W, rows):
+    """Every head its own selector and softmax, in pure Python (tiny sizes): index head h
+    scores w_h ReLU(<q_h, k_s>), the k best visible positions (ties to the lower position),
+    query head h attends over them."""
+    B, nq, k = W["B"], W["n_q"], W["k"]
+    q, kk, w = W["q_idx"].astype(np.float64), W["k_idx"].astype(np.float64), W["w"].astype(np.float64)
+    Q, K, V = W["Q"].astype(np.float64), W["K"].astype(np.float64), W["V"].astype(np.float64)
+    outO = np.zeros((len(rows), W["Hq"], W["d_v"]))
+    sets = []
+    for n, row in enumerate(rows):
+        b, i = divmod(int(row), nq)
+        L = i + 1 if W["causal"] else W["n_kv"]
+        per = []
+        for h in range(W["Hq"]):
+            sc = [w[b, i, h] * max(0.0, sum(q[b, i, h, d] * kk[b, s, d] for d in range(W["d_idx"]))) for s in range(L)]
+            order = sorted(range(L), key=lambda s: (-sc[s], s))[:k]
+            per.append(sorted(order))
+            hk = h // (W["Hq"] // W["Hkv"])
+            logits = [W["scale"] * sum(Q[b, h, i, d] * K[b, hk, s, d] for d in range(W["d_qk"])) for s in order]
+            m = max(logits)
+            e = [math.exp(x - m) for x in logits]
+            for s, ev in zip(order, e):
+                outO[n, h] += ev / sum(e) * V[b, hk, s]
+        sets.append(per)
+    return sets, outO
+
+
+def test_grouped_sets_one_group_is_the_shared_selection():
+    W = sa_synth.custom(seed=41, B=2, n_q=30, n_kv=50, Hq=4, Hkv=4, d_qk=64, d_v=64, Hidx=8, d_idx=32, k=8,
+                        lens=[50, 37], main_dtype=sa_synth.F32, qidx_dtype=sa_synth.F32, kidx_dtype=sa_synth.F32)
+    rows = all_rows(W)
+    idx, O, lse = orc.select_attend_grouped(W, 1, rows)
+    ref = orc.select_attend(W, rows)
+    assert np.array_equal(idx[0], ref["idx"]) and np.array_equal(O, ref["O"]) and np.array_equal(lse, ref["lse"])
+
+
+def test_grouped_sets_one_head_per_group_is_a_per_head_brute_force():
+    rng = np.random.default_rng(42)
+    B, n, H, d, di = 1, 9, 3, 4, 3
+    W = tiny(Q=rand_f32(rng, (B, H, n, d)), K=rand_f32(rng, (B, H, n, d)), V=rand_f32(rng, (B, H, n, d)),
+             q_idx=rand_f32(rng, (B, n, H, di)), k_idx=rand_f32(rng, (B, n, di)),
+             w=rng.uniform(0.2, 1.0, (B, n, H)), k=3, causal=1, scale=0.5)
+    rows = all_rows(W)
+    idx, O, _ = orc.select_attend_grouped(W, H, rows)
+    sets, O_bf = _per_head_brute(W, rows)
+    for n_, row in enumerate(rows):
+        for h in range(H):
+            got = sorted(int(x) for x in idx[h, n_] if x >= 0)
+            assert got == sets[n_][h], (row, h)
+    assert np.allclose(O, O_bf, atol=1e-12)
+
+
+def test_grouped_sets_hand_case_each_group_follows_its_index_heads():
+    # Two groups, one index head each.  Index head 0 matches key 1 only, index head 1 key 3
+    # only; with k = 1 group 0's query heads see position 1 and group 1's position 3, so
+    # each output is that position's value row exactly.
+    n, d = 5, 2
+    kk = np.zeros((1, n, 2)); kk[0, 1] = [1, 0]; kk[0, 3] = [0, 1]
+    qi = np.zeros((1, n, 2, 2)); qi[0, :, 0] = [1, 0]; qi[0, :, 1] = [0, 1]
+    V = np.arange(1 * 2 * n * d, dtype=np.float64).reshape(1, 2, n, d)
+    W = tiny(Q=np.ones((1, 2, n, d)), K=np.ones((1, 2, n, d)), V=V, q_idx=qi, k_idx=kk, w=np.ones((1, n, 2)),
+             k=1, causal=0)
+    idx, O, lse = orc.select_attend_grouped(W, 2, np.array([4], np.int32))
+    assert idx[0, 0, 0] == 1 and idx[1, 0, 0] == 3
+    assert np.array_equal(O[0, 0], V[0, 0, 1]) and np.array_equal(O[0, 1], V[0, 1, 3])
+    assert np.allclose(lse, 2.0)  # one logit <1,1>·<1,1> = 2 at scale 1
+
+
+def test_grouped_sets_swapping_groups_swaps_the_outputs():
+    W = sa_synth.custom(seed=43, B=1, n_q=24, n_kv=40, Hq=4, Hkv=1, d_qk=64, d_v=64, Hidx=8, d_idx=32, k=6,
+                        main_dtype=sa_synth.F32, qidx_dtype=sa_synth.F32, kidx_dtype=sa_synth.F32)
+    rows = all_rows(W)
+    idx, O, lse = orc.select_attend_grouped(W, 2, rows)
+    Ws = dict(W)
+    Ws["q_idx"] = np.ascontiguousarray(np.concatenate([W["q_idx"][:, :, 4:], W["q_idx"][:, :, :4]], axis=2))
+    Ws["w"] = np.ascontiguousarray(np.concatenate([W["w"][:, :, 4:], W["w"][:, :, :4]], axis=2))
+    Ws["Q"] = np.ascontiguousarray(np.concatenate([W["Q"][:, 2:], W["Q"][:, :2]], axis=1))
+    idx2, O2, lse2 = orc.select_attend_grouped(Ws, 2, rows)
+    assert np.array_equal(idx2[0], idx[1]) and np.array_equal(idx2[1], idx[0])
+    assert np.array_equal(O2[:, :2], O[:, 2:]) and np.array_equal(lse2[:, 2:], lse[:, :2])
+    assert not np.array_equal(idx[0], idx[1])  # the two groups really select differently

@@ -62,11 +62,14 @@ def lib():
         L.sa_sparse_attn.argtypes = [P, T, T, T, vp, T, vp, vp, sz, vp]
         L.sa_select_attend.argtypes = [P, T, T, T, T, T, T, vp, T, vp, vp, sz, vp]
         L.sa_sparse_attn_paged.argtypes = [P, T, T, T, i64, vp, i64, ctypes.c_int, vp, T, vp, vp, sz, vp]
+        L.sa_select_attend_grouped.argtypes = [P, ctypes.c_int, T, T, T, T, T, T, vp, T, vp, vp, sz, vp]
+        L.sa_grouped_workspace_bytes.argtypes = [P, ctypes.c_int]
+        L.sa_grouped_workspace_bytes.restype = sz
         L.sa_block_means.argtypes = [P, T, ctypes.c_int, vp, vp]
         L.sa_hisa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         L.sa_misa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         for f in (L.sa_indexer_score, L.sa_topk, L.sa_sparse_attn, L.sa_select_attend, L.sa_block_means,
-                  L.sa_hisa_select, L.sa_misa_select, L.sa_sparse_attn_paged):
+                  L.sa_hisa_select, L.sa_misa_select, L.sa_sparse_attn_paged, L.sa_select_attend_grouped):
             f.restype = st
         L.sa_misa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
         L.sa_misa_workspace_bytes.restype = sz
@@ -191,6 +194,25 @@ def sa_select_attend(p, q_idx, k_idx, w, Q, K, V, idx_out, O, lse, ws, stream=No
                                   _tensor(O, "O"), _ptr(lse), _ptr(ws),
                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "sa_select_attend")
+
+
+def sa_grouped_workspace_bytes(p, groups):
+    return lib().sa_grouped_workspace_bytes(p.ref, int(groups))
+
+
+def grouped_workspace(p, groups, device="cuda"):
+    """A zero-filled workspace for sa_select_attend_grouped."""
+    n = max(256, sa_grouped_workspace_bytes(p, groups))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def sa_select_attend_grouped(p, groups, q_idx, k_idx, w, Q, K, V, idx_out, O, lse, ws, stream=None):
+    """Grouped candidate sets; idx_out is [groups, B, n_q, k] int32 or None."""
+    _check(lib().sa_select_attend_grouped(p.ref, int(groups), _tensor(q_idx, "q_idx"), _tensor(k_idx, "k_idx"),
+                                          _tensor(w, "w"), _tensor(Q, "Q"), _tensor(K, "K"), _tensor(V, "V"),
+                                          _ptr(idx_out), _tensor(O, "O"), _ptr(lse), _ptr(ws),
+                                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "sa_select_attend_grouped")
 
 
 def sa_block_means(p, k_idx, blk, kbar, stream=None):

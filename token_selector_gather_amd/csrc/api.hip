@@ -194,6 +194,7 @@ AttnArgs attn_args(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, 
     a.scale = eff_scale(p);
     a.splits = attn_uses_mla(*p, Q.dtype) ? attn_splits(*p) : 1;
     a.partial = partial;
+    a.lse_bs = (int64_t)p->Hq * p->n_q;
     a.block_table = pg.table;
     a.bt_stride = pg.stride;
     a.page_shift = pg.shift;
@@ -203,9 +204,41 @@ AttnArgs attn_args(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, 
 
 sa_status run_attn(const sa_problem* p, const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V,
                    const int32_t* idx, const sa_tensor& O, float* lse, void* partial, hipStream_t st,
-                   const Pages& pg = Pages()) {
-    return launch_attn(attn_args(p, Q, K, V, idx, O, lse, partial, pg), st) == hipSuccess ? SA_OK : SA_ERR_HIP;
+                   const Pages& pg = Pages(), int64_t lse_bs = 0) {
+    AttnArgs a = attn_args(p, Q, K, V, idx, O, lse, partial, pg);
+    if (lse_bs) a.lse_bs = lse_bs;
+    return launch_attn(a, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
+
+// Grouped candidate sets: the problem of one group (Hq / G query heads, Hidx / G index heads,
+// Hkv / G key/value heads, or the one shared key/value head).  Index-head groups start on
+// 16-byte boundaries of w (Hidx / G a multiple of 4).
+bool group_problem(const sa_problem* p, int G, sa_problem* out) {
+    if (!problem_ok(p) || G < 1 || p->Hq % G != 0 || p->Hidx % G != 0) return false;
+    sa_problem q = *p;
+    q.Hq = p->Hq / G;
+    q.Hidx = p->Hidx / G;
+    if (G > 1 && q.Hidx % 4 != 0) return false;
+    if (p->Hkv % G == 0) q.Hkv = p->Hkv / G;
+    else if (p->Hkv == 1) q.Hkv = 1;
+    else return false;
+    *out = q;
+    return true;
+}
+struct GroupedLayout {
+    size_t scores, idx, partial, scratch, total;
+};
+GroupedLayout grouped_layout(const sa_problem& p, const sa_problem& pg, int G) {
+    GroupedLayout l;
+    size_t o = kStatusBytes;
+    l.scores = o; o += scores_bytes(pg);
+    l.idx = o; o += align256((size_t)G * p.B * p.n_q * p.k * sizeof(int32_t));
+    l.partial = o; o += align256(attn_partial_bytes(pg));
+    l.scratch = o; o += align256(topk_ws_bytes(pg));
+    l.total = o;
+    return l;
+}
+char* offset_bytes(const void* base, int64_t bytes) { return const_cast<char*>(static_cast<const char*>(base)) + bytes; }
 
 }  // namespace
 
@@ -344,6 +377,68 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
 
     return run_attn(p, Q, K, V, idx, O, lse, partial, st);
+}
+
+size_t sa_grouped_workspace_bytes(const sa_problem* p, int groups) {
+    sa_problem pg;
+    if (!group_problem(p, groups, &pg)) return 0;
+    return grouped_layout(*p, pg, groups).total;
+}
+
+sa_status sa_select_attend_grouped(const sa_problem* p, int groups, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w,
+                                   sa_tensor Q, sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    sa_problem pg;
+    if (!group_problem(p, groups, &pg)) return SA_ERR_INVALID_ARG;
+    if (idx_out && ((uintptr_t)idx_out & 15)) return SA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3)) return SA_ERR_INVALID_ARG;
+    sa_status s = check_indexer(p, q_idx, k_idx, w);
+    if (s != SA_OK) return s;
+    if ((s = check_attn(&pg, Q, K, V, O)) != SA_OK) return s;
+    if ((s = ws_ok(ws, ws_bytes, sa_grouped_workspace_bytes(p, groups))) != SA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    const GroupedLayout L = grouped_layout(*p, pg, groups);
+    char* base = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base + L.scores);
+    int32_t* idx_all = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
+    const int64_t per_group = (int64_t)p->B * p->n_q * p->k;
+    const int eq = esize(q_idx.dtype), em = esize(Q.dtype);
+    for (int g = 0; g < groups; ++g) {
+        // the group's index heads: a view starting g Hidx/G heads in (w's heads are contiguous)
+        sa_tensor qg = q_idx, wg = w;
+        qg.data = offset_bytes(q_idx.data, (int64_t)g * pg.Hidx * q_idx.s2 * eq);
+        wg.data = offset_bytes(w.data, (int64_t)g * pg.Hidx * 4);
+        int32_t* idx = idx_all + g * per_group;
+        IndexerArgs ia;
+        ia.p = pg;
+        ia.q = qg; ia.k = k_idx; ia.w = wg;
+        ia.scores = scores;
+        ia.row_stride = p->n_kv;
+        ia.fill_invisible = 0;
+        ia.status = reinterpret_cast<Status*>(base);
+        if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
+        TopkArgs ta;
+        ta.p = pg;
+        ta.scores = scores;
+        ta.row_stride = p->n_kv;
+        ta.idx = idx;
+        ta.vals = nullptr;
+        ta.status = reinterpret_cast<Status*>(base);
+        ta.scratch = base + L.scratch;
+        if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
+        // the group's query heads, their key/value heads (or the one shared head), O and lse
+        sa_tensor Qg = Q, Og = O, Kg = K, Vg = V;
+        Qg.data = offset_bytes(Q.data, (int64_t)g * pg.Hq * Q.s1 * em);
+        Og.data = offset_bytes(O.data, (int64_t)g * pg.Hq * O.s1 * em);
+        if (p->Hkv > 1) {
+            Kg.data = offset_bytes(K.data, (int64_t)g * pg.Hkv * K.s1 * em);
+            Vg.data = offset_bytes(V.data, (int64_t)g * pg.Hkv * V.s1 * em);
+        }
+        float* lg = lse ? lse + (int64_t)g * pg.Hq * p->n_q : nullptr;
+        if ((s = run_attn(&pg, Qg, Kg, Vg, idx, Og, lg, base + L.partial, st, Pages(), (int64_t)p->Hq * p->n_q)) != SA_OK)
+            return s;
+    }
+    return SA_OK;
 }
 
 sa_status sa_block_means(const sa_problem* p, sa_tensor k_idx, int blk, uint16_t* kbar, void* stream) {

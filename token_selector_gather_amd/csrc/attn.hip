@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(256) attn_rows(AttnArgs a) {
                 *reinterpret_cast<uint4*>(Op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
             }
             if (a.lse && sub == 0)
-                a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = l[g] > 0.f ? (m[g] + log2f(l[g])) * kLn2 : -INFINITY;
+                a.lse[b * a.lse_bs + (int64_t)h * p.n_q + i] = l[g] > 0.f ? (m[g] + log2f(l[g])) * kLn2 : -INFINITY;
         }
     }
 }
@@ -420,7 +420,7 @@ __global__ void __launch_bounds__(256) attn_rows_buf(AttnArgs a) {
         *reinterpret_cast<uint4*>(Op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         *reinterpret_cast<uint4*>(Op + HALF) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
         if (a.lse && sub == 0)
-            a.lse[((int64_t)b * p.Hq + h) * p.n_q + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+            a.lse[b * a.lse_bs + (int64_t)h * p.n_q + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(512) attn_mla(AttnArgs a) {
             *reinterpret_cast<uint2*>(op + 16 * t + 4 * gq) = make_uint2(lo, hi);
         }
         if (a.lse && gq == 0)
-            a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
+            a.lse[b * a.lse_bs + (int64_t)head * p.n_q + i] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
     } else {
         // partial: [row, Hq, S] x (m, l) fp32, then [row, Hq, S, DV] o / l in bf16
         float* part = static_cast<float*>(a.partial);
@@ -659,7 +659,7 @@ __global__ void __launch_bounds__(256) lse_merge(AttnArgs a) {
     uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + head * a.O.s1 + (int64_t)i * a.O.s2 + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) op[e] = f32_to_bf16_rne(o[e] * inv);
-    if (a.lse && lane == 0) a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+    if (a.lse && lane == 0) a.lse[b * a.lse_bs + (int64_t)head * p.n_q + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------- attn_mla_lds
@@ -1148,7 +1148,7 @@ __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
     if (S == 1 && a.lse && g == 0) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-            a.lse[((int64_t)b * p.Hq + hk * G + 32 * wv + 16 * q + l15) * p.n_q + i] =
+            a.lse[b * a.lse_bs + (int64_t)(hk * G + 32 * wv + 16 * q + l15) * p.n_q + i] =
                 lsum[q] > 0.f ? (m_ref[q] + log2f(lsum[q])) * kLn2 : -INFINITY;
     }
     // lane holds O^T[d = 32 (MW wv + t2) + 8 (e/4) + 4 h + e%4][head 32 gr + n32]
@@ -1271,7 +1271,7 @@ __global__ void __launch_bounds__(256) lse_merge_frag(AttnArgs a) {
         *reinterpret_cast<uint2*>(op + 8 * q) = make_uint2(lo, hi);
     }
     if (a.lse && mt == 0 && h == 0)
-        a.lse[((int64_t)b * p.Hq + head) * p.n_q + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+        a.lse[b * a.lse_bs + (int64_t)head * p.n_q + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int LPR>

@@ -80,6 +80,8 @@ struct AttnArgs {
     int64_t bt_stride = 0;
     int page_shift = 0;
     int64_t pool_rows = 0;
+    int64_t lse_bs = 0;  // floats between batches of lse (Hq n_q for a whole call; more when
+                         // the call covers one group of a tensor's heads)
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
