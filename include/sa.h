@@ -211,7 +211,7 @@ size_t sa_grouped_workspace_bytes(const sa_problem* p, int groups);
 size_t sa_workspace_bytes(const sa_problem* p, int op);
 
 /*
- * Hierarchical selection.  "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs
+ * Hierarchical selection.  "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the HISA paragraphs
  * (coarse-to-fine search domain, cost O(B d_c + k_b b d_r), conditional recall eq. (7)):
  * the history is cut into blocks of `blk` positions, each block is scored through a
  * representative key, the k_blocks best blocks are kept and the token scores run only
@@ -256,7 +256,7 @@ sa_status sa_hisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, 
                          void* stream);
 
 /*
- * Active index heads.  "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: each
+ * Active index heads.  "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the MISA paragraphs: each
  * query row keeps g of its Hidx index heads and its score sums only those heads.  The heads
  * are chosen from the block representatives of sa_block_means: routing score of head h =
  * |w_h| times the mean over the row's complete visible blocks B of ReLU(<q_h, kbar_B>)

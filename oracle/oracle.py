@@ -234,7 +234,7 @@ def select_attend(W, rows=None):
 
 
 # ------------------------------------------------------------------ hierarchical selection
-# "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs (coarse-to-fine search
+# "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the HISA paragraphs (coarse-to-fine search
 # domain): the history is cut into blocks of b positions, each block is scored through a
 # representative, the k_b best blocks are kept, and the token indexer runs only inside
 # them; the output keeps the token top-k interface.  Readings (the pages leave these open):
@@ -335,7 +335,7 @@ def hisa_select(W, blk, k_blocks, rows=None, kbar=None):
 
 
 # ------------------------------------------------------------------ active index heads
-# "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: each query keeps g of its
+# "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the MISA paragraphs: each query keeps g of its
 # G index heads, chosen from the block-averaged index keys (the absolute value of each
 # head's weighted ReLU response, averaged over the blocks of the current prefix), and the
 # score sums only those heads.  Readings: the blocks are the complete blocks of the visible

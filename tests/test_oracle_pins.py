@@ -492,7 +492,7 @@ def test_kv_byte_accounting_example():
 
 
 # ------------------------------------------------------------------ hierarchical selection
-# "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs: score block
+# "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the HISA paragraphs: score block
 # representatives, keep k_b blocks, run the token indexer inside them, same top-k output.
 
 HISA_CASES = {
@@ -593,7 +593,7 @@ def test_hisa_misses_a_strong_token_inside_a_weak_block():
 
 
 # ------------------------------------------------------------------ active index heads
-# "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: route each query to g of
+# "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the MISA paragraphs: route each query to g of
 # its G index heads by the block-averaged |weighted ReLU| response, score with those only.
 
 @pytest.mark.parametrize("case", list(HISA_CASES))

@@ -1,6 +1,6 @@
 // Hierarchical (coarse-to-fine) selection: the small kernels around the indexer and top-k.
 //
-// "PaperTrace 2.2 · Fine-grained indexing", the HISA paragraphs: the history is cut into
+// "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the HISA paragraphs: the history is cut into
 // blocks of b positions, every block is scored through a representative index key, the
 // k_b best blocks are kept, and the token indexer runs only inside them, so the output is
 // the same token top-k.  The scoring and the two selections reuse the indexer and top-k

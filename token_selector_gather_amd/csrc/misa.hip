@@ -1,6 +1,6 @@
 // Active index heads: routing scores and the gather of each query's active heads.
 //
-// "PaperTrace 2.2 · Fine-grained indexing", the MISA paragraphs: every query keeps g of its
+// "PaperTrace 2.2 · Fine-grained indexing", §1.1 and §2.2, the MISA paragraphs: every query keeps g of its
 // G index heads, chosen from the block-averaged index keys (the absolute value of each
 // head's weighted ReLU response, averaged over the blocks of the current prefix), and the
 // score then sums only those heads.  The head choice and the scores reuse the top-k and
