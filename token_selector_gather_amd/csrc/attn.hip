@@ -257,6 +257,249 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// --------------------------------------------------------------- attn_tile
+// bf16 MHA (d = 128) over selections that, for a block of query rows, cover most key tiles
+// (many query rows, k a large fraction of the history).  One workgroup = 64 query rows of
+// one head: the rows' selections become a bitmap in LDS, every 64-key tile that any of the
+// rows selected is read once into LDS (K rows as they are, V transposed), S = Q K^T and
+// O += P V run on MFMA (16x16x32 bf16), and unselected keys are masked to -inf before the
+// online softmax, so each row's result is the exact softmax over its own selected set.
+// Tiles no row selected are skipped.  Wave w owns query rows 16 w .. 16 w + 15.  With a
+// block table the tile's keys are read from their pool rows (kv_row), and a candidate on a
+// page outside the pools never enters the bitmap.
+namespace tile {
+constexpr int QR = 64;         // query rows per workgroup
+constexpr int KT = 64;         // keys per tile
+constexpr int MAXN = 4096;     // longest history (bitmap words per row = MAXN / 32)
+constexpr int D = 128;
+constexpr int KP = D + 8;      // padded K row (elements): conflict-free 16-byte reads
+constexpr int VP = KT + 8;     // padded V^T row
+}  // namespace tile
+
+__global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
+    using namespace tile;
+    constexpr int NWORD = MAXN / 32;
+    __shared__ __attribute__((aligned(16))) uint32_t bits[QR][NWORD];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * VP];
+    __shared__ int s_L[QR], s_act[4][KT], s_list[KT], s_nt, s_maxL;
+    const sa_problem& p = a.p;
+    const int tid = threadIdx.x, lane = tid & 63, l15 = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nqb = (p.n_q + QR - 1) / QR;
+    int b, h, qb;
+    {
+        const long blk = blockIdx.x;
+        long rest;
+        if (p.Hkv % 8 == 0) {  // one head at a time per XCD: its K/V stay in that L2
+            const long local = blk / 8;
+            h = (int)(blk % 8) + 8 * (int)(local / ((long)p.B * nqb));
+            rest = local % ((long)p.B * nqb);
+        } else {
+            h = (int)(blk % p.Hkv);
+            rest = blk / p.Hkv;
+        }
+        b = (int)(rest / nqb);
+        qb = nqb - 1 - (int)(rest % nqb);  // the longest (latest) row blocks first
+    }
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    if (tid < QR) {
+        const int i = qb * QR + tid;
+        s_L[tid] = i < p.n_q ? visible_len(R, b, i) : 0;
+    }
+    for (int w = tid; w < QR * NWORD; w += 256) (&bits[0][0])[w] = 0u;
+    if (tid == 0) s_maxL = 0;
+    __syncthreads();
+    if (tid < QR) atomicMax(&s_maxL, s_L[tid]);
+    {   // selection bitmap: 4 threads per row, 4 candidates per load
+        const int r = tid >> 2, q = tid & 3;
+        const int i = qb * QR + r, L = s_L[r];
+        if (i < p.n_q && L > 0) {
+            const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
+            for (int e0 = 4 * q; e0 < p.k; e0 += 16 * 8) {
+                int4 jj[8];  // eight loads in flight, then their bits
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                    jj[n] = e0 + 16 * n < p.k ? *reinterpret_cast<const int4*>(ix + e0 + 16 * n) : make_int4(-1, -1, -1, -1);
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const int jv[4] = {jj[n].x, jj[n].y, jj[n].z, jj[n].w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if ((unsigned)jv[u] < (unsigned)L && (!a.block_table || kv_row(a, b, jv[u]) >= 0))
+                            atomicOr(&bits[r][jv[u] >> 5], 1u << (jv[u] & 31));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int ntile = (s_maxL + KT - 1) / KT;
+    {   // tiles holding a selected key of any row: rows 16 (tid / 64) .. + 15 per thread
+        const int t = tid & 63, rq = tid >> 6;
+        uint32_t any = 0;
+        if (t < ntile)
+            for (int r = 16 * rq; r < 16 * rq + 16; ++r) any |= bits[r][2 * t] | bits[r][2 * t + 1];
+        s_act[rq][t] = any != 0;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const bool act = (s_act[0][lane] | s_act[1][lane] | s_act[2][lane] | s_act[3][lane]) != 0;
+        const uint64_t m = __ballot(act);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (act) s_list[pos] = lane;
+        if (lane == 0) s_nt = __popcll(m);
+    }
+    __syncthreads();
+    const int nt = s_nt;
+
+    // Q fragments (A operand): lane row l15 = query row 16 wv + l15, d = 32 s + 8 g .. + 7
+    const int iq = qb * QR + 16 * wv + l15;
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.K.data) + (a.block_table ? 0 : b * a.K.s0) + h * a.K.s1;
+    const uint16_t* Vb = static_cast<const uint16_t*>(a.V.data) + (a.block_table ? 0 : b * a.V.s0) + h * a.V.s1;
+    bf16x8 qa[D / 32];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)min(iq, p.n_q - 1) * a.Q.s2;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s)
+            qa[s] = iq < p.n_q ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g))
+                               : bf16x8{};
+    }
+    // a tile's K: 1024 16-byte pieces, four per thread (key c / 16, columns 8 (c % 16)); its V:
+    // key pairs (2 kp, 2 kp + 1) x 16 column pieces, two per thread, the pair index fastest
+    // across lanes so that the transposed stores of a wave hit consecutive LDS words
+    uint4 kr[4], vr[4];
+    auto fetch = [&](int u) {
+        const int k0 = s_list[u] * KT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = tid + 256 * q, key = k0 + (c >> 4), col = 8 * (c & 15);
+            const int64_t row = key < p.n_kv ? kv_row(a, b, key) : -1;
+            kr[q] = row >= 0 ? *reinterpret_cast<const uint4*>(Kb + row * a.K.s2 + col) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = tid + 256 * q, kp = c & 31, col = 8 * (c >> 5);
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+                const int key = k0 + 2 * kp + z;
+                const int64_t row = key < p.n_kv ? kv_row(a, b, key) : -1;
+                vr[2 * q + z] = row >= 0 ? *reinterpret_cast<const uint4*>(Vb + row * a.V.s2 + col) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    if (nt > 0) fetch(0);
+
+    const float sl2 = a.scale * kLog2e;
+    float m[4], l[4];
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint16_t* Pw = Ps[wv];
+
+    for (int u = 0; u < nt; ++u) {
+        __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = tid + 256 * q, key = c >> 4, col = 8 * (c & 15);
+            *reinterpret_cast<uint4*>(Ks + key * KP + col) = kr[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = tid + 256 * q, kp = c & 31, col = 8 * (c >> 5);
+            const uint32_t w0[4] = {vr[2 * q].x, vr[2 * q].y, vr[2 * q].z, vr[2 * q].w};
+            const uint32_t w1[4] = {vr[2 * q + 1].x, vr[2 * q + 1].y, vr[2 * q + 1].z, vr[2 * q + 1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu, hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                *reinterpret_cast<uint32_t*>(Vt + (col + e) * VP + 2 * kp) = lo | (hi << 16);
+            }
+        }
+        const int k0 = s_list[u] * KT;
+        if (u + 1 < nt) fetch(u + 1);  // in flight while this tile is computed
+        __syncthreads();
+
+        // S = Q K^T: acc[j][e] = S[row 4 g + e][key 16 j + l15]
+        f32x4 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + (16 * j + l15) * KP + 32 * s + 8 * g));
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb, acc[j], 0, 0, 0);
+            }
+        }
+        // mask, online softmax per row (rows 4 g + e live in the 16 lanes of group g)
+        float alpha[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * wv + 4 * g + e;
+            // the row's 64 selection bits of this tile (k0 is a multiple of 64)
+            const uint2 wb = *reinterpret_cast<const uint2*>(&bits[r][k0 >> 5]);
+            float x[4], mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t word = j < 2 ? wb.x : wb.y;
+                const bool sel = (word >> (16 * (j & 1) + l15)) & 1u;
+                x[j] = sel ? acc[j][e] * sl2 : -INFINITY;
+                mx = fmaxf(mx, x[j]);
+            }
+            // maximum over the 16 lanes of the row (one DPP row)
+            mx = fmaxf(mx, dpp_mov<0xB1>(mx));
+            mx = fmaxf(mx, dpp_mov<0x4E>(mx));
+            mx = fmaxf(mx, dpp_mov<0x141>(mx));
+            mx = fmaxf(mx, dpp_mov<0x140>(mx));
+            const float mn = fmaxf(m[e], mx);
+            alpha[e] = m[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[e] - mn);
+            const float mref = mn == -INFINITY ? 0.f : mn;
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pv = __builtin_amdgcn_exp2f(x[j] - mref);
+                const uint16_t pb = f32_to_bf16_rne(pv);
+                ps += pv;
+                Pw[(4 * g + e) * VP + 16 * j + l15] = pb;
+            }
+            ps += dpp_mov<0xB1>(ps);
+            ps += dpp_mov<0x4E>(ps);
+            ps += dpp_mov<0x141>(ps);
+            ps += dpp_mov<0x140>(ps);
+            l[e] = l[e] * alpha[e] + ps;
+            m[e] = mn;
+        }
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[t][e] *= alpha[e];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
+        // O += P V: A = P (row l15, keys 32 s + 8 g ..), B = V (key 32 s + 8 g .., d 16 t + l15)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const bf16x8 pa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pw + l15 * VP + 32 * s + 8 * g));
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) {
+                const bf16x8 vb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vt + (16 * t + l15) * VP + 32 * s + 8 * g));
+                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+            }
+        }
+    }
+    // O[row 4 g + e][d 16 t + l15] / l; LSE per row
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = qb * QR + 16 * wv + 4 * g + e;
+        if (i >= p.n_q) continue;
+        const float inv = l[e] > 0.f ? 1.f / l[e] : 0.f;
+        uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) op[16 * t + l15] = f32_to_bf16_rne(o[t][e] * inv);
+        if (a.lse && l15 == 0)
+            a.lse[b * a.lse_bs + (int64_t)h * p.n_q + i] = l[e] > 0.f ? (m[e] + log2f(l[e])) * kLn2 : -INFINITY;
+    }
+}
+
 // --------------------------------------------------------------- attn_rows_buf
 // bf16, one query head per key/value head, head width D.  Loads stay coalesced and the
 // arithmetic stays in the VALU (the contraction is a GEMV per candidate set):
@@ -1309,8 +1552,18 @@ static bool rows_buf_ok(const AttnArgs& a) {
            ((uintptr_t)a.idx & 15) == 0 && rows < (1 << 24) && a.K.s2 * 2 < (1 << 24) && a.V.s2 * 2 < (1 << 24);
 }
 
+// The tile kernel: bf16 MHA with d = 128, at least one block of query rows, a history of at
+// most tile::MAXN positions, and budgets large enough that a block's selections cover most
+// key tiles (64 rows x k >= 2 n_kv); candidate lists read four at a time.
+static bool tile_ok(const AttnArgs& a) {
+    const sa_problem& p = a.p;
+    return a.Q.dtype == SA_BF16 && p.Hq == p.Hkv && p.d_qk == tile::D && p.d_v == tile::D && p.n_kv <= tile::MAXN &&
+           p.n_q >= tile::QR && p.k % 4 == 0 && ((uintptr_t)a.idx & 15) == 0 &&
+           (int64_t)p.k * tile::QR >= 2LL * p.n_kv;
+}
+
 bool attn_paged_ok(const AttnArgs& a) {
-    return attn_uses_mla(a.p, a.Q.dtype) ? mla_lds_ok(a) : rows_buf_ok(a);
+    return attn_uses_mla(a.p, a.Q.dtype) ? mla_lds_ok(a) : (tile_ok(a) || rows_buf_ok(a));
 }
 
 bool attn_uses_mla(const sa_problem& p, int dtype) {
@@ -1373,6 +1626,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     const int G = p.Hq / p.Hkv;
+    if (tile_ok(a)) {
+        const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + tile::QR - 1) / tile::QR) * p.Hkv);
+        hipLaunchKernelGGL(attn_tile, dim3(nblk), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
         if (rows_buf_ok(a)) {
             const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + 3) / 4) * p.Hkv);
