@@ -90,8 +90,11 @@ def stage_rooflines(W, alg, t):
     out["indexer_score"] = hbm(alg["idx_scan_bytes"], t["indexer_score"]) if alg["decode"] else \
         mfma(alg["idx_flops"], t["indexer_score"])
     out["topk"] = hbm(alg["topk_bytes"], t["topk"])
-    if W["mla"] and not alg["decode"]:
+    if not alg["decode"]:
+        # prefill attention runs on the matrix cores (latent rows, or the tile kernel for
+        # multi-head rows); the logical gather rate is reported beside it
         out["sparse_attn"] = mfma(alg["attn_flops"], t["sparse_attn"])
+        out["sparse_attn"]["gather_gbs_logical"] = round(alg["gather_bytes"] / (t["sparse_attn"] * 1e-3) / 1e9, 1)
     else:
         out["sparse_attn"] = hbm(alg["gather_bytes"], t["sparse_attn"])
     for k in out:
