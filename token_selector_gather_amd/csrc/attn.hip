@@ -284,6 +284,7 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
     __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * VP];
     __shared__ int s_L[QR], s_act[4][KT], s_list[KT], s_nt, s_maxL;
+    __shared__ int64_t s_tbase[KT];  // paged, pages of >= 64 rows: pool row of each active tile's first key
     const sa_problem& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63, l15 = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -352,6 +353,12 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
     }
     __syncthreads();
     const int nt = s_nt;
+    // with pages of at least 64 rows a 64-key tile lies inside one page: one table lookup per tile
+    const bool tile_pages = a.block_table && a.page_shift >= 6;
+    if (tile_pages) {
+        if (tid < nt) s_tbase[tid] = kv_row(a, b, s_list[tid] * KT);
+        __syncthreads();
+    }
 
     // Q fragments (A operand): lane row l15 = query row 16 wv + l15, d = 32 s + 8 g .. + 7
     const int iq = qb * QR + 16 * wv + l15;
@@ -371,10 +378,16 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
     uint4 kr[4], vr[4];
     auto fetch = [&](int u) {
         const int k0 = s_list[u] * KT;
+        const int64_t tb = tile_pages ? s_tbase[u] : 0;
+        auto row_of = [&](int key) -> int64_t {
+            if (key >= p.n_kv) return -1;
+            if (tile_pages) return tb < 0 ? -1 : tb + (key - k0);
+            return kv_row(a, b, key);
+        };
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = tid + 256 * q, key = k0 + (c >> 4), col = 8 * (c & 15);
-            const int64_t row = key < p.n_kv ? kv_row(a, b, key) : -1;
+            const int64_t row = row_of(key);
             kr[q] = row >= 0 ? *reinterpret_cast<const uint4*>(Kb + row * a.K.s2 + col) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -383,7 +396,7 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
 #pragma unroll
             for (int z = 0; z < 2; ++z) {
                 const int key = k0 + 2 * kp + z;
-                const int64_t row = key < p.n_kv ? kv_row(a, b, key) : -1;
+                const int64_t row = row_of(key);
                 vr[2 * q + z] = row >= 0 ? *reinterpret_cast<const uint4*>(Vb + row * a.V.s2 + col) : make_uint4(0, 0, 0, 0);
             }
         }
