@@ -133,3 +133,23 @@ def test_mla_logits_far_above_the_first_tile_rerun_the_set(Hq):
     O_or, lse_or = orc.attend(W, idx, rows)
     assert lse_or.min() > 50
     gc.compare_attention(W, rows, O, lse, O_or, lse_or)
+
+
+def test_tile_attention_skips_unselected_tiles_and_ignores_order():
+    # bf16 MHA d = 128 with 64 k >= 2 n_kv takes the tile kernel.  Caller lists that touch
+    # only two of the eight 64-key tiles (the others must be skipped), in descending order,
+    # mixed with -1, out-of-range and invisible entries, against the oracle.
+    W = sa_synth.custom(seed=71, B=2, n_q=130, n_kv=512, Hq=2, Hkv=2, d_qk=128, d_v=128, k=32, causal=1,
+                        q_pos0=np.array([382, 300], np.int32), lens=[512, 430])
+    rng = np.random.default_rng(72)
+    R = W["B"] * W["n_q"]
+    idx = np.full((R, W["k"]), -1, np.int32)
+    for r in range(R):
+        cand = np.concatenate([np.arange(64, 128), np.arange(256, 320)])
+        pick = rng.choice(cand, 24, replace=False)
+        row = np.concatenate([np.sort(pick)[::-1], [-1, 9999, -5, 600, -1, -1, -1, -1]])
+        idx[r] = row.astype(np.int32)
+    rows = np.arange(R, dtype=np.int32)
+    O, lse = gc.gpu_sparse_attn(W, idx.reshape(W["B"], W["n_q"], -1))
+    O_or, lse_or = orc.attend(W, idx, rows)
+    gc.compare_attention(W, rows, O, lse, O_or, lse_or)
