@@ -472,7 +472,7 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float pv = __builtin_amdgcn_exp2f(x[j] - mref);
-                const uint16_t pb = f32_to_bf16_rne(pv);
+                const uint16_t pb = __builtin_bit_cast(uint16_t, (__bf16)pv);  // hardware RNE (pv is finite)
                 ps += pv;
                 Pw[(4 * g + e) * VP + 16 * j + l15] = pb;
             }
