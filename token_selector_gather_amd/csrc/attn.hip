@@ -276,15 +276,81 @@ constexpr int KP = D + 8;      // padded K row (elements): conflict-free 16-byte
 constexpr int VP = KT + 8;     // padded V^T row
 }  // namespace tile
 
-__global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
+// The selections of a batch's block of 64 query rows, shared by every head: a bitmap per
+// row (bit j of word j / 32 = position j selected) and the list of 64-key tiles any of the
+// rows selected.  One workgroup per (batch, row block); written to the workspace.
+__global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
     __shared__ __attribute__((aligned(16))) uint32_t bits[QR][NWORD];
+    __shared__ int s_L[QR], s_act[4][KT], s_maxL;
+    const sa_problem& p = a.p;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nqb = (p.n_q + QR - 1) / QR;
+    const int b = (int)(blockIdx.x / nqb), qb = (int)(blockIdx.x % nqb);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    if (tid < QR) {
+        const int i = qb * QR + tid;
+        s_L[tid] = i < p.n_q ? visible_len(R, b, i) : 0;
+    }
+    for (int w = tid; w < QR * NWORD; w += 256) (&bits[0][0])[w] = 0u;
+    if (tid == 0) s_maxL = 0;
+    __syncthreads();
+    if (tid < QR) atomicMax(&s_maxL, s_L[tid]);
+    {   // 4 threads per row, eight 16-byte index loads in flight per thread
+        const int r = tid >> 2, q = tid & 3;
+        const int i = qb * QR + r, L = s_L[r];
+        if (i < p.n_q && L > 0) {
+            const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
+            for (int e0 = 4 * q; e0 < p.k; e0 += 16 * 8) {
+                int4 jj[8];
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                    jj[n] = e0 + 16 * n < p.k ? *reinterpret_cast<const int4*>(ix + e0 + 16 * n) : make_int4(-1, -1, -1, -1);
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const int jv[4] = {jj[n].x, jj[n].y, jj[n].z, jj[n].w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if ((unsigned)jv[u] < (unsigned)L && (!a.block_table || kv_row(a, b, jv[u]) >= 0))
+                            atomicOr(&bits[r][jv[u] >> 5], 1u << (jv[u] & 31));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int ntile = (s_maxL + KT - 1) / KT;
+    {
+        const int t = tid & 63, rq = tid >> 6;
+        uint32_t any = 0;
+        if (t < ntile)
+            for (int r = 16 * rq; r < 16 * rq + 16; ++r) any |= bits[r][2 * t] | bits[r][2 * t + 1];
+        s_act[rq][t] = any != 0;
+    }
+    __syncthreads();
+    int32_t* list = glist + (size_t)(b * nqb + qb) * (KT + 1);
+    if (tid < 64) {
+        const bool act = (s_act[0][lane] | s_act[1][lane] | s_act[2][lane] | s_act[3][lane]) != 0;
+        const uint64_t m = __ballot(act);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (act) list[1 + pos] = lane;
+        if (lane == 0) list[0] = __popcll(m);
+    }
+    // the rows' bitmaps, as 16-byte pieces
+    for (int w = tid; w < QR * NWORD / 4; w += 256) {
+        const int r = w / (NWORD / 4), c = w % (NWORD / 4);
+        const int i = qb * QR + r;
+        if (i < p.n_q)
+            reinterpret_cast<uint4*>(gbits + ((size_t)b * p.n_q + i) * NWORD)[c] = reinterpret_cast<const uint4*>(bits[r])[c];
+    }
+}
+
+__global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
+    using namespace tile;
+    constexpr int NWORD = MAXN / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KP];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
     __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * VP];
-    __shared__ int s_L[QR], s_act[4][KT], s_list[KT], s_nt, s_maxL;
-    __shared__ int64_t s_tbase[KT];  // paged, pages of >= 64 rows: pool row of each active tile's first key
     const sa_problem& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63, l15 = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,61 +370,10 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
         b = (int)(rest / nqb);
         qb = nqb - 1 - (int)(rest % nqb);  // the longest (latest) row blocks first
     }
-    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
-    if (tid < QR) {
-        const int i = qb * QR + tid;
-        s_L[tid] = i < p.n_q ? visible_len(R, b, i) : 0;
-    }
-    for (int w = tid; w < QR * NWORD; w += 256) (&bits[0][0])[w] = 0u;
-    if (tid == 0) s_maxL = 0;
-    __syncthreads();
-    if (tid < QR) atomicMax(&s_maxL, s_L[tid]);
-    {   // selection bitmap: 4 threads per row, 4 candidates per load
-        const int r = tid >> 2, q = tid & 3;
-        const int i = qb * QR + r, L = s_L[r];
-        if (i < p.n_q && L > 0) {
-            const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
-            for (int e0 = 4 * q; e0 < p.k; e0 += 16 * 8) {
-                int4 jj[8];  // eight loads in flight, then their bits
-#pragma unroll
-                for (int n = 0; n < 8; ++n)
-                    jj[n] = e0 + 16 * n < p.k ? *reinterpret_cast<const int4*>(ix + e0 + 16 * n) : make_int4(-1, -1, -1, -1);
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const int jv[4] = {jj[n].x, jj[n].y, jj[n].z, jj[n].w};
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if ((unsigned)jv[u] < (unsigned)L && (!a.block_table || kv_row(a, b, jv[u]) >= 0))
-                            atomicOr(&bits[r][jv[u] >> 5], 1u << (jv[u] & 31));
-                }
-            }
-        }
-    }
-    __syncthreads();
-    const int ntile = (s_maxL + KT - 1) / KT;
-    {   // tiles holding a selected key of any row: rows 16 (tid / 64) .. + 15 per thread
-        const int t = tid & 63, rq = tid >> 6;
-        uint32_t any = 0;
-        if (t < ntile)
-            for (int r = 16 * rq; r < 16 * rq + 16; ++r) any |= bits[r][2 * t] | bits[r][2 * t + 1];
-        s_act[rq][t] = any != 0;
-    }
-    __syncthreads();
-    if (wv == 0) {
-        const bool act = (s_act[0][lane] | s_act[1][lane] | s_act[2][lane] | s_act[3][lane]) != 0;
-        const uint64_t m = __ballot(act);
-        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (act) s_list[pos] = lane;
-        if (lane == 0) s_nt = __popcll(m);
-    }
-    __syncthreads();
-    const int nt = s_nt;
+    const int32_t* list = glist + (size_t)(b * nqb + qb) * (KT + 1);
+    const int nt = __builtin_amdgcn_readfirstlane(list[0]);
     // with pages of at least 64 rows a 64-key tile lies inside one page: one table lookup per tile
     const bool tile_pages = a.block_table && a.page_shift >= 6;
-    if (tile_pages) {
-        if (tid < nt) s_tbase[tid] = kv_row(a, b, s_list[tid] * KT);
-        __syncthreads();
-    }
 
     // Q fragments (A operand): lane row l15 = query row 16 wv + l15, d = 32 s + 8 g .. + 7
     const int iq = qb * QR + 16 * wv + l15;
@@ -372,18 +387,32 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
             qa[s] = iq < p.n_q ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g))
                                : bf16x8{};
     }
-    // a tile's K: 1024 16-byte pieces, four per thread (key c / 16, columns 8 (c % 16)); its V:
-    // key pairs (2 kp, 2 kp + 1) x 16 column pieces, two per thread, the pair index fastest
-    // across lanes so that the transposed stores of a wave hit consecutive LDS words
-    uint4 kr[4], vr[4];
-    auto fetch = [&](int u) {
-        const int k0 = s_list[u] * KT;
-        const int64_t tb = tile_pages ? s_tbase[u] : 0;
+    const float sl2 = a.scale * kLog2e;
+    float m[4], l[4];
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint16_t* Pw = Ps[wv];
+    // bitmap rows of this lane's four query rows (16 wv + 4 g + e)
+    const uint32_t* brow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = qb * QR + 16 * wv + 4 * g + e;
+        brow[e] = i < p.n_q ? gbits + ((size_t)b * p.n_q + i) * NWORD : nullptr;
+    }
+
+    for (int u = 0; u < nt; ++u) {
+        const int k0 = __builtin_amdgcn_readfirstlane(list[1 + u]) * KT;
+        const int64_t tb = tile_pages ? kv_row(a, b, k0) : 0;
         auto row_of = [&](int key) -> int64_t {
             if (key >= p.n_kv) return -1;
             if (tile_pages) return tb < 0 ? -1 : tb + (key - k0);
             return kv_row(a, b, key);
         };
+        // this tile's K (1024 16-byte pieces, four per thread) and V (key pairs, two per thread)
+        uint4 kr[4], vr[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = tid + 256 * q, key = k0 + (c >> 4), col = 8 * (c & 15);
@@ -395,24 +424,13 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
             const int c = tid + 256 * q, kp = c & 31, col = 8 * (c >> 5);
 #pragma unroll
             for (int z = 0; z < 2; ++z) {
-                const int key = k0 + 2 * kp + z;
-                const int64_t row = row_of(key);
+                const int64_t row = row_of(k0 + 2 * kp + z);
                 vr[2 * q + z] = row >= 0 ? *reinterpret_cast<const uint4*>(Vb + row * a.V.s2 + col) : make_uint4(0, 0, 0, 0);
             }
         }
-    };
-    if (nt > 0) fetch(0);
-
-    const float sl2 = a.scale * kLog2e;
-    float m[4], l[4];
-    f32x4 o[D / 16];
+        uint2 wb[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint16_t* Pw = Ps[wv];
-
-    for (int u = 0; u < nt; ++u) {
+        for (int e = 0; e < 4; ++e) wb[e] = brow[e] ? *reinterpret_cast<const uint2*>(brow[e] + (k0 >> 5)) : make_uint2(0u, 0u);
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -430,8 +448,6 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
                 *reinterpret_cast<uint32_t*>(Vt + (col + e) * VP + 2 * kp) = lo | (hi << 16);
             }
         }
-        const int k0 = s_list[u] * KT;
-        if (u + 1 < nt) fetch(u + 1);  // in flight while this tile is computed
         __syncthreads();
 
         // S = Q K^T: acc[j][e] = S[row 4 g + e][key 16 j + l15]
@@ -449,13 +465,10 @@ __global__ void __launch_bounds__(256) attn_tile(AttnArgs a) {
         float alpha[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = 16 * wv + 4 * g + e;
-            // the row's 64 selection bits of this tile (k0 is a multiple of 64)
-            const uint2 wb = *reinterpret_cast<const uint2*>(&bits[r][k0 >> 5]);
             float x[4], mx = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t word = j < 2 ? wb.x : wb.y;
+                const uint32_t word = j < 2 ? wb[e].x : wb[e].y;
                 const bool sel = (word >> (16 * (j & 1) + l15)) & 1u;
                 x[j] = sel ? acc[j][e] * sl2 : -INFINITY;
                 mx = fmaxf(mx, x[j]);
@@ -1568,11 +1581,20 @@ static bool rows_buf_ok(const AttnArgs& a) {
 // The tile kernel: bf16 MHA with d = 128, at least one block of query rows, a history of at
 // most tile::MAXN positions, and budgets large enough that a block's selections cover most
 // key tiles (64 rows x k >= 2 n_kv); candidate lists read four at a time.
+static bool tile_shape_ok(const sa_problem& p) {
+    return p.Hq == p.Hkv && p.d_qk == tile::D && p.d_v == tile::D && p.n_kv <= tile::MAXN && p.n_q >= tile::QR &&
+           p.k % 4 == 0 && (int64_t)p.k * tile::QR >= 2LL * p.n_kv;
+}
 static bool tile_ok(const AttnArgs& a) {
-    const sa_problem& p = a.p;
-    return a.Q.dtype == SA_BF16 && p.Hq == p.Hkv && p.d_qk == tile::D && p.d_v == tile::D && p.n_kv <= tile::MAXN &&
-           p.n_q >= tile::QR && p.k % 4 == 0 && ((uintptr_t)a.idx & 15) == 0 &&
-           (int64_t)p.k * tile::QR >= 2LL * p.n_kv;
+    return a.Q.dtype == SA_BF16 && tile_shape_ok(a.p) && ((uintptr_t)a.idx & 15) == 0;
+}
+// workspace of the tile kernel: the rows' selection bitmaps, then the row blocks' tile lists
+static size_t tile_bits_bytes(const sa_problem& p) {
+    return ((size_t)p.B * p.n_q * (tile::MAXN / 8) + 255) & ~(size_t)255;
+}
+static size_t tile_ws_bytes(const sa_problem& p) {
+    const size_t nqb = (size_t)(p.n_q + tile::QR - 1) / tile::QR;
+    return tile_bits_bytes(p) + (size_t)p.B * nqb * (tile::KT + 1) * sizeof(int32_t);
 }
 
 bool attn_paged_ok(const AttnArgs& a) {
@@ -1599,11 +1621,14 @@ int attn_splits(const sa_problem& p) {
 }
 
 size_t attn_partial_bytes(const sa_problem& p) {
+    // the tile kernel's selection bitmaps and tile lists, or the latent kernel's split partials
+    const size_t tile = tile_shape_ok(p) ? tile_ws_bytes(p) : 0;
     const int S = attn_splits(p);
-    if (S <= 1) return 0;
+    if (S <= 1) return tile;
     // (m, l) in fp32 and o / l in bf16 per (row, head, split), the o block 256-byte aligned
     const size_t slots = (size_t)p.B * p.n_q * p.Hq * S;
-    return ((slots * 8 + 255) & ~(size_t)255) + slots * (size_t)p.d_v * sizeof(uint16_t);
+    const size_t part = ((slots * 8 + 255) & ~(size_t)255) + slots * (size_t)p.d_v * sizeof(uint16_t);
+    return part > tile ? part : tile;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
@@ -1640,8 +1665,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     }
     const int G = p.Hq / p.Hkv;
     if (tile_ok(a)) {
-        const unsigned nblk = (unsigned)((long)p.B * ((p.n_q + tile::QR - 1) / tile::QR) * p.Hkv);
-        hipLaunchKernelGGL(attn_tile, dim3(nblk), dim3(256), 0, s, a);
+        // selections once per (batch, row block), then every head's tiles
+        const long nqb = (p.n_q + tile::QR - 1) / tile::QR;
+        uint32_t* gbits = static_cast<uint32_t*>(a.partial);
+        int32_t* glist = reinterpret_cast<int32_t*>(static_cast<char*>(a.partial) + tile_bits_bytes(p));
+        hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nqb)), dim3(256), 0, s, a, gbits, glist);
+        hipLaunchKernelGGL(attn_tile, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
         return hipGetLastError();
     }
     if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
