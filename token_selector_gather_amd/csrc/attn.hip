@@ -411,7 +411,8 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
             if (tile_pages) return tb < 0 ? -1 : tb + (key - k0);
             return kv_row(a, b, key);
         };
-        // this tile's K (1024 16-byte pieces, four per thread) and V (key pairs, two per thread)
+        // this tile's K (1024 16-byte pieces, four per thread) and V (four consecutive keys at
+        // one column piece per thread: key quad c % 16 fastest across lanes)
         uint4 kr[4], vr[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -419,13 +420,12 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
             const int64_t row = row_of(key);
             kr[q] = row >= 0 ? *reinterpret_cast<const uint4*>(Kb + row * a.K.s2 + col) : make_uint4(0, 0, 0, 0);
         }
+        {
+            const int kq = tid & 15, col = 8 * (tid >> 4);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + 256 * q, kp = c & 31, col = 8 * (c >> 5);
-#pragma unroll
-            for (int z = 0; z < 2; ++z) {
-                const int64_t row = row_of(k0 + 2 * kp + z);
-                vr[2 * q + z] = row >= 0 ? *reinterpret_cast<const uint4*>(Vb + row * a.V.s2 + col) : make_uint4(0, 0, 0, 0);
+            for (int z = 0; z < 4; ++z) {
+                const int64_t row = row_of(k0 + 4 * kq + z);
+                vr[z] = row >= 0 ? *reinterpret_cast<const uint4*>(Vb + row * a.V.s2 + col) : make_uint4(0, 0, 0, 0);
             }
         }
         uint2 wb[4];
@@ -437,15 +437,16 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
             const int c = tid + 256 * q, key = c >> 4, col = 8 * (c & 15);
             *reinterpret_cast<uint4*>(Ks + key * KP + col) = kr[q];
         }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + 256 * q, kp = c & 31, col = 8 * (c >> 5);
-            const uint32_t w0[4] = {vr[2 * q].x, vr[2 * q].y, vr[2 * q].z, vr[2 * q].w};
-            const uint32_t w1[4] = {vr[2 * q + 1].x, vr[2 * q + 1].y, vr[2 * q + 1].z, vr[2 * q + 1].w};
+        {
+            const int kq = tid & 15, col = 8 * (tid >> 4);
+            const uint32_t w[4][4] = {{vr[0].x, vr[0].y, vr[0].z, vr[0].w}, {vr[1].x, vr[1].y, vr[1].z, vr[1].w},
+                                      {vr[2].x, vr[2].y, vr[2].z, vr[2].w}, {vr[3].x, vr[3].y, vr[3].z, vr[3].w}};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu, hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *reinterpret_cast<uint32_t*>(Vt + (col + e) * VP + 2 * kp) = lo | (hi << 16);
+                uint32_t h[4];
+#pragma unroll
+                for (int z = 0; z < 4; ++z) h[z] = (w[z][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                *reinterpret_cast<uint2*>(Vt + (col + e) * VP + 4 * kq) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
         }
         __syncthreads();
