@@ -1,16 +1,19 @@
 """Benchmark: selected-token attention queries/s on one MI355X.
 
 A step is one sa_select_attend call over the whole batch: indexer score -> per-row top-k
--> sparse gather attention, inputs resident in HBM.  The default workload is the bf16
-causal prefill B=2, n=4096 (16 heads of width 128, 8 index heads of width 64, k = 512,
-batch 1 padded after 3584 positions).
+-> sparse gather attention, inputs resident in HBM.  The headline workload is the largest
+one that fits one GPU: the latent (MLA-style) causal prefill with n = 32768 query rows,
+128 query heads sharing one 576-wide latent key/value head, 64 index heads of width 128
+(e4m3 index keys) and k = 2048.  The bf16 multi-head prefill (B = 2, n = 4096), the
+64-request latent decode over a 65536-long cache and the planted-needle decode are timed
+under "workloads".
 
 Prints ONE JSON line.  Besides the headline value it reports per-stage times, the
-indexer TFLOP/s, and a roofline object for the dominant kernel (the gather attention),
-timed live with HIP events on the stream the library launches on, plus the CPU oracle's
-rate on a bounded row sample of the same workload.  It also reports the p10 / median / p90
-of single-step times and each stage timed with cold caches (a 512 MiB write between calls
-evicts L2 and the MALL), the numbers to use for claims against the HBM roofline.
+indexer TFLOP/s, a roofline object for the dominant kernel, timed live with HIP events on
+the stream the library launches on, and the CPU oracle's rate on a stratified row sample of
+the headline workload.  It also reports the p10 / median / p90 of single-step times and
+each stage timed with cold caches (a 512 MiB write between calls evicts L2 and the MALL),
+the numbers to use for claims against the HBM roofline.
 """
 import argparse
 import json
@@ -90,6 +93,9 @@ def stage_rooflines(W, alg, t):
     out["indexer_score"] = hbm(alg["idx_scan_bytes"], t["indexer_score"]) if alg["decode"] else \
         mfma(alg["idx_flops"], t["indexer_score"])
     out["topk"] = hbm(alg["topk_bytes"], t["topk"])
+    if "select" in t:  # score + select in one call: the indexer's work, no score matrix
+        out["select"] = hbm(alg["idx_scan_bytes"] - alg["pairs"] * 4, t["select"]) if alg["decode"] else \
+            mfma(alg["idx_flops"], t["select"])
     if not alg["decode"]:
         # prefill attention runs on the matrix cores (latent rows, or the tile kernel for
         # multi-head rows); the logical gather rate is reported beside it
@@ -213,7 +219,7 @@ def paged_stage(W, P, d, stream, timed, cold, reps, idx, t_attn, t_attn_cold, O_
 
     import sa_synth
     import token_selector_gather_amd as sa
-    from token_selector_gather_amd.inputs import device_pool, empty_outputs
+    from tests.device_inputs import device_pool, empty_outputs
 
     ps = 64
     bt, pool_rows = sa_synth.paged_layout(W["seed"] + 7, W["B"], W["n_kv"], ps, 3)
@@ -244,7 +250,7 @@ def grouped_stage(W, P, d, stream, timed, reps, G, t_step):
     import torch
 
     import token_selector_gather_amd as sa
-    from token_selector_gather_amd.inputs import empty_outputs
+    from tests.device_inputs import empty_outputs
 
     if sa.sa_grouped_workspace_bytes(P, G) == 0:
         return None
@@ -264,74 +270,63 @@ def grouped_stage(W, P, d, stream, timed, reps, G, t_step):
             "over_shared": round(t / t_step, 3), "iou_group0_group1": round(float(np.mean(iou)), 4) if iou else None}
 
 
-def cpu_baseline(W, budget_rows):
-    """The oracle (unchanged) on a stratified sample of rows: score, select and attend."""
-    import numpy as np
-    from oracle import oracle as orc
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    rng = np.random.default_rng(0)
+
+def stratified_rows(W, n_first=64, n_last=64, n_rand=384, seed=0):
+    """The first n_first and last n_last valid query rows of the flattened batch plus n_rand
+    other valid rows drawn at random (seed 0): the stratified sample of the oracle's CPU runs."""
+    import numpy as np
+
     L = visible_counts(W).reshape(-1)
     valid = np.where(L > 0)[0]
-    rows = np.sort(rng.choice(valid, size=min(budget_rows, valid.size), replace=False)).astype(np.int32)
+    if valid.size <= n_first + n_last + n_rand:
+        return valid.astype(np.int32), "all %d valid query rows" % valid.size
+    ends = np.concatenate([valid[:n_first], valid[-n_last:]])
+    rest = np.setdiff1d(valid, ends)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(rest, size=n_rand, replace=False)
+    rows = np.sort(np.concatenate([ends, pick])).astype(np.int32)
+    return rows, ("first %d, last %d and %d random (seed %d) of %d valid query rows"
+                  % (n_first, n_last, n_rand, seed, valid.size))
+
+
+def cpu_baseline(W, rows, what):
+    """The oracle (unchanged) on the given query rows: fp64 score, select and attend."""
+    from oracle import oracle as orc
+
     threads = orc.threads()
     t0 = time.perf_counter()
     orc.select_attend(W, rows)
     dt = time.perf_counter() - t0
     return {"value": rows.size / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d valid query rows (uniform random, seed 0), fp64 score+select+attend, %.1f s"
-                      % (rows.size, valid.size, dt)}
+            "sample": "%s; fp64 score + select + attend on %d threads, %.1f s" % (what, threads, dt),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, help="workload id (1 = bf16 prefill B=2 n=4096)")
-    ap.add_argument("--cpu-rows", type=int, default=7680, help="rows in the oracle's CPU-baseline sample (0 = skip)")
-    ap.add_argument("--hisa", type=int, default=-1,
-                    help="time the hierarchical selection beside the flat one (default: decode workloads only)")
-    ap.add_argument("--misa", type=int, default=-1,
-                    help="time the active-head selection beside the flat one (default: prefill workloads with 64 index heads)")
-    ap.add_argument("--paged", type=int, default=1,
-                    help="time the sparse attention over paged K/V beside the contiguous call")
-    ap.add_argument("--groups", type=int, default=2,
-                    help="time grouped candidate sets with this many groups beside the shared step (0 = skip)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
-        return
-    if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (--gpus 1); multi-GPU runs are not supported",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure(W, args, stream, full):
+    """Times one workload: the fused step, each stage (warm and cold), single-step spread;
+    with `full`, also the optional selectors and layouts beside it."""
     import numpy as np
     import torch
 
-    import sa_synth
     import token_selector_gather_amd as sa
-    from token_selector_gather_amd.inputs import device_workload, empty_outputs
+    from token_selector_gather_amd.inputs import device_workload
+    from tests.device_inputs import empty_outputs
 
-    os.environ.setdefault("OMP_NUM_THREADS", "16")
-    W = sa_synth.make_config(args.config)
     alg = algorithmic(W)
-    if args.config != 1:
-        args.cpu_rows = min(args.cpu_rows, 64)
     P, d = device_workload(W)
-    dt = torch.float32 if W["main_dtype"] == sa_synth.F32 else torch.bfloat16
+    dt = torch.float32 if W["main_dtype"] == 0 else torch.bfloat16
     O, lse, idx = empty_outputs(W, dt)
     ws = sa.workspace(P, sa.SA_OP_SELECT_ATTEND)
-    stream = torch.cuda.current_stream()
 
     def step():
         sa.sa_select_attend(P, d["q_idx"], d["k_idx"], d["w"], d["Q"], d["K"], d["V"], idx, O, lse, ws, stream)
@@ -348,9 +343,8 @@ def main():
     if st != sa.SA_OK:
         raise RuntimeError("device status " + sa.sa_status_str(st))
     ms_step = 1e3 * elapsed / args.steps
-    value = alg["rows"] / (elapsed / args.steps)
 
-    # per-stage timing with HIP events on the library's stream
+    # per-stage timing with HIP events recorded on the stream the library launches on
     def timed(fn, reps):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
@@ -365,14 +359,17 @@ def main():
     reps = max(3, args.steps)
     scores = torch.empty((W["B"], W["n_q"], W["n_kv"]), dtype=torch.float32, device="cuda")
     ws_t = sa.workspace(P, sa.SA_OP_TOPK)
+    ws_s = sa.workspace(P, sa.SA_OP_SELECT)
     ws_a = sa.workspace(P, sa.SA_OP_SPARSE_ATTN)
-    idx2 = idx.clone()
+    idx2, idx3 = idx.clone(), idx.clone()
     O2, lse2 = O.clone(), lse.clone()
-    t_idx = timed(lambda: sa.sa_indexer_score(P, d["q_idx"], d["k_idx"], d["w"], scores, stream), reps)
-    t_topk = timed(lambda: sa.sa_topk(P, scores, W["n_kv"], idx2, None, ws_t, stream), reps)
-    t_attn = timed(lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream), reps)
-    idx_tflops = alg["idx_flops"] / (t_idx * 1e-3) / 1e12
-    times = {"indexer_score": t_idx, "topk": t_topk, "sparse_attn": t_attn}
+    stage_fns = {
+        "indexer_score": lambda: sa.sa_indexer_score(P, d["q_idx"], d["k_idx"], d["w"], scores, stream),
+        "topk": lambda: sa.sa_topk(P, scores, W["n_kv"], idx2, None, ws_t, stream),
+        "select": lambda: sa.sa_select(P, d["q_idx"], d["k_idx"], d["w"], idx3, ws_s, stream),
+        "sparse_attn": lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream),
+    }
+    times = {k: timed(f, reps) for k, f in stage_fns.items()}
 
     # distribution of single-step times (HIP events around each step, after the timed region)
     nrep = max(20, args.steps)
@@ -400,52 +397,135 @@ def main():
             ts.append(e0.elapsed_time(e1))
         return float(np.median(ts))
 
-    cold_times = {
-        "indexer_score": cold(lambda: sa.sa_indexer_score(P, d["q_idx"], d["k_idx"], d["w"], scores, stream)),
-        "topk": cold(lambda: sa.sa_topk(P, scores, W["n_kv"], idx2, None, ws_t, stream)),
-        "sparse_attn": cold(lambda: sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O2, lse2, ws_a, stream)),
-    }
+    cold_times = {k: cold(f) for k, f in stage_fns.items()}
+    if sa.sa_device_status(ws_s) != sa.SA_OK:
+        raise RuntimeError("select: device status")
     roofs = stage_rooflines(W, alg, times)
-    dominant = max(times, key=times.get)
+    out = {
+        "workload": W["name"],
+        "value": round(alg["rows"] / (elapsed / args.steps), 2),
+        "ms_per_step": round(ms_step, 4),
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "config": {"workload": W["name"], "B": W["B"], "n_q": W["n_q"], "n_kv": W["n_kv"], "Hq": W["Hq"],
+                   "Hkv": W["Hkv"], "d_qk": W["d_qk"], "d_v": W["d_v"], "Hidx": W["Hidx"], "d_idx": W["d_idx"],
+                   "k": W["k"], "causal": W["causal"], "valid_rows": alg["rows"]},
+        "stages_ms": {k: round(v, 4) for k, v in times.items()},
+        "step_ms_dist": {"p10": round(float(np.percentile(step_ms, 10)), 4), "p50": round(float(np.median(step_ms)), 4),
+                         "p90": round(float(np.percentile(step_ms, 90)), 4), "reps": nrep},
+        "stages_ms_cold": {k: round(v, 4) for k, v in cold_times.items()},
+        "indexer": {"tflops": round(alg["idx_flops"] / (times["indexer_score"] * 1e-3) / 1e12, 3),
+                    "frac_bf16_peak": round(alg["idx_flops"] / (times["indexer_score"] * 1e-3) / 1e12 /
+                                            BF16_PEAK_TFLOPS, 5),
+                    "flops_per_call": alg["idx_flops"]},
+        "stage_rooflines": roofs,
+        "stage_rooflines_cold": stage_rooflines(W, alg, cold_times),
+        "_times": times,
+        "_alg": alg,
+    }
+    if args.hisa == 1 or (args.hisa == -1 and alg["decode"]):
+        out["hisa"] = hisa_stage(W, P, d, stream, timed, reps, idx, times["indexer_score"] + times["topk"])
+    if full:
+        if args.misa == 1 or (args.misa == -1 and not alg["decode"] and W["Hidx"] == 64):
+            out["misa"] = misa_stage(W, P, d, stream, timed, reps, idx, times["indexer_score"] + times["topk"])
+        if args.groups > 1:
+            out["grouped"] = grouped_stage(W, P, d, stream, timed, reps, args.groups, float(np.median(step_ms)))
+        if args.paged == 1:
+            out["paged"] = paged_stage(W, P, d, stream, timed, cold, reps, idx, times["sparse_attn"],
+                                       cold_times["sparse_attn"], O2, lse2)
+    del P, d, O, lse, idx, ws, scores, ws_t, ws_s, ws_a, idx2, idx3, O2, lse2, flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2,
+                    help="headline workload id (2 = latent prefill n=32768, the largest single-GPU workload)")
+    ap.add_argument("--others", type=str, default="1,3,4",
+                    help="other workload ids timed under 'workloads' (empty = none)")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="rows in the oracle's stratified CPU-baseline sample (first 64, last 64, the rest random; "
+                         "0 = skip)")
+    ap.add_argument("--hisa", type=int, default=-1,
+                    help="time the hierarchical selection beside the flat one (default: decode workloads only)")
+    ap.add_argument("--misa", type=int, default=-1,
+                    help="time the active-head selection beside the flat one (default: prefill workloads with 64 index heads)")
+    ap.add_argument("--paged", type=int, default=1,
+                    help="time the sparse attention over paged K/V beside the contiguous call")
+    ap.add_argument("--groups", type=int, default=2,
+                    help="time grouped candidate sets with this many groups beside the shared step (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (--gpus 1); multi-GPU runs are not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sa_synth
+
+    os.environ.setdefault("OMP_NUM_THREADS", "16")
+    stream = torch.cuda.current_stream()
+    print("bench: workload %d" % args.config, file=sys.stderr, flush=True)
+    W = sa_synth.make_config(args.config)
+    head = measure(W, args, stream, full=True)
+    times, alg = head.pop("_times"), head.pop("_alg")
+    roofs = head["stage_rooflines"]
+    step_stages = {k: v for k, v in times.items() if k in ("select", "sparse_attn")}
+    dominant = max(step_stages, key=step_stages.get)
     roof = dict(roofs[dominant])
     roof["traffic"] = counted_traffic(W["name"], dominant)
-
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head.pop("value"),
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "dtype": head.pop("dtype"),
         "data": "synthetic (seeded generator, seed = workload id)",
-        "config": {"workload": W["name"], "B": W["B"], "n_q": W["n_q"], "n_kv": W["n_kv"], "Hq": W["Hq"],
-                   "Hkv": W["Hkv"], "d_qk": W["d_qk"], "d_v": W["d_v"], "Hidx": W["Hidx"], "d_idx": W["d_idx"],
-                   "k": W["k"], "causal": W["causal"], "valid_rows": alg["rows"]},
-        "stages_ms": {"indexer_score": round(t_idx, 4), "topk": round(t_topk, 4), "sparse_attn": round(t_attn, 4)},
-        "step_ms_dist": {"p10": round(float(np.percentile(step_ms, 10)), 4), "p50": round(float(np.median(step_ms)), 4),
-                         "p90": round(float(np.percentile(step_ms, 90)), 4), "reps": nrep},
-        "stages_ms_cold": {k: round(v, 4) for k, v in cold_times.items()},
-        "indexer": {"tflops": round(idx_tflops, 3), "frac_bf16_peak": round(idx_tflops / BF16_PEAK_TFLOPS, 5),
-                    "flops_per_call": alg["idx_flops"]},
+        "config": head.pop("config"),
         "roofline": roof,
-        "stage_rooflines": roofs,
-        "stage_rooflines_cold": stage_rooflines(W, alg, cold_times),
     }
-    if args.hisa == 1 or (args.hisa == -1 and alg["decode"]):
-        out["hisa"] = hisa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
-    if args.misa == 1 or (args.misa == -1 and not alg["decode"] and W["Hidx"] == 64):
-        out["misa"] = misa_stage(W, P, d, stream, timed, reps, idx, t_idx + t_topk)
-    if args.groups > 1:
-        out["grouped"] = grouped_stage(W, P, d, stream, timed, reps, args.groups, float(np.median(step_ms)))
-    if args.paged == 1:
-        out["paged"] = paged_stage(W, P, d, stream, timed, cold, reps, idx, t_attn, cold_times["sparse_attn"], O2, lse2)
+    head.pop("workload")
+    out.update(head)
+    others = {}
+    for cid in [int(c) for c in args.others.split(",") if c.strip()]:
+        if cid == args.config:
+            continue
+        print("bench: workload %d" % cid, file=sys.stderr, flush=True)
+        Wo = sa_synth.make_config(cid)
+        r = measure(Wo, args, stream, full=False)
+        r.pop("_times"), r.pop("_alg")
+        r["queries_per_s"] = r.pop("value")
+        others[r.pop("workload")] = r
+        del Wo
+    if others:
+        out["workloads"] = others
     if args.cpu_rows > 0:
-        out["cpu_baseline"] = cpu_baseline(W, args.cpu_rows)
+        print("bench: oracle on the host", file=sys.stderr, flush=True)
+        n_rand = max(0, args.cpu_rows - 128)
+        rows, what = stratified_rows(W, 64, 64, n_rand)
+        out["cpu_baseline"] = cpu_baseline(W, rows, what)
     print(json.dumps(out))
 
 

@@ -67,7 +67,8 @@ typedef enum sa_op {
     SA_OP_TOPK = 1,
     SA_OP_SPARSE_ATTN = 2,
     SA_OP_SELECT_ATTEND = 3,
-    SA_OP_SPARSE_ATTN_PAGED = 4
+    SA_OP_SPARSE_ATTN_PAGED = 4,
+    SA_OP_SELECT = 5
 } sa_op;
 
 typedef struct sa_tensor {
@@ -125,6 +126,28 @@ sa_status sa_topk(const sa_problem* p, const float* scores, int64_t row_stride, 
                   void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sa_select -- score and select in one call: the output of sa_indexer_score followed by
+ * sa_topk (idx as there, bit for bit), without the scores.  "PaperTrace 2.2 · Fine-grained
+ * indexing", §2.1: the selector works through the history slice by slice, keeps local
+ * candidates and merges them down to k, which gives the global top-k; the full score
+ * matrix is never materialised.  This streaming form runs when the index queries are bf16,
+ * the index keys bf16 or e4m3, Hidx is 16, 32 or 64, d_idx 64 or 128 and there are enough
+ * query rows (at least 512 blocks of 512 / Hidx rows); there each row's candidates above a
+ * running threshold are kept in the workspace (about 2k + 128 entries per row of a
+ * bounded number of rows in flight) and cut back to k when full.  Other calls store the
+ * visible scores of each row in the workspace and select from them.
+ *   q_idx, k_idx, w   as for sa_indexer_score
+ *   idx               [B, n_q, k] int32, contiguous, as for sa_topk
+ *   ws                sa_workspace_bytes(p, SA_OP_SELECT) bytes, 256-byte aligned,
+ *                     zero-filled once after allocation (status word: non-finite index
+ *                     inputs of valid rows or visible keys set SA_ERR_NONFINITE).
+ * The workspace size depends on the shape only: for a shape that takes the streaming form
+ * but f32 index inputs, the rows are scored and selected in slices through the same space.
+ */
+sa_status sa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, int32_t* idx, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
  * sa_sparse_attn -- exact softmax attention over the selected history rows.
  * "PaperTrace 2.1.1 · Hashing and clustering", §1.1 eq. (1): logits, mask, softmax and
  * value aggregation only over the candidate set; §5.1: every piece of the set shares one
@@ -134,7 +157,12 @@ sa_status sa_topk(const sa_problem* p, const float* scores, int64_t row_stride, 
  *      (latent layout: V = the first d_v columns of each K row, same strides).
  *   idx [B, n_q, k] int32, contiguous; entries that are -1, out of range or not visible
  *      are ignored (never read).  Valid entries must be unique (a duplicate would count
- *      twice in the softmax); their order does not matter.
+ *      twice in the softmax); their order does not matter.  K/V rows that no entry selects
+ *      are never read.  The multi-head kernel for many query rows (bf16, d_qk = d_v = 128)
+ *      computes blocks of 64 query rows of a batch together: a row selected by any query
+ *      row of the block is read for the whole block and enters the other rows' value
+ *      product with weight 0, so a non-finite value in a SELECTED K/V row can reach the
+ *      outputs of other rows of that block.
  *   O   [B, Hq, n_q, d_v] output; query head h reads key/value head h / (Hq / Hkv).
  *   lse [B, Hq, n_q] f32 or NULL: natural-log log-sum-exp of the scaled logits
  *      (-inf when a row has no valid entry; then O = 0).
@@ -174,10 +202,11 @@ sa_status sa_sparse_attn_paged(const sa_problem* p, sa_tensor Q, sa_tensor K, sa
                                sa_tensor O, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * sa_select_attend -- score, select and attend in one call; arguments as in the three
- * entry points above.  idx_out [B, n_q, k] int32 receives the selection if not NULL.
- * ws must hold sa_workspace_bytes(p, SA_OP_SELECT_ATTEND) bytes (it includes the score
- * buffer of the visible part of every row).
+ * sa_select_attend -- sa_select, then sa_sparse_attn, in one call; arguments as in those
+ * entry points.  idx_out [B, n_q, k] int32 receives the selection if not NULL.
+ * ws must hold sa_workspace_bytes(p, SA_OP_SELECT_ATTEND) bytes, zero-filled once (status
+ * word); it includes the space of the selection (candidate lists, or the visible scores
+ * where the streaming form does not apply).
  */
 sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, sa_tensor Q,
                            sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O, float* lse, void* ws,

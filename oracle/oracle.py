@@ -66,7 +66,12 @@ def lib():
 
 
 def threads():
-    return max(1, min(64, os.cpu_count() or 1))
+    """Worker threads: the CPUs this process may run on, capped by OMP_NUM_THREADS when set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, min(64, n))
 
 
 def _dtype_code(a):

@@ -5,7 +5,8 @@ import torch
 
 import sa_synth
 import token_selector_gather_amd as sa
-from token_selector_gather_amd.inputs import device_workload, empty_outputs
+from token_selector_gather_amd.inputs import device_workload
+from tests.device_inputs import empty_outputs
 from oracle import oracle as orc
 
 _cache = {}
@@ -122,24 +123,45 @@ def sample_rows(W, n_each=32, n_rand=64, seed=0):
     return np.array(sorted(rows), dtype=np.int32)
 
 
-def full_check(W, rows=None, tie_groups=None, check_sparse=True):
+def stratified_rows(W, n_first=64, n_last=64, n_rand=384, seed=0):
+    """The first n_first and last n_last valid query rows of the flattened batch plus n_rand
+    other valid rows drawn at random: the stratified sample for workloads whose every row
+    the oracle cannot score in a test's time."""
+    from tests.checker import visible_len
+    B, nq = W["B"], W["n_q"]
+    valid = np.array([r for r in range(B * nq) if visible_len(W, r // nq, r % nq) > 0], dtype=np.int64)
+    if valid.size <= n_first + n_last + n_rand:
+        return valid.astype(np.int32)
+    ends = np.concatenate([valid[:n_first], valid[-n_last:]])
+    rest = np.setdiff1d(valid, ends)
+    pick = np.random.default_rng(seed).choice(rest, size=n_rand, replace=False)
+    return np.sort(np.concatenate([ends, pick])).astype(np.int32)
+
+
+def full_check(W, rows=None, tie_groups=None, check_sparse=True, say=None):
     """End-to-end select+attend against the oracle on `rows` (default: all rows), plus the
     attention kernel alone on the oracle's own candidate sets."""
     from tests.checker import check_index_rows
     if rows is None:
         rows = np.arange(W["B"] * W["n_q"], dtype=np.int32)
+    say = say or (lambda x: None)
     idx, O, lse, st = gpu_select_attend(W)
     assert st == sa.SA_OK, sa.sa_status_str(st)
     idx_r = idx.reshape(-1, W["k"])[rows]
+    say("oracle scores and selection")
     ref_sc = orc.scores(W, rows)
     ref_idx, sk, skp1, nsel = orc.select(W, ref_sc, rows)
     stats = check_index_rows(W, rows, idx_r, ref_sc, ref_idx, sk, tie_groups=tie_groups)
+    say("oracle attention on the GPU's sets")
     O_or, lse_or = orc.attend(W, idx_r, rows)
     errs = compare_attention(W, rows, O, lse, O_or, lse_or)
+    errs_sparse = (None, None)
     if check_sparse:
+        say("attention on the oracle's sets")
         full = np.full((W["B"] * W["n_q"], W["k"]), -1, dtype=np.int32)
         full[rows] = ref_idx
         O2, lse2 = gpu_sparse_attn(W, full.reshape(W["B"], W["n_q"], W["k"]))
         O_or2, lse_or2 = orc.attend(W, ref_idx, rows)
-        compare_attention(W, rows, O2, lse2, O_or2, lse_or2)
-    return dict(stats, err_o=errs[0], err_lse=errs[1], idx=idx, ref_idx=ref_idx, rows=rows)
+        errs_sparse = compare_attention(W, rows, O2, lse2, O_or2, lse_or2)
+    return dict(stats, err_o=errs[0], err_lse=errs[1], err_o_sparse=errs_sparse[0], idx=idx, ref_idx=ref_idx,
+                rows=rows)

@@ -78,7 +78,36 @@ def test_workspace_errors():
     assert L.sa_topk(ctypes.byref(p), FAKE, 64, FAKE, None, FAKE + 16, need, None) == sa.SA_ERR_WORKSPACE
     assert L.sa_topk(ctypes.byref(p), FAKE, 63, FAKE, None, FAKE, need, None) == sa.SA_ERR_INVALID_ARG
     sel = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SELECT_ATTEND)
-    assert sel >= 256 + 2 * 64 * 64 * 4 + 2 * 64 * 8 * 4  # status + score rows + selection
+    assert sel >= 256 + 2 * 64 * 64 * 4 + 2 * 64 * 8 * 4  # status + score rows + selection (small: two-pass)
+
+
+@needs_lib
+def test_streaming_selection_workspace_holds_no_score_matrix():
+    # the latent prefill (n = 32768, 64 x 128 index heads, k = 2048): the fused call's
+    # workspace holds candidate lists of the rows in flight, not B n_q n_kv scores
+    L = sa.lib()
+    p = sa._Problem(1, 32768, 32768, 128, 1, 576, 512, 64, 128, 2048, 1, None, None, 0.0)
+    scores = 32768 * 32768 * 4
+    for op in (sa.SA_OP_SELECT, sa.SA_OP_SELECT_ATTEND):
+        need = L.sa_workspace_bytes(ctypes.byref(p), op)
+        assert 0 < need < scores // 4, (op, need)  # candidate lists (+ the selection buffer), not scores
+    # a small problem keeps the stored scores (the two-pass selection)
+    q = _prob()
+    assert L.sa_workspace_bytes(ctypes.byref(q), sa.SA_OP_SELECT) >= 256 + 2 * 64 * 64 * 4
+
+
+@needs_lib
+def test_select_argument_errors():
+    L = sa.lib()
+    p = _prob()
+    need = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SELECT)
+    q, k, w = _t(s0=64 * 4 * 32, s1=4 * 32, s2=32), _t(s0=64 * 32, s1=32, s2=0), _t(dtype=sa.SA_F32, s0=64 * 4, s1=4, s2=0)
+    call = lambda idx=FAKE, ws=FAKE, n=need, qq=q: L.sa_select(ctypes.byref(p), qq, k, w, idx, ws, n, None)
+    assert call(idx=None) == sa.SA_ERR_INVALID_ARG
+    assert call(idx=FAKE + 2) == sa.SA_ERR_INVALID_ARG
+    assert call(ws=None) == sa.SA_ERR_WORKSPACE
+    assert call(n=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(qq=_t(dtype=sa.SA_FP8_E4M3, s0=64 * 4 * 32, s1=4 * 32, s2=32)) == sa.SA_ERR_UNSUPPORTED
 
 
 @needs_lib

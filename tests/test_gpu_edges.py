@@ -8,7 +8,8 @@ import sa_synth
 import token_selector_gather_amd as sa
 from oracle import oracle as orc
 from tests import gpu_common as gc
-from token_selector_gather_amd.inputs import device_workload, empty_outputs
+from token_selector_gather_amd.inputs import device_workload
+from tests.device_inputs import empty_outputs
 
 pytestmark = pytest.mark.gpu
 BF16, F32, E4M3 = sa_synth.BF16, sa_synth.F32, sa_synth.E4M3

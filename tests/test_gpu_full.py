@@ -32,12 +32,15 @@ def test_full_c1_bf16_prefill():
 
 
 def test_full_c2_mla_prefill():
+    # the stratified sample: the first 64 and last 64 query rows and 384 random ones
     _say("full c2: generate")
     W = sa_synth.make_config(2)
-    rows = gc.sample_rows(W, n_each=8, n_rand=24)
+    rows = gc.stratified_rows(W, 64, 64, 384)
+    assert rows.size == 512
     _say("full c2: %d rows" % rows.size)
-    r = gc.full_check(W, rows=rows, check_sparse=False)
-    _say("full c2: exact rows %d band rows %d |dO| %.3g" % (r["exact_rows"], r["band_rows"], r["err_o"]))
+    r = gc.full_check(W, rows=rows, check_sparse=True, say=lambda x: _say("full c2: " + x))
+    _say("full c2: exact rows %d band rows %d |dO| %.3g (bound 2e-2), on the oracle's sets %.3g"
+         % (r["exact_rows"], r["band_rows"], r["err_o"], r["err_o_sparse"]))
 
 
 def test_full_c3_mla_decode():

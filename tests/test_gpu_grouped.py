@@ -15,7 +15,8 @@ import token_selector_gather_amd as sa
 from oracle import oracle as orc
 from tests import gpu_common as gc
 from tests.checker import check_index_rows
-from token_selector_gather_amd.inputs import device_workload, empty_outputs
+from token_selector_gather_amd.inputs import device_workload
+from tests.device_inputs import empty_outputs
 
 pytestmark = pytest.mark.gpu
 

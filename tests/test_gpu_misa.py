@@ -98,6 +98,12 @@ def test_misa_matches_oracle(case):
     _say("misa %s blk %d g %d" % (case, blk, g))
     kbar, idx, heads, st = gpu_misa(W, blk, g)
     assert st == sa.SA_OK
+    # the representatives the routing used against the oracle's own
+    ref_kbar = orc.block_means(W, blk)
+    if W["kidx_dtype"] == E4M3:  # fp32 sums of e4m3 keys are exact: identical representatives
+        np.testing.assert_array_equal(kbar, ref_kbar)
+    else:  # fp32 sums of bf16 keys: at most one bf16 unit apart after the rounding
+        assert np.abs(kbar.astype(np.int64) - ref_kbar.astype(np.int64)).max() <= 1
     rows = np.arange(W["B"] * W["n_q"], dtype=np.int32)
     frac = check_rows(W, blk, g, rows, idx, heads, kbar)
     _say("misa %s: %.1f%% of rows identical to the oracle" % (case, 100 * frac))

@@ -14,7 +14,8 @@ import sa_synth
 import token_selector_gather_amd as sa
 from oracle import oracle as orc
 from tests import gpu_common as gc
-from token_selector_gather_amd.inputs import device_pool, device_workload, empty_outputs
+from token_selector_gather_amd.inputs import device_workload
+from tests.device_inputs import device_pool, empty_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +24,10 @@ def _say(x):
     print(x, flush=True)
 
 
-def _run_both(W, idx_np, ps, bt=None, pool_rows=None, spare=3, call_bt=None):
+def _run_both(W, idx_np, ps, bt=None, pool_rows=None, spare=3, call_bt=None, fill=3.0e4):
     """(contiguous O, lse), (paged O, lse) on the same candidates; returns numpy arrays.
-    The pool is filled along bt; the paged call reads through call_bt (default bt)."""
+    The pool is filled along bt, its unused rows with `fill`; the paged call reads through
+    call_bt (default bt)."""
     P, d = device_workload(W)
     idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32).reshape(W["B"], W["n_q"], -1)).cuda()
     ws = sa.workspace(P, sa.SA_OP_SPARSE_ATTN)
@@ -34,7 +36,6 @@ def _run_both(W, idx_np, ps, bt=None, pool_rows=None, spare=3, call_bt=None):
     sa.sa_sparse_attn(P, d["Q"], d["K"], d["V"], idx, O1, l1, ws)
     if bt is None:
         bt, pool_rows = sa_synth.paged_layout(W["seed"] + 7, W["B"], W["n_kv"], ps, spare)
-    fill = 3.0e4
     Kp = device_pool(d["K"], bt, ps, pool_rows, fill)
     latent = W.get("V") is None
     Vp = Kp[..., : W["d_v"]] if latent else device_pool(d["V"], bt, ps, pool_rows, fill)
@@ -137,3 +138,37 @@ def test_full_size_paged_equals_contiguous(cid, ps):
     rows = gc.sample_rows(W, n_each=4, n_rand=12)
     O_or, l_or = orc.attend(W, idx.reshape(W["B"] * W["n_q"], -1)[rows], rows)
     gc.compare_attention(W, rows, b[0], b[1], O_or, l_or)
+
+
+@pytest.mark.parametrize("name,ps", [("mha_bf16_ragged_p16", 16), ("mha_bf16_ragged_p16", 64),
+                                     ("c3_b8_kv3000_k256_p64", 64)])
+def test_nan_in_rows_no_entry_selects_never_reaches_the_outputs(name, ps):
+    # K/V rows past kv_len (kv_len not a multiple of 64), visible rows that no query row of
+    # the batch selected, and the pool's unused rows all hold bf16 NaN: neither the
+    # contiguous nor the paged call may let them into an output.  The multi-head shape runs
+    # the tile kernel (whole 64-key tiles per block of 64 query rows), the latent one the
+    # gather kernel.
+    W, _ = _workload(name)
+    rows = np.arange(W["B"] * W["n_q"], dtype=np.int32)
+    ref = orc.select_attend(W, rows)
+    idx = ref["idx"].reshape(W["B"], W["n_q"], -1)
+    Wn = W.__class__(W)
+    keys = ("K",) if W.get("V") is None else ("K", "V")
+    for key in keys:
+        Wn[key] = W[key].copy()
+    n_poison = 0
+    for b in range(W["B"]):
+        used = np.zeros(W["n_kv"], bool)
+        sel = idx[b][idx[b] >= 0]
+        used[sel] = True
+        used[int(W["kv_len"][b]):] = False
+        poison = np.where(~used)[0]
+        assert int(W["kv_len"][b]) % 64 != 0 or b > 0
+        n_poison += poison.size
+        for key in keys:
+            Wn[key][b][:, poison, :] = 0x7FC0
+    _say("nan rows %s p%d: %d poisoned rows" % (name, ps, n_poison))
+    assert n_poison > 0
+    a, b2 = _run_both(Wn, idx, ps, fill=float("nan"))
+    _same(a, b2)
+    gc.compare_attention(W, rows, a[0], a[1], ref["O"], ref["lse"])

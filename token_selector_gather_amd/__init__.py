@@ -6,7 +6,7 @@ memory and the stream.  Importing works without a GPU; every call needs the buil
 library and raises if it is missing.
 
 The functions mirror the C ABI in include/sa.h and keep its names:
-    sa_indexer_score, sa_topk, sa_sparse_attn, sa_select_attend,
+    sa_indexer_score, sa_topk, sa_select, sa_sparse_attn, sa_select_attend,
     sa_block_means, sa_hisa_select, sa_hisa_workspace_bytes, sa_misa_select, sa_misa_workspace_bytes,
     sa_workspace_bytes, sa_device_status, sa_status_str, sa_abi_version
 Tensors are torch tensors on the GPU whose last dimension is contiguous: float32,
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libsa.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_NONFINITE = range(6)
 SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
-SA_OP_INDEXER_SCORE, SA_OP_TOPK, SA_OP_SPARSE_ATTN, SA_OP_SELECT_ATTEND, SA_OP_SPARSE_ATTN_PAGED = range(5)
+SA_OP_INDEXER_SCORE, SA_OP_TOPK, SA_OP_SPARSE_ATTN, SA_OP_SELECT_ATTEND, SA_OP_SPARSE_ATTN_PAGED, SA_OP_SELECT = range(6)
 ABI_VERSION = 1
 
 _TORCH_DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
@@ -59,6 +59,7 @@ def lib():
         st = ctypes.c_int
         L.sa_indexer_score.argtypes = [P, T, T, T, vp, vp]
         L.sa_topk.argtypes = [P, vp, i64, vp, vp, vp, sz, vp]
+        L.sa_select.argtypes = [P, T, T, T, vp, vp, sz, vp]
         L.sa_sparse_attn.argtypes = [P, T, T, T, vp, T, vp, vp, sz, vp]
         L.sa_select_attend.argtypes = [P, T, T, T, T, T, T, vp, T, vp, vp, sz, vp]
         L.sa_sparse_attn_paged.argtypes = [P, T, T, T, i64, vp, i64, ctypes.c_int, vp, T, vp, vp, sz, vp]
@@ -68,7 +69,7 @@ def lib():
         L.sa_block_means.argtypes = [P, T, ctypes.c_int, vp, vp]
         L.sa_hisa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         L.sa_misa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
-        for f in (L.sa_indexer_score, L.sa_topk, L.sa_sparse_attn, L.sa_select_attend, L.sa_block_means,
+        for f in (L.sa_indexer_score, L.sa_topk, L.sa_select, L.sa_sparse_attn, L.sa_select_attend, L.sa_block_means,
                   L.sa_hisa_select, L.sa_misa_select, L.sa_sparse_attn_paged, L.sa_select_attend_grouped):
             f.restype = st
         L.sa_misa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
@@ -164,6 +165,12 @@ def sa_indexer_score(p, q_idx, k_idx, w, scores, stream=None):
 def sa_topk(p, scores, row_stride, idx, vals, ws, stream=None):
     _check(lib().sa_topk(p.ref, _ptr(scores), int(row_stride), _ptr(idx), _ptr(vals), _ptr(ws),
                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "sa_topk")
+
+
+def sa_select(p, q_idx, k_idx, w, idx, ws, stream=None):
+    _check(lib().sa_select(p.ref, _tensor(q_idx, "q_idx"), _tensor(k_idx, "k_idx"), _tensor(w, "w"), _ptr(idx),
+                           _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "sa_select")
 
 
 def sa_sparse_attn(p, Q, K, V, idx, O, lse, ws, stream=None):

@@ -175,6 +175,53 @@ MisaLayout misa_layout(const sa_problem& p, int g) {
     return l;
 }
 
+// Workspace region of a selection (after the status word): the fused score + select's
+// candidate lists, or the score rows and the top-k scratch.  A shape that the fused path
+// takes but whose index dtypes it does not (f32 index queries or keys) scores and selects
+// slices of at least 64 rows through the same region.
+size_t select_slice_rows(const sa_problem& p, size_t region) { return region / ((size_t)p.n_kv * sizeof(float)); }
+size_t select_region_bytes(const sa_problem& p) {
+    if (select_fused_shape_ok(p)) {
+        const size_t fused = select_fused_bytes(p), slice = (size_t)64 * p.n_kv * sizeof(float);
+        return align256(fused > slice ? fused : slice);
+    }
+    return scores_bytes(p) + align256(topk_ws_bytes(p));
+}
+
+sa_status run_select(const sa_problem* p, const sa_tensor& q, const sa_tensor& k, const sa_tensor& w, int32_t* idx,
+                     Status* status, char* region, hipStream_t st) {
+    IndexerArgs ia;
+    ia.p = *p;
+    ia.q = q; ia.k = k; ia.w = w;
+    ia.status = status;
+    if (select_fused_ok(*p, q.dtype, k.dtype))
+        return launch_select_fused(ia, idx, region, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
+    TopkArgs ta;
+    ta.p = *p;
+    ta.idx = idx;
+    ta.vals = nullptr;
+    ta.status = status;
+    ta.row_stride = p->n_kv;
+    ia.row_stride = p->n_kv;
+    ia.fill_invisible = 0;  // the selection reads only the visible prefix of each row
+    ia.scores = reinterpret_cast<float*>(region);
+    ta.scores = ia.scores;
+    if (select_fused_shape_ok(*p)) {
+        const long rows = (long)p->B * p->n_q;
+        const long per = (long)select_slice_rows(*p, select_region_bytes(*p));
+        for (long r0 = 0; r0 < rows; r0 += per) {
+            ia.row0 = ta.row0 = (int)r0;
+            ia.nrows = ta.nrows = (int)(rows - r0 < per ? rows - r0 : per);
+            if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
+            if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
+        }
+        return SA_OK;
+    }
+    ta.scratch = region + scores_bytes(*p);
+    if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
+    return launch_topk(ta, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
 float eff_scale(const sa_problem* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d_qk); }
 
 // Block-table view of paged K/V pools (table null: K and V hold each batch's rows).
@@ -269,9 +316,9 @@ size_t sa_workspace_bytes(const sa_problem* p, int op) {
         const size_t part = align256(attn_partial_bytes(*p)), rows = idx_bytes(*p);
         return kStatusBytes + (part > rows ? part : rows);
     }
+    case SA_OP_SELECT: return kStatusBytes + select_region_bytes(*p);
     case SA_OP_SELECT_ATTEND:
-        return kStatusBytes + scores_bytes(*p) + idx_bytes(*p) + align256(attn_partial_bytes(*p)) +
-               align256(topk_ws_bytes(*p));
+        return kStatusBytes + idx_bytes(*p) + align256(attn_partial_bytes(*p)) + select_region_bytes(*p);
     default: return 0;
     }
 }
@@ -306,6 +353,17 @@ sa_status sa_topk(const sa_problem* p, const float* scores, int64_t row_stride, 
     a.status = static_cast<Status*>(ws);
     a.scratch = static_cast<char*>(ws) + kStatusBytes;
     return launch_topk(a, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+sa_status sa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, int32_t* idx, void* ws,
+                    size_t ws_bytes, void* stream) {
+    if (!problem_ok(p) || !idx || ((uintptr_t)idx & 3)) return SA_ERR_INVALID_ARG;
+    sa_status s = check_indexer(p, q_idx, k_idx, w);
+    if (s != SA_OK) return s;
+    if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SELECT))) != SA_OK) return s;
+    char* base = static_cast<char*>(ws);
+    return run_select(p, q_idx, k_idx, w, idx, reinterpret_cast<Status*>(base), base + kStatusBytes,
+                      (hipStream_t)stream);
 }
 
 sa_status sa_sparse_attn(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tensor V, const int32_t* idx, sa_tensor O,
@@ -352,30 +410,11 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SELECT_ATTEND))) != SA_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     char* base = static_cast<char*>(ws);
-    float* scores = reinterpret_cast<float*>(base + kStatusBytes);
-    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + kStatusBytes + scores_bytes(*p));
-    void* partial = base + kStatusBytes + scores_bytes(*p) + idx_bytes(*p);
-    void* tk_scratch = static_cast<char*>(partial) + align256(attn_partial_bytes(*p));
-
-    IndexerArgs ia;
-    ia.p = *p;
-    ia.q = q_idx; ia.k = k_idx; ia.w = w;
-    ia.scores = scores;
-    ia.row_stride = p->n_kv;
-    ia.fill_invisible = 0;  // the selection reads only the visible prefix of each row
-    ia.status = reinterpret_cast<Status*>(base);
-    if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
-
-    TopkArgs ta;
-    ta.p = *p;
-    ta.scores = scores;
-    ta.row_stride = p->n_kv;
-    ta.idx = idx;
-    ta.vals = nullptr;
-    ta.status = reinterpret_cast<Status*>(base);
-    ta.scratch = tk_scratch;
-    if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
-
+    // status word, selection (when the caller does not take it), split partials, selection region
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + kStatusBytes);
+    void* partial = base + kStatusBytes + idx_bytes(*p);
+    char* region = static_cast<char*>(partial) + align256(attn_partial_bytes(*p));
+    if ((s = run_select(p, q_idx, k_idx, w, idx, reinterpret_cast<Status*>(base), region, st)) != SA_OK) return s;
     return run_attn(p, Q, K, V, idx, O, lse, partial, st);
 }
 

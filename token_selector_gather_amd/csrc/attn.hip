@@ -264,9 +264,12 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // rows selected is read once into LDS (K rows as they are, V transposed), S = Q K^T and
 // O += P V run on MFMA (16x16x32 bf16), and unselected keys are masked to -inf before the
 // online softmax, so each row's result is the exact softmax over its own selected set.
-// Tiles no row selected are skipped.  Wave w owns query rows 16 w .. 16 w + 15.  With a
-// block table the tile's keys are read from their pool rows (kv_row), and a candidate on a
-// page outside the pools never enters the bitmap.
+// Tiles no row selected are skipped, and inside a tile only the keys that some row of the
+// block selected are read: the others enter LDS as zeros, so the value product (P = 0 for
+// them) never touches an unselected row, which may hold anything (padding, stale pool
+// rows, NaN).  Wave w owns query rows 16 w .. 16 w + 15.  With a block table the tile's keys
+// are read from their pool rows (kv_row), and a candidate on a page outside the pools never
+// enters the bitmap.
 namespace tile {
 constexpr int QR = 64;         // query rows per workgroup
 constexpr int KT = 64;         // keys per tile
@@ -274,16 +277,21 @@ constexpr int MAXN = 4096;     // longest history (bitmap words per row = MAXN /
 constexpr int D = 128;
 constexpr int KP = D + 8;      // padded K row (elements): conflict-free 16-byte reads
 constexpr int VP = KT + 8;     // padded V^T row
+// per row block: [0] active tile count, [1 .. KT] active tiles, then two words per list
+// slot: the union over the block's rows of that tile's selection bits
+constexpr int LIST = 1 + 3 * KT;
 }  // namespace tile
 
 // The selections of a batch's block of 64 query rows, shared by every head: a bitmap per
-// row (bit j of word j / 32 = position j selected) and the list of 64-key tiles any of the
-// rows selected.  One workgroup per (batch, row block); written to the workspace.
+// row (bit j of word j / 32 = position j selected), the list of 64-key tiles any of the
+// rows selected and, per listed tile, the union of the rows' selection bits.  One
+// workgroup per (batch, row block); written to the workspace.
 __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
     __shared__ __attribute__((aligned(16))) uint32_t bits[QR][NWORD];
-    __shared__ int s_L[QR], s_act[4][KT], s_maxL;
+    __shared__ int s_L[QR], s_maxL;
+    __shared__ uint32_t s_uni[4][KT][2];
     const sa_problem& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63;
     const int nqb = (p.n_q + QR - 1) / QR;
@@ -322,18 +330,28 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
     const int ntile = (s_maxL + KT - 1) / KT;
     {
         const int t = tid & 63, rq = tid >> 6;
-        uint32_t any = 0;
+        uint32_t u0 = 0, u1 = 0;
         if (t < ntile)
-            for (int r = 16 * rq; r < 16 * rq + 16; ++r) any |= bits[r][2 * t] | bits[r][2 * t + 1];
-        s_act[rq][t] = any != 0;
+            for (int r = 16 * rq; r < 16 * rq + 16; ++r) {
+                u0 |= bits[r][2 * t];
+                u1 |= bits[r][2 * t + 1];
+            }
+        s_uni[rq][t][0] = u0;
+        s_uni[rq][t][1] = u1;
     }
     __syncthreads();
-    int32_t* list = glist + (size_t)(b * nqb + qb) * (KT + 1);
+    int32_t* list = glist + (size_t)(b * nqb + qb) * LIST;
     if (tid < 64) {
-        const bool act = (s_act[0][lane] | s_act[1][lane] | s_act[2][lane] | s_act[3][lane]) != 0;
+        const uint32_t u0 = s_uni[0][lane][0] | s_uni[1][lane][0] | s_uni[2][lane][0] | s_uni[3][lane][0];
+        const uint32_t u1 = s_uni[0][lane][1] | s_uni[1][lane][1] | s_uni[2][lane][1] | s_uni[3][lane][1];
+        const bool act = (u0 | u1) != 0;
         const uint64_t m = __ballot(act);
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (act) list[1 + pos] = lane;
+        if (act) {
+            list[1 + pos] = lane;
+            list[1 + KT + 2 * pos] = (int32_t)u0;
+            list[2 + KT + 2 * pos] = (int32_t)u1;
+        }
         if (lane == 0) list[0] = __popcll(m);
     }
     // the rows' bitmaps, as 16-byte pieces
@@ -370,7 +388,7 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         b = (int)(rest / nqb);
         qb = nqb - 1 - (int)(rest % nqb);  // the longest (latest) row blocks first
     }
-    const int32_t* list = glist + (size_t)(b * nqb + qb) * (KT + 1);
+    const int32_t* list = glist + (size_t)(b * nqb + qb) * LIST;
     const int nt = __builtin_amdgcn_readfirstlane(list[0]);
     // with pages of at least 64 rows a 64-key tile lies inside one page: one table lookup per tile
     const bool tile_pages = a.block_table && a.page_shift >= 6;
@@ -405,9 +423,12 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
 
     for (int u = 0; u < nt; ++u) {
         const int k0 = __builtin_amdgcn_readfirstlane(list[1 + u]) * KT;
+        // keys of the tile that some row of the block selected (all visible, all in range)
+        const uint64_t uni = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(list[1 + KT + 2 * u]) |
+                             ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(list[2 + KT + 2 * u]) << 32);
         const int64_t tb = tile_pages ? kv_row(a, b, k0) : 0;
         auto row_of = [&](int key) -> int64_t {
-            if (key >= p.n_kv) return -1;
+            if (!((uni >> (key - k0)) & 1u)) return -1;
             if (tile_pages) return tb < 0 ? -1 : tb + (key - k0);
             return kv_row(a, b, key);
         };
@@ -1595,7 +1616,7 @@ static size_t tile_bits_bytes(const sa_problem& p) {
 }
 static size_t tile_ws_bytes(const sa_problem& p) {
     const size_t nqb = (size_t)(p.n_q + tile::QR - 1) / tile::QR;
-    return tile_bits_bytes(p) + (size_t)p.B * nqb * (tile::KT + 1) * sizeof(int32_t);
+    return tile_bits_bytes(p) + (size_t)p.B * nqb * tile::LIST * sizeof(int32_t);
 }
 
 bool attn_paged_ok(const AttnArgs& a) {

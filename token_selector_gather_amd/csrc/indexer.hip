@@ -21,6 +21,8 @@
 // clipped to zero by the ReLU: the VALU path uses (z > 0 ? z : 0*z); the matrix-core paths
 // use a one-instruction integer-max ReLU and either add z * 0 to each score, check the
 // inputs in a pre-pass (fused call), or mark rows and keys with non-finite inputs apart.
+#include <algorithm>
+
 #include "gfx950_mem.h"
 #include "sa_internal.h"
 
@@ -73,12 +75,12 @@ __device__ __forceinline__ float load_elem(const void* base, int dtype, int64_t 
 __global__ void __launch_bounds__(256) indexer_valu(IndexerArgs a) {
     extern __shared__ float smem[];
     const sa_problem& p = a.p;
-    const int row = blockIdx.x;
+    const int row = a.row0 + (int)blockIdx.x;
     const int b = row / p.n_q, i = row % p.n_q;
     const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int j = blockIdx.y * 256 + threadIdx.x;
-    float* out = a.scores + (int64_t)row * a.row_stride;
+    float* out = a.scores + (int64_t)(row - a.row0) * a.row_stride;
     if ((int)(blockIdx.y * 256) >= L) {
         if (a.fill_invisible && j < p.n_kv) out[j] = -INFINITY;
         return;
@@ -248,6 +250,332 @@ __global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, 
     }
 }
 
+// ------------------------------------------------------------ streaming selection
+// The fused score + select of the many-row layout keeps, per query row, a list of candidate
+// (key, position) pairs in the workgroup's own slice of the workspace instead of the row's
+// scores ("PaperTrace 2.2 · Fine-grained indexing", §2.1: score the history slice by slice,
+// keep local candidates and merge down to k; the result is the global top-k).  Keys are the
+// order-preserving uint32 images of the fp32 scores (-0 folded onto +0).  A score enters the
+// list only if its key is above the row's threshold tau, and the list stays in position
+// order (ballot ranks inside a tile, tiles in order).
+//
+// tau stays below the k-th largest key seen so far, so every key that can still be in the
+// row's top k is in the list (a key at or below tau has k larger keys before it).  It is
+// raised from a histogram of the list's keys kept in LDS: after the first chunk the row's
+// keys fix the bins (bin 0 = below `base`, bin b = [base + (b-1) 2^sh, base + b 2^sh), the
+// last bin open above), every append adds its key, and tau becomes the lowest key of the
+// bin that holds the k-th largest listed key, minus one.  When the list could overflow at
+// the next chunk, the keys at or below tau are dropped (one ordered pass; the bins below
+// tau's bin empty exactly).  If that frees too little (keys far outside the bins), the list
+// is cut to its exact top k and the bins are rebuilt around the cut.  At the end the exact
+// k-th key comes from the histogram and digits of its bin, and one ordered pass writes the
+// selection.  Passes over a list issue their loads in batches, so a pass costs a few
+// memory round trips.
+
+__device__ __forceinline__ uint32_t sel_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) == 0) u = 0;  // -0 == +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// The smallest score whose key is above tau (key > tau <=> score >= sel_floor(tau), NaN
+// aside), so the hot loop compares floats and computes keys only for appended scores.
+__device__ __forceinline__ float sel_floor(uint32_t tau) {
+    if (tau == 0u) return -INFINITY;  // nothing is cut yet
+    const uint32_t k = tau + 1u;
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// threadIdx.x through an opaque move: values derived from it are recomputed where they are
+// used instead of being hoisted out of the persistent loop and kept live across the MFMA loop
+__device__ __forceinline__ int opaque_tid() {
+    int t;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+    return t;
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Cross-lane steps on DPP (no LDS round trip): row shifts with zero fill, row broadcasts,
+// quad / half-row / row mirrors.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, true);
+}
+// wave-wide exclusive prefix sum and total: inclusive scans inside each 16-lane row by
+// shifts of 1, 2, 4 and 8, then row 0's total into rows 1 and 3 and rows 0-1's into 2 and 3
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t x, int lane, uint32_t& total) {
+    (void)lane;
+    uint32_t incl = x;
+    incl += dpp_u32<0x111>(incl);       // row_shr:1
+    incl += dpp_u32<0x112>(incl);       // row_shr:2
+    incl += dpp_u32<0x114>(incl);       // row_shr:4
+    incl += dpp_u32<0x118>(incl);       // row_shr:8
+    incl += dpp_u32<0x142, 0xa>(incl);  // row_bcast:15
+    incl += dpp_u32<0x143, 0xc>(incl);  // row_bcast:31
+    total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    return incl - x;
+}
+// wave-uniform minimum / maximum: inside each row by mirrors, then the four rows' lanes
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));
+    const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return min(a, b);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
+// Bins of a row's histogram: 0 below base, b in [1, NB - 1) for [base + (b-1) 2^sh, base +
+// b 2^sh), NB - 1 for everything above.
+template <int NB>
+__device__ __forceinline__ int key_bin(uint32_t key, uint32_t base, uint32_t sh) {
+    if (key < base) return 0;
+    return (int)min(((key - base) >> sh) + 1u, (uint32_t)(NB - 1));
+}
+__device__ __forceinline__ uint32_t bin_lowest(int b, uint32_t base, uint32_t sh) {  // b >= 1
+    const uint64_t e = (uint64_t)base + ((uint64_t)(b - 1) << sh);
+    return e > 0xffffffffull ? 0xffffffffu : (uint32_t)e;
+}
+// bin width for keys spanning [lo, hi]: the span takes at most NB / 2 bins, the rest is
+// room above
+template <int NB>
+__device__ __forceinline__ uint32_t bin_shift(uint32_t lo, uint32_t hi) {
+    const uint32_t span = hi - lo;
+    uint32_t sh = 0;
+    while ((span >> sh) >= (uint32_t)(NB / 2)) ++sh;
+    return sh;
+}
+
+// In an NB-bin histogram (bins ascending in key), the bin holding the need-th largest
+// counted key and the number of keys in higher bins (need <= total).  Lane l reads bins
+// NB - 1 - 4 l down to NB - 4 - 4 l.
+template <int NB>
+__device__ __forceinline__ void sel_find_bin(const uint32_t* h, uint32_t need, int lane, int& bin, uint32_t& above) {
+    static_assert(NB % 4 == 0 && NB <= 256, "four bins per lane");
+    uint4 c = make_uint4(0u, 0u, 0u, 0u);
+    if (4 * lane < NB) c = *reinterpret_cast<const uint4*>(h + NB - 4 - 4 * lane);
+    const uint32_t cnt[4] = {c.w, c.z, c.y, c.x};  // bins NB - 1 - 4 lane - e, e = 0 .. 3
+    const uint32_t local = c.x + c.y + c.z + c.w;
+    uint32_t total;
+    const uint32_t excl = wave_excl_scan(local, lane, total);
+    int bl = 0;
+    uint32_t ab = 0, run = excl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (bl == 0 && run + cnt[e] >= need) {
+            bl = NB - 4 * lane - e;  // bin + 1
+            ab = run;
+        }
+        run += cnt[e];
+    }
+    const uint64_t m = __ballot(excl < need && excl + local >= need);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    bin = max(__builtin_amdgcn_readlane(bl, src) - 1, 0);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+}
+
+// Scratch of one wave for exact thresholds: a 256-bin digit histogram and a short list.
+struct SelScratch {
+    uint32_t hist[256];
+    uint32_t list[64];
+};
+
+constexpr int kSelU = 8;  // 16-byte loads per lane in flight in a pass over a list
+
+// A batch of up to kSelU x 256 keys from entry e0 (lane: 4 consecutive keys per load).
+__device__ __forceinline__ void sel_load(const uint32_t* keys, int n, int e0, int lane, uint4 (&v)[kSelU]) {
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+        const int e = e0 + 256 * u + 4 * lane;
+        if (e + 3 < n) {
+            v[u] = *reinterpret_cast<const uint4*>(keys + e);
+        } else {
+            v[u].x = e < n ? keys[e] : 0u;
+            v[u].y = e + 1 < n ? keys[e + 1] : 0u;
+            v[u].z = e + 2 < n ? keys[e + 2] : 0u;
+            v[u].w = e + 3 < n ? keys[e + 3] : 0u;
+        }
+    }
+}
+
+// Exact threshold of the top `need` keys among the keys of [lo, lo + 2^bits) (nB of them),
+// refining the digit below `bits` (a 256-bin histogram per step, or the short list once the
+// open bin holds at most 64 keys).  tu: relative prefix so far.  Returns T and the number
+// of keys equal to T that the selection keeps.
+__device__ __forceinline__ void sel_refine(const uint32_t* keys, int n, uint32_t lo, int bits, uint32_t tu, uint32_t nB,
+                                           uint32_t need, SelScratch* sc, int lane, uint32_t& T, uint32_t& need_eq) {
+    while (bits > 0) {
+        if (nB <= 64u) {
+            // the open bin's keys to a list, ranked by one lane each
+            const uint32_t pref = (uint32_t)((uint64_t)tu >> bits);
+            uint32_t cntl = 0;
+            for (int e0 = 0; e0 < n; e0 += 256 * kSelU) {
+                uint4 v[kSelU];
+                sel_load(keys, n, e0, lane, v);
+#pragma unroll
+                for (int u = 0; u < kSelU; ++u) {
+                    const int e = e0 + 256 * u + 4 * lane;
+                    const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    bool hit[4];
+                    uint32_t c = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        hit[i] = e + i < n && k4[i] >= lo && (uint32_t)((uint64_t)(k4[i] - lo) >> bits) == pref;
+                        c += hit[i];
+                    }
+                    uint32_t tot;
+                    uint32_t at = cntl + wave_excl_scan(c, lane, tot);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (hit[i]) sc->list[at++] = k4[i] - lo;
+                    cntl += tot;
+                }
+            }
+            wait_lgkmcnt0();
+            const uint32_t c = lane < (int)nB ? sc->list[lane] : 0u;
+            uint32_t gt = 0, eq = 0;
+            for (uint32_t t = 0; t < nB; ++t) {
+                const uint32_t ct = sc->list[t];
+                gt += ct > c;
+                eq += ct == c;
+            }
+            const uint64_t m = __ballot(lane < (int)nB && gt < need && need <= gt + eq);
+            const int src = m ? __builtin_ctzll(m) : 0;
+            tu = (uint32_t)__builtin_amdgcn_readlane((int)c, src);
+            need -= (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+            bits = 0;
+            break;
+        }
+        const int d = bits < 8 ? bits : 8;
+        bits -= d;
+        const uint32_t pref = (uint32_t)((uint64_t)tu >> (bits + d)), dmask = (1u << d) - 1u;
+        *reinterpret_cast<uint4*>(sc->hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        for (int e0 = 0; e0 < n; e0 += 256 * kSelU) {
+            uint4 v[kSelU];
+            sel_load(keys, n, e0, lane, v);
+#pragma unroll
+            for (int u = 0; u < kSelU; ++u) {
+                const int e = e0 + 256 * u + 4 * lane;
+                const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t r = k4[i] - lo;
+                    if (e + i < n && k4[i] >= lo && (uint32_t)((uint64_t)r >> (bits + d)) == pref)
+                        atomicAdd(&sc->hist[(r >> bits) & dmask], 1u);
+                }
+            }
+        }
+        wait_lgkmcnt0();
+        int bin;
+        uint32_t above;
+        sel_find_bin<256>(sc->hist, need, lane, bin, above);
+        nB = sc->hist[bin];
+        tu |= (uint32_t)bin << bits;
+        need -= above;
+    }
+    T = lo + tu;
+    need_eq = need;
+}
+
+// Exact threshold of the top K of n keys (K < n) with no other information: the key range
+// (a pass), then the refinement over the whole range.  Also returns the largest key.
+__device__ __forceinline__ void sel_threshold(const uint32_t* keys, int n, uint32_t K, SelScratch* sc, int lane,
+                                              uint32_t& T, uint32_t& need_eq, uint32_t& hi) {
+    uint32_t lo = 0xffffffffu;
+    hi = 0u;
+    for (int e0 = 0; e0 < n; e0 += 256 * kSelU) {
+        uint4 v[kSelU];
+        sel_load(keys, n, e0, lane, v);
+#pragma unroll
+        for (int u = 0; u < kSelU; ++u) {
+            const int e = e0 + 256 * u + 4 * lane;
+            const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (e + i < n) {
+                    lo = min(lo, k4[i]);
+                    hi = max(hi, k4[i]);
+                }
+        }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    const uint32_t range = hi - lo;
+    const int bits = range == 0 ? 0 : 32 - __clz((int)range);  // every key has (key - lo) >> bits == 0
+    sel_refine(keys, n, lo, bits, 0u, (uint32_t)n, K, sc, lane, T, need_eq);
+}
+
+// Ordered compaction of a list: keeps the entries with key > T and the first need_eq
+// entries with key == T (T = 0xffffffff with need_eq = 0 is never used: keys > T do not
+// exist), writing them to (okeys, opos) -- which may be the source arrays -- or only the
+// positions when okeys is null.  Returns the number kept.
+__device__ __forceinline__ uint32_t sel_compact(uint32_t* keys, int32_t* pos, int n, uint32_t T, uint32_t need_eq,
+                                                uint32_t* okeys, int32_t* opos, int lane) {
+    constexpr int U = kSelU / 2;
+    uint32_t run_gt = 0, run_eq = 0;
+    for (int e0 = 0; e0 < n; e0 += 256 * U) {
+        uint4 kv[U], pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + 256 * u + 4 * lane;
+            if (e + 3 < n) {
+                kv[u] = *reinterpret_cast<const uint4*>(keys + e);
+                pv[u] = *reinterpret_cast<const uint4*>(pos + e);
+            } else {
+                kv[u].x = e < n ? keys[e] : 0u;
+                kv[u].y = e + 1 < n ? keys[e + 1] : 0u;
+                kv[u].z = e + 2 < n ? keys[e + 2] : 0u;
+                kv[u].w = e + 3 < n ? keys[e + 3] : 0u;
+                pv[u].x = e < n ? pos[e] : 0;
+                pv[u].y = e + 1 < n ? pos[e + 1] : 0;
+                pv[u].z = e + 2 < n ? pos[e + 2] : 0;
+                pv[u].w = e + 3 < n ? pos[e + 3] : 0;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + 256 * u + 4 * lane;
+            const uint32_t k4[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+            const int32_t p4[4] = {(int32_t)pv[u].x, (int32_t)pv[u].y, (int32_t)pv[u].z, (int32_t)pv[u].w};
+            uint32_t cg = 0, ce = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cg += e + i < n && k4[i] > T;
+                ce += e + i < n && k4[i] == T;
+            }
+            uint32_t tot;
+            const uint32_t ex = wave_excl_scan(cg | (ce << 16), lane, tot);
+            uint32_t G = run_gt + (ex & 0xffffu), E = run_eq + (ex >> 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool gt = e + i < n && k4[i] > T, eq = e + i < n && k4[i] == T;
+                if (gt || (eq && E < need_eq)) {
+                    const uint32_t slot = G + (E < need_eq ? E : need_eq);
+                    if (okeys) okeys[slot] = k4[i];
+                    opos[slot] = p4[i];
+                }
+                G += gt;
+                E += eq;
+            }
+            run_gt += tot & 0xffffu;
+            run_eq += tot >> 16;
+        }
+    }
+    return run_gt + (run_eq < need_eq ? run_eq : need_eq);
+}
+
 // ------------------------------------------------------------------ indexer_pf
 // Prefill layout for many query rows: a workgroup takes QB = 4 * 128 / H consecutive query
 // rows of one batch and walks their causal history once, in chunks of 128 keys that are
@@ -255,8 +583,17 @@ __global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, 
 // keeps the A fragments of its 128 (query, head) rows (eight 16-row M-tiles) in registers,
 // so each 16-key B fragment read from LDS feeds 8 x KSTEPS MFMAs, and the ReLU /
 // head-weighting / head-sum arithmetic is about 2.5 VALU instructions per MFMA.
-template <int KSTEPS, bool KE4M3, int H>
-__global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
+// SEL: the fused score + select.  The grid is persistent (at most kSelSlots workgroups,
+// each with its own candidate lists); workgroup w takes the blocks of rows w, 2G - 1 - w,
+// 2G + w, ... of the list ordered by history length (G = grid size), which evens out the
+// causal triangle.  Scores are not stored: each lane group appends its query's scores
+// above the row threshold to the row's candidate list and histogram (see the streaming
+// selection above); at chunk boundaries each wave raises its rows' thresholds and drops
+// dead entries when a list is nearly full, and at the end it writes the selection.  The
+// non-finite check of the index inputs is done on the way (query fragments, weights, and
+// each key chunk as it is widened) and reported in the status word.
+template <int KSTEPS, bool KE4M3, int H, bool SEL>
+__global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, SelectArgs sel) {
     static_assert(H >= 16 && H <= 64, "one query per 16-row M-tile");
     constexpr int D = 32 * KSTEPS;
     constexpr int QW = 128 / H;              // queries per wave
@@ -268,16 +605,44 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
     constexpr int RB = D * (KE4M3 ? 1 : 2);  // bytes per key row in memory
     constexpr int PPR = RB / 16;             // 16-byte pieces per key row
     constexpr int PPT = CK * PPR / 256;      // pieces per thread per chunk
+    constexpr int NZ = QW > 4 ? 2 : 1;       // queries per lane group
     static_assert(PPT >= 1 && PPT * 256 == CK * PPR, "chunk pieces must split evenly over the threads");
+    // SEL: per-row key histograms in the LDS left for two workgroups per CU
+    constexpr int NBR0 = ((81920 - 2 * CK * KP - 64 - 4 * (int)sizeof(SelScratch)) / QB - 8) / 4;
+    constexpr int NBR = NBR0 >= 256 ? 256 : (NBR0 / 16) * 16;
+    static_assert(!SEL || NBR >= 32, "row histograms");
     __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][CK * KP];
     __shared__ int s_L[QB];
+    __shared__ __attribute__((aligned(16))) SelScratch s_sel[SEL ? 4 : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t s_rh[SEL ? QB : 1][SEL ? NBR : 4];  // row histograms
+    __shared__ uint32_t s_rp[SEL ? QB : 1][2];                                         // bins: base, shift
 
     const sa_problem& p = a.p;
     const int lane = threadIdx.x & 63, l15 = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long wg = blockIdx.x;
-    const int qb = p.causal ? n_qb - 1 - (int)(wg % n_qb) : (int)(wg % n_qb);  // longest histories first
-    const int b = (int)(wg / n_qb);
+    const long n_items = (long)p.B * n_qb;
+    const int K = p.k;
+    bool bad_input = false;  // SEL: a non-finite index input this thread saw
+
+    for (long rnd = 0;; ++rnd) {
+    long wg;
+    int b, qb;
+    if constexpr (SEL) {
+        const long base = rnd * (long)gridDim.x;
+        if (base >= n_items) break;
+        wg = base + ((rnd & 1) ? (long)gridDim.x - 1 - (long)blockIdx.x : (long)blockIdx.x);
+        if (wg >= n_items) continue;
+        // batches interleaved so that the list runs from the longest histories down
+        const long r = wg / p.B;
+        b = (int)(wg % p.B);
+        qb = p.causal ? n_qb - 1 - (int)r : (int)r;
+        __syncthreads();  // the previous block's readers of s_L are done
+    } else {
+        if (rnd > 0) break;
+        wg = blockIdx.x;
+        qb = p.causal ? n_qb - 1 - (int)(wg % n_qb) : (int)(wg % n_qb);  // longest histories first
+        b = (int)(wg / n_qb);
+    }
     const int i0 = qb * QB;
     const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     if (threadIdx.x < QB) s_L[threadIdx.x] = i0 + (int)threadIdx.x < p.n_q ? visible_len(R, b, i0 + threadIdx.x) : 0;
@@ -292,7 +657,7 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
     for (int q = 0; q < QW; ++q) Lq[q] = s_L[QW * wv + q];
     const int nch = (Lwg + CK - 1) / CK;
 
-    if (a.fill_invisible) {
+    if (!SEL && a.fill_invisible) {
         // -inf for the positions past the computed chunks, issued first so that the stores
         // drain while the chunks are computed; 16-byte stores where the rows allow it
         const int start = min(nch * CK, p.n_kv);
@@ -308,6 +673,19 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
             for (int j = head + 4 * lane; j < body; j += 256) *reinterpret_cast<float4*>(row + j) = ninf;
             for (int j = body + lane; j < p.n_kv; j += 64) row[j] = -INFINITY;
         }
+    }
+
+    // SEL: candidate lists of this wave's queries (keys, then positions, cap entries each)
+    // and the per-lane state of the query of this lane's group: list length and threshold
+    uint32_t* slot_base = SEL ? sel.buf + (size_t)blockIdx.x * QB * 2 * sel.cap : nullptr;
+    auto row_keys = [&](int q) { return slot_base + (size_t)(QW * wv + q) * 2 * sel.cap; };
+    uint32_t cnt[NZ], tau[NZ];
+    float tauf[NZ];  // sel_floor(tau)
+#pragma unroll
+    for (int z = 0; z < NZ; ++z) {
+        cnt[z] = 0;
+        tau[z] = 0;
+        tauf[z] = -INFINITY;
     }
 
     if (nch > 0) {
@@ -332,7 +710,7 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
         bool qbad[QW];
 #pragma unroll
         for (int q = 0; q < QW; ++q) qbad[q] = false;
-        if (a.fix_nonfinite) {
+        if (SEL || a.fix_nonfinite) {
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 bool bad = false;
@@ -341,7 +719,17 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
                     const uint4 u = __builtin_bit_cast(uint4, av[m][s2]);
                     bad |= bf16x2_nonfinite(u.x) | bf16x2_nonfinite(u.y) | bf16x2_nonfinite(u.z) | bf16x2_nonfinite(u.w);
                 }
-                if (__ballot(bad) != 0) qbad[m / TPQ] = true;
+                if constexpr (SEL) {
+                    int Lm = 0;
+#pragma unroll
+                    for (int q = 0; q < QW; ++q)
+                        if (q == m / TPQ) Lm = Lq[q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bad |= !isfinite(wvv[m][e]);
+                    bad_input |= bad && Lm > 0;
+                } else {
+                    if (__ballot(bad) != 0) qbad[m / TPQ] = true;
+                }
             }
         }
         const uint32_t kstride = (uint32_t)(a.k.s1 * (KE4M3 ? 1 : 2));
@@ -350,9 +738,10 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
             (int)((uint32_t)Lwg * kstride), 0x00020000);
         uint4 stage[PPT];
         auto fetch = [&](int c) {
+            const int tid = SEL ? opaque_tid() : (int)threadIdx.x;
 #pragma unroll
             for (int e = 0; e < PPT; ++e) {
-                const int u = threadIdx.x + 256 * e;
+                const int u = tid + 256 * e;
                 const int r = u / PPR, col = u % PPR;
                 const int j = c * CK + r;
                 const uint32_t off = j < Lwg ? (uint32_t)j * kstride + 16u * col : 0x80000000u;
@@ -361,11 +750,20 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
             }
         };
         auto commit = [&](int buf) {
+            const int tid = SEL ? opaque_tid() : (int)threadIdx.x;
 #pragma unroll
             for (int e = 0; e < PPT; ++e) {
-                const int u = threadIdx.x + 256 * e;
+                const int u = tid + 256 * e;
                 const int r = u / PPR, col = u % PPR;
                 uint8_t* dst = &kbuf[buf][r * KP + (KE4M3 ? 32 : 16) * col];
+                if constexpr (SEL) {  // keys past Lwg were loaded as zeros
+                    if constexpr (KE4M3)
+                        bad_input |= e4m3x4_nan(stage[e].x) | e4m3x4_nan(stage[e].y) | e4m3x4_nan(stage[e].z) |
+                                     e4m3x4_nan(stage[e].w);
+                    else
+                        bad_input |= bf16x2_nonfinite(stage[e].x) | bf16x2_nonfinite(stage[e].y) |
+                                     bf16x2_nonfinite(stage[e].z) | bf16x2_nonfinite(stage[e].w);
+                }
                 if constexpr (KE4M3) {
                     const uint32_t w4[4] = {stage[e].x, stage[e].y, stage[e].z, stage[e].w};
                     uint32_t o[8];
@@ -384,20 +782,20 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
             }
         };
         // scores of this wave: lane group g stores query g (and g + 4 when QW = 8)
-        float* srow[QW > 4 ? 2 : 1];
-        int Ls[QW > 4 ? 2 : 1];
-        bool qok[QW > 4 ? 2 : 1];
+        float* srow[NZ];
+        int Ls[NZ];
+        bool qok[NZ];
 #pragma unroll
-        for (int z = 0; z < (QW > 4 ? 2 : 1); ++z) {
+        for (int z = 0; z < NZ; ++z) {
             const int q = g + 4 * z;
             const int qi = iw + q;
             qok[z] = q < QW && qi < p.n_q;
-            srow[z] = a.scores + (int64_t)(b * p.n_q + (qok[z] ? qi : 0)) * a.row_stride;
+            srow[z] = SEL ? nullptr : a.scores + (int64_t)(b * p.n_q + (qok[z] ? qi : 0)) * a.row_stride;
             int Lz = 0;
 #pragma unroll
             for (int qq = 0; qq < QW; ++qq)
                 if (qq == q) Lz = Lq[qq];
-            Ls[z] = Lz;
+            Ls[z] = qok[z] ? Lz : 0;
         }
         fetch(0);
         commit(0);
@@ -434,22 +832,147 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb) {
                 }
                 const int j = c * CK + nt * 16 + l15;
 #pragma unroll
-                for (int z = 0; z < (QW > 4 ? 2 : 1); ++z) {
+                for (int z = 0; z < NZ; ++z) {
                     float v = 0.f;
 #pragma unroll
                     for (int q = 0; q < QW; ++q)
                         if (q == g + 4 * z) v = sc[q];
                     const bool vis = j < Ls[z];
-                    bool qb = false;
+                    if constexpr (SEL) {
+                        // append above-threshold scores in position order (lanes of a group
+                        // hold consecutive keys)
+                        const bool pass = vis && v >= tauf[z];
+                        const uint64_t mk = __ballot(pass);
+                        const uint32_t gm = (uint32_t)(mk >> (16 * g)) & 0xffffu;
+                        if (pass) {
+                            const uint32_t key = sel_key(v);
+                            const uint32_t slot = cnt[z] + (uint32_t)__builtin_popcount(gm & ((1u << l15) - 1u));
+                            uint32_t* lk = row_keys(g + 4 * z);
+                            lk[slot] = key;
+                            lk[sel.cap + slot] = (uint32_t)j;
+                            if (c > 0) {  // the row's bins exist from the second chunk on
+                                const int r = QW * wv + g + 4 * z;
+                                atomicAdd(&s_rh[r][key_bin<NBR>(key, s_rp[r][0], s_rp[r][1])], 1u);
+                            }
+                        }
+                        cnt[z] += (uint32_t)__builtin_popcount(gm);
+                    } else {
+                        bool qb = false;
 #pragma unroll
-                    for (int q = 0; q < QW; ++q)
-                        if (q == g + 4 * z) qb = qbad[q];
-                    if (qok[z] && j < p.n_kv && (vis || a.fill_invisible)) srow[z][j] = vis ? (qb ? __builtin_nanf("") : v) : -INFINITY;
+                        for (int q = 0; q < QW; ++q)
+                            if (q == g + 4 * z) qb = qbad[q];
+                        if (qok[z] && j < p.n_kv && (vis || a.fill_invisible)) srow[z][j] = vis ? (qb ? __builtin_nanf("") : v) : -INFINITY;
+                    }
                 }
             }
             if (c + 1 < nch) commit(buf ^ 1);
             __syncthreads();
+            if constexpr (SEL) {
+                // per row of this wave: bins after the first chunk, a higher threshold from
+                // the histogram, and dead entries dropped when the next chunk could overflow
+                if (c + 1 < nch) {
+                    const int ln = opaque_tid() & 63;
+#pragma unroll
+                    for (int q = 0; q < QW; ++q) {
+                        const int z = q >> 2, gq = q & 3, r = QW * wv + q;
+                        uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cnt[z], 16 * gq);
+                        uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tau[z], 16 * gq);
+                        uint32_t* keys = row_keys(q);
+                        int32_t* pos = reinterpret_cast<int32_t*>(keys + sel.cap);
+                        if (c == 0) {  // every visible key of the first chunk is listed (n <= 128)
+                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                            const uint32_t k0 = ln < (int)n ? keys[ln] : 0xffffffffu;
+                            const uint32_t k1 = ln + 64 < (int)n ? keys[ln + 64] : 0xffffffffu;
+                            const uint32_t lo = wave_min(min(k0, k1));
+                            const uint32_t hi = wave_max(max(ln < (int)n ? k0 : 0u, ln + 64 < (int)n ? k1 : 0u));
+                            const uint32_t sh = n ? bin_shift<NBR>(lo, hi) : 0u;
+                            if (ln == 0) {
+                                s_rp[r][0] = lo;
+                                s_rp[r][1] = sh;
+                            }
+                            if (4 * ln < NBR) *reinterpret_cast<uint4*>(&s_rh[r][4 * ln]) = make_uint4(0u, 0u, 0u, 0u);
+                            if (ln < (int)n) atomicAdd(&s_rh[r][key_bin<NBR>(k0, lo, sh)], 1u);
+                            if (ln + 64 < (int)n) atomicAdd(&s_rh[r][key_bin<NBR>(k1, lo, sh)], 1u);
+                            wait_lgkmcnt0();
+                        }
+                        const uint32_t base = s_rp[r][0], sh = s_rp[r][1];
+                        const bool full = n + CK > (uint32_t)sel.cap;
+                        if (n >= (uint32_t)K && ((c & 1) == 0 || full)) {  // every other chunk, or before a cut
+                            int bk;
+                            uint32_t above;
+                            sel_find_bin<NBR>(s_rh[r], (uint32_t)K, ln, bk, above);
+                            if (bk >= 1) t = max(t, bin_lowest(bk, base, sh) - 1u);
+                        }
+                        if (full) {
+                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's appends have landed
+                            n = sel_compact(keys, pos, (int)n, t, 0u, keys, pos, ln);  // keys > t
+                            const int bt = key_bin<NBR>(t + 1u, base, sh);  // the bins below hold keys <= t
+                            for (int e = ln; e < bt; e += 64) s_rh[r][e] = 0u;
+                            if (n + CK > (uint32_t)sel.cap) {
+                                // keys far outside the bins: cut to the exact top k, new bins from there
+                                uint32_t T, need_eq, hi;
+                                sel_threshold(keys, (int)n, (uint32_t)K, &s_sel[wv], ln, T, need_eq, hi);
+                                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                                n = sel_compact(keys, pos, (int)n, T, need_eq, keys, pos, ln);
+                                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                                const uint32_t sh2 = bin_shift<NBR>(T, hi);
+                                if (ln == 0) {
+                                    s_rp[r][0] = T;
+                                    s_rp[r][1] = sh2;
+                                }
+                                for (int e = ln; e < NBR; e += 64) s_rh[r][e] = 0u;
+                                for (int e = ln; e < (int)n; e += 64) atomicAdd(&s_rh[r][key_bin<NBR>(keys[e], T, sh2)], 1u);
+                                t = T > 0u ? T - 1u : 0u;
+                            }
+                            wait_lgkmcnt0();
+                        }
+                        if (g == gq) {
+                            cnt[z] = n;
+                            tau[z] = t;
+                            tauf[z] = sel_floor(t);
+                        }
+                    }
+                }
+            }
         }
+    }
+    if constexpr (SEL) {
+        // the selection of each of this wave's rows, in ascending position, -1 padded: the
+        // k-th key from the histogram's bin and digits of it, then one ordered pass
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int ln = opaque_tid() & 63;
+        const bool binned = nch > 1;  // the bins were made after the first of several chunks
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+            const int qi = iw + q;
+            if (qi >= p.n_q) break;
+            const int z = q >> 2, gq = q & 3, r = QW * wv + q;
+            int32_t* out = sel.idx + ((int64_t)b * p.n_q + qi) * K;
+            const uint32_t n = Lq[q] > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)cnt[z], 16 * gq) : 0u;
+            uint32_t* keys = row_keys(q);
+            int32_t* pos = reinterpret_cast<int32_t*>(keys + sel.cap);
+            if (n <= (uint32_t)K) {
+                for (int e = ln; e < K; e += 64) out[e] = e < (int)n ? pos[e] : -1;
+            } else {
+                uint32_t T, need_eq;
+                int bk = 0;
+                uint32_t above = 0;
+                if (binned) sel_find_bin<NBR>(s_rh[r], (uint32_t)K, ln, bk, above);
+                if (binned && bk >= 1 && bk < NBR - 1) {
+                    const uint32_t base = s_rp[r][0], sh = s_rp[r][1];
+                    sel_refine(keys, (int)n, bin_lowest(bk, base, sh), (int)sh, 0u, s_rh[r][bk], (uint32_t)K - above,
+                               &s_sel[wv], ln, T, need_eq);
+                } else {
+                    uint32_t hi;
+                    sel_threshold(keys, (int)n, (uint32_t)K, &s_sel[wv], ln, T, need_eq, hi);
+                }
+                sel_compact(keys, pos, (int)n, T, need_eq, nullptr, out, ln);
+            }
+        }
+    }
+    }  // rounds
+    if constexpr (SEL) {
+        if (__ballot(bad_input) != 0 && (threadIdx.x & 63) == 0) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
     }
 }
 
@@ -751,10 +1274,72 @@ __global__ void __launch_bounds__(256) index_key_fix(IndexerArgs a) {
 
 }  // namespace
 
+// The fused score + select runs on the many-row prefill layout: bf16 index queries, bf16 or
+// e4m3 index keys, 16 / 32 / 64 index heads of width 64 or 128, and enough blocks of query
+// rows to fill the chip.  A candidate list holds min(4k + 512, n_kv + 128) entries: room
+// for the k(1 + ln(L / k)) or so keys a row of L positions appends when its scores come in
+// no particular order, so that lists are rarely cut before the end, and never less than k
+// plus one chunk of keys (n_kv >= k) or the whole history (n_kv < k).
+namespace {
+int sel_qb(const sa_problem& p) { return 4 * 128 / p.Hidx; }
+int sel_cap(const sa_problem& p) {
+    const long c = std::min(4L * p.k + 512, (long)p.n_kv + 128);
+    return (int)((c + 63) & ~63L);
+}
+long sel_slots(const sa_problem& p) {
+    const long items = (long)p.B * ((p.n_q + sel_qb(p) - 1) / sel_qb(p));
+    return std::min(items, (long)kSelSlots);
+}
+}  // namespace
+
+bool select_fused_shape_ok(const sa_problem& p) {
+    const int H = p.Hidx, D = p.d_idx;
+    if (!(H == 16 || H == 32 || H == 64) || !(D == 64 || D == 128)) return false;
+    const long rows = (long)p.B * p.n_q;
+    if (rows < 512 || (H == 64 && rows < 1024)) return false;  // the few-row and decode layouts
+    const long n_qb = (p.n_q + sel_qb(p) - 1) / sel_qb(p);
+    return (long)p.B * n_qb >= 512;
+}
+
+bool select_fused_ok(const sa_problem& p, int q_dtype, int k_dtype) {
+    return q_dtype == SA_BF16 && (k_dtype == SA_BF16 || k_dtype == SA_FP8_E4M3) && select_fused_shape_ok(p);
+}
+
+size_t select_fused_bytes(const sa_problem& p) {
+    return (size_t)sel_slots(p) * sel_qb(p) * 2 * (size_t)sel_cap(p) * sizeof(uint32_t);
+}
+
+hipError_t launch_select_fused(const IndexerArgs& a, int32_t* idx, void* buf, hipStream_t s) {
+    const sa_problem& p = a.p;
+    if (!select_fused_ok(p, a.q.dtype, a.k.dtype) || !a.status) return hipErrorInvalidValue;
+    SelectArgs sel;
+    sel.buf = static_cast<uint32_t*>(buf);
+    sel.cap = sel_cap(p);
+    sel.idx = idx;
+    const int QB = sel_qb(p);
+    const int n_qb = (p.n_q + QB - 1) / QB;
+    const dim3 grid((unsigned)sel_slots(p)), block(256);
+    const bool e4 = a.k.dtype == SA_FP8_E4M3;
+    IndexerArgs af = a;
+    af.fill_invisible = 0;
+    af.fix_nonfinite = 0;
+#define SA_SEL(KS, E4, HH)                                                                                    \
+    if (p.Hidx == HH) {                                                                                       \
+        hipLaunchKernelGGL((indexer_pf<KS, E4, HH, true>), grid, block, 0, s, af, n_qb, sel);                 \
+        return hipGetLastError();                                                                             \
+    }
+#define SA_SEL_H(KS, E4) do { SA_SEL(KS, E4, 16) SA_SEL(KS, E4, 32) SA_SEL(KS, E4, 64) } while (0)
+    if (p.d_idx == 64) { if (e4) SA_SEL_H(2, true); else SA_SEL_H(2, false); }
+    else { if (e4) SA_SEL_H(4, true); else SA_SEL_H(4, false); }
+#undef SA_SEL_H
+#undef SA_SEL
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     const sa_problem& p = a.p;
     const int H = p.Hidx, D = p.d_idx;
-    const bool mfma_ok = a.q.dtype == SA_BF16 && (a.k.dtype == SA_BF16 || a.k.dtype == SA_FP8_E4M3) &&
+    const bool mfma_ok = a.nrows == 0 && a.q.dtype == SA_BF16 && (a.k.dtype == SA_BF16 || a.k.dtype == SA_FP8_E4M3) &&
                          (H == 4 || H == 8 || H == 16 || H == 32 || H == 64) &&
                          (D == 32 || D == 64 || D == 128);
     if (mfma_ok) {
@@ -799,7 +1384,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
                 const dim3 gk((unsigned)max(1L, min(512L, 65536L / p.B)), p.B);
 #define SA_IDXPF(KS, E4, HH)                                                                                  \
     if (H == HH) {                                                                                            \
-        hipLaunchKernelGGL((indexer_pf<KS, E4, HH>), gp, bp, 0, s, af, n_qb);                                 \
+        hipLaunchKernelGGL((indexer_pf<KS, E4, HH, false>), gp, bp, 0, s, af, n_qb, SelectArgs());            \
         if (!fast) hipLaunchKernelGGL(index_key_fix, gk, dim3(256), 0, s, af);                                \
         return hipGetLastError();                                                                             \
     }
@@ -836,7 +1421,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
 #undef SA_IDX3
         return hipGetLastError();
     }
-    dim3 grid(p.B * p.n_q, (p.n_kv + 255) / 256);
+    dim3 grid(a.nrows > 0 ? a.nrows : p.B * p.n_q, (p.n_kv + 255) / 256);
     size_t shm = sizeof(float) * ((size_t)H * D + H);
     hipLaunchKernelGGL(indexer_valu, grid, dim3(256), shm, s, a);
     return hipGetLastError();

@@ -49,8 +49,25 @@ struct IndexerArgs {
     int fix_nonfinite = 0;  // set by the launcher: the plain-max kernel writes NaN for query rows
                             // with non-finite inputs, and a later pass for such keys
     const int32_t* row_len = nullptr;  // explicit visible length per row (see Rows)
+    int row0 = 0, nrows = 0;  // nrows > 0: only flat rows [row0, row0 + nrows), whose scores start at
+                              // `scores` (the plain vector path only)
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+
+// Fused score + select for many query rows (the prefill layout of the indexer with a
+// streaming top-k instead of stored scores).  A persistent grid of at most kSelSlots
+// workgroups; workgroup w keeps the candidate lists of its rows in slice w of `buf`.
+constexpr int kSelSlots = 512;
+struct SelectArgs {
+    uint32_t* buf = nullptr;  // select_fused_bytes(p) bytes
+    int cap = 0;              // candidate entries per row
+    int32_t* idx = nullptr;   // [B, n_q, k] output
+};
+bool select_fused_ok(const sa_problem& p, int q_dtype, int k_dtype);  // dtypes and shape
+bool select_fused_shape_ok(const sa_problem& p);                       // shape only
+size_t select_fused_bytes(const sa_problem& p);
+// a.status must be set: non-finite index inputs are reported there
+hipError_t launch_select_fused(const IndexerArgs& a, int32_t* idx, void* buf, hipStream_t s);
 
 struct TopkArgs {
     sa_problem p;
@@ -61,6 +78,8 @@ struct TopkArgs {
     Status* status;
     void* scratch;  // topk_ws_bytes(p) bytes of workspace (per-row histograms of the sliced path)
     const int32_t* row_len = nullptr;  // explicit visible length per row (see Rows)
+    int row0 = 0, nrows = 0;  // nrows > 0: only flat rows [row0, row0 + nrows), whose scores start at
+                              // `scores` (the one-workgroup-per-row kernels only)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 size_t topk_ws_bytes(const sa_problem& p);

@@ -125,12 +125,12 @@ __global__ void __launch_bounds__(NT) topk_rows_reg(TopkArgs a) {
     __shared__ int s_bad;
 
     const sa_problem& p = a.p;
-    const int row = blockIdx.x;
+    const int row = a.row0 + (int)blockIdx.x;
     const int b = row / p.n_q, i = row % p.n_q;
     const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int K = p.k;
-    const float* sc = a.scores + (int64_t)row * a.row_stride;
+    const float* sc = a.scores + (int64_t)(row - a.row0) * a.row_stride;
     int32_t* out = a.idx + (int64_t)row * K;
     float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
     const int t = threadIdx.x;
@@ -256,12 +256,12 @@ __global__ void __launch_bounds__(NT) topk_rows_long(TopkArgs a) {
     __shared__ int s_bad;
 
     const sa_problem& p = a.p;
-    const int row = blockIdx.x;
+    const int row = a.row0 + (int)blockIdx.x;
     const int b = row / p.n_q, i = row % p.n_q;
     const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal, a.row_len};
     const int L = visible_len(R, b, i);
     const int K = p.k;
-    const float* sc = a.scores + (int64_t)row * a.row_stride;
+    const float* sc = a.scores + (int64_t)(row - a.row0) * a.row_stride;
     int32_t* out = a.idx + (int64_t)row * K;
     float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -749,10 +749,11 @@ size_t topk_ws_bytes(const sa_problem& p) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-    const long rows = (long)a.p.B * a.p.n_q;
+    const long rows = a.nrows > 0 ? a.nrows : (long)a.p.B * a.p.n_q;
     const int n = a.p.n_kv;
     const dim3 g((unsigned)rows);
     if (topk_sliced(a.p)) {
+        if (a.nrows > 0) return hipErrorInvalidValue;  // the sliced path takes whole problems
         SlicedWs w;
         w.S = (n + kSlice - 1) / kSlice;
         w.hist = static_cast<uint32_t*>(a.scratch);
