@@ -213,6 +213,25 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
                            size_t ws_bytes, void* stream);
 
 /*
+ * sa_select_attend_noalloc -- sa_select_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid it): the
+ * same kernels and results, with the workspace replaced by a fixed 64 MiB array of device
+ * memory inside the library.  Each GPU the library runs on holds its own copy of that array
+ * until the process ends.  Nothing is allocated or freed by the call.
+ *   arguments as for sa_select_attend, without ws / ws_bytes;
+ *   status  device pointer to a zero-filled, 256-byte aligned block of 256 bytes, or NULL:
+ *           receives the status word (SA_ERR_NONFINITE), read and cleared by
+ *           sa_device_status(status, stream); NULL = not reported.
+ * Problems whose sa_workspace_bytes(p, SA_OP_SELECT_ATTEND) exceeds 64 MiB (for example
+ * long prefills) return SA_ERR_WORKSPACE before anything is launched.  All calls on one GPU
+ * share its array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give undefined results; calls ordered on one stream are safe.
+ */
+sa_status sa_select_attend_noalloc(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, sa_tensor Q,
+                                   sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O, float* lse,
+                                   uint32_t* status, void* stream);
+
+/*
  * sa_select_attend_grouped -- grouped candidate sets.  "PaperTrace 2.2 · Fine-grained
  * indexing", §2 eq. (5) and the paragraphs around it (shared versus per-head candidates):
  * the Hq main heads form G groups, each with its own selector, S_{t,g} = TopK(Agg over the

@@ -111,6 +111,22 @@ def test_select_argument_errors():
 
 
 @needs_lib
+def test_no_alloc_argument_errors():
+    # checked on the host before the library looks for its scratch or launches anything
+    L = sa.lib()
+    q, k, w = _t(s0=64 * 4 * 32, s1=4 * 32, s2=32), _t(s0=64 * 32, s1=32, s2=0), _t(dtype=sa.SA_F32, s0=64 * 4, s1=4, s2=0)
+    ok = _t()
+    call = lambda pp, status=None, idx=FAKE: L.sa_select_attend_noalloc(ctypes.byref(pp), q, k, w, ok, ok, ok, idx, ok,
+                                                                         None, status, None)
+    assert call(_prob(), status=FAKE + 16) == sa.SA_ERR_INVALID_ARG  # status word not 256-byte aligned
+    assert call(_prob(), idx=FAKE + 2) == sa.SA_ERR_INVALID_ARG
+    assert call(_prob(k=0)) == sa.SA_ERR_INVALID_ARG
+    big = _prob(n_q=4096, n_kv=4096, k=64)  # scores of 64 MiB plus the rest: beyond the fixed scratch
+    assert L.sa_workspace_bytes(ctypes.byref(big), sa.SA_OP_SELECT_ATTEND) > 64 << 20
+    assert call(big) == sa.SA_ERR_WORKSPACE
+
+
+@needs_lib
 def test_attention_argument_errors():
     L = sa.lib()
     p = _prob()

@@ -1,6 +1,7 @@
 // Host side of libsa.so: argument validation, workspace layout and kernel dispatch.
 // Every argument error is detected here, before anything is enqueued.
 #include <math.h>
+#include <atomic>
 #include <string.h>
 
 #include "sa_internal.h"
@@ -224,6 +225,26 @@ sa_status run_select(const sa_problem* p, const sa_tensor& q, const sa_tensor& k
 
 float eff_scale(const sa_problem* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d_qk); }
 
+// Scratch of the entry point that allocates nothing (sa_select_attend_noalloc): a fixed
+// array in device memory, one per GPU the library runs on, held until the process ends.
+// Its device address comes from hipGetSymbolAddress once per device (the array's name is
+// only a host-side stand-in); every call on a device shares that device's copy.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch[kMaxDevices];
+
+char* noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    char* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch[dev].store(static_cast<char*>(ptr), std::memory_order_release);  // same value from any thread
+    return static_cast<char*>(ptr);
+}
+
 // Block-table view of paged K/V pools (table null: K and V hold each batch's rows).
 struct Pages {
     const int32_t* table = nullptr;
@@ -286,6 +307,19 @@ GroupedLayout grouped_layout(const sa_problem& p, const sa_problem& pg, int G) {
     return l;
 }
 char* offset_bytes(const void* base, int64_t bytes) { return const_cast<char*>(static_cast<const char*>(base)) + bytes; }
+
+// Score, select and attend with the space after the status word at `body`: the selection
+// (when the caller does not take it), the split partials, then the selection region.
+sa_status select_attend_in(const sa_problem* p, const sa_tensor& q_idx, const sa_tensor& k_idx, const sa_tensor& w,
+                           const sa_tensor& Q, const sa_tensor& K, const sa_tensor& V, int32_t* idx_out,
+                           const sa_tensor& O, float* lse, Status* status, char* body, hipStream_t st) {
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(body);
+    void* partial = body + idx_bytes(*p);
+    char* region = static_cast<char*>(partial) + align256(attn_partial_bytes(*p));
+    sa_status s = run_select(p, q_idx, k_idx, w, idx, status, region, st);
+    if (s != SA_OK) return s;
+    return run_attn(p, Q, K, V, idx, O, lse, partial, st);
+}
 
 }  // namespace
 
@@ -408,14 +442,28 @@ sa_status sa_select_attend(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx
     if (s != SA_OK) return s;
     if ((s = check_attn(p, Q, K, V, O)) != SA_OK) return s;
     if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SELECT_ATTEND))) != SA_OK) return s;
-    hipStream_t st = (hipStream_t)stream;
     char* base = static_cast<char*>(ws);
-    // status word, selection (when the caller does not take it), split partials, selection region
-    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + kStatusBytes);
-    void* partial = base + kStatusBytes + idx_bytes(*p);
-    char* region = static_cast<char*>(partial) + align256(attn_partial_bytes(*p));
-    if ((s = run_select(p, q_idx, k_idx, w, idx, reinterpret_cast<Status*>(base), region, st)) != SA_OK) return s;
-    return run_attn(p, Q, K, V, idx, O, lse, partial, st);
+    return select_attend_in(p, q_idx, k_idx, w, Q, K, V, idx_out, O, lse, reinterpret_cast<Status*>(base),
+                            base + kStatusBytes, (hipStream_t)stream);
+}
+
+sa_status sa_select_attend_noalloc(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, sa_tensor Q,
+                                   sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O, float* lse,
+                                   uint32_t* status, void* stream) {
+    if (!problem_ok(p)) return SA_ERR_INVALID_ARG;
+    if (idx_out && ((uintptr_t)idx_out & 3)) return SA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3)) return SA_ERR_INVALID_ARG;
+    if (status && ((uintptr_t)status & 255)) return SA_ERR_INVALID_ARG;
+    sa_status s = check_indexer(p, q_idx, k_idx, w);
+    if (s != SA_OK) return s;
+    if ((s = check_attn(p, Q, K, V, O)) != SA_OK) return s;
+    if (sa_workspace_bytes(p, SA_OP_SELECT_ATTEND) > kNoAllocScratchBytes) return SA_ERR_WORKSPACE;
+    char* base = noalloc_scratch();
+    if (!base) return SA_ERR_HIP;
+    // the caller's status word, or the scratch's own (then nothing reports non-finite inputs)
+    Status* st_word = status ? reinterpret_cast<Status*>(status) : reinterpret_cast<Status*>(base);
+    return select_attend_in(p, q_idx, k_idx, w, Q, K, V, idx_out, O, lse, st_word, base + kStatusBytes,
+                            (hipStream_t)stream);
 }
 
 size_t sa_grouped_workspace_bytes(const sa_problem* p, int groups) {
