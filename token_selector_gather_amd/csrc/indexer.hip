@@ -577,6 +577,7 @@ __device__ __forceinline__ uint32_t sel_compact(uint32_t* keys, int32_t* pos, in
 }
 
 // ------------------------------------------------------------------ indexer_pf
+
 // Prefill layout for many query rows: a workgroup takes QB = 4 * 128 / H consecutive query
 // rows of one batch and walks their causal history once, in chunks of 128 keys that are
 // widened to bf16 once per chunk while being written to LDS (double buffered).  Wave w
@@ -804,32 +805,36 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
             const int buf = c & 1;
             if (c + 1 < nch) fetch(c + 1);
             const uint8_t* kb = kbuf[buf] + l15 * KP + 16 * g;
-#pragma unroll 2
-            for (int nt = 0; nt < CK / 16; ++nt) {
-                bf16x8 bv[KSTEPS];
+            // Software pipeline over the chunk's 16-key tiles: a query's accumulators are
+            // reduced (ReLU, weights, head sum) and then refilled by the next tile's MFMAs, so
+            // the epilogue's vector work sits among matrix instructions that do not depend on
+            // it (no extra accumulator or B-fragment registers).
+            f32x4 acc[MT];
+            bf16x8 bv[KSTEPS];
+            auto load_b = [&](int nt) {
 #pragma unroll
                 for (int s2 = 0; s2 < KSTEPS; ++s2)
                     bv[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + nt * 16 * KP + 64 * s2));
-                f32x4 acc[MT];
-#pragma unroll
-                for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            };
+            auto mfma_tiles = [&](int m0, int m1) {  // M-tiles [m0, m1) of the tile in bv
 #pragma unroll
                 for (int s2 = 0; s2 < KSTEPS; ++s2)
 #pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][s2], bv[s2], acc[m], 0, 0, 0);
-                float sc[QW];
+                    for (int m = m0; m < m1; ++m)
+                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][s2], bv[s2], s2 == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[m],
+                                                                       0, 0, 0);
+            };
+            auto reduce_q = [&](int q) {
+                // four partial sums (short dependency chains); the ReLU is the
+                // one-instruction integer max (non-finite inputs are handled apart)
+                float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < QW; ++q) {
-                    // four partial sums (short dependency chains); the ReLU is the
-                    // one-instruction integer max (non-finite inputs are handled apart)
-                    float t[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int m = q * TPQ; m < (q + 1) * TPQ; ++m)
 #pragma unroll
-                    for (int m = q * TPQ; m < (q + 1) * TPQ; ++m)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) t[e] = fmaf(wvv[m][e], relu_finite(acc[m][e]), t[e]);
-                    sc[q] = xsum32(xsum16((t[0] + t[1]) + (t[2] + t[3])));
-                }
+                    for (int e = 0; e < 4; ++e) t[e] = fmaf(wvv[m][e], relu_finite(acc[m][e]), t[e]);
+                return xsum32(xsum16((t[0] + t[1]) + (t[2] + t[3])));
+            };
+            auto emit = [&](int nt, const float (&sc)[QW]) {
                 const int j = c * CK + nt * 16 + l15;
 #pragma unroll
                 for (int z = 0; z < NZ; ++z) {
@@ -864,6 +869,27 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
                         if (qok[z] && j < p.n_kv && (vis || a.fill_invisible)) srow[z][j] = vis ? (qb ? __builtin_nanf("") : v) : -INFINITY;
                     }
                 }
+            };
+            // Rotation per tile nt: reduce query 0 of nt beside the MFMAs of nt's last query,
+            // then (B fragment of nt + 1) for q >= 1 reduce query q of nt beside the MFMAs of
+            // nt + 1 for query q - 1, then store or list the scores.  (Pinning the MFMA / vector
+            // interleave with scheduling-group barriers measured no faster.)
+            constexpr int NT = CK / 16;
+            load_b(0);
+            mfma_tiles(0, (QW - 1) * TPQ);
+#pragma unroll 1
+            for (int nt = 0; nt < NT; ++nt) {
+                float sc[QW];
+                sc[0] = reduce_q(0);
+                mfma_tiles((QW - 1) * TPQ, QW * TPQ);
+                const bool more = nt + 1 < NT;
+                if (more) load_b(nt + 1);
+#pragma unroll
+                for (int q = 1; q < QW; ++q) {
+                    sc[q] = reduce_q(q);
+                    if (more) mfma_tiles((q - 1) * TPQ, q * TPQ);
+                }
+                emit(nt, sc);
             }
             if (c + 1 < nch) commit(buf ^ 1);
             __syncthreads();
