@@ -396,3 +396,47 @@ def misa_select(W, blk, g, rows=None, kbar=None, heads=None):
     sc = scores(Wa)
     idx, sk, skp1, _ = select(Wa, sc)
     return dict(idx=idx, heads=heads, route=route, scores=sc, sk=sk, skp1=skp1)
+
+
+# ------------------------------------------------------------------ shared linear term + residual heads
+# "PaperTrace 2.2 · Fine-grained indexing", §2.2, the ResMiSA paragraph: with
+# ReLU(z) = z + ReLU(-z), the heads' linear terms add up to ONE shared dot product,
+# sum_h w_h <q_h, k> = <sum_h w_h q_h, k>, and the non-linear residual w_h ReLU(-<q_h, k>)
+# is computed for some heads only.  Readings: the residual heads are the active heads of
+# the MISA routing above (misa_route / misa_heads), so that with every head active the
+# score is the indexer's own; the shared query sum_h w_h q_h is formed exactly (fp64).
+
+def resmisa_scores(W, heads, rows=None):
+    """ResMiSA scores [n, n_kv] of the listed rows with the given residual heads per row
+    ([n, g] head indices; g may be 0): <sum_h w_h q_h, k_j> + sum_{h in heads} w_h
+    max(0, -<q_h, k_j>) over the visible j, -inf elsewhere (fp64)."""
+    rows = _rows(W, rows)
+    L = np.isfinite(scores(W, rows)).sum(axis=1)  # visible prefix [0, L)
+    out = np.full((rows.size, W["n_kv"]), -np.inf)
+    for r, row in enumerate(rows):
+        b, i = divmod(int(row), W["n_q"])
+        n = int(L[r])
+        if n == 0:
+            continue
+        q = decode_array(W["q_idx"][b, i])                  # [Hidx, d_idx]
+        w = W["w"][b, i].astype(np.float64)                  # [Hidx]
+        k = decode_array(W["k_idx"][b, :n])                  # [n, d_idx]
+        qbar = (w[:, None] * q).sum(axis=0)                  # the shared query
+        s = k @ qbar
+        for h in np.asarray(heads[r], dtype=np.int64):
+            s = s + w[h] * np.maximum(0.0, -(k @ q[h]))
+        out[r, :n] = s
+    return out
+
+
+def resmisa_select(W, blk, g, rows=None, kbar=None, heads=None):
+    """Selection of the listed rows with the shared linear term and g residual heads (the
+    MISA routing's active heads unless `heads` overrides them).  Returns dict(idx, heads,
+    route, scores, sk, skp1)."""
+    rows = _rows(W, rows)
+    route = misa_route(W, blk, rows, kbar)
+    if heads is None:
+        heads = misa_heads(route, g)
+    sc = resmisa_scores(W, heads, rows)
+    idx, sk, skp1, _ = select(W, sc, rows)
+    return dict(idx=idx, heads=heads, route=route, scores=sc, sk=sk, skp1=skp1)

@@ -808,3 +808,84 @@ def test_grouped_sets_swapping_groups_swaps_the_outputs():
     assert np.array_equal(idx2[0], idx[1]) and np.array_equal(idx2[1], idx[0])
     assert np.array_equal(O2[:, :2], O[:, 2:]) and np.array_equal(lse2[:, 2:], lse[:, :2])
     assert not np.array_equal(idx[0], idx[1])  # the two groups really select differently
+
+
+# ---------------------------------------------------------------- shared linear term + residual heads
+# "PaperTrace 2.2 · Fine-grained indexing", §2.2 (ResMiSA): ReLU(z) = z + ReLU(-z) turns the
+# heads' linear terms into one shared dot product; the residual ReLU(-z) runs on some heads.
+
+@pytest.mark.parametrize("case", list(HISA_CASES))
+def test_resmisa_with_every_head_residual_is_the_flat_score(case):
+    # every head keeps its residual: shared linear term + all residuals = the indexer's own
+    # score (the C oracle's, computed head by head), to rounding
+    kw = dict(HISA_CASES[case])
+    lens, q_pos0 = kw.pop("lens", None), kw.pop("q_pos0", None)
+    W = sa_synth.custom(seed=9, lens=lens, q_pos0=q_pos0, with_main=False, **kw)
+    rows = all_rows(W)
+    flat = orc.scores(W, rows)
+    heads = np.tile(np.arange(W["Hidx"], dtype=np.int32), (rows.size, 1))
+    res = orc.resmisa_scores(W, heads, rows)
+    fin = np.isfinite(flat)
+    assert np.array_equal(fin, np.isfinite(res))
+    scale = np.abs(flat[fin]).max()
+    assert np.abs(res[fin] - flat[fin]).max() <= 1e-12 * scale
+    r = orc.resmisa_select(W, 8, W["Hidx"], rows)
+    ref, sk, skp1, _ = orc.select(W, flat, rows)
+    # the selections agree wherever the cutoff margin is above the rounding
+    ok = (sk - skp1) > 1e-9 * scale
+    assert ok.sum() > rows.size // 2
+    np.testing.assert_array_equal(r["idx"][ok], ref[ok])
+
+
+def test_resmisa_hand_case_keeps_the_inactive_heads_linear_term():
+    # two heads, q1 = (1, 0), q2 = (0, 1), w = (1, 2); keys k0 = (1, -1), k1 = (-1, 1), k2 = (2, 2)
+    # flat r = w1 ReLU(z1) + w2 ReLU(z2):          k0: 1,  k1: 2,  k2: 6
+    # residual on head 2 only: (z1 + 2 z2) + 2 ReLU(-z2): k0: -1 + 2 = 1, k1: 1 + 0 = 1, k2: 6
+    #   (head 1 is inactive: its linear term z1 replaces ReLU(z1), exact for z1 >= 0, -1 for k1)
+    # residual on head 1 only: (z1 + 2 z2) + ReLU(-z1):   k0: -1 + 0 = -1, k1: 1 + 1 = 2, k2: 6
+    # no residual (shared linear term only):             k0: -1, k1: 1, k2: 6
+    q = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    kk = np.array([[[1.0, -1.0], [-1.0, 1.0], [2.0, 2.0]]])
+    W = tiny(q_idx=q, k_idx=kk, w=np.array([[[1.0, 2.0]]]), k=2, causal=0)
+    np.testing.assert_allclose(orc.scores(W)[0], [1.0, 2.0, 6.0])
+    np.testing.assert_allclose(orc.resmisa_scores(W, [[1]])[0], [1.0, 1.0, 6.0])
+    np.testing.assert_allclose(orc.resmisa_scores(W, [[0]])[0], [-1.0, 2.0, 6.0])
+    np.testing.assert_allclose(orc.resmisa_scores(W, np.zeros((1, 0), np.int32))[0], [-1.0, 1.0, 6.0])
+    # top 2: with head 2's residual k0 and k1 tie at 1 (lower position wins) -> {0, 2}
+    assert orc.resmisa_select(W, 1, 1, heads=[[1]])["idx"][0].tolist() == [0, 2]
+    assert orc.resmisa_select(W, 1, 1, heads=[[0]])["idx"][0].tolist() == [1, 2]
+
+
+def _brute_resmisa(q, kk, w, L, heads, K):
+    dot = lambda a, b: sum(x * y for x, y in zip(a, b))
+    H = len(q)
+    sc = []
+    for j in range(L):
+        z = [dot(q[h], kk[j]) for h in range(H)]
+        lin = sum(w[h] * z[h] for h in range(H))
+        sc.append((-(lin + sum(w[h] * max(0.0, -z[h]) for h in heads)), j))
+    return sorted(j for _, j in sorted(sc)[:K])
+
+
+def test_resmisa_matches_brute_force_on_tiny_rows():
+    rng = np.random.default_rng(19)
+    B, n_q, n_kv, H, D = 1, 9, 20, 5, 4
+    q = rand_f32(rng, (B, n_q, H, D))
+    kk = rand_f32(rng, (B, n_kv, D))
+    w = rng.uniform(-1, 1, (B, n_q, H)).astype(np.float32)
+    for causal, q0 in ((1, 2), (0, 0)):
+        W = tiny(q_idx=q, k_idx=kk, w=w, k=3, causal=causal, q_pos0=[q0], kv_len=[18])
+        # g < H: with every head residual, scores that the flat formula makes exactly 0 come
+        # out as +-1e-16 (linear term plus residual), so exact ties there break by rounding
+        for blk, g in ((3, 2), (4, 1), (2, 4)):
+            got = orc.resmisa_select(W, blk, g)
+            mis = orc.misa_select(W, blk, g)
+            for i in range(n_q):
+                L = 0 if q0 + i >= 18 else (q0 + i + 1 if causal else 18)
+                if L == 0:
+                    assert (got["idx"][i] == -1).all()
+                    continue
+                assert got["heads"][i].tolist() == mis["heads"][i].tolist()  # the MISA routing
+                ref = _brute_resmisa(q[0, i].astype(np.float64).tolist(), kk[0].astype(np.float64).tolist(),
+                                     w[0, i].astype(np.float64).tolist(), L, got["heads"][i].tolist(), 3)
+                assert got["idx"][i, : len(ref)].tolist() == ref and (got["idx"][i, len(ref):] == -1).all()
