@@ -174,25 +174,29 @@ def hisa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat):
             "bytes_per_call": nbytes, "achieved_gbs": round(nbytes / (t_h * 1e-3) / 1e9, 1)}
 
 
-def misa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat):
+def misa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat, residual=False):
     """Active index heads (g = Hidx / 4 of the heads per query, routed by the block
-    representatives, b = 128) timed beside the flat score + select, with the overlap of
-    the two selections; the representatives are prebuilt index state."""
+    representatives, b = 128) timed beside the flat fused score + select, with the overlap
+    of the two selections; the representatives are prebuilt index state.  With `residual`,
+    the shared linear term plus g = Hidx / 4 - 6 residual heads: the same Hidx / 4 scored
+    heads per query (the shared query takes six)."""
     import numpy as np
     import torch
 
     import token_selector_gather_amd as sa
 
-    blk, g = 128, W["Hidx"] // 4
+    blk = 128
+    g = W["Hidx"] // 4 - (6 if residual else 0)
+    ws_bytes = sa.sa_resmisa_workspace_bytes if residual else sa.sa_misa_workspace_bytes
     nb = W["n_kv"] // blk
-    if nb < 1 or g < 1 or sa.sa_misa_workspace_bytes(P, blk, g) == 0:
+    if nb < 1 or g < 1 or ws_bytes(P, blk, g) == 0:
         return None
     kbar = torch.empty((W["B"], nb, W["d_idx"]), dtype=torch.bfloat16, device="cuda")
     sa.sa_block_means(P, d["k_idx"], blk, kbar, stream)
-    ws_m = sa.misa_workspace(P, blk, g)
+    ws_m = (sa.resmisa_workspace if residual else sa.misa_workspace)(P, blk, g)
     idx_m = torch.empty((W["B"], W["n_q"], W["k"]), dtype=torch.int32, device="cuda")
-    t_m = timed(lambda: sa.sa_misa_select(P, d["q_idx"], d["k_idx"], d["w"], kbar, blk, g, idx_m, ws_m, stream=stream),
-                reps)
+    call = sa.sa_resmisa_select if residual else sa.sa_misa_select
+    t_m = timed(lambda: call(P, d["q_idx"], d["k_idx"], d["w"], kbar, blk, g, idx_m, ws_m, stream=stream), reps)
     st = sa.sa_device_status(ws_m)
     if st != sa.SA_OK:
         raise RuntimeError("active-head selection: device status " + sa.sa_status_str(st))
@@ -204,8 +208,9 @@ def misa_stage(W, P, d, stream, timed, reps, flat_idx, t_flat):
     iou = [np.intersect1d(a[r][a[r] >= 0], f[r][f[r] >= 0]).size /
            max(1, np.union1d(a[r][a[r] >= 0], f[r][f[r] >= 0]).size) for r in rows]
     pairs = int(L.sum())
-    flops = 2 * W["d_idx"] * g * pairs + 2 * W["d_idx"] * W["Hidx"] * int((L // blk).sum())
-    return {"blk": blk, "g": g, "select_ms": round(t_m, 4), "flat_score_select_ms": round(t_flat, 4),
+    hs = W["Hidx"] // 4  # scored heads per query
+    flops = 2 * W["d_idx"] * hs * pairs + 2 * W["d_idx"] * W["Hidx"] * int((L // blk).sum())
+    return {"blk": blk, "g": g, "scored_heads": hs, "select_ms": round(t_m, 4), "flat_score_select_ms": round(t_flat, 4),
             "speedup_vs_flat": round(t_flat / t_m, 3), "iou_vs_flat": round(float(np.mean(iou)), 4),
             "iou_rows": int(len(rows)), "flops_per_call": flops, "tflops": round(flops / (t_m * 1e-3) / 1e12, 2)}
 
@@ -426,7 +431,8 @@ def measure(W, args, stream, full):
         out["hisa"] = hisa_stage(W, P, d, stream, timed, reps, idx, times["indexer_score"] + times["topk"])
     if full:
         if args.misa == 1 or (args.misa == -1 and not alg["decode"] and W["Hidx"] == 64):
-            out["misa"] = misa_stage(W, P, d, stream, timed, reps, idx, times["indexer_score"] + times["topk"])
+            out["misa"] = misa_stage(W, P, d, stream, timed, reps, idx, times["select"])
+            out["resmisa"] = misa_stage(W, P, d, stream, timed, reps, idx, times["select"], residual=True)
         if args.groups > 1:
             out["grouped"] = grouped_stage(W, P, d, stream, timed, reps, args.groups, float(np.median(step_ms)))
         if args.paged == 1:

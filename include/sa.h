@@ -320,13 +320,37 @@ sa_status sa_hisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, 
  *   heads             [B, n_q, g] int32, contiguous, or NULL: the active heads, ascending
  *   ws                sa_misa_workspace_bytes(p, blk, g) bytes, 256-byte aligned,
  *                     zero-filled once after allocation (status word as for sa_topk; it
- *                     includes a score row of n_kv floats per query row).
+ *                     includes the token selection's space, as for sa_select with g index
+ *                     heads: candidate lists for many query rows, score rows otherwise).
  */
 sa_status sa_misa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, const uint16_t* kbar,
                          int blk, int g, int32_t* idx, int32_t* heads, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes of sa_misa_select; 0 for malformed or unsupported arguments. */
 size_t sa_misa_workspace_bytes(const sa_problem* p, int blk, int g);
+
+/*
+ * Shared linear term plus residual heads (ResMiSA).  "PaperTrace 2.2 · Fine-grained
+ * indexing", §2.2, the ResMiSA paragraph: since ReLU(z) = z + ReLU(-z), the heads' linear
+ * terms add up to one shared dot product and only some heads keep the non-linear part:
+ *     r = <sum_h w_h q_h, k> + sum_{h active} w_h ReLU(-<q_h, k>),
+ * which equals the indexer's score when every head is active.  Reading where the pages
+ * leave the step open: the active heads are those of sa_misa_select's routing (same kbar,
+ * blk and g), so an inactive head contributes its linear term w_h <q_h, k> instead of
+ * nothing; the top-k is taken as by sa_topk.  The shared query is formed in fp32 and enters
+ * the matrix cores as three exact bf16 parts, so the score keeps fp32 precision.
+ * sa_resmisa_select
+ *   arguments as for sa_misa_select; 1 <= g <= min(Hidx, 58)
+ *   idx    [B, n_q, k] int32, contiguous, as for sa_topk
+ *   heads  [B, n_q, g] int32 or NULL: the residual heads, ascending
+ *   ws     sa_resmisa_workspace_bytes(p, blk, g) bytes, 256-byte aligned, zero-filled once
+ *          after allocation (status word).
+ */
+sa_status sa_resmisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, const uint16_t* kbar,
+                            int blk, int g, int32_t* idx, int32_t* heads, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sa_resmisa_select; 0 for malformed or unsupported arguments. */
+size_t sa_resmisa_workspace_bytes(const sa_problem* p, int blk, int g);
 
 /* Synchronises `stream`, returns the status word accumulated in ws by earlier calls
  * (SA_OK or SA_ERR_NONFINITE) and clears it.  ws is a host-visible pointer to device

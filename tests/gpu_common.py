@@ -165,3 +165,16 @@ def full_check(W, rows=None, tie_groups=None, check_sparse=True, say=None):
         errs_sparse = compare_attention(W, rows, O2, lse2, O_or2, lse_or2)
     return dict(stats, err_o=errs[0], err_lse=errs[1], err_o_sparse=errs_sparse[0], idx=idx, ref_idx=ref_idx,
                 rows=rows)
+
+
+def route_tolerance(W, kbar, rows):
+    """Bound on |routing score (GPU) - routing score (oracle)| per row."""
+    kb = decode_f64(kbar)
+    n = W["d_idx"] + 8
+    out = np.empty(len(rows))
+    for r, row in enumerate(rows):
+        b, i = divmod(int(row), W["n_q"])
+        q = decode_f64(W["q_idx"][b, i])
+        a = np.abs(q) @ np.abs(kb[b]).T  # [H, nb]
+        out[r] = 2 * n * 2.0 ** -24 * (np.abs(W["w"][b, i]) * a.max(axis=1)).max() + 1e-30
+    return out

@@ -94,6 +94,12 @@ def test_streaming_selection_workspace_holds_no_score_matrix():
     # a small problem keeps the stored scores (the two-pass selection)
     q = _prob()
     assert L.sa_workspace_bytes(ctypes.byref(q), sa.SA_OP_SELECT) >= 256 + 2 * 64 * 64 * 4
+    # the active-head selections at that size score their (16) heads through the same
+    # streaming selection: no score rows either (with 16 heads a block holds 64 query rows,
+    # so four times the rows are in flight)
+    for g in (8, 16):
+        assert 0 < L.sa_misa_workspace_bytes(ctypes.byref(p), 128, g) < scores // 2
+    assert 0 < L.sa_resmisa_workspace_bytes(ctypes.byref(p), 128, 10) < scores // 2
 
 
 @needs_lib
@@ -242,6 +248,36 @@ def test_hierarchical_selection_argument_errors():
     assert bm(blk=12) == sa.SA_ERR_INVALID_ARG
     assert bm(out=None) == sa.SA_ERR_INVALID_ARG
     assert bm(kb_=_t(data=None, s0=64 * 32, s1=32, s2=0)) == sa.SA_ERR_INVALID_ARG
+
+
+@needs_lib
+@pytest.mark.parametrize("residual", [False, True])
+def test_active_head_selection_argument_errors(residual):
+    L = sa.lib()
+    p = _prob(n_kv=256, Hidx=64, d_idx=64)
+    q = _t(s0=64 * 64 * 64, s1=64 * 64, s2=64)
+    k = _t(s0=256 * 64, s1=64, s2=0)
+    w = sa._Tensor(FAKE, sa.SA_F32, 64 * 64, 64, 0)
+    ws_fn = L.sa_resmisa_workspace_bytes if residual else L.sa_misa_workspace_bytes
+    fn = L.sa_resmisa_select if residual else L.sa_misa_select
+    g_max = 58 if residual else 64  # the shared query takes six of at most 64 scored slots
+    assert ws_fn(ctypes.byref(p), 64, g_max) > 0
+    assert ws_fn(ctypes.byref(p), 64, g_max + 1) == 0
+    assert ws_fn(ctypes.byref(p), 64, 0) == 0
+    assert ws_fn(ctypes.byref(p), 512, 4) == 0                          # no complete block
+    assert ws_fn(ctypes.byref(_prob(n_kv=256, Hidx=8, d_idx=64)), 64, 4) == 0  # routing: 16, 32 or 64 heads
+    need = ws_fn(ctypes.byref(p), 64, 8)
+    call = lambda blk=64, g=8, q=q, w=w, kbar=FAKE, idx=FAKE, heads=None, ws=FAKE, n=need: fn(
+        ctypes.byref(p), q, k, w, kbar, blk, g, idx, heads, ws, n, None)
+    assert call(blk=48) == sa.SA_ERR_INVALID_ARG
+    assert call(g=0) == sa.SA_ERR_INVALID_ARG
+    assert call(g=g_max + 1) == sa.SA_ERR_INVALID_ARG
+    assert call(kbar=FAKE + 8) == sa.SA_ERR_INVALID_ARG
+    assert call(idx=None) == sa.SA_ERR_INVALID_ARG
+    assert call(heads=FAKE + 2) == sa.SA_ERR_INVALID_ARG
+    assert call(q=_t(dtype=sa.SA_F32, s0=64 * 64 * 64, s1=64 * 64, s2=64)) == sa.SA_ERR_UNSUPPORTED
+    assert call(n=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == sa.SA_ERR_WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -39,22 +39,9 @@ def gpu_misa(W, blk, g):
             heads.cpu().numpy().reshape(-1, g), st)
 
 
-def route_tolerance(W, kbar, rows, blk):
-    """Bound on |routing score (GPU) - routing score (oracle)| per row."""
-    kb = orc.decode_array(kbar)
-    n = W["d_idx"] + 8
-    out = np.empty(len(rows))
-    for r, row in enumerate(rows):
-        b, i = divmod(int(row), W["n_q"])
-        q = orc.decode_array(W["q_idx"][b, i])
-        a = np.abs(q) @ np.abs(kb[b]).T  # [H, nb]
-        out[r] = 2 * n * 2.0 ** -24 * (np.abs(W["w"][b, i]) * a.max(axis=1)).max() + 1e-30
-    return out
-
-
 def check_rows(W, blk, g, rows, got_idx, got_heads, kbar):
     ref = orc.misa_select(W, blk, g, rows, kbar=kbar)
-    tr = route_tolerance(W, kbar, rows, blk)
+    tr = gc.route_tolerance(W, kbar, rows)
     H = W["Hidx"]
     for r, row in enumerate(rows):
         h = got_heads[row]

@@ -70,12 +70,15 @@ def lib():
         L.sa_block_means.argtypes = [P, T, ctypes.c_int, vp, vp]
         L.sa_hisa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         L.sa_misa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
+        L.sa_resmisa_select.argtypes = [P, T, T, T, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         for f in (L.sa_indexer_score, L.sa_topk, L.sa_select, L.sa_sparse_attn, L.sa_select_attend,
                   L.sa_select_attend_noalloc, L.sa_block_means,
-                  L.sa_hisa_select, L.sa_misa_select, L.sa_sparse_attn_paged, L.sa_select_attend_grouped):
+                  L.sa_hisa_select, L.sa_misa_select, L.sa_resmisa_select, L.sa_sparse_attn_paged, L.sa_select_attend_grouped):
             f.restype = st
         L.sa_misa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
         L.sa_misa_workspace_bytes.restype = sz
+        L.sa_resmisa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
+        L.sa_resmisa_workspace_bytes.restype = sz
         L.sa_hisa_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
         L.sa_hisa_workspace_bytes.restype = sz
         L.sa_workspace_bytes.argtypes = [P, ctypes.c_int]
@@ -273,6 +276,23 @@ def sa_misa_select(p, q_idx, k_idx, w, kbar, blk, g, idx, ws, heads=None, stream
                                 int(blk), int(g), _ptr(idx), _ptr(heads), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "sa_misa_select")
+
+
+def sa_resmisa_workspace_bytes(p, blk, g):
+    return lib().sa_resmisa_workspace_bytes(p.ref, int(blk), int(g))
+
+
+def resmisa_workspace(p, blk, g, device="cuda"):
+    """A zero-filled workspace for sa_resmisa_select."""
+    n = max(256, sa_resmisa_workspace_bytes(p, blk, g))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def sa_resmisa_select(p, q_idx, k_idx, w, kbar, blk, g, idx, ws, heads=None, stream=None):
+    _check(lib().sa_resmisa_select(p.ref, _tensor(q_idx, "q_idx"), _tensor(k_idx, "k_idx"), _tensor(w, "w"),
+                                   _ptr(kbar), int(blk), int(g), _ptr(idx), _ptr(heads), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "sa_resmisa_select")
 
 
 def sa_device_status(ws, stream=None):

@@ -135,12 +135,6 @@ HisaLayout hisa_layout(const sa_problem& p, int blk, int k_blocks, int k_es) {
     return l;
 }
 
-// Workspace of the active-head selection: status word, complete visible blocks per row,
-// routing scores, active heads, the active heads' queries and weights, the score rows of
-// the token selection, top-k scratch.
-struct MisaLayout {
-    size_t row_blk, route, heads, qa, wa, scores, scratch, total;
-};
 bool misa_args_ok(const sa_problem* p, int blk, int g) {
     if (!problem_ok(p)) return false;
     if (blk != 16 && blk != 32 && blk != 64 && blk != 128 && blk != 256) return false;
@@ -158,24 +152,6 @@ sa_problem misa_head_problem(const sa_problem& p, int g) {
     q.q_pos0 = nullptr;
     return q;
 }
-MisaLayout misa_layout(const sa_problem& p, int g) {
-    const size_t R = (size_t)p.B * p.n_q;
-    sa_problem pa = p;
-    pa.Hidx = g;
-    MisaLayout l;
-    size_t o = kStatusBytes;
-    l.row_blk = o; o += align256(R * 4);
-    l.route = o; o += align256(R * (size_t)p.Hidx * 4);
-    l.heads = o; o += align256(R * (size_t)g * 4);
-    l.qa = o; o += align256(R * (size_t)g * p.d_idx * 2);
-    l.wa = o; o += align256(R * (size_t)g * 4);
-    l.scores = o; o += align256(R * (size_t)p.n_kv * 4);
-    const size_t t1 = topk_ws_bytes(misa_head_problem(p, g)), t2 = topk_ws_bytes(pa);
-    l.scratch = o; o += align256(t1 > t2 ? t1 : t2);
-    l.total = o;
-    return l;
-}
-
 // Workspace region of a selection (after the status word): the fused score + select's
 // candidate lists, or the score rows and the top-k scratch.  A shape that the fused path
 // takes but whose index dtypes it does not (f32 index queries or keys) scores and selects
@@ -221,6 +197,67 @@ sa_status run_select(const sa_problem* p, const sa_tensor& q, const sa_tensor& k
     ta.scratch = region + scores_bytes(*p);
     if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
     return launch_topk(ta, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+// Workspace of the active-head selections (plain and with the shared linear term): status
+// word, complete visible blocks per row, routing scores, active heads, the scored heads'
+// queries and weights (Hs heads per row: misa_heads(g) for the active heads padded with zero
+// heads, resmisa_heads(g) for the residual-head problem), top-k scratch of the head choice,
+// the token selection's region.
+struct MisaLayout {
+    size_t row_blk, route, heads, qa, wa, scratch, region, total;
+};
+sa_problem scored_problem(const sa_problem& p, int Hs) {
+    sa_problem q = p;
+    q.Hidx = Hs;
+    return q;
+}
+MisaLayout misa_layout(const sa_problem& p, int g, int Hs) {
+    const size_t R = (size_t)p.B * p.n_q;
+    MisaLayout l;
+    size_t o = kStatusBytes;
+    l.row_blk = o; o += align256(R * 4);
+    l.route = o; o += align256(R * (size_t)p.Hidx * 4);
+    l.heads = o; o += align256(R * (size_t)g * 4);
+    l.qa = o; o += align256(R * (size_t)Hs * p.d_idx * 2);
+    l.wa = o; o += align256(R * (size_t)Hs * 4);
+    l.scratch = o; o += align256(topk_ws_bytes(misa_head_problem(p, g)));
+    l.region = o; o += select_region_bytes(scored_problem(p, Hs));
+    l.total = o;
+    return l;
+}
+
+// Routing, head choice and the gather of the scored heads (plain active heads, or the
+// residual-head problem), then the token selection over them.
+sa_status misa_run(const sa_problem* p, const sa_tensor& q_idx, const sa_tensor& k_idx, const sa_tensor& w,
+                   const uint16_t* kbar, int blk, int g, bool residual, int32_t* idx, int32_t* heads, char* base,
+                   hipStream_t st) {
+    const int Hs = residual ? resmisa_heads(g) : misa_heads(g);
+    const MisaLayout l = misa_layout(*p, g, Hs);
+    int32_t* row_blk = reinterpret_cast<int32_t*>(base + l.row_blk);
+    float* route = reinterpret_cast<float*>(base + l.route);
+    int32_t* hsel = heads ? heads : reinterpret_cast<int32_t*>(base + l.heads);
+    uint16_t* qa = reinterpret_cast<uint16_t*>(base + l.qa);
+    float* wa = reinterpret_cast<float*>(base + l.wa);
+    Status* status = reinterpret_cast<Status*>(base);
+    if (launch_hisa_rows(*p, blk, row_blk, st) != hipSuccess) return SA_ERR_HIP;
+    if (launch_misa_route(*p, q_idx, w, kbar, blk, row_blk, route, st) != hipSuccess) return SA_ERR_HIP;
+    TopkArgs th;  // g heads of Hidx per row, ranked by (routing score desc, head asc)
+    th.p = misa_head_problem(*p, g);
+    th.scores = route;
+    th.row_stride = p->Hidx;
+    th.idx = hsel;
+    th.vals = nullptr;
+    th.status = status;
+    th.scratch = base + l.scratch;
+    if (launch_topk(th, st) != hipSuccess) return SA_ERR_HIP;
+    const hipError_t e = residual ? launch_resmisa_gather(*p, q_idx, w, g, hsel, qa, wa, st)
+                                  : launch_misa_gather(*p, q_idx, w, g, hsel, qa, wa, st);
+    if (e != hipSuccess) return SA_ERR_HIP;
+    const sa_problem pa = scored_problem(*p, Hs);
+    const sa_tensor qt{qa, SA_BF16, (int64_t)p->n_q * Hs * p->d_idx, (int64_t)Hs * p->d_idx, p->d_idx};
+    const sa_tensor wt{wa, SA_F32, (int64_t)p->n_q * Hs, Hs, 0};
+    return run_select(&pa, qt, k_idx, wt, idx, status, base + l.region, st);
 }
 
 float eff_scale(const sa_problem* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d_qk); }
@@ -620,7 +657,7 @@ sa_status sa_hisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, 
 
 size_t sa_misa_workspace_bytes(const sa_problem* p, int blk, int g) {
     if (!misa_args_ok(p, blk, g)) return 0;
-    return misa_layout(*p, g).total;
+    return misa_layout(*p, g, misa_heads(g)).total;
 }
 
 sa_status sa_misa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, const uint16_t* kbar,
@@ -633,50 +670,25 @@ sa_status sa_misa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, 
     if (s != SA_OK) return s;
     if (q_idx.dtype != SA_BF16 || !misa_route_supported(*p)) return SA_ERR_UNSUPPORTED;
     if ((s = ws_ok(ws, ws_bytes, sa_misa_workspace_bytes(p, blk, g))) != SA_OK) return s;
-    hipStream_t st = (hipStream_t)stream;
-    char* base = static_cast<char*>(ws);
-    const MisaLayout l = misa_layout(*p, g);
-    int32_t* row_blk = reinterpret_cast<int32_t*>(base + l.row_blk);
-    float* route = reinterpret_cast<float*>(base + l.route);
-    int32_t* hsel = heads ? heads : reinterpret_cast<int32_t*>(base + l.heads);
-    uint16_t* qa = reinterpret_cast<uint16_t*>(base + l.qa);
-    float* wa = reinterpret_cast<float*>(base + l.wa);
-    float* scores = reinterpret_cast<float*>(base + l.scores);
-    Status* status = reinterpret_cast<Status*>(base);
+    return misa_run(p, q_idx, k_idx, w, kbar, blk, g, false, idx, heads, static_cast<char*>(ws), (hipStream_t)stream);
+}
 
-    if (launch_hisa_rows(*p, blk, row_blk, st) != hipSuccess) return SA_ERR_HIP;
-    if (launch_misa_route(*p, q_idx, w, kbar, blk, row_blk, route, st) != hipSuccess) return SA_ERR_HIP;
-    TopkArgs th;  // g heads of Hidx per row, ranked by (routing score desc, head asc)
-    th.p = misa_head_problem(*p, g);
-    th.scores = route;
-    th.row_stride = p->Hidx;
-    th.idx = hsel;
-    th.vals = nullptr;
-    th.status = status;
-    th.scratch = base + l.scratch;
-    if (launch_topk(th, st) != hipSuccess) return SA_ERR_HIP;
-    if (launch_misa_gather(*p, q_idx, w, g, hsel, qa, wa, st) != hipSuccess) return SA_ERR_HIP;
-    sa_problem pa = *p;
-    pa.Hidx = g;
-    IndexerArgs ia;
-    ia.p = pa;
-    ia.q = sa_tensor{qa, SA_BF16, (int64_t)p->n_q * g * p->d_idx, (int64_t)g * p->d_idx, p->d_idx};
-    ia.k = k_idx;
-    ia.w = sa_tensor{wa, SA_F32, (int64_t)p->n_q * g, g, 0};
-    ia.scores = scores;
-    ia.row_stride = p->n_kv;
-    ia.fill_invisible = 0;
-    ia.status = nullptr;  // non-finite scores stay visible and are reported by the selection
-    if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
-    TopkArgs ta;
-    ta.p = pa;
-    ta.scores = scores;
-    ta.row_stride = p->n_kv;
-    ta.idx = idx;
-    ta.vals = nullptr;
-    ta.status = status;
-    ta.scratch = base + l.scratch;
-    return launch_topk(ta, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
+size_t sa_resmisa_workspace_bytes(const sa_problem* p, int blk, int g) {
+    if (!misa_args_ok(p, blk, g) || g + 6 > 64) return 0;
+    return misa_layout(*p, g, resmisa_heads(g)).total;
+}
+
+sa_status sa_resmisa_select(const sa_problem* p, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w, const uint16_t* kbar,
+                            int blk, int g, int32_t* idx, int32_t* heads, void* ws, size_t ws_bytes, void* stream) {
+    if (!problem_ok(p) || !kbar || ((uintptr_t)kbar & 15) || !idx || ((uintptr_t)idx & 3)) return SA_ERR_INVALID_ARG;
+    if (heads && ((uintptr_t)heads & 3)) return SA_ERR_INVALID_ARG;
+    if (blk != 16 && blk != 32 && blk != 64 && blk != 128 && blk != 256) return SA_ERR_INVALID_ARG;
+    if (g < 1 || g > p->Hidx || g + 6 > 64 || p->n_kv / blk < 1) return SA_ERR_INVALID_ARG;
+    sa_status s = check_indexer(p, q_idx, k_idx, w);
+    if (s != SA_OK) return s;
+    if (q_idx.dtype != SA_BF16 || !misa_route_supported(*p)) return SA_ERR_UNSUPPORTED;
+    if ((s = ws_ok(ws, ws_bytes, sa_resmisa_workspace_bytes(p, blk, g))) != SA_OK) return s;
+    return misa_run(p, q_idx, k_idx, w, kbar, blk, g, true, idx, heads, static_cast<char*>(ws), (hipStream_t)stream);
 }
 
 sa_status sa_device_status(void* ws, void* stream) {

@@ -12,7 +12,20 @@
 //    B fragment read straight from memory (a batch's representatives stay in L2), the
 //    ReLU'd products summed per head in registers, then across the 16 lanes of a head and
 //    the four waves in a fixed order;
-//  * misa_gather: the active heads' index queries and weights, in ascending head order.
+//  * misa_gather: the active heads' index queries and weights, in ascending head order,
+//    then zero heads up to 16, 32 or 64.
+//  * resmisa_gather (the ResMiSA paragraph of the same section: ReLU(z) = z + ReLU(-z) makes
+//    the heads' linear terms ONE shared dot product, and only some heads keep their
+//    non-linear residual): the query heads of a derived indexer problem whose score is
+//    <qbar, k> + sum_{h active} w_h ReLU(-<q_h, k>) with qbar = sum_h w_h q_h:
+//      slots 0 .. g-1    residual heads, query -q_h (exact bf16 negation), weight w_h;
+//      slots g .. g+5    the shared term: qbar in fp32 split exactly into three bf16 parts
+//                        b1 + b2 + b3, each as the pair (b, +1), (-b, -1), since
+//                        ReLU(<b, k>) - ReLU(<-b, k>) = <b, k>;
+//      the rest          zero query and weight (padding to the indexer's 16 / 32 / 64 heads).
+//    qbar is summed in fp32 in ascending head order; the split is exact for normal values
+//    (each part takes the next 8 significant bits), so the indexer's fp32 accumulation sees
+//    the shared query to fp32 precision.
 #include "sa_internal.h"
 
 namespace sa {
@@ -87,20 +100,68 @@ __global__ void __launch_bounds__(256) misa_route(sa_problem p, sa_tensor q, sa_
     }
 }
 
-// thread (r, j, piece): piece of active head j of row r (16 bytes of its bf16 query)
-__global__ void __launch_bounds__(256) misa_gather(sa_problem p, sa_tensor q, sa_tensor w, int g, const int32_t* heads,
-                                                   uint16_t* qa, float* wa) {
+// thread (r, j, piece): piece of slot j of row r (16 bytes of a bf16 query); slots g .. Hs-1
+// are zero heads
+__global__ void __launch_bounds__(256) misa_gather(sa_problem p, sa_tensor q, sa_tensor w, int g, int Hs,
+                                                   const int32_t* heads, uint16_t* qa, float* wa) {
     const int pieces = p.d_idx / 8;
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (long)p.B * p.n_q * g * pieces) return;
+    if (e >= (long)p.B * p.n_q * Hs * pieces) return;
     const int c = (int)(e % pieces);
     const long rj = e / pieces;
-    const long r = rj / g;
+    const long r = rj / Hs;
+    const int j = (int)(rj % Hs);
     const int b = (int)(r / p.n_q), i = (int)(r % p.n_q);
-    const int h = heads[rj];
-    const uint16_t* src = static_cast<const uint16_t*>(q.data) + b * q.s0 + (int64_t)i * q.s1 + (int64_t)h * q.s2 + 8 * c;
-    *reinterpret_cast<uint4*>(qa + rj * p.d_idx + 8 * c) = *reinterpret_cast<const uint4*>(src);
-    if (c == 0) wa[rj] = static_cast<const float*>(w.data)[b * w.s0 + (int64_t)i * w.s1 + h];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    float wv = 0.f;
+    if (j < g) {
+        const int h = heads[r * g + j];
+        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.data) + b * q.s0 + (int64_t)i * q.s1 +
+                                            (int64_t)h * q.s2 + 8 * c);
+        wv = static_cast<const float*>(w.data)[b * w.s0 + (int64_t)i * w.s1 + h];
+    }
+    *reinterpret_cast<uint4*>(qa + rj * p.d_idx + 8 * c) = v;
+    if (c == 0) wa[rj] = wv;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// one workgroup of d_idx threads per query row; thread t owns element t of every slot
+__global__ void __launch_bounds__(128) resmisa_gather(sa_problem p, sa_tensor q, sa_tensor w, int g, int Hp,
+                                                      const int32_t* heads, uint16_t* qa, float* wa) {
+    const long r = blockIdx.x;
+    const int b = (int)(r / p.n_q), i = (int)(r % p.n_q);
+    const int t = threadIdx.x;
+    const uint16_t* qr = static_cast<const uint16_t*>(q.data) + b * q.s0 + (int64_t)i * q.s1;
+    const float* wr = static_cast<const float*>(w.data) + b * w.s0 + (int64_t)i * w.s1;
+    uint16_t* out = qa + r * (int64_t)Hp * p.d_idx;
+    float qbar = 0.f;
+    for (int h = 0; h < p.Hidx; ++h) qbar = fmaf(wr[h], bf16_val(qr[(int64_t)h * q.s2 + t]), qbar);
+    const uint16_t b1 = bf16_rne(qbar);
+    const float r1 = qbar - bf16_val(b1);
+    const uint16_t b2 = bf16_rne(r1);
+    const uint16_t b3 = bf16_rne(r1 - bf16_val(b2));
+    const uint16_t part[3] = {b1, b2, b3};
+    for (int j = 0; j < g; ++j) {
+        const int h = heads[r * g + j];
+        out[(int64_t)j * p.d_idx + t] = qr[(int64_t)h * q.s2 + t] ^ 0x8000u;
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        out[(int64_t)(g + 2 * m) * p.d_idx + t] = part[m];
+        out[(int64_t)(g + 2 * m + 1) * p.d_idx + t] = part[m] ^ 0x8000u;
+    }
+    for (int j = g + 6; j < Hp; ++j) out[(int64_t)j * p.d_idx + t] = 0;
+    float* wo = wa + r * Hp;
+    if (t < g) wo[t] = wr[heads[r * g + t]];
+    else if (t < g + 6) wo[t] = ((t - g) & 1) ? -1.f : 1.f;
+    else if (t < Hp) wo[t] = 0.f;
 }
 
 }  // namespace
@@ -126,9 +187,23 @@ hipError_t launch_misa_route(const sa_problem& p, const sa_tensor& q, const sa_t
 
 hipError_t launch_misa_gather(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, int g, const int32_t* heads,
                               uint16_t* qa, float* wa, hipStream_t s) {
-    const long n = (long)p.B * p.n_q * g * (p.d_idx / 8);
-    hipLaunchKernelGGL(misa_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, q, w, g, heads, qa, wa);
+    const int Hs = misa_heads(g);
+    const long n = (long)p.B * p.n_q * Hs * (p.d_idx / 8);
+    hipLaunchKernelGGL(misa_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, q, w, g, Hs, heads, qa, wa);
     return hipGetLastError();
 }
 
+}  // namespace sa
+
+namespace sa {
+int misa_heads(int g) { return g <= 16 ? 16 : (g <= 32 ? 32 : 64); }
+int resmisa_heads(int g) { return misa_heads(g + 6); }
+
+hipError_t launch_resmisa_gather(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, int g, const int32_t* heads,
+                                 uint16_t* qa, float* wa, hipStream_t s) {
+    const int Hp = resmisa_heads(g);
+    hipLaunchKernelGGL(resmisa_gather, dim3((unsigned)((long)p.B * p.n_q)), dim3(p.d_idx), 0, s, p, q, w, g, Hp, heads,
+                       qa, wa);
+    return hipGetLastError();
+}
 }  // namespace sa

@@ -121,8 +121,17 @@ hipError_t launch_hisa_map(const sa_problem& p, int blk, int k_blocks, const int
 bool misa_route_supported(const sa_problem& p);
 hipError_t launch_misa_route(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, const uint16_t* kbar, int blk,
                              const int32_t* row_blk, float* route, hipStream_t s);
+// Scored heads of the derived indexer problem: the g active heads padded with zero heads to
+// misa_heads(g) (16, 32 or 64, the head counts the streaming selection takes; a zero head
+// adds exactly +0 to every score).
+int misa_heads(int g);
 hipError_t launch_misa_gather(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, int g, const int32_t* heads,
                               uint16_t* qa, float* wa, hipStream_t s);
+// Shared linear term + residual heads: the derived problem's heads (resmisa_heads(g) of them:
+// g residual heads, six parts of the shared query, zero padding), queries and weights.
+int resmisa_heads(int g);
+hipError_t launch_resmisa_gather(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, int g, const int32_t* heads,
+                                 uint16_t* qa, float* wa, hipStream_t s);
 
 // Host-side planning shared by workspace sizing and launches.
 int attn_splits(const sa_problem& p);
