@@ -119,6 +119,37 @@ def test_fused_selection_with_heavy_exact_ties(pool):
             assert g[i, :m].tolist() == list(range(m)) and (g[i, m:] == -1).all()
 
 
+@pytest.mark.parametrize("sign", ["alternating", "negative", "sparse"])
+@pytest.mark.parametrize("case", ["h64_d128_e4m3_k64", "h16_d128_bf16", "h32_d64_e4m3_chunked"])
+def test_fused_selection_with_signed_scores(case, sign):
+    # head weights of both signs (scores straddle zero), all negative (every score <= 0), or
+    # zero on all but three heads (about 1/8 of the scores are exactly zero): the histogram
+    # bins, uniform in score, must stay exact across the sign change and the zero ties
+    W = _workload(CASES[case], seed=51)
+    w = W["w"].astype(np.float32)
+    H = W["Hidx"]
+    if sign == "alternating":
+        w = w * np.where(np.arange(H) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    elif sign == "negative":
+        w = -w
+    else:
+        w = w * (np.arange(H) < 3).astype(np.float32)
+    W["w"] = np.ascontiguousarray(w)
+    P, d = device_workload(W, with_main=False)
+    _say("fused select %s, %s weights" % (case, sign))
+    ref, sc = two_pass(W, P, d)
+    got, st = fused(W, P, d)
+    assert st == sa.SA_OK
+    r = _first_diff(got, ref)
+    assert r is None, ("row", r)
+    rows = gc.sample_rows(W, n_each=4, n_rand=12)
+    ref_sc = orc.scores(W, rows)
+    ref_idx, sk, _, _ = orc.select(W, ref_sc, rows)
+    g = got.reshape(-1, W["k"]).cpu().numpy()[rows]
+    gsc = sc.reshape(-1, W["n_kv"]).cpu().numpy()[rows]
+    check_index_rows(W, rows, g, ref_sc, ref_idx, sk, gpu_scores=gsc)
+
+
 def test_select_attend_uses_the_fused_selection():
     # the fused call's selection (idx_out) equals sa_select's and the attention matches the
     # oracle on sampled rows

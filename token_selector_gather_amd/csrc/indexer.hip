@@ -262,9 +262,9 @@ __global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, 
 // tau stays below the k-th largest key seen so far, so every key that can still be in the
 // row's top k is in the list (a key at or below tau has k larger keys before it).  It is
 // raised from a histogram of the list's keys kept in LDS: after the first chunk the row's
-// keys fix the bins (bin 0 = below `base`, bin b = [base + (b-1) 2^sh, base + b 2^sh), the
-// last bin open above), every append adds its key, and tau becomes the lowest key of the
-// bin that holds the k-th largest listed key, minus one.  When the list could overflow at
+// scores fix the bins (uniform in score, see below; bin 0 below the first boundary, the last
+// bin open above), every append adds its score, and tau becomes the key of the lower
+// boundary of the bin that holds the k-th largest listed key, minus one.  When the list could overflow at
 // the next chunk, the keys at or below tau are dropped (one ordered pass; the bins below
 // tau's bin empty exactly).  If that frees too little (keys far outside the bins), the list
 // is cut to its exact top k and the bins are rebuilt around the cut.  At the end the exact
@@ -337,25 +337,44 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     return max(a, b);
 }
 
-// Bins of a row's histogram: 0 below base, b in [1, NB - 1) for [base + (b-1) 2^sh, base +
-// b 2^sh), NB - 1 for everything above.
-template <int NB>
-__device__ __forceinline__ int key_bin(uint32_t key, uint32_t base, uint32_t sh) {
-    if (key < base) return 0;
-    return (int)min(((key - base) >> sh) + 1u, (uint32_t)(NB - 1));
+// Bins of a row's histogram, uniform in score: with a power-of-two width W = 2^e and an
+// integer origin j0, bin 0 holds the scores below j0 W, bin b in [1, NB - 1) the scores in
+// [(j0 + b - 1) W, (j0 + b) W), bin NB - 1 everything above.  Bins uniform in the score keep
+// their resolution where a row's scores change sign (bins uniform in the key would spend
+// themselves on the tiny magnitudes around zero).  Exactness: every boundary (j0 + b - 1) W
+// is a float (|j0| + NB < 2^24 and e in [-126, 103]), and floor(v / W) is exact (v 2^-e is
+// exact when |v| >= W, and |v| < W is decided by a comparison), so a key lies in a bin >= b
+// exactly when it is at least the key of that bin's lower boundary.  The row's bin state
+// is (W as float bits, j0).
+__device__ __forceinline__ float sel_val(uint32_t key) {  // inverse of sel_key (+0 for a folded -0)
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
-__device__ __forceinline__ uint32_t bin_lowest(int b, uint32_t base, uint32_t sh) {  // b >= 1
-    const uint64_t e = (uint64_t)base + ((uint64_t)(b - 1) << sh);
-    return e > 0xffffffffull ? 0xffffffffu : (uint32_t)e;
+__device__ __forceinline__ float sel_ffloor(float v, uint32_t wbits) {  // floor(v / W)
+    const float W = __uint_as_float(wbits);
+    const float Wi = __uint_as_float((254u - (wbits >> 23)) << 23);  // 2^-e
+    return fabsf(v) < W ? (v < 0.f ? -1.f : 0.f) : floorf(v * Wi);
 }
-// bin width for keys spanning [lo, hi]: the span takes at most NB / 2 bins, the rest is
-// room above
 template <int NB>
-__device__ __forceinline__ uint32_t bin_shift(uint32_t lo, uint32_t hi) {
-    const uint32_t span = hi - lo;
-    uint32_t sh = 0;
-    while ((span >> sh) >= (uint32_t)(NB / 2)) ++sh;
-    return sh;
+__device__ __forceinline__ int sel_bin(float v, uint32_t wbits, int j0) {
+    const float x = sel_ffloor(v, wbits) - (float)j0 + 1.f;
+    return (int)fminf(fmaxf(x, 0.f), (float)(NB - 1));
+}
+__device__ __forceinline__ uint32_t bin_lowest(int b, uint32_t wbits, int j0) {  // b >= 1: key of the lower boundary
+    return sel_key((float)(j0 + b - 1) * __uint_as_float(wbits));
+}
+// bins for keys spanning [lo, hi]: the span takes at most NB / 2 bins (the rest is room
+// above), the width is at least 2^-22 of the larger magnitude (|j0| < 2^23)
+template <int NB>
+__device__ __forceinline__ void sel_bins(uint32_t lo, uint32_t hi, uint32_t& wbits, int& j0) {
+    const float vlo = sel_val(lo), vhi = sel_val(hi);
+    const float span = (vhi - vlo) * (1.f / (float)(NB / 2 - 1));
+    const int ex_span = span > 0.f ? (int)((__float_as_uint(fminf(span, 3.0e38f)) >> 23) & 0xff) - 127 + 1 : -126;
+    const float mag = fminf(fmaxf(fabsf(vlo), fabsf(vhi)), 3.0e38f);
+    const int ex_mag = (int)((__float_as_uint(mag) >> 23) & 0xff) - 127 - 22;
+    const int e = min(max(max(ex_span, ex_mag), -126), 103);
+    wbits = (uint32_t)(e + 127) << 23;
+    const float f = fminf(fmaxf(sel_ffloor(vlo, wbits), -8388608.f), 8388608.f);
+    j0 = (int)f;
 }
 
 // In an NB-bin histogram (bins ascending in key), the bin holding the need-th largest
@@ -410,12 +429,13 @@ __device__ __forceinline__ void sel_load(const uint32_t* keys, int n, int e0, in
     }
 }
 
-// Exact threshold of the top `need` keys among the keys of [lo, lo + 2^bits) (nB of them),
-// refining the digit below `bits` (a 256-bin histogram per step, or the short list once the
-// open bin holds at most 64 keys).  tu: relative prefix so far.  Returns T and the number
-// of keys equal to T that the selection keeps.
-__device__ __forceinline__ void sel_refine(const uint32_t* keys, int n, uint32_t lo, int bits, uint32_t tu, uint32_t nB,
-                                           uint32_t need, SelScratch* sc, int lane, uint32_t& T, uint32_t& need_eq) {
+// Exact threshold of the top `need` keys among the keys of [lo, top] (nB of them, all in
+// [lo, lo + 2^bits)), refining the digit below `bits` (a 256-bin histogram per step, or the
+// short list once the open bin holds at most 64 keys).  tu: relative prefix so far.
+// Returns T and the number of keys equal to T that the selection keeps.
+__device__ __forceinline__ void sel_refine(const uint32_t* keys, int n, uint32_t lo, uint32_t top, int bits, uint32_t tu,
+                                           uint32_t nB, uint32_t need, SelScratch* sc, int lane, uint32_t& T,
+                                           uint32_t& need_eq) {
     while (bits > 0) {
         if (nB <= 64u) {
             // the open bin's keys to a list, ranked by one lane each
@@ -432,7 +452,7 @@ __device__ __forceinline__ void sel_refine(const uint32_t* keys, int n, uint32_t
                     uint32_t c = 0;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        hit[i] = e + i < n && k4[i] >= lo && (uint32_t)((uint64_t)(k4[i] - lo) >> bits) == pref;
+                        hit[i] = e + i < n && k4[i] >= lo && k4[i] <= top && (uint32_t)((uint64_t)(k4[i] - lo) >> bits) == pref;
                         c += hit[i];
                     }
                     uint32_t tot;
@@ -472,7 +492,7 @@ __device__ __forceinline__ void sel_refine(const uint32_t* keys, int n, uint32_t
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t r = k4[i] - lo;
-                    if (e + i < n && k4[i] >= lo && (uint32_t)((uint64_t)r >> (bits + d)) == pref)
+                    if (e + i < n && k4[i] >= lo && k4[i] <= top && (uint32_t)((uint64_t)r >> (bits + d)) == pref)
                         atomicAdd(&sc->hist[(r >> bits) & dmask], 1u);
                 }
             }
@@ -514,7 +534,7 @@ __device__ __forceinline__ void sel_threshold(const uint32_t* keys, int n, uint3
     hi = wave_max(hi);
     const uint32_t range = hi - lo;
     const int bits = range == 0 ? 0 : 32 - __clz((int)range);  // every key has (key - lo) >> bits == 0
-    sel_refine(keys, n, lo, bits, 0u, (uint32_t)n, K, sc, lane, T, need_eq);
+    sel_refine(keys, n, lo, hi, bits, 0u, (uint32_t)n, K, sc, lane, T, need_eq);
 }
 
 // Ordered compaction of a list: keeps the entries with key > T and the first need_eq
@@ -857,7 +877,7 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
                             lk[sel.cap + slot] = (uint32_t)j;
                             if (c > 0) {  // the row's bins exist from the second chunk on
                                 const int r = QW * wv + g + 4 * z;
-                                atomicAdd(&s_rh[r][key_bin<NBR>(key, s_rp[r][0], s_rp[r][1])], 1u);
+                                atomicAdd(&s_rh[r][sel_bin<NBR>(v, s_rp[r][0], (int)s_rp[r][1])], 1u);
                             }
                         }
                         cnt[z] += (uint32_t)__builtin_popcount(gm);
@@ -911,28 +931,31 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
                             const uint32_t k1 = ln + 64 < (int)n ? keys[ln + 64] : 0xffffffffu;
                             const uint32_t lo = wave_min(min(k0, k1));
                             const uint32_t hi = wave_max(max(ln < (int)n ? k0 : 0u, ln + 64 < (int)n ? k1 : 0u));
-                            const uint32_t sh = n ? bin_shift<NBR>(lo, hi) : 0u;
+                            uint32_t wb = 127u << 23;
+                            int j0 = 0;
+                            if (n) sel_bins<NBR>(lo, hi, wb, j0);
                             if (ln == 0) {
-                                s_rp[r][0] = lo;
-                                s_rp[r][1] = sh;
+                                s_rp[r][0] = wb;
+                                s_rp[r][1] = (uint32_t)j0;
                             }
                             if (4 * ln < NBR) *reinterpret_cast<uint4*>(&s_rh[r][4 * ln]) = make_uint4(0u, 0u, 0u, 0u);
-                            if (ln < (int)n) atomicAdd(&s_rh[r][key_bin<NBR>(k0, lo, sh)], 1u);
-                            if (ln + 64 < (int)n) atomicAdd(&s_rh[r][key_bin<NBR>(k1, lo, sh)], 1u);
+                            if (ln < (int)n) atomicAdd(&s_rh[r][sel_bin<NBR>(sel_val(k0), wb, j0)], 1u);
+                            if (ln + 64 < (int)n) atomicAdd(&s_rh[r][sel_bin<NBR>(sel_val(k1), wb, j0)], 1u);
                             wait_lgkmcnt0();
                         }
-                        const uint32_t base = s_rp[r][0], sh = s_rp[r][1];
+                        const uint32_t wb = s_rp[r][0];
+                        const int j0 = (int)s_rp[r][1];
                         const bool full = n + CK > (uint32_t)sel.cap;
                         if (n >= (uint32_t)K && ((c & 1) == 0 || full)) {  // every other chunk, or before a cut
                             int bk;
                             uint32_t above;
                             sel_find_bin<NBR>(s_rh[r], (uint32_t)K, ln, bk, above);
-                            if (bk >= 1) t = max(t, bin_lowest(bk, base, sh) - 1u);
+                            if (bk >= 1) t = max(t, bin_lowest(bk, wb, j0) - 1u);
                         }
                         if (full) {
                             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's appends have landed
                             n = sel_compact(keys, pos, (int)n, t, 0u, keys, pos, ln);  // keys > t
-                            const int bt = key_bin<NBR>(t + 1u, base, sh);  // the bins below hold keys <= t
+                            const int bt = sel_bin<NBR>(sel_val(t + 1u), wb, j0);  // the bins below hold keys <= t
                             for (int e = ln; e < bt; e += 64) s_rh[r][e] = 0u;
                             if (n + CK > (uint32_t)sel.cap) {
                                 // keys far outside the bins: cut to the exact top k, new bins from there
@@ -941,13 +964,15 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
                                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                                 n = sel_compact(keys, pos, (int)n, T, need_eq, keys, pos, ln);
                                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                                const uint32_t sh2 = bin_shift<NBR>(T, hi);
+                                uint32_t wb2;
+                                int j02;
+                                sel_bins<NBR>(T, hi, wb2, j02);
                                 if (ln == 0) {
-                                    s_rp[r][0] = T;
-                                    s_rp[r][1] = sh2;
+                                    s_rp[r][0] = wb2;
+                                    s_rp[r][1] = (uint32_t)j02;
                                 }
                                 for (int e = ln; e < NBR; e += 64) s_rh[r][e] = 0u;
-                                for (int e = ln; e < (int)n; e += 64) atomicAdd(&s_rh[r][key_bin<NBR>(keys[e], T, sh2)], 1u);
+                                for (int e = ln; e < (int)n; e += 64) atomicAdd(&s_rh[r][sel_bin<NBR>(sel_val(keys[e]), wb2, j02)], 1u);
                                 t = T > 0u ? T - 1u : 0u;
                             }
                             wait_lgkmcnt0();
@@ -985,9 +1010,13 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
                 uint32_t above = 0;
                 if (binned) sel_find_bin<NBR>(s_rh[r], (uint32_t)K, ln, bk, above);
                 if (binned && bk >= 1 && bk < NBR - 1) {
-                    const uint32_t base = s_rp[r][0], sh = s_rp[r][1];
-                    sel_refine(keys, (int)n, bin_lowest(bk, base, sh), (int)sh, 0u, s_rh[r][bk], (uint32_t)K - above,
-                               &s_sel[wv], ln, T, need_eq);
+                    const uint32_t wb = s_rp[r][0];
+                    const int j0 = (int)s_rp[r][1];
+                    const uint32_t lo = bin_lowest(bk, wb, j0), top = bin_lowest(bk + 1, wb, j0) - 1u;
+                    const uint32_t span = top - lo;
+                    const int bits = span == 0 ? 0 : 32 - __clz((int)span);
+                    sel_refine(keys, (int)n, lo, top, bits, 0u, s_rh[r][bk], (uint32_t)K - above, &s_sel[wv], ln, T,
+                               need_eq);
                 } else {
                     uint32_t hi;
                     sel_threshold(keys, (int)n, (uint32_t)K, &s_sel[wv], ln, T, need_eq, hi);
