@@ -532,6 +532,24 @@ def main():
         n_rand = max(0, args.cpu_rows - 128)
         rows, what = stratified_rows(W, 64, 64, n_rand)
         out["cpu_baseline"] = cpu_baseline(W, rows, what)
+        # single-core rates of the two small workloads (all of c0, a stratified 256-row
+        # sample of c1), as context for the per-core cost of the oracle
+        one = {}
+        saved = os.environ.get("OMP_NUM_THREADS")
+        os.environ["OMP_NUM_THREADS"] = "1"
+        try:
+            for cid, n_rand in ((0, 1 << 30), (1, 128)):
+                Wc = sa_synth.make_config(cid)
+                rows_c, what_c = stratified_rows(Wc, 64, 64, n_rand)
+                r = cpu_baseline(Wc, rows_c, what_c)
+                one[Wc["name"]] = {"value": r["value"], "unit": r["unit"], "cores": r["cores"], "sample": r["sample"]}
+                del Wc
+        finally:
+            if saved is None:
+                os.environ.pop("OMP_NUM_THREADS", None)
+            else:
+                os.environ["OMP_NUM_THREADS"] = saved
+        out["cpu_baseline"]["one_core"] = one
     print(json.dumps(out))
 
 
