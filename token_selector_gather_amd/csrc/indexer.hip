@@ -405,6 +405,40 @@ __device__ __forceinline__ void sel_find_bin(const uint32_t* h, uint32_t need, i
     above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
 }
 
+// The same search for four rows at once, one per 16-lane group (h: the group's histogram):
+// lane l of a group reads bins NB - 1 - BPL l down to NB - BPL (l + 1), the group scans
+// inside its DPP row, and every lane of the group gets the bin (0 when need exceeds the
+// total).
+template <int NB>
+__device__ __forceinline__ int sel_find_bin_rows(const uint32_t* h, uint32_t need, int l15) {
+    constexpr int BPL = (NB + 15) / 16;
+    uint32_t cnt[BPL], local = 0;
+#pragma unroll
+    for (int e = 0; e < BPL; ++e) {
+        const int b = NB - 1 - BPL * l15 - e;
+        cnt[e] = b >= 0 ? h[b] : 0u;
+        local += cnt[e];
+    }
+    uint32_t incl = local;
+    incl += dpp_u32<0x111>(incl);  // row_shr:1
+    incl += dpp_u32<0x112>(incl);  // row_shr:2
+    incl += dpp_u32<0x114>(incl);  // row_shr:4
+    incl += dpp_u32<0x118>(incl);  // row_shr:8
+    uint32_t run = incl - local;
+    uint32_t bl = 0;  // bin + 1 on the lane where the count crosses need
+#pragma unroll
+    for (int e = 0; e < BPL; ++e) {
+        if (bl == 0 && run < need && run + cnt[e] >= need) bl = (uint32_t)(NB - BPL * l15 - e);
+        run += cnt[e];
+    }
+    // maximum over the row: quad swaps, half-row mirror, row mirror
+    bl = max(bl, (uint32_t)__builtin_amdgcn_update_dpp((int)bl, (int)bl, 0xB1, 0xf, 0xf, false));
+    bl = max(bl, (uint32_t)__builtin_amdgcn_update_dpp((int)bl, (int)bl, 0x4E, 0xf, 0xf, false));
+    bl = max(bl, (uint32_t)__builtin_amdgcn_update_dpp((int)bl, (int)bl, 0x141, 0xf, 0xf, false));
+    bl = max(bl, (uint32_t)__builtin_amdgcn_update_dpp((int)bl, (int)bl, 0x140, 0xf, 0xf, false));
+    return bl > 0 ? (int)bl - 1 : 0;
+}
+
 // Scratch of one wave for exact thresholds: a 256-bin digit histogram and a short list.
 struct SelScratch {
     uint32_t hist[256];
@@ -918,15 +952,14 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
                 // the histogram, and dead entries dropped when the next chunk could overflow
                 if (c + 1 < nch) {
                     const int ln = opaque_tid() & 63;
+                    if (c == 0) {
+                        // bins from each row's first chunk: every visible key of it is listed (n <= 128)
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-                    for (int q = 0; q < QW; ++q) {
-                        const int z = q >> 2, gq = q & 3, r = QW * wv + q;
-                        uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cnt[z], 16 * gq);
-                        uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tau[z], 16 * gq);
-                        uint32_t* keys = row_keys(q);
-                        int32_t* pos = reinterpret_cast<int32_t*>(keys + sel.cap);
-                        if (c == 0) {  // every visible key of the first chunk is listed (n <= 128)
-                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        for (int q = 0; q < QW; ++q) {
+                            const int z = q >> 2, gq = q & 3, r = QW * wv + q;
+                            const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cnt[z], 16 * gq);
+                            const uint32_t* keys = row_keys(q);
                             const uint32_t k0 = ln < (int)n ? keys[ln] : 0xffffffffu;
                             const uint32_t k1 = ln + 64 < (int)n ? keys[ln + 64] : 0xffffffffu;
                             const uint32_t lo = wave_min(min(k0, k1));
@@ -941,42 +974,74 @@ __global__ void __launch_bounds__(256, 2) indexer_pf(IndexerArgs a, int n_qb, Se
                             if (4 * ln < NBR) *reinterpret_cast<uint4*>(&s_rh[r][4 * ln]) = make_uint4(0u, 0u, 0u, 0u);
                             if (ln < (int)n) atomicAdd(&s_rh[r][sel_bin<NBR>(sel_val(k0), wb, j0)], 1u);
                             if (ln + 64 < (int)n) atomicAdd(&s_rh[r][sel_bin<NBR>(sel_val(k1), wb, j0)], 1u);
-                            wait_lgkmcnt0();
                         }
+                        wait_lgkmcnt0();
+                    }
+                    // every other chunk, and before a cut: a higher threshold from each row's
+                    // histogram; with four or eight rows per wave all rows at once (lane group g
+                    // holds row g + 4 z), with two (and many more bins) one row after the other
+                    if constexpr (QW >= 4) {
+#pragma unroll
+                        for (int z = 0; z < NZ; ++z) {
+                            const int r = QW * wv + g + 4 * z;
+                            const bool full = cnt[z] + CK > (uint32_t)sel.cap;
+                            const bool upd = cnt[z] >= (uint32_t)K && ((c & 1) == 0 || full);
+                            if (__ballot(upd) != 0) {
+                                const int bk = sel_find_bin_rows<NBR>(s_rh[r], (uint32_t)K, l15);
+                                if (upd && bk >= 1) tau[z] = max(tau[z], bin_lowest(bk, s_rp[r][0], (int)s_rp[r][1]) - 1u);
+                            }
+                            tauf[z] = sel_floor(tau[z]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < QW; ++q) {
+                            const int r = QW * wv + q;
+                            const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cnt[0], 16 * q);
+                            const bool full = n + CK > (uint32_t)sel.cap;
+                            if (n >= (uint32_t)K && ((c & 1) == 0 || full)) {
+                                int bk;
+                                uint32_t above;
+                                sel_find_bin<NBR>(s_rh[r], (uint32_t)K, ln, bk, above);
+                                if (bk >= 1 && g == q) tau[0] = max(tau[0], bin_lowest(bk, s_rp[r][0], (int)s_rp[r][1]) - 1u);
+                            }
+                        }
+                        tauf[0] = sel_floor(tau[0]);
+                    }
+                    // rows whose list could overflow at the next chunk: drop the entries at or
+                    // below the threshold, or cut to the exact top k when that frees too little
+#pragma unroll
+                    for (int q = 0; q < QW; ++q) {
+                        const int z = q >> 2, gq = q & 3, r = QW * wv + q;
+                        uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cnt[z], 16 * gq);
+                        if (n + CK <= (uint32_t)sel.cap) continue;
+                        uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tau[z], 16 * gq);
+                        uint32_t* keys = row_keys(q);
+                        int32_t* pos = reinterpret_cast<int32_t*>(keys + sel.cap);
                         const uint32_t wb = s_rp[r][0];
                         const int j0 = (int)s_rp[r][1];
-                        const bool full = n + CK > (uint32_t)sel.cap;
-                        if (n >= (uint32_t)K && ((c & 1) == 0 || full)) {  // every other chunk, or before a cut
-                            int bk;
-                            uint32_t above;
-                            sel_find_bin<NBR>(s_rh[r], (uint32_t)K, ln, bk, above);
-                            if (bk >= 1) t = max(t, bin_lowest(bk, wb, j0) - 1u);
-                        }
-                        if (full) {
-                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's appends have landed
-                            n = sel_compact(keys, pos, (int)n, t, 0u, keys, pos, ln);  // keys > t
-                            const int bt = sel_bin<NBR>(sel_val(t + 1u), wb, j0);  // the bins below hold keys <= t
-                            for (int e = ln; e < bt; e += 64) s_rh[r][e] = 0u;
-                            if (n + CK > (uint32_t)sel.cap) {
-                                // keys far outside the bins: cut to the exact top k, new bins from there
-                                uint32_t T, need_eq, hi;
-                                sel_threshold(keys, (int)n, (uint32_t)K, &s_sel[wv], ln, T, need_eq, hi);
-                                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                                n = sel_compact(keys, pos, (int)n, T, need_eq, keys, pos, ln);
-                                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                                uint32_t wb2;
-                                int j02;
-                                sel_bins<NBR>(T, hi, wb2, j02);
-                                if (ln == 0) {
-                                    s_rp[r][0] = wb2;
-                                    s_rp[r][1] = (uint32_t)j02;
-                                }
-                                for (int e = ln; e < NBR; e += 64) s_rh[r][e] = 0u;
-                                for (int e = ln; e < (int)n; e += 64) atomicAdd(&s_rh[r][sel_bin<NBR>(sel_val(keys[e]), wb2, j02)], 1u);
-                                t = T > 0u ? T - 1u : 0u;
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's appends have landed
+                        n = sel_compact(keys, pos, (int)n, t, 0u, keys, pos, ln);  // keys > t
+                        const int bt = sel_bin<NBR>(sel_val(t + 1u), wb, j0);  // the bins below hold keys <= t
+                        for (int e = ln; e < bt; e += 64) s_rh[r][e] = 0u;
+                        if (n + CK > (uint32_t)sel.cap) {
+                            // keys far outside the bins: cut to the exact top k, new bins from there
+                            uint32_t T, need_eq, hi;
+                            sel_threshold(keys, (int)n, (uint32_t)K, &s_sel[wv], ln, T, need_eq, hi);
+                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                            n = sel_compact(keys, pos, (int)n, T, need_eq, keys, pos, ln);
+                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                            uint32_t wb2;
+                            int j02;
+                            sel_bins<NBR>(T, hi, wb2, j02);
+                            if (ln == 0) {
+                                s_rp[r][0] = wb2;
+                                s_rp[r][1] = (uint32_t)j02;
                             }
-                            wait_lgkmcnt0();
+                            for (int e = ln; e < NBR; e += 64) s_rh[r][e] = 0u;
+                            for (int e = ln; e < (int)n; e += 64) atomicAdd(&s_rh[r][sel_bin<NBR>(sel_val(keys[e]), wb2, j02)], 1u);
+                            t = T > 0u ? T - 1u : 0u;
                         }
+                        wait_lgkmcnt0();
                         if (g == gq) {
                             cnt[z] = n;
                             tau[z] = t;
