@@ -38,6 +38,20 @@
  *   size a multiple of 16 bytes.  Dimension order per tensor is given at each argument.
  * Dtypes.  SA_F32, SA_BF16 (bit pattern of the upper half of an f32) and SA_FP8_E4M3
  *   (OCP e4m3fn: bias 7, no infinities, 0x7f/0xff are NaN, max 448).
+ * Environment (read at every call):
+ *   SA_DEBUG_CHECKS=1  before the attention of sa_sparse_attn, sa_sparse_attn_paged and
+ *                      sa_select_attend, a check kernel reads every candidate list and sets
+ *                      SA_ERR_INDEX in the status word when a list holds the same position
+ *                      twice (duplicates must be removed before the softmax: "PaperTrace 2.2",
+ *                      §2.1, and "PaperTrace 2.1.1", §5.1) or an entry other than -1 that is
+ *                      not visible to its row (such entries are otherwise skipped).  Repeats
+ *                      are checked for histories of at most 2^19 positions.
+ *   SA_FORCE_UNFUSED=1 sa_select and sa_select_attend store score rows and run the separate
+ *                      top-k (in row slices that fit the same workspace) instead of the
+ *                      streaming selection; the result is the same.
+ *   SA_SPLITS=n        candidate splits of the latent-head attention (clamped to what the
+ *                      kernel takes); workspace sizes depend on it, so size and call with
+ *                      the same setting.
  */
 #ifndef SA_H
 #define SA_H
@@ -49,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -57,7 +71,9 @@ typedef enum sa_status {
     SA_ERR_UNSUPPORTED = 2, /* valid but not implemented: dtype combination or head size */
     SA_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than sa_workspace_bytes() */
     SA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
-    SA_ERR_NONFINITE = 5    /* device side: a visible score was NaN or infinite */
+    SA_ERR_NONFINITE = 5,   /* device side: a visible score was NaN or infinite */
+    SA_ERR_INDEX = 6        /* device side, SA_DEBUG_CHECKS=1 only: a candidate list holds a
+                               position twice, or an entry that is neither -1 nor visible */
 } sa_status;
 
 typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_FP8_E4M3 = 2 } sa_dtype;

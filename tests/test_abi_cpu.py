@@ -40,6 +40,7 @@ def test_abi_version_and_status_strings():
     assert sa.sa_abi_version() == sa.ABI_VERSION
     assert sa.sa_status_str(sa.SA_OK) == "SA_OK"
     assert sa.sa_status_str(sa.SA_ERR_NONFINITE) == "SA_ERR_NONFINITE"
+    assert sa.sa_status_str(sa.SA_ERR_INDEX) == "SA_ERR_INDEX"
     assert sa.sa_status_str(99) == "SA_ERR_UNKNOWN"
 
 
@@ -285,3 +286,18 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(sa, "LIB_PATH", "/nonexistent/libsa.so")
     with pytest.raises(RuntimeError, match="not built"):
         sa.lib()
+
+
+@needs_lib
+def test_environment_splits_change_the_latent_workspace(monkeypatch):
+    # SA_SPLITS sets the latent attention's split count, and with it the partials' space
+    L = sa.lib()
+    p = sa._Problem(8, 1, 65536, 128, 1, 576, 512, 64, 128, 2048, 1, None, None, 0.0)
+    base = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SPARSE_ATTN)
+    monkeypatch.setenv("SA_SPLITS", "1")
+    one = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SPARSE_ATTN)
+    monkeypatch.setenv("SA_SPLITS", "64")  # clamped to one 32-row tile per split
+    many = L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SPARSE_ATTN)
+    monkeypatch.setenv("SA_SPLITS", "x")  # not a number: ignored
+    assert L.sa_workspace_bytes(ctypes.byref(p), sa.SA_OP_SPARSE_ATTN) == base
+    assert one < base < many

@@ -20,10 +20,10 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsa.so")
 
-SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_NONFINITE = range(6)
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_NONFINITE, SA_ERR_INDEX = range(7)
 SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
 SA_OP_INDEXER_SCORE, SA_OP_TOPK, SA_OP_SPARSE_ATTN, SA_OP_SELECT_ATTEND, SA_OP_SPARSE_ATTN_PAGED, SA_OP_SELECT = range(6)
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _TORCH_DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
 

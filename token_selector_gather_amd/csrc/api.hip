@@ -171,7 +171,7 @@ sa_status run_select(const sa_problem* p, const sa_tensor& q, const sa_tensor& k
     ia.p = *p;
     ia.q = q; ia.k = k; ia.w = w;
     ia.status = status;
-    if (select_fused_ok(*p, q.dtype, k.dtype))
+    if (select_fused_ok(*p, q.dtype, k.dtype) && !env_flag("SA_FORCE_UNFUSED"))
         return launch_select_fused(ia, idx, region, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
     TopkArgs ta;
     ta.p = *p;
@@ -355,6 +355,7 @@ sa_status select_attend_in(const sa_problem* p, const sa_tensor& q_idx, const sa
     char* region = static_cast<char*>(partial) + align256(attn_partial_bytes(*p));
     sa_status s = run_select(p, q_idx, k_idx, w, idx, status, region, st);
     if (s != SA_OK) return s;
+    if (env_flag("SA_DEBUG_CHECKS") && launch_check_indices(*p, idx, status, st) != hipSuccess) return SA_ERR_HIP;
     return run_attn(p, Q, K, V, idx, O, lse, partial, st);
 }
 
@@ -372,6 +373,7 @@ const char* sa_status_str(sa_status s) {
     case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
     case SA_ERR_HIP: return "SA_ERR_HIP";
     case SA_ERR_NONFINITE: return "SA_ERR_NONFINITE";
+    case SA_ERR_INDEX: return "SA_ERR_INDEX";
     default: return "SA_ERR_UNKNOWN";
     }
 }
@@ -445,6 +447,9 @@ sa_status sa_sparse_attn(const sa_problem* p, sa_tensor Q, sa_tensor K, sa_tenso
     if (s != SA_OK) return s;
     if ((s = ws_ok(ws, ws_bytes, sa_workspace_bytes(p, SA_OP_SPARSE_ATTN))) != SA_OK) return s;
     void* partial = static_cast<char*>(ws) + kStatusBytes;
+    if (env_flag("SA_DEBUG_CHECKS") &&
+        launch_check_indices(*p, idx, reinterpret_cast<Status*>(ws), (hipStream_t)stream) != hipSuccess)
+        return SA_ERR_HIP;
     return run_attn(p, Q, K, V, idx, O, lse, partial, (hipStream_t)stream);
 }
 
@@ -466,6 +471,9 @@ sa_status sa_sparse_attn_paged(const sa_problem* p, sa_tensor Q, sa_tensor K, sa
     while ((1 << pg.shift) < page_size) ++pg.shift;
     void* partial = static_cast<char*>(ws) + kStatusBytes;
     if (!attn_paged_ok(attn_args(p, Q, K, V, idx, O, lse, partial, pg))) return SA_ERR_UNSUPPORTED;
+    if (env_flag("SA_DEBUG_CHECKS") &&
+        launch_check_indices(*p, idx, reinterpret_cast<Status*>(ws), (hipStream_t)stream) != hipSuccess)
+        return SA_ERR_HIP;
     return run_attn(p, Q, K, V, idx, O, lse, partial, (hipStream_t)stream, pg);
 }
 
@@ -700,6 +708,7 @@ sa_status sa_device_status(void* ws, void* stream) {
     zero.flags = 0;
     if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return SA_ERR_HIP;
     if (st.flags & (1u << SA_ERR_NONFINITE)) return SA_ERR_NONFINITE;
+    if (st.flags & (1u << SA_ERR_INDEX)) return SA_ERR_INDEX;
     return SA_OK;
 }
 

@@ -1623,6 +1623,33 @@ bool attn_paged_ok(const AttnArgs& a) {
     return attn_uses_mla(a.p, a.Q.dtype) ? mla_lds_ok(a) : (tile_ok(a) || rows_buf_ok(a));
 }
 
+// one workgroup per query row; the row's history as a bitmap in LDS marks the positions seen
+__global__ void __launch_bounds__(256) check_indices(sa_problem p, const int32_t* idx, Status* status, int repeats) {
+    extern __shared__ uint32_t seen[];
+    const long row = blockIdx.x;
+    const int b = (int)(row / p.n_q), i = (int)(row % p.n_q);
+    const Rows R{p.kv_len, p.q_pos0, p.n_q, p.n_kv, p.causal};
+    const int L = visible_len(R, b, i);
+    if (repeats)
+        for (int w = threadIdx.x; w < (p.n_kv + 31) >> 5; w += 256) seen[w] = 0u;
+    __syncthreads();
+    bool bad = false;
+    const int32_t* ix = idx + row * (int64_t)p.k;
+    for (int e = threadIdx.x; e < p.k; e += 256) {
+        const int j = ix[e];
+        if (j == -1) continue;
+        if (j < 0 || j >= L) {
+            bad = true;
+            continue;
+        }
+        if (repeats) {
+            const uint32_t bit = 1u << (j & 31);
+            if (atomicOr(&seen[j >> 5], bit) & bit) bad = true;
+        }
+    }
+    if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) atomicOr(&status->flags, 1u << SA_ERR_INDEX);
+}
+
 bool attn_uses_mla(const sa_problem& p, int dtype) {
     const int G = p.Hq / p.Hkv;
     return dtype == SA_BF16 && G % 16 == 0 && G <= 128 && p.d_qk == 576 && p.d_v == 512;
@@ -1630,16 +1657,26 @@ bool attn_uses_mla(const sa_problem& p, int dtype) {
 
 int attn_splits(const sa_problem& p) {
     // about one workgroup per CU, at least 4 tiles of candidates per split, and at most
-    // mla::MAXE candidates per workgroup
+    // mla::MAXE candidates per workgroup; SA_SPLITS overrides the first two (at least one
+    // tile per split)
     const long units = (long)p.B * p.n_q * p.Hkv;
     long s = (256 + units - 1) / units;
     long cap = p.k / (4 * kTile);
     if (cap < 1) cap = 1;
     if (s > cap) s = cap;
+    const int forced = env_int("SA_SPLITS", 0);
+    if (forced > 0) s = std::min<long>(forced, std::max<long>(1, (p.k + kTile - 1) / kTile));
     const long need = (p.k + mla::MAXE - 1) / mla::MAXE;
     if (s < need) s = need;
     if (s < 1) s = 1;
     return (int)s;
+}
+
+hipError_t launch_check_indices(const sa_problem& p, const int32_t* idx, Status* status, hipStream_t s) {
+    const int repeats = p.n_kv <= kCheckMaxPositions;
+    const size_t lds = repeats ? (size_t)((p.n_kv + 31) >> 5) * sizeof(uint32_t) : 0;
+    hipLaunchKernelGGL(check_indices, dim3((unsigned)((long)p.B * p.n_q)), dim3(256), lds, s, p, idx, status, repeats);
+    return hipGetLastError();
 }
 
 size_t attn_partial_bytes(const sa_problem& p) {

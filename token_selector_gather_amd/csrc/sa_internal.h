@@ -1,6 +1,8 @@
 // Internal declarations shared by the host dispatcher and the kernels of libsa.so.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <cstdlib>
 #include <stdint.h>
 
 #include "sa.h"
@@ -132,6 +134,22 @@ hipError_t launch_misa_gather(const sa_problem& p, const sa_tensor& q, const sa_
 int resmisa_heads(int g);
 hipError_t launch_resmisa_gather(const sa_problem& p, const sa_tensor& q, const sa_tensor& w, int g, const int32_t* heads,
                                  uint16_t* qa, float* wa, hipStream_t s);
+
+// SA_DEBUG_CHECKS: candidate lists checked for repeated positions (histories of at most
+// kCheckMaxPositions) and for entries that are neither -1 nor visible; sets SA_ERR_INDEX.
+constexpr int kCheckMaxPositions = 1 << 18;
+hipError_t launch_check_indices(const sa_problem& p, const int32_t* idx, Status* status, hipStream_t s);
+
+// Environment switches, read at every call (debugging and tuning only): an integer value,
+// or dflt when the variable is unset, empty or not a number.
+inline int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    const long x = std::strtol(v, &end, 10);
+    return (*end == 0 && x >= -(1L << 30) && x <= (1L << 30)) ? (int)x : dflt;
+}
+inline bool env_flag(const char* name) { return env_int(name, 0) != 0; }
 
 // Host-side planning shared by workspace sizing and launches.
 int attn_splits(const sa_problem& p);
