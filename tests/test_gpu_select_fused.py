@@ -150,6 +150,24 @@ def test_fused_selection_with_signed_scores(case, sign):
     check_index_rows(W, rows, g, ref_sc, ref_idx, sk, gpu_scores=gsc)
 
 
+def test_fused_selection_with_empty_and_tiny_histories():
+    # a batch whose history is empty (every row padded), one of 37 positions (rows shorter
+    # than k return their whole prefix) and a chunked one whose first rows sit at position 0
+    W = _workload(dict(B=4, n_q=1024, n_kv=3000, Hidx=64, d_idx=128, kidx_dtype=E4M3, k=64,
+                       lens=[3000, 0, 37, 2000], q_pos0=[1976, 0, 0, 0]), seed=53)
+    P, d = device_workload(W, with_main=False)
+    ref, _ = two_pass(W, P, d)
+    got, st = fused(W, P, d)
+    assert st == sa.SA_OK
+    assert _first_diff(got, ref) is None
+    g = got.cpu().numpy()
+    assert (g[1] == -1).all()                            # empty history: nothing selected
+    assert (g[2, 37:] == -1).all()                       # padded rows of the 37-position batch
+    for i in (0, 5, 36):                                 # rows shorter than k: the whole prefix
+        assert g[2, i, : i + 1].tolist() == list(range(i + 1)) and (g[2, i, i + 1:] == -1).all()
+    assert g[3, 0, 0] == 0 and (g[3, 0, 1:] == -1).all()  # a row at position 0 sees only itself
+
+
 def test_select_attend_uses_the_fused_selection():
     # the fused call's selection (idx_out) equals sa_select's and the attention matches the
     # oracle on sampled rows

@@ -53,7 +53,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libsa.so is not built (run __graft_entry__.build()); there is no fallback path")
+            raise RuntimeError("libsa.so is not built (build it with token_selector_gather_amd.build.build()); there is no fallback path")
         L = ctypes.CDLL(LIB_PATH)
         T, P, vp, sz, i64 = _Tensor, ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
         st = ctypes.c_int
