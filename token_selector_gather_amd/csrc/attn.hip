@@ -472,15 +472,30 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         }
         __syncthreads();
 
-        // S = Q K^T: acc[j][e] = S[row 4 g + e][key 16 j + l15]
+        // S = Q K^T: acc[j][e] = S[row 4 g + e][key 16 j + l15]; k-step s runs the four key
+        // tiles' independent chains while the K fragments of k-step s + 1 are read
         f32x4 acc[4];
+        auto kread = [&](int j, int s) {
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + (16 * j + l15) * KP + 32 * s + 8 * g));
+        };
+        bf16x8 kc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            kc[j] = kread(j, 0);
+        }
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-                const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + (16 * j + l15) * KP + 32 * s + 8 * g));
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb, acc[j], 0, 0, 0);
+        for (int s = 0; s < D / 32; ++s) {
+            bf16x8 kn[4];
+            if (s + 1 < D / 32) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kn[j] = kread(j, s + 1);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kc[j], acc[j], 0, 0, 0);
+            if (s + 1 < D / 32) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kc[j] = kn[j];
             }
         }
         // mask, online softmax per row (rows 4 g + e live in the 16 lanes of group g)
@@ -524,14 +539,21 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
             for (int e = 0; e < 4; ++e) o[t][e] *= alpha[e];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
         // O += P V: A = P (row l15, keys 32 s + 8 g ..), B = V (key 32 s + 8 g .., d 16 t + l15)
+        // (V fragments read two MFMAs ahead of their use)
+        auto vread = [&](int s, int t) {
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vt + (16 * t + l15) * VP + 32 * s + 8 * g));
+        };
+        bf16x8 pa[2], vq[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const bf16x8 pa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pw + l15 * VP + 32 * s + 8 * g));
+        for (int s = 0; s < 2; ++s) pa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pw + l15 * VP + 32 * s + 8 * g));
+        vq[0] = vread(0, 0);
+        vq[1] = vread(0, 1);
 #pragma unroll
-            for (int t = 0; t < D / 16; ++t) {
-                const bf16x8 vb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vt + (16 * t + l15) * VP + 32 * s + 8 * g));
-                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
-            }
+        for (int st = 0; st < 2 * (D / 16); ++st) {
+            const int s = st / (D / 16), t = st % (D / 16);
+            const bf16x8 vb = vq[st & 1];
+            if (st + 2 < 2 * (D / 16)) vq[st & 1] = vread((st + 2) / (D / 16), (st + 2) % (D / 16));
+            o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[s], vb, o[t], 0, 0, 0);
         }
     }
     // O[row 4 g + e][d 16 t + l15] / l; LSE per row
