@@ -263,7 +263,8 @@ sa_status sa_select_attend_noalloc(const sa_problem* p, sa_tensor q_idx, sa_tens
  *   idx_out [G, B, n_q, k] int32 (16-byte aligned) or NULL: group g's selection at
  *           idx_out + g*B*n_q*k;
  *   ws      sa_grouped_workspace_bytes(p, groups) bytes, zero-filled once (status word).
- * The groups run one after another on the stream, each as score, select and attend.
+ * The groups run one after another on the stream, each as select (sa_select's streaming
+ * form where it applies, so no score rows are stored) and attend.
  */
 sa_status sa_select_attend_grouped(const sa_problem* p, int groups, sa_tensor q_idx, sa_tensor k_idx, sa_tensor w,
                                    sa_tensor Q, sa_tensor K, sa_tensor V, int32_t* idx_out, sa_tensor O,

@@ -330,16 +330,18 @@ bool group_problem(const sa_problem* p, int G, sa_problem* out) {
     *out = q;
     return true;
 }
+// Workspace of the grouped call: status word, the groups' selections (when the caller does
+// not take them), the split partials, and one group's selection region (streaming lists or
+// score rows, as for sa_select), reused group after group.
 struct GroupedLayout {
-    size_t scores, idx, partial, scratch, total;
+    size_t idx, partial, region, total;
 };
 GroupedLayout grouped_layout(const sa_problem& p, const sa_problem& pg, int G) {
     GroupedLayout l;
     size_t o = kStatusBytes;
-    l.scores = o; o += scores_bytes(pg);
     l.idx = o; o += align256((size_t)G * p.B * p.n_q * p.k * sizeof(int32_t));
     l.partial = o; o += align256(attn_partial_bytes(pg));
-    l.scratch = o; o += align256(topk_ws_bytes(pg));
+    l.region = o; o += select_region_bytes(pg);
     l.total = o;
     return l;
 }
@@ -531,7 +533,6 @@ sa_status sa_select_attend_grouped(const sa_problem* p, int groups, sa_tensor q_
     hipStream_t st = (hipStream_t)stream;
     const GroupedLayout L = grouped_layout(*p, pg, groups);
     char* base = static_cast<char*>(ws);
-    float* scores = reinterpret_cast<float*>(base + L.scores);
     int32_t* idx_all = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
     const int64_t per_group = (int64_t)p->B * p->n_q * p->k;
     const int eq = esize(q_idx.dtype), em = esize(Q.dtype);
@@ -541,23 +542,8 @@ sa_status sa_select_attend_grouped(const sa_problem* p, int groups, sa_tensor q_
         qg.data = offset_bytes(q_idx.data, (int64_t)g * pg.Hidx * q_idx.s2 * eq);
         wg.data = offset_bytes(w.data, (int64_t)g * pg.Hidx * 4);
         int32_t* idx = idx_all + g * per_group;
-        IndexerArgs ia;
-        ia.p = pg;
-        ia.q = qg; ia.k = k_idx; ia.w = wg;
-        ia.scores = scores;
-        ia.row_stride = p->n_kv;
-        ia.fill_invisible = 0;
-        ia.status = reinterpret_cast<Status*>(base);
-        if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
-        TopkArgs ta;
-        ta.p = pg;
-        ta.scores = scores;
-        ta.row_stride = p->n_kv;
-        ta.idx = idx;
-        ta.vals = nullptr;
-        ta.status = reinterpret_cast<Status*>(base);
-        ta.scratch = base + L.scratch;
-        if (launch_topk(ta, st) != hipSuccess) return SA_ERR_HIP;
+        if ((s = run_select(&pg, qg, k_idx, wg, idx, reinterpret_cast<Status*>(base), base + L.region, st)) != SA_OK)
+            return s;
         // the group's query heads, their key/value heads (or the one shared head), O and lse
         sa_tensor Qg = Q, Og = O, Kg = K, Vg = V;
         Qg.data = offset_bytes(Q.data, (int64_t)g * pg.Hq * Q.s1 * em);
