@@ -363,6 +363,10 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
     }
 }
 
+// BUF: contiguous K/V whose per-(batch, head) slice fits a 32-bit buffer range: rows are
+// read with raw buffer loads at 32-bit offsets (an unselected key gets an offset past the
+// range, which reads zeros), with no per-key branch or 64-bit address arithmetic.
+template <bool BUF>
 __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
@@ -397,6 +401,11 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
     const int iq = qb * QR + 16 * wv + l15;
     const uint16_t* Kb = static_cast<const uint16_t*>(a.K.data) + (a.block_table ? 0 : b * a.K.s0) + h * a.K.s1;
     const uint16_t* Vb = static_cast<const uint16_t*>(a.V.data) + (a.block_table ? 0 : b * a.V.s0) + h * a.V.s1;
+    const uint32_t krow = (uint32_t)(a.K.s2 * 2), vrow = (uint32_t)(a.V.s2 * 2);  // bytes per row (BUF)
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kb), (short)0, (int)((uint32_t)p.n_kv * krow), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vb), (short)0, (int)((uint32_t)p.n_kv * vrow), 0x00020000);
     bf16x8 qa[D / 32];
     {
         const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)min(iq, p.n_q - 1) * a.Q.s2;
@@ -435,13 +444,29 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         // this tile's K (1024 16-byte pieces, four per thread) and V (four consecutive keys at
         // one column piece per thread: key quad c % 16 fastest across lanes)
         uint4 kr[4], vr[4];
+        if constexpr (BUF) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = tid + 256 * q, key = k0 + (c >> 4), col = 8 * (c & 15);
-            const int64_t row = row_of(key);
-            kr[q] = row >= 0 ? *reinterpret_cast<const uint4*>(Kb + row * a.K.s2 + col) : make_uint4(0, 0, 0, 0);
-        }
-        {
+            for (int q = 0; q < 4; ++q) {
+                const int c = tid + 256 * q, r = c >> 4, col = 8 * (c & 15);
+                const uint32_t off = ((uni >> r) & 1u) ? (uint32_t)(k0 + r) * krow + 2u * (uint32_t)col : 0x80000000u;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+                kr[q] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+            const int kq = tid & 15, col = 8 * (tid >> 4);
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const int r = 4 * kq + z;
+                const uint32_t off = ((uni >> r) & 1u) ? (uint32_t)(k0 + r) * vrow + 2u * (uint32_t)col : 0x80000000u;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+                vr[z] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = tid + 256 * q, key = k0 + (c >> 4), col = 8 * (c & 15);
+                const int64_t row = row_of(key);
+                kr[q] = row >= 0 ? *reinterpret_cast<const uint4*>(Kb + row * a.K.s2 + col) : make_uint4(0, 0, 0, 0);
+            }
             const int kq = tid & 15, col = 8 * (tid >> 4);
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
@@ -533,10 +558,13 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
             l[e] = l[e] * alpha[e] + ps;
             m[e] = mn;
         }
+        // rescale only when some row's maximum moved (alpha = exp2(0) = 1 exactly otherwise)
+        if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f) != 0) {
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
+            for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[t][e] *= alpha[e];
+                for (int e = 0; e < 4; ++e) o[t][e] *= alpha[e];
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
         // O += P V: A = P (row l15, keys 32 s + 8 g ..), B = V (key 32 s + 8 g .., d 16 t + l15)
         // (V fragments read two MFMAs ahead of their use)
@@ -1751,7 +1779,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         uint32_t* gbits = static_cast<uint32_t*>(a.partial);
         int32_t* glist = reinterpret_cast<int32_t*>(static_cast<char*>(a.partial) + tile_bits_bytes(p));
         hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nqb)), dim3(256), 0, s, a, gbits, glist);
-        hipLaunchKernelGGL(attn_tile, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
+        // 32-bit buffer offsets when the K and V slices of one (batch, head) fit 2 GiB
+        const bool buf = !a.block_table && (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) &&
+                         (int64_t)p.n_kv * a.V.s2 * 2 < (1LL << 31);
+        if (buf) hipLaunchKernelGGL(attn_tile<true>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
+        else hipLaunchKernelGGL(attn_tile<false>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
         return hipGetLastError();
     }
     if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
