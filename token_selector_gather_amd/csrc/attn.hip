@@ -429,6 +429,10 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         const int i = qb * QR + 16 * wv + 4 * g + e;
         brow[e] = i < p.n_q ? gbits + ((size_t)b * p.n_q + i) * NWORD : nullptr;
     }
+    // (BUF) the batch's bitmap rows as one buffer of n_q rows; rows past n_q fall outside it
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(gbits + (size_t)b * p.n_q * NWORD), (short)0, (int)((uint32_t)p.n_q * (NWORD * 4)), 0x00020000);
+    const uint32_t boff = (uint32_t)(qb * QR + 16 * wv + 4 * g) * (NWORD * 4);
 
     for (int u = 0; u < nt; ++u) {
         const int k0 = __builtin_amdgcn_readfirstlane(list[1 + u]) * KT;
@@ -445,18 +449,21 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         // one column piece per thread: key quad c % 16 fastest across lanes)
         uint4 kr[4], vr[4];
         if constexpr (BUF) {
+            // K: this thread's rows r0 + 16 q (r0 = tid / 16); V: rows 4 kq .. 4 kq + 3
+            const int r0 = tid >> 4, kq = tid & 15;
+            const uint64_t uk = uni >> r0;
+            const uint32_t uv = (uint32_t)(uni >> (4 * kq)) & 15u;
+            const uint32_t kbase = (uint32_t)(k0 + r0) * krow + 16u * (uint32_t)(tid & 15);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int c = tid + 256 * q, r = c >> 4, col = 8 * (c & 15);
-                const uint32_t off = ((uni >> r) & 1u) ? (uint32_t)(k0 + r) * krow + 2u * (uint32_t)col : 0x80000000u;
+                const uint32_t off = ((uint32_t)(uk >> (16 * q)) & 1u) ? kbase + (uint32_t)(16 * q) * krow : 0x80000000u;
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
                 kr[q] = make_uint4(v[0], v[1], v[2], v[3]);
             }
-            const int kq = tid & 15, col = 8 * (tid >> 4);
+            const uint32_t vbase = (uint32_t)(k0 + 4 * kq) * vrow + 16u * (uint32_t)(tid >> 4);
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
-                const int r = 4 * kq + z;
-                const uint32_t off = ((uni >> r) & 1u) ? (uint32_t)(k0 + r) * vrow + 2u * (uint32_t)col : 0x80000000u;
+                const uint32_t off = ((uv >> z) & 1u) ? vbase + (uint32_t)z * vrow : 0x80000000u;
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
                 vr[z] = make_uint4(v[0], v[1], v[2], v[3]);
             }
@@ -475,8 +482,17 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
             }
         }
         uint2 wb[4];
+        if constexpr (BUF) {
+            // 32-bit offsets into the bitmaps (rows past n_q read zeros)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wb[e] = brow[e] ? *reinterpret_cast<const uint2*>(brow[e] + (k0 >> 5)) : make_uint2(0u, 0u);
+            for (int e = 0; e < 4; ++e) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(brs, boff + (uint32_t)e * (NWORD * 4) + 4u * (uint32_t)(k0 >> 5), 0, 0);
+                wb[e] = make_uint2(v[0], v[1]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wb[e] = brow[e] ? *reinterpret_cast<const uint2*>(brow[e] + (k0 >> 5)) : make_uint2(0u, 0u);
+        }
         __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1781,7 +1797,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nqb)), dim3(256), 0, s, a, gbits, glist);
         // 32-bit buffer offsets when the K and V slices of one (batch, head) fit 2 GiB
         const bool buf = !a.block_table && (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) &&
-                         (int64_t)p.n_kv * a.V.s2 * 2 < (1LL << 31);
+                         (int64_t)p.n_kv * a.V.s2 * 2 < (1LL << 31) && (int64_t)p.n_q * (tile::MAXN / 8) < (1LL << 30);
         if (buf) hipLaunchKernelGGL(attn_tile<true>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
         else hipLaunchKernelGGL(attn_tile<false>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
         return hipGetLastError();
