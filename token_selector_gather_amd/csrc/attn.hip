@@ -275,8 +275,12 @@ constexpr int QR = 64;         // query rows per workgroup
 constexpr int KT = 64;         // keys per tile
 constexpr int MAXN = 4096;     // longest history (bitmap words per row = MAXN / 32)
 constexpr int D = 128;
-constexpr int KP = D + 8;      // padded K row (elements): conflict-free 16-byte reads
-constexpr int VP = KT + 8;     // padded V^T row
+// LDS rows are not padded (K 256 B, V^T and P 128 B per row, 40 KB per workgroup, so four
+// workgroups share a CU): the 16-byte chunks of a row are XOR-swizzled instead, K by the
+// row's low four bits, V^T and P by bits 1..3, which keeps the 16-row fragment reads of
+// the MFMA operands on distinct banks
+__device__ __forceinline__ int kslot(int row, int chunk) { return chunk ^ (row & 15); }
+__device__ __forceinline__ int vslot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 // per row block: [0] active tile count, [1 .. KT] active tiles, then two words per list
 // slot: the union over the block's rows of that tile's selection bits
 constexpr int LIST = 1 + 3 * KT;
@@ -367,12 +371,12 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
 // read with raw buffer loads at 32-bit offsets (an unselected key gets an offset past the
 // range, which reads zeros), with no per-key branch or 64-bit address arithmetic.
 template <bool BUF>
-__global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * VP];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * KT];
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * KT];
     const sa_problem& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63, l15 = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -406,6 +410,7 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kb), (short)0, (int)((uint32_t)p.n_kv * krow), 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vb), (short)0, (int)((uint32_t)p.n_kv * vrow), 0x00020000);
+    const v4i krs4 = buffer_rsrc(Kb, (uint32_t)p.n_kv * krow);  // (BUF) K rows straight into LDS
     bf16x8 qa[D / 32];
     {
         const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)min(iq, p.n_q - 1) * a.Q.s2;
@@ -422,13 +427,6 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     uint16_t* Pw = Ps[wv];
-    // bitmap rows of this lane's four query rows (16 wv + 4 g + e)
-    const uint32_t* brow[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int i = qb * QR + 16 * wv + 4 * g + e;
-        brow[e] = i < p.n_q ? gbits + ((size_t)b * p.n_q + i) * NWORD : nullptr;
-    }
     // (BUF) the batch's bitmap rows as one buffer of n_q rows; rows past n_q fall outside it
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(gbits + (size_t)b * p.n_q * NWORD), (short)0, (int)((uint32_t)p.n_q * (NWORD * 4)), 0x00020000);
@@ -448,18 +446,11 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         // this tile's K (1024 16-byte pieces, four per thread) and V (four consecutive keys at
         // one column piece per thread: key quad c % 16 fastest across lanes)
         uint4 kr[4], vr[4];
+        (void)kr;
         if constexpr (BUF) {
-            // K: this thread's rows r0 + 16 q (r0 = tid / 16); V: rows 4 kq .. 4 kq + 3
-            const int r0 = tid >> 4, kq = tid & 15;
-            const uint64_t uk = uni >> r0;
+            // V: rows 4 kq .. 4 kq + 3 into registers (K goes to LDS directly after the barrier)
+            const int kq = tid & 15;
             const uint32_t uv = (uint32_t)(uni >> (4 * kq)) & 15u;
-            const uint32_t kbase = (uint32_t)(k0 + r0) * krow + 16u * (uint32_t)(tid & 15);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t off = ((uint32_t)(uk >> (16 * q)) & 1u) ? kbase + (uint32_t)(16 * q) * krow : 0x80000000u;
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-                kr[q] = make_uint4(v[0], v[1], v[2], v[3]);
-            }
             const uint32_t vbase = (uint32_t)(k0 + 4 * kq) * vrow + 16u * (uint32_t)(tid >> 4);
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
@@ -490,14 +481,31 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
                 wb[e] = make_uint2(v[0], v[1]);
             }
         } else {
+            // bitmap rows of this lane's four query rows (16 wv + 4 g + e)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wb[e] = brow[e] ? *reinterpret_cast<const uint2*>(brow[e] + (k0 >> 5)) : make_uint2(0u, 0u);
+            for (int e = 0; e < 4; ++e) {
+                const int i = qb * QR + 16 * wv + 4 * g + e;
+                wb[e] = i < p.n_q ? *reinterpret_cast<const uint2*>(gbits + ((size_t)b * p.n_q + i) * NWORD + (k0 >> 5))
+                                  : make_uint2(0u, 0u);
+            }
         }
         __syncthreads();  // every wave is done with the previous tile
+        if constexpr (BUF) {
+            // K rows straight into LDS: block 4 wv + i (1 KB) holds rows 4 (4 wv + i) .. + 3, lane
+            // l writing row 4 (4 wv + i) + l / 16 at slot l % 16, which holds the chunk
+            // kslot(row, l % 16) maps there; unselected rows read past the buffer (zeros)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = tid + 256 * q, key = c >> 4, col = 8 * (c & 15);
-            *reinterpret_cast<uint4*>(Ks + key * KP + col) = kr[q];
+            for (int i = 0; i < 4; ++i) {
+                const int bk = 4 * wv + i, r = 4 * bk + (lane >> 4), c = kslot(r, lane & 15);
+                const uint32_t off = ((uni >> r) & 1u) ? (uint32_t)(k0 + r) * krow + 16u * (uint32_t)c : 0x80000000u;
+                lds_dma16(krs4, lds_addr(Ks) + 1024u * (uint32_t)bk, off, 0u);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = tid + 256 * q, key = c >> 4, col = 8 * (c & 15);
+                *reinterpret_cast<uint4*>(Ks + key * D + 8 * kslot(key, col / 8)) = kr[q];
+            }
         }
         {
             const int kq = tid & 15, col = 8 * (tid >> 4);
@@ -508,37 +516,26 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
                 uint32_t h[4];
 #pragma unroll
                 for (int z = 0; z < 4; ++z) h[z] = (w[z][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *reinterpret_cast<uint2*>(Vt + (col + e) * VP + 4 * kq) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                *reinterpret_cast<uint2*>(Vt + (col + e) * KT + 8 * vslot(col + e, kq >> 1) + 4 * (kq & 1)) =
+                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
         }
+        if constexpr (BUF) wait_vmcnt<0>();  // this wave's K rows have landed in LDS
         __syncthreads();
 
         // S = Q K^T: acc[j][e] = S[row 4 g + e][key 16 j + l15]; k-step s runs the four key
-        // tiles' independent chains while the K fragments of k-step s + 1 are read
+        // tiles' independent chains
         f32x4 acc[4];
-        auto kread = [&](int j, int s) {
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + (16 * j + l15) * KP + 32 * s + 8 * g));
-        };
-        bf16x8 kc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            kc[j] = kread(j, 0);
-        }
+        for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            bf16x8 kn[4];
-            if (s + 1 < D / 32) {
+        for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) kn[j] = kread(j, s + 1);
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 kb = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4*>(Ks + (16 * j + l15) * D + 8 * kslot(16 * j + l15, 4 * s + g)));
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb, acc[j], 0, 0, 0);
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kc[j], acc[j], 0, 0, 0);
-            if (s + 1 < D / 32) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kc[j] = kn[j];
-            }
-        }
         // mask, online softmax per row (rows 4 g + e live in the 16 lanes of group g)
         float alpha[4];
 #pragma unroll
@@ -565,7 +562,7 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
                 const float pv = __builtin_amdgcn_exp2f(x[j] - mref);
                 const uint16_t pb = __builtin_bit_cast(uint16_t, (__bf16)pv);  // hardware RNE (pv is finite)
                 ps += pv;
-                Pw[(4 * g + e) * VP + 16 * j + l15] = pb;
+                Pw[(4 * g + e) * KT + 8 * vslot(4 * g + e, 2 * j + (l15 >> 3)) + (l15 & 7)] = pb;
             }
             ps += dpp_mov<0xB1>(ps);
             ps += dpp_mov<0x4E>(ps);
@@ -585,11 +582,11 @@ __global__ void __launch_bounds__(256, 3) attn_tile(AttnArgs a, const uint32_t* 
         // O += P V: A = P (row l15, keys 32 s + 8 g ..), B = V (key 32 s + 8 g .., d 16 t + l15)
         // (V fragments read two MFMAs ahead of their use)
         auto vread = [&](int s, int t) {
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vt + (16 * t + l15) * VP + 32 * s + 8 * g));
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vt + (16 * t + l15) * KT + 8 * vslot(16 * t + l15, 4 * s + g)));
         };
         bf16x8 pa[2], vq[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) pa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pw + l15 * VP + 32 * s + 8 * g));
+        for (int s = 0; s < 2; ++s) pa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pw + l15 * KT + 8 * vslot(l15, 4 * s + g)));
         vq[0] = vread(0, 0);
         vq[1] = vread(0, 1);
 #pragma unroll
