@@ -260,30 +260,32 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // --------------------------------------------------------------- attn_tile
 // bf16 MHA (d = 128) over selections that, for a block of query rows, cover most key tiles
 // (many query rows, k a large fraction of the history).  One workgroup = 64 query rows of
-// one head: the rows' selections become a bitmap in LDS, every 64-key tile that any of the
-// rows selected is read once into LDS (K rows as they are, V transposed), S = Q K^T and
-// O += P V run on MFMA (16x16x32 bf16), and unselected keys are masked to -inf before the
-// online softmax, so each row's result is the exact softmax over its own selected set.
-// Tiles no row selected are skipped, and inside a tile only the keys that some row of the
-// block selected are read: the others enter LDS as zeros, so the value product (P = 0 for
-// them) never touches an unselected row, which may hold anything (padding, stale pool
-// rows, NaN).  Wave w owns query rows 16 w .. 16 w + 15.  With a block table the tile's keys
-// are read from their pool rows (kv_row), and a candidate on a page outside the pools never
-// enters the bitmap.
+// one head: the rows' selections become a bitmap (tile_bits), every 64-key tile that any of
+// the rows selected is read once into LDS, S^T = K Q^T and O^T += V^T P^T run on MFMA
+// (16x16x32 bf16), and unselected keys get probability 0, so each row's result is the exact
+// softmax over its own selected set.  Tiles no row selected are skipped, and the V rows of
+// keys that no row of the block selected enter LDS as zeros, so the value product never
+// touches an unselected row, which may hold anything (padding, stale pool rows, NaN); an
+// unselected K row only produces a logit that is masked.  Wave w owns query rows
+// 16 w .. 16 w + 15.  With a block table the tile's keys are read from their pool rows
+// (kv_row), and a candidate on a page outside the pools never enters the bitmap.
 namespace tile {
 constexpr int QR = 64;         // query rows per workgroup
 constexpr int KT = 64;         // keys per tile
 constexpr int MAXN = 4096;     // longest history (bitmap words per row = MAXN / 32)
 constexpr int D = 128;
-// LDS rows are not padded (K 256 B, V^T and P 128 B per row, 40 KB per workgroup, so four
-// workgroups share a CU): the 16-byte chunks of a row are XOR-swizzled instead, K by the
-// row's low four bits, V^T and P by bits 1..3, which keeps the 16-row fragment reads of
-// the MFMA operands on distinct banks
+static_assert(MAXN / KT <= 64, "a row block's tile list fits one register per wave");
+// LDS rows are not padded (256 B per K or V row, 32 KB per workgroup, so four workgroups
+// share a CU); the 16-byte chunks of a row are XOR-swizzled instead.  K: chunk c of row r at
+// slot c ^ (r & 15), so the 16-row operand reads touch distinct banks.  V: slot c ^ 2 (r & 7),
+// so each transposing read (16 rows x two adjacent chunks, half a wave per pass) touches
+// every bank once per pass.
 __device__ __forceinline__ int kslot(int row, int chunk) { return chunk ^ (row & 15); }
-__device__ __forceinline__ int vslot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int vslot(int row, int chunk) { return chunk ^ (2 * (row & 7)); }
 // per row block: [0] active tile count, [1 .. KT] active tiles, then two words per list
 // slot: the union over the block's rows of that tile's selection bits
 constexpr int LIST = 1 + 3 * KT;
+constexpr float kLazy = 0x1p64f;  // exp2(64): largest probability against a row's reference
 }  // namespace tile
 
 // The selections of a batch's block of 64 query rows, shared by every head: a bitmap per
@@ -367,16 +369,47 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
     }
 }
 
-// BUF: contiguous K/V whose per-(batch, head) slice fits a 32-bit buffer range: rows are
-// read with raw buffer loads at 32-bit offsets (an unselected key gets an offset past the
-// range, which reads zeros), with no per-key branch or 64-bit address arithmetic.
-template <bool BUF>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// maximum over the lanes l, l^16, l^32, l^48 (lane swaps between rows, no LDS round trip)
+__device__ __forceinline__ float colmax4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+__device__ __forceinline__ v4s lds_tr_read(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+}
+
+// Zeros that stand in for a row no lane may read (an unselected or unmapped pool row)
+constexpr int kZeroRowBytes = 4096;
+__device__ __align__(16) const uint8_t kZeroRow[kZeroRowBytes] = {};
+
+// The tile kernel.  S^T = K Q^T leaves one query row in each lane (keys 16 j + 4 g + e of the
+// tile in its accumulators), so the row's mask bits come from its own bitmap word, the
+// softmax needs no lane exchange unless a row's reference maximum moves, and the
+// probabilities are already the B operand of O^T += V^T P^T (no LDS round trip).  K and V
+// tiles reach LDS through loads that write LDS directly (K of tile u + 1 while tile u's
+// values are used, V of tile u + 1 while its scores run); V^T operands come from transposing
+// LDS reads of the row-major tile.  A row's reference maximum is raised only when one of its
+// selected logits exceeds it by more than 64 (exp2 units): below that margin every
+// probability and sum stays far inside fp32 range, and any reference gives the same
+// softmax.  A row's sum is kept per lane in fp32 (from the unrounded probabilities) and
+// added over the row's four lanes at the end.
+// Tile sources: contiguous K/V and pages of at least 64 rows give each tile one contiguous
+// run of rows, read through a buffer resource made per tile (rows past the history read
+// zeros); ROWS (pages shorter than a tile) looks up each row's pool row and reads it by its
+// own 64-bit address, unselected rows from the zero row.
+template <bool ROWS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * KT];
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * KT];
+    __shared__ __attribute__((aligned(16))) uint8_t Ks[KT * D * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t Vs[KT * D * 2];
     const sa_problem& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63, l15 = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,19 +431,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
     }
     const int32_t* list = glist + (size_t)(b * nqb + qb) * LIST;
     const int nt = __builtin_amdgcn_readfirstlane(list[0]);
-    // with pages of at least 64 rows a 64-key tile lies inside one page: one table lookup per tile
-    const bool tile_pages = a.block_table && a.page_shift >= 6;
+    const int iq = qb * QR + 16 * wv + l15;  // this lane's query row
+    const char* Kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.K.data) + (a.block_table ? 0 : b * a.K.s0) + h * a.K.s1);
+    const char* Vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.V.data) + (a.block_table ? 0 : b * a.V.s0) + h * a.V.s1);
+    const int64_t krow = a.K.s2 * 2, vrow = a.V.s2 * 2;  // bytes per row
+    // the block's bitmap rows; rows past n_q read zeros
+    const int nrows = min(QR, p.n_q - qb * QR);
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(gbits + ((size_t)b * p.n_q + (size_t)qb * QR) * NWORD), (short)0, nrows * (NWORD * 4), 0x00020000);
+    const uint32_t boff = (uint32_t)(16 * wv + l15) * (NWORD * 4);
 
-    // Q fragments (A operand): lane row l15 = query row 16 wv + l15, d = 32 s + 8 g .. + 7
-    const int iq = qb * QR + 16 * wv + l15;
-    const uint16_t* Kb = static_cast<const uint16_t*>(a.K.data) + (a.block_table ? 0 : b * a.K.s0) + h * a.K.s1;
-    const uint16_t* Vb = static_cast<const uint16_t*>(a.V.data) + (a.block_table ? 0 : b * a.V.s0) + h * a.V.s1;
-    const uint32_t krow = (uint32_t)(a.K.s2 * 2), vrow = (uint32_t)(a.V.s2 * 2);  // bytes per row (BUF)
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kb), (short)0, (int)((uint32_t)p.n_kv * krow), 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vb), (short)0, (int)((uint32_t)p.n_kv * vrow), 0x00020000);
-    const v4i krs4 = buffer_rsrc(Kb, (uint32_t)p.n_kv * krow);  // (BUF) K rows straight into LDS
+    // Q^T fragments (B operand of S^T): query row iq, d = 32 s + 8 g .. + 7
     bf16x8 qa[D / 32];
     {
         const uint16_t* qp = static_cast<const uint16_t*>(a.Q.data) + b * a.Q.s0 + h * a.Q.s1 + (int64_t)min(iq, p.n_q - 1) * a.Q.s2;
@@ -419,195 +450,234 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) a
             qa[s] = iq < p.n_q ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g))
                                : bf16x8{};
     }
-    const float sl2 = a.scale * kLog2e;
-    float m[4], l[4];
-    f32x4 o[D / 16];
+    // tile loads: wave wv fills the 1 KB LDS blocks 4 wv + i, i.e. tile rows r_i = 16 wv + 4 i +
+    // lane / 16, lane l writing slot l % 16 of its row (the chunk whose swizzled slot that is)
+    uint32_t koff[4], voff[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint16_t* Pw = Ps[wv];
-    // (BUF) the batch's bitmap rows as one buffer of n_q rows; rows past n_q fall outside it
-    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint32_t*>(gbits + (size_t)b * p.n_q * NWORD), (short)0, (int)((uint32_t)p.n_q * (NWORD * 4)), 0x00020000);
-    const uint32_t boff = (uint32_t)(qb * QR + 16 * wv + 4 * g) * (NWORD * 4);
-
-    for (int u = 0; u < nt; ++u) {
-        const int k0 = __builtin_amdgcn_readfirstlane(list[1 + u]) * KT;
-        // keys of the tile that some row of the block selected (all visible, all in range)
-        const uint64_t uni = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(list[1 + KT + 2 * u]) |
-                             ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(list[2 + KT + 2 * u]) << 32);
-        const int64_t tb = tile_pages ? kv_row(a, b, k0) : 0;
-        auto row_of = [&](int key) -> int64_t {
-            if (!((uni >> (key - k0)) & 1u)) return -1;
-            if (tile_pages) return tb < 0 ? -1 : tb + (key - k0);
-            return kv_row(a, b, key);
-        };
-        // this tile's K (1024 16-byte pieces, four per thread) and V (four consecutive keys at
-        // one column piece per thread: key quad c % 16 fastest across lanes)
-        uint4 kr[4], vr[4];
-        (void)kr;
-        if constexpr (BUF) {
-            // V: rows 4 kq .. 4 kq + 3 into registers (K goes to LDS directly after the barrier)
-            const int kq = tid & 15;
-            const uint32_t uv = (uint32_t)(uni >> (4 * kq)) & 15u;
-            const uint32_t vbase = (uint32_t)(k0 + 4 * kq) * vrow + 16u * (uint32_t)(tid >> 4);
-#pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                const uint32_t off = ((uv >> z) & 1u) ? vbase + (uint32_t)z * vrow : 0x80000000u;
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-                vr[z] = make_uint4(v[0], v[1], v[2], v[3]);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = tid + 256 * q, key = k0 + (c >> 4), col = 8 * (c & 15);
-                const int64_t row = row_of(key);
-                kr[q] = row >= 0 ? *reinterpret_cast<const uint4*>(Kb + row * a.K.s2 + col) : make_uint4(0, 0, 0, 0);
-            }
-            const int kq = tid & 15, col = 8 * (tid >> 4);
-#pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                const int64_t row = row_of(k0 + 4 * kq + z);
-                vr[z] = row >= 0 ? *reinterpret_cast<const uint4*>(Vb + row * a.V.s2 + col) : make_uint4(0, 0, 0, 0);
-            }
-        }
-        uint2 wb[4];
-        if constexpr (BUF) {
-            // 32-bit offsets into the bitmaps (rows past n_q read zeros)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(brs, boff + (uint32_t)e * (NWORD * 4) + 4u * (uint32_t)(k0 >> 5), 0, 0);
-                wb[e] = make_uint2(v[0], v[1]);
-            }
-        } else {
-            // bitmap rows of this lane's four query rows (16 wv + 4 g + e)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = qb * QR + 16 * wv + 4 * g + e;
-                wb[e] = i < p.n_q ? *reinterpret_cast<const uint2*>(gbits + ((size_t)b * p.n_q + i) * NWORD + (k0 >> 5))
-                                  : make_uint2(0u, 0u);
-            }
-        }
-        __syncthreads();  // every wave is done with the previous tile
-        if constexpr (BUF) {
-            // K rows straight into LDS: block 4 wv + i (1 KB) holds rows 4 (4 wv + i) .. + 3, lane
-            // l writing row 4 (4 wv + i) + l / 16 at slot l % 16, which holds the chunk
-            // kslot(row, l % 16) maps there; unselected rows read past the buffer (zeros)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int bk = 4 * wv + i, r = 4 * bk + (lane >> 4), c = kslot(r, lane & 15);
-                const uint32_t off = ((uni >> r) & 1u) ? (uint32_t)(k0 + r) * krow + 16u * (uint32_t)c : 0x80000000u;
-                lds_dma16(krs4, lds_addr(Ks) + 1024u * (uint32_t)bk, off, 0u);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = tid + 256 * q, key = c >> 4, col = 8 * (c & 15);
-                *reinterpret_cast<uint4*>(Ks + key * D + 8 * kslot(key, col / 8)) = kr[q];
-            }
-        }
-        {
-            const int kq = tid & 15, col = 8 * (tid >> 4);
-            const uint32_t w[4][4] = {{vr[0].x, vr[0].y, vr[0].z, vr[0].w}, {vr[1].x, vr[1].y, vr[1].z, vr[1].w},
-                                      {vr[2].x, vr[2].y, vr[2].z, vr[2].w}, {vr[3].x, vr[3].y, vr[3].z, vr[3].w}};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t h[4];
-#pragma unroll
-                for (int z = 0; z < 4; ++z) h[z] = (w[z][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *reinterpret_cast<uint2*>(Vt + (col + e) * KT + 8 * vslot(col + e, kq >> 1) + 4 * (kq & 1)) =
-                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-            }
-        }
-        if constexpr (BUF) wait_vmcnt<0>();  // this wave's K rows have landed in LDS
-        __syncthreads();
-
-        // S = Q K^T: acc[j][e] = S[row 4 g + e][key 16 j + l15]; k-step s runs the four key
-        // tiles' independent chains
-        f32x4 acc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 kb = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(Ks + (16 * j + l15) * D + 8 * kslot(16 * j + l15, 4 * s + g)));
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb, acc[j], 0, 0, 0);
-            }
-        // mask, online softmax per row (rows 4 g + e live in the 16 lanes of group g)
-        float alpha[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float x[4], mx = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t word = j < 2 ? wb[e].x : wb[e].y;
-                const bool sel = (word >> (16 * (j & 1) + l15)) & 1u;
-                x[j] = sel ? acc[j][e] * sl2 : -INFINITY;
-                mx = fmaxf(mx, x[j]);
-            }
-            // maximum over the 16 lanes of the row (one DPP row)
-            mx = fmaxf(mx, dpp_mov<0xB1>(mx));
-            mx = fmaxf(mx, dpp_mov<0x4E>(mx));
-            mx = fmaxf(mx, dpp_mov<0x141>(mx));
-            mx = fmaxf(mx, dpp_mov<0x140>(mx));
-            const float mn = fmaxf(m[e], mx);
-            alpha[e] = m[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[e] - mn);
-            const float mref = mn == -INFINITY ? 0.f : mn;
-            float ps = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float pv = __builtin_amdgcn_exp2f(x[j] - mref);
-                const uint16_t pb = __builtin_bit_cast(uint16_t, (__bf16)pv);  // hardware RNE (pv is finite)
-                ps += pv;
-                Pw[(4 * g + e) * KT + 8 * vslot(4 * g + e, 2 * j + (l15 >> 3)) + (l15 & 7)] = pb;
-            }
-            ps += dpp_mov<0xB1>(ps);
-            ps += dpp_mov<0x4E>(ps);
-            ps += dpp_mov<0x141>(ps);
-            ps += dpp_mov<0x140>(ps);
-            l[e] = l[e] * alpha[e] + ps;
-            m[e] = mn;
-        }
-        // rescale only when some row's maximum moved (alpha = exp2(0) = 1 exactly otherwise)
-        if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f) != 0) {
-#pragma unroll
-            for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[t][e] *= alpha[e];
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
-        // O += P V: A = P (row l15, keys 32 s + 8 g ..), B = V (key 32 s + 8 g .., d 16 t + l15)
-        // (V fragments read two MFMAs ahead of their use)
-        auto vread = [&](int s, int t) {
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vt + (16 * t + l15) * KT + 8 * vslot(16 * t + l15, 4 * s + g)));
-        };
-        bf16x8 pa[2], vq[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) pa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pw + l15 * KT + 8 * vslot(l15, 4 * s + g)));
-        vq[0] = vread(0, 0);
-        vq[1] = vread(0, 1);
-#pragma unroll
-        for (int st = 0; st < 2 * (D / 16); ++st) {
-            const int s = st / (D / 16), t = st % (D / 16);
-            const bf16x8 vb = vq[st & 1];
-            if (st + 2 < 2 * (D / 16)) vq[st & 1] = vread((st + 2) / (D / 16), (st + 2) % (D / 16));
-            o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[s], vb, o[t], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wv + 4 * i + (lane >> 4);
+        koff[i] = 16u * (uint32_t)kslot(r, lane & 15);
+        voff[i] = 16u * (uint32_t)vslot(r, lane & 15);
+        if constexpr (!ROWS) {
+            koff[i] += (uint32_t)(r * krow);
+            voff[i] += (uint32_t)(r * vrow);
         }
     }
-    // O[row 4 g + e][d 16 t + l15] / l; LSE per row
+    const uint32_t kl = lds_addr(Ks) + 4096u * (uint32_t)wv, vl = lds_addr(Vs) + 4096u * (uint32_t)wv;
+    // where a tile's rows come from: a per-tile buffer resource, or (ROWS) each row's pool row
+    struct Src {
+        v4i krs, vrs;
+        int64_t prow[4];
+    };
+    auto tile_src = [&](int k0, uint64_t uni) {
+        Src t;
+        if constexpr (ROWS) {
+            const uint64_t un = uni >> (16 * wv);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int i = qb * QR + 16 * wv + 4 * g + e;
-        if (i >= p.n_q) continue;
-        const float inv = l[e] > 0.f ? 1.f / l[e] : 0.f;
-        uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)i * a.O.s2;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                t.prow[i] = ((un >> r) & 1u) ? kv_row(a, b, k0 + 16 * wv + r) : -1;
+            }
+        } else {
+            int64_t r0;
+            int n;
+            if (a.block_table) {  // the tile lies inside one page
+                r0 = kv_row(a, b, k0);
+                n = r0 >= 0 ? KT : 0;
+            } else {
+                r0 = k0;
+                n = min(KT, p.n_kv - k0);
+            }
+            t.krs = buffer_rsrc(Kb + max(r0, (int64_t)0) * krow, (uint32_t)(n * krow));
+            t.vrs = buffer_rsrc(Vb + max(r0, (int64_t)0) * vrow, (uint32_t)(n * vrow));
+        }
+        return t;
+    };
+    auto issue_k = [&](const Src& t) {
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) op[16 * t + l15] = f32_to_bf16_rne(o[t][e] * inv);
-        if (a.lse && l15 == 0)
-            a.lse[b * a.lse_bs + (int64_t)h * p.n_q + i] = l[e] > 0.f ? (m[e] + log2f(l[e])) * kLn2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (ROWS)
+                lds_dma16_g(kl + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Kb + t.prow[i] * krow + koff[i] : reinterpret_cast<const char*>(kZeroRow));
+            else
+                lds_dma16(t.krs, kl + 1024u * (uint32_t)i, koff[i], 0u);
+        }
+    };
+    auto issue_v = [&](const Src& t, uint64_t uni) {
+        const uint64_t un = uni >> (16 * wv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (ROWS) {
+                lds_dma16_g(vl + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Vb + t.prow[i] * vrow + voff[i] : reinterpret_cast<const char*>(kZeroRow));
+            } else {
+                // keys no row of the block selected read past the resource: zeros
+                const bool sel = ((uint32_t)(un >> (4 * i)) >> (lane >> 4)) & 1u;
+                lds_dma16(t.vrs, vl + 1024u * (uint32_t)i, sel ? voff[i] : 0x80000000u, 0u);
+            }
+        }
+    };
+    auto load_bits = [&](int k0) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(brs, boff + 4u * (uint32_t)(k0 >> 5), 0, 0);
+        return make_uint2(v[0], v[1]);
+    };
+    // LDS read offsets.  K (A operand of S^T: key 16 j + l15, chunk 4 s + g): kad[s] + 4096 j.
+    // V^T (A operand of O^T by transposing reads): this lane supplies row 32 s + 16 hf + rr,
+    // rr = 4 g + l15 / 4, and 8 bytes at column 16 t + 4 (l15 % 4): vad[t] + 8192 s + 4096 hf
+    int kad[D / 32], vad[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) kad[s] = 256 * l15 + 16 * kslot(l15, 4 * s + g);
+    {
+        const int rr = 4 * g + (l15 >> 2);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) vad[t] = 256 * rr + 16 * vslot(rr, 2 * t + ((l15 >> 1) & 1)) + 8 * (l15 & 1);
+    }
+
+    const float sl2 = a.scale * kLog2e;
+    float ref = -INFINITY;  // reference maximum of row iq (scaled log2 units)
+    bool all_ref = false;   // every valid row of the wave has a finite reference
+    float lrow = 0.f;       // this lane's part of the row's sum (keys 16 j + 4 g + e)
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // the tile list in registers: lane u holds tile u's first key and union bits (nt <= KT = 64)
+    const int lt = lane < nt ? list[1 + lane] : 0;
+    const uint32_t lu0 = lane < nt ? (uint32_t)list[1 + KT + 2 * lane] : 0u;
+    const uint32_t lu1 = lane < nt ? (uint32_t)list[2 + KT + 2 * lane] : 0u;
+    auto tile_keys = [&](int u) { return __builtin_amdgcn_readlane(lt, u) * KT; };
+    auto tile_union = [&](int u) {
+        return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lu0, u) | ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lu1, u) << 32);
+    };
+    uint2 wcur = make_uint2(0u, 0u);
+    if (nt > 0) {
+        const int k0 = tile_keys(0);
+        const uint64_t un = tile_union(0);
+        const Src t = tile_src(k0, un);
+        issue_k(t);
+        issue_v(t, un);
+        wcur = load_bits(k0);
+        wait_vmcnt<0>();
+        tile_barrier();
+    }
+    for (int u = 0; u < nt; ++u) {
+        const bool more = u + 1 < nt;
+        const int k1 = more ? tile_keys(u + 1) : 0;
+        const uint64_t un1 = more ? tile_union(u + 1) : 0;
+        Src nxt;
+        if (more) nxt = tile_src(k1, un1);
+        // does any row of this wave select a key of the tile?
+        const bool act = __ballot((wcur.x | wcur.y) != 0u) != 0;
+        // S^T = K Q^T: acc[j][e] = S[row iq][key 16 j + 4 g + e]
+        f32x4 acc[4];
+        if (act) {
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + kad[s] + 4096 * j));
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[j], 0, 0, 0);
+                }
+        }
+        wait_lgkmcnt0();
+        wait_vmcnt<0>();  // this wave's part of V(u) has landed
+        tile_barrier();   // every wave is done with K(u); V(u) is complete
+        uint2 wnext = make_uint2(0u, 0u);
+        if (more) {
+            issue_k(nxt);
+            wnext = load_bits(k1);
+        }
+        if (act) {
+            // mask of row iq for keys 16 j + 4 g + e: bit 16 (j % 2) + e of word j / 2 after a shift
+            // by 4 g; all ones where selected (one bit-field extract, kept opaque so that the
+            // masking stays a single AND per element)
+            const uint32_t w0 = wcur.x >> (4 * g), w1 = wcur.y >> (4 * g);
+            auto msk = [&](int j, int e) -> uint32_t {
+                uint32_t m;
+                asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(j < 2 ? w0 : w1), "i"(16 * (j & 1) + e));
+                return m;
+            };
+            float pr[4][4];
+            auto probs = [&](float nref) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pr[j][e] = __uint_as_float(__float_as_uint(__builtin_amdgcn_exp2f(fmaf(acc[j][e], sl2, nref))) & msk(j, e));
+            };
+            bool slow = !all_ref;
+            if (!slow) {
+                probs(-ref);
+                float pm = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pm = fmaxf(fmaxf(pm, fmaxf(pr[j][0], pr[j][1])), fmaxf(pr[j][2], pr[j][3]));
+                slow = __ballot(pm > kLazy) != 0;
+            }
+            if (slow) {
+                // the row's maximum over its selected keys (all four lanes of the row)
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t m = msk(j, e);
+                        mx = fmaxf(mx, __uint_as_float((__float_as_uint(acc[j][e] * sl2) & m) | (0xff800000u & ~m)));
+                    }
+                const float mn = fmaxf(ref, colmax4(mx));
+                const float alpha = ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ref - mn);
+#pragma unroll
+                for (int t = 0; t < D / 16; ++t) o[t] *= alpha;
+                lrow *= alpha;
+                ref = mn;
+                all_ref = __ballot(iq < p.n_q && ref == -INFINITY) == 0;
+                probs(ref == -INFINITY ? 0.f : -ref);
+            }
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ps += (pr[j][0] + pr[j][1]) + (pr[j][2] + pr[j][3]);
+            lrow += ps;
+            // P^T fragments (B operand): k-step s holds keys 32 s + 4 g + 0..3, then 32 s + 16 + 4 g + 0..3
+            bf16x8 pb[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pb[s][e] = (__bf16)pr[2 * s][e];
+                    pb[s][4 + e] = (__bf16)pr[2 * s + 1][e];
+                }
+            // O^T[d 16 t + 4 g + e][row iq] += V^T P^T; the first of a pair of transposing reads
+            // brings keys 32 s + 4 g + 0..3 of column 16 t + l15, the second 32 s + 16 + 4 g + 0..3
+            auto vread = [&](int s, int t) {
+                const uint8_t* vp = Vs + vad[t] + 8192 * s;
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lds_tr_read(vp), lds_tr_read(vp + 4096), 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int t = 0; t < D / 16; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vread(s, t), pb[s], o[t], 0, 0, 0);
+        }
+        wait_lgkmcnt0();
+        wait_vmcnt<0>();  // this wave's part of K(u + 1) and the next bitmap words have landed
+        tile_barrier();   // every wave is done with V(u); K(u + 1) is complete
+        if (more) {
+            issue_v(nxt, un1);
+            wcur = wnext;
+        }
+    }
+    // O[row iq][d 16 t + 4 g + e] = O^T / l; LSE per row
+    float l;
+    {
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(lrow), __float_as_uint(lrow), false, false);
+        const float y = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+        l = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+    }
+    if (iq < p.n_q) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* op = static_cast<uint16_t*>(a.O.data) + b * a.O.s0 + h * a.O.s1 + (int64_t)iq * a.O.s2;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) op[16 * t + 4 * g + e] = f32_to_bf16_rne(o[t][e] * inv);
+        if (a.lse && g == 0) a.lse[b * a.lse_bs + (int64_t)h * p.n_q + iq] = l > 0.f ? (ref + log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -1060,26 +1130,10 @@ __device__ __forceinline__ int cslot_inv(int r, int y) { return y ^ rswz(r); }
 __device__ __forceinline__ int tswz(int r) { return (r >> 1) & 7; }
 }  // namespace mla
 
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef short v4s __attribute__((ext_vector_type(4)));
-
-// maximum over the lanes l, l^16, l^32, l^48 (lane swaps between rows, no LDS round trip)
-__device__ __forceinline__ float colmax4(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-
-__device__ __forceinline__ v4s lds_tr_read(const uint8_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
-}
 
 // IDX: paged pools.  The offset list holds pool row indices, and every lane of a tile load
 // forms its own 64-bit address (pool base + row * row stride + column), since a pool may
 // exceed the 4 GiB a buffer resource reaches; an empty slot reads the zero row instead.
-constexpr int kZeroRowBytes = 4096;
-__device__ __align__(16) const uint8_t kZeroRow[kZeroRowBytes] = {};
 
 template <int NW, bool IDX>
 __global__ void __launch_bounds__(64 * NW) attn_mla_lds(AttnArgs a) {
@@ -1792,11 +1846,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         uint32_t* gbits = static_cast<uint32_t*>(a.partial);
         int32_t* glist = reinterpret_cast<int32_t*>(static_cast<char*>(a.partial) + tile_bits_bytes(p));
         hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nqb)), dim3(256), 0, s, a, gbits, glist);
-        // 32-bit buffer offsets when the K and V slices of one (batch, head) fit 2 GiB
-        const bool buf = !a.block_table && (int64_t)p.n_kv * a.K.s2 * 2 < (1LL << 31) &&
-                         (int64_t)p.n_kv * a.V.s2 * 2 < (1LL << 31) && (int64_t)p.n_q * (tile::MAXN / 8) < (1LL << 30);
-        if (buf) hipLaunchKernelGGL(attn_tile<true>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
-        else hipLaunchKernelGGL(attn_tile<false>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
+        // pages shorter than a tile: each row's pool row is looked up on its own
+        if (a.block_table && a.page_shift < 6)
+            hipLaunchKernelGGL(attn_tile<true>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
+        else
+            hipLaunchKernelGGL(attn_tile<false>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
         return hipGetLastError();
     }
     if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
