@@ -292,12 +292,13 @@ constexpr float kLazy = 0x1p64f;  // exp2(64): largest probability against a row
 // row (bit j of word j / 32 = position j selected), the list of 64-key tiles any of the
 // rows selected and, per listed tile, the union of the rows' selection bits.  One
 // workgroup per (batch, row block); written to the workspace.
-__global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, int32_t* glist) {
+__global__ void __launch_bounds__(1024) tile_bits(AttnArgs a, uint32_t* gbits, int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
+    constexpr int NT = 1024;
     __shared__ __attribute__((aligned(16))) uint32_t bits[QR][NWORD];
     __shared__ int s_L[QR], s_maxL;
-    __shared__ uint32_t s_uni[4][KT][2];
+    __shared__ uint32_t s_uni[NT / 64][KT][2];
     const sa_problem& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63;
     const int nqb = (p.n_q + QR - 1) / QR;
@@ -307,20 +308,20 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
         const int i = qb * QR + tid;
         s_L[tid] = i < p.n_q ? visible_len(R, b, i) : 0;
     }
-    for (int w = tid; w < QR * NWORD; w += 256) (&bits[0][0])[w] = 0u;
+    for (int w = tid; w < QR * NWORD; w += NT) (&bits[0][0])[w] = 0u;
     if (tid == 0) s_maxL = 0;
     __syncthreads();
     if (tid < QR) atomicMax(&s_maxL, s_L[tid]);
-    {   // 4 threads per row, eight 16-byte index loads in flight per thread
-        const int r = tid >> 2, q = tid & 3;
+    {   // 16 threads per row, eight 16-byte index loads in flight per thread
+        const int r = tid >> 4, q = tid & 15;
         const int i = qb * QR + r, L = s_L[r];
         if (i < p.n_q && L > 0) {
             const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
-            for (int e0 = 4 * q; e0 < p.k; e0 += 16 * 8) {
+            for (int e0 = 4 * q; e0 < p.k; e0 += 64 * 8) {
                 int4 jj[8];
 #pragma unroll
                 for (int n = 0; n < 8; ++n)
-                    jj[n] = e0 + 16 * n < p.k ? *reinterpret_cast<const int4*>(ix + e0 + 16 * n) : make_int4(-1, -1, -1, -1);
+                    jj[n] = e0 + 64 * n < p.k ? *reinterpret_cast<const int4*>(ix + e0 + 64 * n) : make_int4(-1, -1, -1, -1);
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
                     const int jv[4] = {jj[n].x, jj[n].y, jj[n].z, jj[n].w};
@@ -334,11 +335,12 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
     }
     __syncthreads();
     const int ntile = (s_maxL + KT - 1) / KT;
-    {
+    {   // union over four rows per thread, then over the sixteen row groups
         const int t = tid & 63, rq = tid >> 6;
         uint32_t u0 = 0, u1 = 0;
         if (t < ntile)
-            for (int r = 16 * rq; r < 16 * rq + 16; ++r) {
+#pragma unroll
+            for (int r = 4 * rq; r < 4 * rq + 4; ++r) {
                 u0 |= bits[r][2 * t];
                 u1 |= bits[r][2 * t + 1];
             }
@@ -348,8 +350,12 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
     __syncthreads();
     int32_t* list = glist + (size_t)(b * nqb + qb) * LIST;
     if (tid < 64) {
-        const uint32_t u0 = s_uni[0][lane][0] | s_uni[1][lane][0] | s_uni[2][lane][0] | s_uni[3][lane][0];
-        const uint32_t u1 = s_uni[0][lane][1] | s_uni[1][lane][1] | s_uni[2][lane][1] | s_uni[3][lane][1];
+        uint32_t u0 = 0, u1 = 0;
+#pragma unroll
+        for (int rq = 0; rq < NT / 64; ++rq) {
+            u0 |= s_uni[rq][lane][0];
+            u1 |= s_uni[rq][lane][1];
+        }
         const bool act = (u0 | u1) != 0;
         const uint64_t m = __ballot(act);
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
@@ -361,7 +367,7 @@ __global__ void __launch_bounds__(256) tile_bits(AttnArgs a, uint32_t* gbits, in
         if (lane == 0) list[0] = __popcll(m);
     }
     // the rows' bitmaps, as 16-byte pieces
-    for (int w = tid; w < QR * NWORD / 4; w += 256) {
+    for (int w = tid; w < QR * NWORD / 4; w += NT) {
         const int r = w / (NWORD / 4), c = w % (NWORD / 4);
         const int i = qb * QR + r;
         if (i < p.n_q)
@@ -1845,7 +1851,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         const long nqb = (p.n_q + tile::QR - 1) / tile::QR;
         uint32_t* gbits = static_cast<uint32_t*>(a.partial);
         int32_t* glist = reinterpret_cast<int32_t*>(static_cast<char*>(a.partial) + tile_bits_bytes(p));
-        hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nqb)), dim3(256), 0, s, a, gbits, glist);
+        hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nqb)), dim3(1024), 0, s, a, gbits, glist);
         // pages shorter than a tile: each row's pool row is looked up on its own
         if (a.block_table && a.page_shift < 6)
             hipLaunchKernelGGL(attn_tile<true>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
