@@ -270,7 +270,8 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // 16 w .. 16 w + 15.  With a block table the tile's keys are read from their pool rows
 // (kv_row), and a candidate on a page outside the pools never enters the bitmap.
 namespace tile {
-constexpr int QR = 64;         // query rows per workgroup
+constexpr int QR = 128;        // query rows per workgroup (16 per wave)
+constexpr int NWV = QR / 16;   // waves per workgroup of the attention kernel
 constexpr int KT = 64;         // keys per tile
 constexpr int MAXN = 4096;     // longest history (bitmap words per row = MAXN / 32)
 constexpr int D = 128;
@@ -282,20 +283,25 @@ static_assert(MAXN / KT <= 64, "a row block's tile list fits one register per wa
 // every bank once per pass.
 __device__ __forceinline__ int kslot(int row, int chunk) { return chunk ^ (row & 15); }
 __device__ __forceinline__ int vslot(int row, int chunk) { return chunk ^ (2 * (row & 7)); }
-// per row block: [0] active tile count, [1 .. KT] active tiles, then two words per list
-// slot: the union over the block's rows of that tile's selection bits
-constexpr int LIST = 1 + 3 * KT;
+// The selections pre-pass works on blocks of SUB rows (more workgroups than the attention's
+// QR-row blocks); per SUB-row block: [0, 1] the 64-bit mask of tiles that any of its rows
+// selected, then for tile t at [2 + 2 t, 3 + 2 t] the union over its rows of that tile's
+// selection bits
+constexpr int SUB = 64;
+constexpr int LIST = 2 + 2 * KT;
+static_assert(QR % SUB == 0, "an attention row block is whole selection blocks");
 constexpr float kLazy = 0x1p64f;  // exp2(64): largest probability against a row's reference
 }  // namespace tile
 
-// The selections of a batch's block of 64 query rows, shared by every head: a bitmap per
-// row (bit j of word j / 32 = position j selected), the list of 64-key tiles any of the
-// rows selected and, per listed tile, the union of the rows' selection bits.  One
-// workgroup per (batch, row block); written to the workspace.
+// The selections of a batch's block of SUB query rows, shared by every head: a bitmap per
+// row (bit j of word j / 32 = position j selected), the mask of 64-key tiles any of the
+// rows selected and, per tile, the union of the rows' selection bits.  One workgroup per
+// (batch, row block); written to the workspace.
 __global__ void __launch_bounds__(1024) tile_bits(AttnArgs a, uint32_t* gbits, int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
     constexpr int NT = 1024;
+    constexpr int QR = SUB;  // rows of this pre-pass block
     __shared__ __attribute__((aligned(16))) uint32_t bits[QR][NWORD];
     __shared__ int s_L[QR], s_maxL;
     __shared__ uint32_t s_uni[NT / 64][KT][2];
@@ -312,16 +318,17 @@ __global__ void __launch_bounds__(1024) tile_bits(AttnArgs a, uint32_t* gbits, i
     if (tid == 0) s_maxL = 0;
     __syncthreads();
     if (tid < QR) atomicMax(&s_maxL, s_L[tid]);
-    {   // 16 threads per row, eight 16-byte index loads in flight per thread
-        const int r = tid >> 4, q = tid & 15;
+    {   // TPR threads per row, eight 16-byte index loads in flight per thread
+        constexpr int TPR = NT / QR;
+        const int r = tid / TPR, q = tid % TPR;
         const int i = qb * QR + r, L = s_L[r];
         if (i < p.n_q && L > 0) {
             const int32_t* ix = a.idx + ((int64_t)b * p.n_q + i) * p.k;
-            for (int e0 = 4 * q; e0 < p.k; e0 += 64 * 8) {
+            for (int e0 = 4 * q; e0 < p.k; e0 += 4 * TPR * 8) {
                 int4 jj[8];
 #pragma unroll
                 for (int n = 0; n < 8; ++n)
-                    jj[n] = e0 + 64 * n < p.k ? *reinterpret_cast<const int4*>(ix + e0 + 64 * n) : make_int4(-1, -1, -1, -1);
+                    jj[n] = e0 + 4 * TPR * n < p.k ? *reinterpret_cast<const int4*>(ix + e0 + 4 * TPR * n) : make_int4(-1, -1, -1, -1);
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
                     const int jv[4] = {jj[n].x, jj[n].y, jj[n].z, jj[n].w};
@@ -335,12 +342,13 @@ __global__ void __launch_bounds__(1024) tile_bits(AttnArgs a, uint32_t* gbits, i
     }
     __syncthreads();
     const int ntile = (s_maxL + KT - 1) / KT;
-    {   // union over four rows per thread, then over the sixteen row groups
+    {   // union over QR / 16 rows per thread, then over the sixteen row groups
+        constexpr int RG = QR / (NT / 64);
         const int t = tid & 63, rq = tid >> 6;
         uint32_t u0 = 0, u1 = 0;
         if (t < ntile)
 #pragma unroll
-            for (int r = 4 * rq; r < 4 * rq + 4; ++r) {
+            for (int r = RG * rq; r < RG * rq + RG; ++r) {
                 u0 |= bits[r][2 * t];
                 u1 |= bits[r][2 * t + 1];
             }
@@ -356,15 +364,13 @@ __global__ void __launch_bounds__(1024) tile_bits(AttnArgs a, uint32_t* gbits, i
             u0 |= s_uni[rq][lane][0];
             u1 |= s_uni[rq][lane][1];
         }
-        const bool act = (u0 | u1) != 0;
-        const uint64_t m = __ballot(act);
-        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (act) {
-            list[1 + pos] = lane;
-            list[1 + KT + 2 * pos] = (int32_t)u0;
-            list[2 + KT + 2 * pos] = (int32_t)u1;
+        const uint64_t m = __ballot((u0 | u1) != 0);
+        list[2 + 2 * lane] = (int32_t)u0;
+        list[3 + 2 * lane] = (int32_t)u1;
+        if (lane == 0) {
+            list[0] = (int32_t)(uint32_t)m;
+            list[1] = (int32_t)(uint32_t)(m >> 32);
         }
-        if (lane == 0) list[0] = __popcll(m);
     }
     // the rows' bitmaps, as 16-byte pieces
     for (int w = tid; w < QR * NWORD / 4; w += NT) {
@@ -410,7 +416,7 @@ __device__ __align__(16) const uint8_t kZeroRow[kZeroRowBytes] = {};
 // zeros); ROWS (pages shorter than a tile) looks up each row's pool row and reads it by its
 // own 64-bit address, unselected rows from the zero row.
 template <bool ROWS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(64 * tile::NWV) __attribute__((amdgpu_waves_per_eu(3)))
 attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
@@ -424,19 +430,42 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
     {
         const long blk = blockIdx.x;
         long rest;
-        if (p.Hkv % 8 == 0) {  // one head at a time per XCD: its K/V stay in that L2
+        // the longest (latest) row blocks first; with Hkv % 8 == 0 each XCD keeps to heads
+        // h = XCD (mod 8), so those heads' K/V stay in its L2
+        if (p.Hkv % 8 == 0) {
             const long local = blk / 8;
-            h = (int)(blk % 8) + 8 * (int)(local / ((long)p.B * nqb));
-            rest = local % ((long)p.B * nqb);
+            const int hb = (p.Hkv / 8) * p.B;  // (head, batch) pairs per XCD
+            const int rr = (int)(local % hb);
+            h = (int)(blk % 8) + 8 * (rr / p.B);
+            b = rr % p.B;
+            qb = nqb - 1 - (int)(local / hb);
         } else {
             h = (int)(blk % p.Hkv);
             rest = blk / p.Hkv;
+            b = (int)(rest / nqb);
+            qb = nqb - 1 - (int)(rest % nqb);
         }
-        b = (int)(rest / nqb);
-        qb = nqb - 1 - (int)(rest % nqb);  // the longest (latest) row blocks first
     }
-    const int32_t* list = glist + (size_t)(b * nqb + qb) * LIST;
-    const int nt = __builtin_amdgcn_readfirstlane(list[0]);
+    // the block's active tiles (mask) and, in lane t, tile t's union of selection bits: ORed
+    // over the block's selection blocks
+    uint64_t tmask = 0;
+    uint32_t lu0 = 0u, lu1 = 0u;
+    {
+        const int nsb = (p.n_q + SUB - 1) / SUB;
+#pragma unroll
+        for (int k = 0; k < QR / SUB; ++k) {
+            const int sb = qb * (QR / SUB) + k;
+            if (sb < nsb) {
+                const int32_t* list = glist + (size_t)(b * nsb + sb) * LIST;
+                tmask |= (uint64_t)(uint32_t)list[0] | ((uint64_t)(uint32_t)list[1] << 32);
+                lu0 |= (uint32_t)list[2 + 2 * lane];
+                lu1 |= (uint32_t)list[3 + 2 * lane];
+            }
+        }
+        tmask = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tmask)) |
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tmask >> 32)) << 32);
+    }
+    const int nt = __popcll(tmask);
     const int iq = qb * QR + 16 * wv + l15;  // this lane's query row
     const char* Kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.K.data) + (a.block_table ? 0 : b * a.K.s0) + h * a.K.s1);
     const char* Vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.V.data) + (a.block_table ? 0 : b * a.V.s0) + h * a.V.s1);
@@ -456,12 +485,13 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
             qa[s] = iq < p.n_q ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g))
                                : bf16x8{};
     }
-    // tile loads: wave wv fills the 1 KB LDS blocks 4 wv + i, i.e. tile rows r_i = 16 wv + 4 i +
-    // lane / 16, lane l writing slot l % 16 of its row (the chunk whose swizzled slot that is)
-    uint32_t koff[4], voff[4];
+    // tile loads: wave wv fills the 1 KB LDS blocks LPW wv + i, i.e. tile rows r_i = 4 (LPW wv + i)
+    // + lane / 16, lane l writing slot l % 16 of its row (the chunk whose swizzled slot that is)
+    constexpr int LPW = 16 / NWV;  // 1 KB blocks per wave and tile
+    uint32_t koff[LPW], voff[LPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wv + 4 * i + (lane >> 4);
+    for (int i = 0; i < LPW; ++i) {
+        const int r = 4 * (LPW * wv + i) + (lane >> 4);
         koff[i] = 16u * (uint32_t)kslot(r, lane & 15);
         voff[i] = 16u * (uint32_t)vslot(r, lane & 15);
         if constexpr (!ROWS) {
@@ -469,20 +499,20 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
             voff[i] += (uint32_t)(r * vrow);
         }
     }
-    const uint32_t kl = lds_addr(Ks) + 4096u * (uint32_t)wv, vl = lds_addr(Vs) + 4096u * (uint32_t)wv;
+    const uint32_t kl = lds_addr(Ks) + 1024u * LPW * (uint32_t)wv, vl = lds_addr(Vs) + 1024u * LPW * (uint32_t)wv;
     // where a tile's rows come from: a per-tile buffer resource, or (ROWS) each row's pool row
     struct Src {
         v4i krs, vrs;
-        int64_t prow[4];
+        int64_t prow[LPW];
     };
     auto tile_src = [&](int k0, uint64_t uni) {
         Src t;
         if constexpr (ROWS) {
-            const uint64_t un = uni >> (16 * wv);
+            const uint64_t un = uni >> (4 * LPW * wv);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < LPW; ++i) {
                 const int r = 4 * i + (lane >> 4);
-                t.prow[i] = ((un >> r) & 1u) ? kv_row(a, b, k0 + 16 * wv + r) : -1;
+                t.prow[i] = ((un >> r) & 1u) ? kv_row(a, b, k0 + 4 * LPW * wv + r) : -1;
             }
         } else {
             int64_t r0;
@@ -501,7 +531,7 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
     };
     auto issue_k = [&](const Src& t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < LPW; ++i) {
             if constexpr (ROWS)
                 lds_dma16_g(kl + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Kb + t.prow[i] * krow + koff[i] : reinterpret_cast<const char*>(kZeroRow));
             else
@@ -509,11 +539,14 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
         }
     };
     auto issue_v = [&](const Src& t, uint64_t uni) {
-        const uint64_t un = uni >> (16 * wv);
+        const uint64_t un = uni >> (4 * LPW * wv);
+        constexpr uint32_t ALL = (1u << (4 * LPW)) - 1u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < LPW; ++i) {
             if constexpr (ROWS) {
                 lds_dma16_g(vl + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Vb + t.prow[i] * vrow + voff[i] : reinterpret_cast<const char*>(kZeroRow));
+            } else if (((uint32_t)un & ALL) == ALL) {  // every row of this wave's part selected
+                lds_dma16(t.vrs, vl + 1024u * (uint32_t)i, voff[i], 0u);
             } else {
                 // keys no row of the block selected read past the resource: zeros
                 const bool sel = ((uint32_t)(un >> (4 * i)) >> (lane >> 4)) & 1u;
@@ -545,18 +578,17 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // the tile list in registers: lane u holds tile u's first key and union bits (nt <= KT = 64)
-    const int lt = lane < nt ? list[1 + lane] : 0;
-    const uint32_t lu0 = lane < nt ? (uint32_t)list[1 + KT + 2 * lane] : 0u;
-    const uint32_t lu1 = lane < nt ? (uint32_t)list[2 + KT + 2 * lane] : 0u;
-    auto tile_keys = [&](int u) { return __builtin_amdgcn_readlane(lt, u) * KT; };
-    auto tile_union = [&](int u) {
-        return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lu0, u) | ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lu1, u) << 32);
+    // active tiles in ascending order: tile u is the lowest set bit of rem after u steps
+    uint64_t rem = tmask;
+    auto tile_union = [&](int t) {
+        return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lu0, t) | ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lu1, t) << 32);
     };
     uint2 wcur = make_uint2(0u, 0u);
     if (nt > 0) {
-        const int k0 = tile_keys(0);
-        const uint64_t un = tile_union(0);
+        const int t0 = __builtin_ctzll(rem);
+        rem &= rem - 1;
+        const int k0 = t0 * KT;
+        const uint64_t un = tile_union(t0);
         const Src t = tile_src(k0, un);
         issue_k(t);
         issue_v(t, un);
@@ -565,9 +597,11 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
         tile_barrier();
     }
     for (int u = 0; u < nt; ++u) {
-        const bool more = u + 1 < nt;
-        const int k1 = more ? tile_keys(u + 1) : 0;
-        const uint64_t un1 = more ? tile_union(u + 1) : 0;
+        const bool more = rem != 0;
+        const int t1 = more ? __builtin_ctzll(rem) : 0;
+        rem &= rem - 1;
+        const int k1 = t1 * KT;
+        const uint64_t un1 = more ? tile_union(t1) : 0;
         Src nxt;
         if (more) nxt = tile_src(k1, un1);
         // does any row of this wave select a key of the tile?
@@ -612,10 +646,14 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
             bool slow = !all_ref;
             if (!slow) {
                 probs(-ref);
-                float pm = 0.f;
+                // largest probability of the lane, compared as bit patterns (all are >= +0; inf and
+                // NaN order above every finite value and so take the slow path too)
+                uint32_t pm = 0u;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pm = fmaxf(fmaxf(pm, fmaxf(pr[j][0], pr[j][1])), fmaxf(pr[j][2], pr[j][3]));
-                slow = __ballot(pm > kLazy) != 0;
+                for (int j = 0; j < 4; ++j)
+                    pm = max(max(pm, max(__float_as_uint(pr[j][0]), __float_as_uint(pr[j][1]))),
+                             max(__float_as_uint(pr[j][2]), __float_as_uint(pr[j][3])));
+                slow = __ballot(pm > __float_as_uint(kLazy)) != 0;
             }
             if (slow) {
                 // the row's maximum over its selected keys (all four lanes of the row)
@@ -636,9 +674,9 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
                 all_ref = __ballot(iq < p.n_q && ref == -INFINITY) == 0;
                 probs(ref == -INFINITY ? 0.f : -ref);
             }
-            float ps = 0.f;
+            float ps = (pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ps += (pr[j][0] + pr[j][1]) + (pr[j][2] + pr[j][3]);
+            for (int j = 1; j < 4; ++j) ps += (pr[j][0] + pr[j][1]) + (pr[j][2] + pr[j][3]);
             lrow += ps;
             // P^T fragments (B operand): k-step s holds keys 32 s + 4 g + 0..3, then 32 s + 16 + 4 g + 0..3
             bf16x8 pb[2];
@@ -1723,12 +1761,12 @@ static bool rows_buf_ok(const AttnArgs& a) {
            ((uintptr_t)a.idx & 15) == 0 && rows < (1 << 24) && a.K.s2 * 2 < (1 << 24) && a.V.s2 * 2 < (1 << 24);
 }
 
-// The tile kernel: bf16 MHA with d = 128, at least one block of query rows, a history of at
-// most tile::MAXN positions, and budgets large enough that a block's selections cover most
-// key tiles (64 rows x k >= 2 n_kv); candidate lists read four at a time.
+// The tile kernel: bf16 MHA with d = 128, at least 64 query rows, a history of at most
+// tile::MAXN positions, and budgets large enough that a block's selections cover most key
+// tiles (64 rows x k >= 2 n_kv); candidate lists read four at a time.
 static bool tile_shape_ok(const sa_problem& p) {
-    return p.Hq == p.Hkv && p.d_qk == tile::D && p.d_v == tile::D && p.n_kv <= tile::MAXN && p.n_q >= tile::QR &&
-           p.k % 4 == 0 && (int64_t)p.k * tile::QR >= 2LL * p.n_kv;
+    return p.Hq == p.Hkv && p.d_qk == tile::D && p.d_v == tile::D && p.n_kv <= tile::MAXN && p.n_q >= 64 &&
+           p.k % 4 == 0 && (int64_t)p.k * 64 >= 2LL * p.n_kv;
 }
 static bool tile_ok(const AttnArgs& a) {
     return a.Q.dtype == SA_BF16 && tile_shape_ok(a.p) && ((uintptr_t)a.idx & 15) == 0;
@@ -1738,8 +1776,8 @@ static size_t tile_bits_bytes(const sa_problem& p) {
     return ((size_t)p.B * p.n_q * (tile::MAXN / 8) + 255) & ~(size_t)255;
 }
 static size_t tile_ws_bytes(const sa_problem& p) {
-    const size_t nqb = (size_t)(p.n_q + tile::QR - 1) / tile::QR;
-    return tile_bits_bytes(p) + (size_t)p.B * nqb * tile::LIST * sizeof(int32_t);
+    const size_t nsb = (size_t)(p.n_q + tile::SUB - 1) / tile::SUB;
+    return tile_bits_bytes(p) + (size_t)p.B * nsb * tile::LIST * sizeof(int32_t);
 }
 
 bool attn_paged_ok(const AttnArgs& a) {
@@ -1851,12 +1889,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         const long nqb = (p.n_q + tile::QR - 1) / tile::QR;
         uint32_t* gbits = static_cast<uint32_t*>(a.partial);
         int32_t* glist = reinterpret_cast<int32_t*>(static_cast<char*>(a.partial) + tile_bits_bytes(p));
-        hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nqb)), dim3(1024), 0, s, a, gbits, glist);
+        const long nsb = (p.n_q + tile::SUB - 1) / tile::SUB;
+        hipLaunchKernelGGL(tile_bits, dim3((unsigned)(p.B * nsb)), dim3(1024), 0, s, a, gbits, glist);
         // pages shorter than a tile: each row's pool row is looked up on its own
         if (a.block_table && a.page_shift < 6)
-            hipLaunchKernelGGL(attn_tile<true>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
+            hipLaunchKernelGGL(attn_tile<true>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(64 * tile::NWV), 0, s, a, gbits, glist);
         else
-            hipLaunchKernelGGL(attn_tile<false>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(256), 0, s, a, gbits, glist);
+            hipLaunchKernelGGL(attn_tile<false>, dim3((unsigned)(p.B * nqb * p.Hkv)), dim3(64 * tile::NWV), 0, s, a, gbits, glist);
         return hipGetLastError();
     }
     if (a.Q.dtype == SA_BF16 && G == 1 && p.d_qk == p.d_v && (p.d_qk == 64 || p.d_qk == 128 || p.d_qk == 256)) {
