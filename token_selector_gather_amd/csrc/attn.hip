@@ -396,6 +396,11 @@ __device__ __forceinline__ v4s lds_tr_read(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
 }
 
+template <int N>
+struct ICst {
+    static constexpr int value = N;
+};
+
 // Zeros that stand in for a row no lane may read (an unselected or unmapped pool row)
 constexpr int kZeroRowBytes = 4096;
 __device__ __align__(16) const uint8_t kZeroRow[kZeroRowBytes] = {};
@@ -420,8 +425,9 @@ __global__ void __launch_bounds__(64 * tile::NWV) __attribute__((amdgpu_waves_pe
 attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
     using namespace tile;
     constexpr int NWORD = MAXN / 32;
-    __shared__ __attribute__((aligned(16))) uint8_t Ks[KT * D * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t Vs[KT * D * 2];
+    constexpr int TB = KT * D * 2;  // bytes of one K or V tile
+    __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * TB];
+    __shared__ __attribute__((aligned(16))) uint8_t Vs[2 * TB];
     const sa_problem& p = a.p;
     const int tid = threadIdx.x, lane = tid & 63, l15 = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -529,28 +535,28 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
         }
         return t;
     };
-    auto issue_k = [&](const Src& t) {
+    // K and V of a tile into LDS buffer bf
+    auto issue = [&](const Src& t, uint64_t uni, int bf) {
+        const uint32_t kb = kl + (uint32_t)(TB * bf), vb = vl + (uint32_t)(TB * bf);
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             if constexpr (ROWS)
-                lds_dma16_g(kl + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Kb + t.prow[i] * krow + koff[i] : reinterpret_cast<const char*>(kZeroRow));
+                lds_dma16_g(kb + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Kb + t.prow[i] * krow + koff[i] : reinterpret_cast<const char*>(kZeroRow));
             else
-                lds_dma16(t.krs, kl + 1024u * (uint32_t)i, koff[i], 0u);
+                lds_dma16(t.krs, kb + 1024u * (uint32_t)i, koff[i], 0u);
         }
-    };
-    auto issue_v = [&](const Src& t, uint64_t uni) {
         const uint64_t un = uni >> (4 * LPW * wv);
         constexpr uint32_t ALL = (1u << (4 * LPW)) - 1u;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             if constexpr (ROWS) {
-                lds_dma16_g(vl + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Vb + t.prow[i] * vrow + voff[i] : reinterpret_cast<const char*>(kZeroRow));
+                lds_dma16_g(vb + 1024u * (uint32_t)i, t.prow[i] >= 0 ? Vb + t.prow[i] * vrow + voff[i] : reinterpret_cast<const char*>(kZeroRow));
             } else if (((uint32_t)un & ALL) == ALL) {  // every row of this wave's part selected
-                lds_dma16(t.vrs, vl + 1024u * (uint32_t)i, voff[i], 0u);
+                lds_dma16(t.vrs, vb + 1024u * (uint32_t)i, voff[i], 0u);
             } else {
                 // keys no row of the block selected read past the resource: zeros
                 const bool sel = ((uint32_t)(un >> (4 * i)) >> (lane >> 4)) & 1u;
-                lds_dma16(t.vrs, vl + 1024u * (uint32_t)i, sel ? voff[i] : 0x80000000u, 0u);
+                lds_dma16(t.vrs, vb + 1024u * (uint32_t)i, sel ? voff[i] : 0x80000000u, 0u);
             }
         }
     };
@@ -589,21 +595,25 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
         rem &= rem - 1;
         const int k0 = t0 * KT;
         const uint64_t un = tile_union(t0);
-        const Src t = tile_src(k0, un);
-        issue_k(t);
-        issue_v(t, un);
+        issue(tile_src(k0, un), un, 0);
         wcur = load_bits(k0);
         wait_vmcnt<0>();
         tile_barrier();
     }
-    for (int u = 0; u < nt; ++u) {
+    // one tile: the next tile's K, V (other buffer) and bitmap words are issued first and have
+    // the whole tile's work to land; one barrier per tile
+    auto step = [&](auto BFC) {
+        constexpr int BF = decltype(BFC)::value;
         const bool more = rem != 0;
         const int t1 = more ? __builtin_ctzll(rem) : 0;
         rem &= rem - 1;
-        const int k1 = t1 * KT;
-        const uint64_t un1 = more ? tile_union(t1) : 0;
-        Src nxt;
-        if (more) nxt = tile_src(k1, un1);
+        uint2 wnext = make_uint2(0u, 0u);
+        if (more) {
+            const int k1 = t1 * KT;
+            const uint64_t un1 = tile_union(t1);
+            issue(tile_src(k1, un1), un1, 1 - BF);
+            wnext = load_bits(k1);
+        }
         // does any row of this wave select a key of the tile?
         const bool act = __ballot((wcur.x | wcur.y) != 0u) != 0;
         // S^T = K Q^T: acc[j][e] = S[row iq][key 16 j + 4 g + e]
@@ -613,19 +623,9 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
             for (int s = 0; s < D / 32; ++s)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + kad[s] + 4096 * j));
+                    const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + TB * BF + kad[s] + 4096 * j));
                     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[j], 0, 0, 0);
                 }
-        }
-        wait_lgkmcnt0();
-        wait_vmcnt<0>();  // this wave's part of V(u) has landed
-        tile_barrier();   // every wave is done with K(u); V(u) is complete
-        uint2 wnext = make_uint2(0u, 0u);
-        if (more) {
-            issue_k(nxt);
-            wnext = load_bits(k1);
-        }
-        if (act) {
             // mask of row iq for keys 16 j + 4 g + e: bit 16 (j % 2) + e of word j / 2 after a shift
             // by 4 g; all ones where selected (one bit-field extract, kept opaque so that the
             // masking stays a single AND per element)
@@ -690,7 +690,7 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
             // O^T[d 16 t + 4 g + e][row iq] += V^T P^T; the first of a pair of transposing reads
             // brings keys 32 s + 4 g + 0..3 of column 16 t + l15, the second 32 s + 16 + 4 g + 0..3
             auto vread = [&](int s, int t) {
-                const uint8_t* vp = Vs + vad[t] + 8192 * s;
+                const uint8_t* vp = Vs + TB * BF + vad[t] + 8192 * s;
                 return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lds_tr_read(vp), lds_tr_read(vp + 4096), 0, 1, 2, 3, 4, 5, 6, 7));
             };
 #pragma unroll
@@ -699,12 +699,13 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
                 for (int t = 0; t < D / 16; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vread(s, t), pb[s], o[t], 0, 0, 0);
         }
         wait_lgkmcnt0();
-        wait_vmcnt<0>();  // this wave's part of K(u + 1) and the next bitmap words have landed
-        tile_barrier();   // every wave is done with V(u); K(u + 1) is complete
-        if (more) {
-            issue_v(nxt, un1);
-            wcur = wnext;
-        }
+        wait_vmcnt<0>();  // this wave's part of the next tile and its bitmap words have landed
+        tile_barrier();   // every wave is done with buffer BF; the next tile is complete
+        wcur = wnext;
+    };
+    for (int u = 0; u < nt; u += 2) {
+        step(ICst<0>{});
+        if (u + 1 < nt) step(ICst<1>{});
     }
     // O[row iq][d 16 t + 4 g + e] = O^T / l; LSE per row
     float l;
