@@ -693,10 +693,14 @@ attn_tile(AttnArgs a, const uint32_t* gbits, const int32_t* glist) {
                 const uint8_t* vp = Vs + TB * BF + vad[t] + 8192 * s;
                 return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lds_tr_read(vp), lds_tr_read(vp + 4096), 0, 1, 2, 3, 4, 5, 6, 7));
             };
+            // (raised issue priority while the value products run, so that this wave's MFMAs and
+            // transposing reads go ahead of the other waves' softmax arithmetic)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int t = 0; t < D / 16; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vread(s, t), pb[s], o[t], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
         }
         wait_lgkmcnt0();
         wait_vmcnt<0>();  // this wave's part of the next tile and its bitmap words have landed
