@@ -111,3 +111,31 @@ def test_splits_override_keeps_the_latent_attention(monkeypatch):
         O, lse = gc.gpu_sparse_attn(W, idx)
         err_o, err_l = gc.compare_attention(W, rows, O, lse, O_or, lse_or)
         _say("SA_SPLITS=%s: max|dO| %.3g max|dLSE| %.3g" % (s, err_o, err_l))
+
+
+def test_bf16_split_partials_cost_about_one_rounding(monkeypatch):
+    """The latent attention stores each split's o / l in bf16 before the log-sum-exp merge
+    (block-mixture identity, COBS reading note eq. (P3)).  That is one extra rounding of a
+    value of the output's own size: against the unsplit run (no partials) every output stays
+    within two bf16 steps of its (row, head)'s largest value, and the error against the oracle
+    does not grow beyond that."""
+    W = sa_synth.custom(seed=65, B=4, n_q=1, n_kv=6000, Hq=128, Hkv=1, d_qk=576, d_v=512, mla=True, Hidx=8,
+                        d_idx=64, kidx_dtype=E4M3, k=2048, lens=[6000, 4100, 2500, 2048],
+                        q_pos0=[5999, 4099, 2499, 2047])
+    idx = _clean_lists(W)
+    rows = np.arange(W["B"] * W["n_q"], dtype=np.int32)
+    O_or, lse_or = orc.attend(W, idx.reshape(len(rows), -1), rows)
+    monkeypatch.setenv("SA_SPLITS", "1")
+    O1, lse1 = gc.gpu_sparse_attn(W, idx)
+    e1, _ = gc.compare_attention(W, rows, O1, lse1, O_or, lse_or)
+    scale = np.abs(O1).max(axis=-1, keepdims=True)  # per (batch, head, row)
+    for s in ("4", "16"):
+        monkeypatch.setenv("SA_SPLITS", s)
+        Os, lses = gc.gpu_sparse_attn(W, idx)
+        es, _ = gc.compare_attention(W, rows, Os, lses, O_or, lse_or)
+        steps = np.abs(Os - O1) / (scale * 2.0 ** -8)  # in bf16 steps of the largest value
+        _say("SA_SPLITS=%s: max|O_split - O_unsplit| = %.2f bf16 steps of the row's largest value; "
+             "max|dO| vs oracle %.3g (unsplit %.3g)" % (s, steps.max(), es, e1))
+        assert steps.max() <= 2.0
+        assert es <= e1 + 2.0 ** -7 * scale.max()
+        np.testing.assert_allclose(lses, lse1, rtol=0, atol=1e-5 * max(1.0, np.abs(lse1).max()))
