@@ -259,7 +259,7 @@ __device__ __forceinline__ float dpp_mov(float x) {
 
 // --------------------------------------------------------------- attn_tile
 // bf16 MHA (d = 128) over selections that, for a block of query rows, cover most key tiles
-// (many query rows, k a large fraction of the history).  One workgroup = 64 query rows of
+// (many query rows, k a large fraction of the history).  One workgroup = 128 query rows of
 // one head: the rows' selections become a bitmap (tile_bits), every 64-key tile that any of
 // the rows selected is read once into LDS, S^T = K Q^T and O^T += V^T P^T run on MFMA
 // (16x16x32 bf16), and unselected keys get probability 0, so each row's result is the exact
@@ -276,8 +276,9 @@ constexpr int KT = 64;         // keys per tile
 constexpr int MAXN = 4096;     // longest history (bitmap words per row = MAXN / 32)
 constexpr int D = 128;
 static_assert(MAXN / KT <= 64, "a row block's tile list fits one register per wave");
-// LDS rows are not padded (256 B per K or V row, 32 KB per workgroup, so four workgroups
-// share a CU); the 16-byte chunks of a row are XOR-swizzled instead.  K: chunk c of row r at
+// LDS rows are not padded (256 B per K or V row; K and V double-buffered, 64 KB per workgroup,
+// so two workgroups of eight waves share a CU); the 16-byte chunks of a row are XOR-swizzled
+// instead.  K: chunk c of row r at
 // slot c ^ (r & 15), so the 16-row operand reads touch distinct banks.  V: slot c ^ 2 (r & 7),
 // so each transposing read (16 rows x two adjacent chunks, half a wave per pass) touches
 // every bank once per pass.
