@@ -195,6 +195,12 @@ sa_status run_select(const sa_problem* p, const sa_tensor& q, const sa_tensor& k
         return SA_OK;
     }
     ta.scratch = region + scores_bytes(*p);
+    if (topk_sliced(*p) && indexer_dec_path(ia)) {
+        // few long rows: the index scan also fills the first radix digit of the selection
+        if (topk_sliced_clear(ta, st) != hipSuccess) return SA_ERR_HIP;
+        ia.hist0 = topk_sliced_hist(ta);
+        ta.digit0_done = 1;
+    }
     if (launch_indexer(ia, st) != hipSuccess) return SA_ERR_HIP;
     return launch_topk(ta, st) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

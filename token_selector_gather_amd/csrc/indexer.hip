@@ -248,6 +248,27 @@ __global__ void __launch_bounds__(256, 4) indexer_dec(IndexerArgs a, int n_rng, 
         if (vis) srow[j] = s_sc[j - j_begin];
         else if (a.fill_invisible) srow[j] = -INFINITY;
     }
+    if (a.hist0 != nullptr && j_comp > j_begin) {  // (uniform)
+        // the first radix digit (top 11 bits of the order-preserving key, -0 folded onto +0) of
+        // this range's visible scores, into the row's histogram of the sliced top-k
+        uint32_t* lh = reinterpret_cast<uint32_t*>(ring);  // (the tile ring is free now)
+        for (int e = threadIdx.x; e < 2048; e += 256) lh[e] = 0u;
+        __syncthreads();
+        int bad = 0;
+        for (int j = j_begin + (int)threadIdx.x; j < j_comp; j += 256) {
+            const float v = s_sc[j - j_begin];
+            uint32_t u = __float_as_uint(v);
+            if ((u & 0x7fffffffu) == 0) u = 0;
+            const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            bad |= !isfinite(v);
+            atomicAdd(&lh[key >> 21], 1u);
+        }
+        __syncthreads();
+        uint32_t* gh = a.hist0 + row * (int64_t)(3 * 2048);
+        for (int e = threadIdx.x; e < 2048; e += 256)
+            if (lh[e]) atomicAdd(&gh[e], lh[e]);
+        if (__ballot(bad) != 0 && lane == 0 && a.status) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+    }
 }
 
 // ------------------------------------------------------------ streaming selection
@@ -1456,8 +1477,18 @@ hipError_t launch_select_fused(const IndexerArgs& a, int32_t* idx, void* buf, hi
     return hipErrorInvalidValue;
 }
 
+bool indexer_dec_path(const IndexerArgs& a) {
+    const sa_problem& p = a.p;
+    const int H = p.Hidx, D = p.d_idx;
+    const bool mfma_ok = a.nrows == 0 && a.q.dtype == SA_BF16 && (a.k.dtype == SA_BF16 || a.k.dtype == SA_FP8_E4M3) &&
+                         (H == 4 || H == 8 || H == 16 || H == 32 || H == 64) &&
+                         (D == 32 || D == 64 || D == 128);
+    return mfma_ok && (long)p.B * p.n_q < 512 && H >= 16 && D >= 64;
+}
+
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     const sa_problem& p = a.p;
+    if (a.hist0 && !indexer_dec_path(a)) return hipErrorInvalidValue;  // only indexer_dec fills it
     const int H = p.Hidx, D = p.d_idx;
     const bool mfma_ok = a.nrows == 0 && a.q.dtype == SA_BF16 && (a.k.dtype == SA_BF16 || a.k.dtype == SA_FP8_E4M3) &&
                          (H == 4 || H == 8 || H == 16 || H == 32 || H == 64) &&
@@ -1467,7 +1498,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
         const int n_groups = (p.n_q + QPG - 1) / QPG;
         // decode layout (the four waves split one query's 64 index heads) for few query groups
         const bool decode = H == 64 && (long)p.B * n_groups < 1024;
-        const bool few_rows = (long)p.B * p.n_q < 512 && H >= 16 && D >= 64;  // indexer_dec below
+        const bool few_rows = indexer_dec_path(a);  // indexer_dec below
         const bool fast = a.status != nullptr && !decode && !few_rows;
         if (fast) {
             const dim3 gc((unsigned)max(1L, min(512L, 65536L / p.B)), p.B);

@@ -53,8 +53,13 @@ struct IndexerArgs {
     const int32_t* row_len = nullptr;  // explicit visible length per row (see Rows)
     int row0 = 0, nrows = 0;  // nrows > 0: only flat rows [row0, row0 + nrows), whose scores start at
                               // `scores` (the plain vector path only)
+    uint32_t* hist0 = nullptr;  // (few-row layout only, see indexer_dec_path) the sliced top-k's
+                                // per-row histograms: the scan adds the first digit of every
+                                // visible score and reports non-finite scores in `status`
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+// The indexer takes its few-row layout (indexer_dec), the one that can fill hist0.
+bool indexer_dec_path(const IndexerArgs& a);
 
 // Fused score + select for many query rows (the prefill layout of the indexer with a
 // streaming top-k instead of stored scores).  A persistent grid of at most kSelSlots
@@ -82,9 +87,15 @@ struct TopkArgs {
     const int32_t* row_len = nullptr;  // explicit visible length per row (see Rows)
     int row0 = 0, nrows = 0;  // nrows > 0: only flat rows [row0, row0 + nrows), whose scores start at
                               // `scores` (the one-workgroup-per-row kernels only)
+    int digit0_done = 0;  // sliced path: the histograms were cleared (topk_sliced_clear) before the
+                          // scores were written and hold the first digit already (indexer hist0)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 size_t topk_ws_bytes(const sa_problem& p);
+bool topk_sliced(const sa_problem& p);
+// The sliced path's per-row histograms in its scratch, and a kernel that clears them.
+uint32_t* topk_sliced_hist(const TopkArgs& a);
+hipError_t topk_sliced_clear(const TopkArgs& a, hipStream_t s);
 
 struct AttnArgs {
     sa_problem p;

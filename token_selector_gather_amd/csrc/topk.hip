@@ -578,24 +578,7 @@ __global__ void __launch_bounds__(kSliceT) topk_sl_hist(TopkArgs a, SlicedWs w) 
     const float* sc = a.scores + (int64_t)row * a.row_stride;
     if (threadIdx.x == 0) { s_bad = 0; s_bin = 0; s_above = 0; }
     __syncthreads();
-    if (L <= K) {
-        if (DIGIT == 0) {  // short row: all visible positions, then -1
-            int32_t* out = a.idx + (int64_t)row * K;
-            float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
-            int bad = 0;
-            for (int j = j0 + threadIdx.x; j < min(K, j0 + kSlice) || (slice == w.S - 1 && j < K); j += kSliceT) {
-                const float v = j < L ? sc[j] : -INFINITY;
-                if (j < L && !isfinite(v)) bad = 1;
-                out[j] = j < L ? j : -1;
-                if (vout) vout[j] = v;
-            }
-            if (bad) s_bad = 1;
-            __syncthreads();
-            if (threadIdx.x == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
-        }
-        return;
-    }
-    if (j0 >= L) return;
+    if (L <= K || j0 >= L) return;  // (short rows are written by topk_sl_count)
     uint32_t* gh = w.hist + (int64_t)row * 3 * 2048;
     uint32_t pre, above;
     sliced_prefix(gh, DIGIT, (uint32_t)K, lh, wave_tot, &s_bin, &s_above, pre, above);
@@ -636,7 +619,25 @@ __global__ void __launch_bounds__(kSliceT) topk_sl_count(TopkArgs a, SlicedWs w)
     const int L = visible_len(R, b, i);
     const int K = p.k;
     const int j0 = slice * kSlice;
-    if (L <= K) return;
+    if (L <= K) {  // short row: all visible positions, then -1
+        __shared__ int s_bad;
+        const float* sc = a.scores + (int64_t)row * a.row_stride;
+        int32_t* out = a.idx + (int64_t)row * K;
+        float* vout = a.vals ? a.vals + (int64_t)row * K : nullptr;
+        if (threadIdx.x == 0) s_bad = 0;
+        __syncthreads();
+        int bad = 0;
+        for (int j = j0 + threadIdx.x; j < min(K, j0 + kSlice) || (slice == w.S - 1 && j < K); j += kSliceT) {
+            const float v = j < L ? sc[j] : -INFINITY;
+            if (j < L && !isfinite(v)) bad = 1;
+            out[j] = j < L ? j : -1;
+            if (vout) vout[j] = v;
+        }
+        if (bad) s_bad = 1;
+        __syncthreads();
+        if (threadIdx.x == 0 && s_bad) atomicOr(&a.status->flags, 1u << SA_ERR_NONFINITE);
+        return;
+    }
     if (threadIdx.x == 0) { s_bin = 0; s_above = 0; }
     __syncthreads();
     uint32_t* gh = w.hist + (int64_t)row * 3 * 2048;
@@ -741,6 +742,18 @@ __global__ void __launch_bounds__(kSliceT) topk_sl_compact(TopkArgs a, SlicedWs 
 
 bool topk_sliced(const sa_problem& p) { return (long)p.B * p.n_q <= 512 && p.n_kv > 8192; }
 
+uint32_t* topk_sliced_hist(const TopkArgs& a) { return static_cast<uint32_t*>(a.scratch); }
+
+hipError_t topk_sliced_clear(const TopkArgs& a, hipStream_t s) {
+    if (!topk_sliced(a.p) || a.nrows > 0) return hipErrorInvalidValue;
+    const long rows = (long)a.p.B * a.p.n_q, words = rows * 3 * 2048;
+    SlicedWs w;
+    w.hist = topk_sliced_hist(a);
+    hipLaunchKernelGGL(topk_sl_zero, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                       dim3(256), 0, s, w, words);
+    return hipGetLastError();
+}
+
 size_t topk_ws_bytes(const sa_problem& p) {
     if (!topk_sliced(p)) return 0;
     const long rows = (long)p.B * p.n_q;
@@ -760,10 +773,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
         w.counts = w.hist + rows * 3 * 2048;
         w.state = w.counts + rows * 2 * w.S;
         const long words = rows * 3 * 2048;
-        hipLaunchKernelGGL(topk_sl_zero, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
-                           dim3(256), 0, s, w, words);
         const dim3 gs((unsigned)(rows * w.S));
-        hipLaunchKernelGGL(topk_sl_hist<0>, gs, dim3(kSliceT), 0, s, a, w);
+        if (!a.digit0_done) {  // (otherwise cleared and filled with the first digit already)
+            hipLaunchKernelGGL(topk_sl_zero, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                               dim3(256), 0, s, w, words);
+            hipLaunchKernelGGL(topk_sl_hist<0>, gs, dim3(kSliceT), 0, s, a, w);
+        }
         hipLaunchKernelGGL(topk_sl_hist<1>, gs, dim3(kSliceT), 0, s, a, w);
         hipLaunchKernelGGL(topk_sl_hist<2>, gs, dim3(kSliceT), 0, s, a, w);
         hipLaunchKernelGGL(topk_sl_count, gs, dim3(kSliceT), 0, s, a, w);
