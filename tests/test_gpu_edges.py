@@ -8,6 +8,7 @@ import sa_synth
 import token_selector_gather_amd as sa
 from oracle import oracle as orc
 from tests import gpu_common as gc
+from tests.checker import check_index_rows
 from token_selector_gather_amd.inputs import device_workload
 from tests.device_inputs import empty_outputs
 
@@ -154,3 +155,27 @@ def test_tile_attention_skips_unselected_tiles_and_ignores_order():
     O, lse = gc.gpu_sparse_attn(W, idx.reshape(W["B"], W["n_q"], -1))
     O_or, lse_or = orc.attend(W, idx, rows)
     gc.compare_attention(W, rows, O, lse, O_or, lse_or)
+
+
+def test_decode_selection_fills_its_first_digit_in_the_index_scan():
+    # Few long rows take the sliced top-k, whose first radix digit the index scan adds while it
+    # writes the scores: the selection still matches the oracle, a row shorter than k lists all
+    # its positions, a NaN key at a visible position is reported and one past kv_len is not read.
+    def work():
+        return sa_synth.custom(seed=71, B=3, n_q=1, n_kv=9000, Hq=2, Hkv=2, d_qk=64, d_v=64, Hidx=16, d_idx=64,
+                               kidx_dtype=E4M3, k=256, lens=[9000, 8500, 200], q_pos0=[8999, 8499, 199])
+    W = work()
+    rows = np.arange(3, dtype=np.int32)
+    idx, _, _, st = gc.gpu_select_attend(W)
+    assert st == sa.SA_OK
+    ref_sc = orc.scores(W, rows)
+    ref_idx, sk, _, _ = orc.select(W, ref_sc, rows)
+    check_index_rows(W, rows, idx.reshape(3, -1), ref_sc, ref_idx, sk)
+    assert list(idx[2, 0, :200]) == list(range(200)) and (idx[2, 0, 200:] == -1).all()
+    gc.full_check(W)
+    for b, j, want in [(0, 1234, sa.SA_ERR_NONFINITE), (1, 8700, sa.SA_OK)]:
+        W = work()
+        W["k_idx"] = W["k_idx"].copy()
+        W["k_idx"][b, j, 3] = 0x7F  # e4m3 NaN
+        _, _, _, st = gc.gpu_select_attend(W)
+        assert st == want, (b, j)
