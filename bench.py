@@ -103,6 +103,10 @@ def stage_rooflines(W, alg, t):
         out["sparse_attn"]["gather_gbs_logical"] = round(alg["gather_bytes"] / (t["sparse_attn"] * 1e-3) / 1e9, 1)
     else:
         out["sparse_attn"] = hbm(alg["gather_bytes"], t["sparse_attn"])
+        # the same launch against the matrix cores: with many query heads per gathered latent
+        # row, decode attention does hundreds of FLOPs per gathered byte
+        out["sparse_attn"]["mfma_view"] = {k: v for k, v in mfma(alg["attn_flops"], t["sparse_attn"]).items()
+                                           if k in ("achieved", "peak", "unit", "frac", "flops_per_launch")}
     for k in out:
         out[k]["kernel"] = k
     return out
