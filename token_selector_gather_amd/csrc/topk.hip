@@ -507,8 +507,11 @@ __global__ void __launch_bounds__(NT) topk_rows_long(TopkArgs a) {
 // select above runs as a short chain of kernels with per-row digit histograms in the
 // workspace, accumulated atomically by the row's workgroups; each kernel re-derives the
 // threshold prefix from the finished histograms of the earlier digits.  The last two
-// kernels count keys > T and == T per slice and compact in position order, each slice
-// starting after the counts of the row's earlier slices.
+// kernels count keys > T and == T per slice (the count kernel also writes the rows with
+// L <= k) and compact in position order, each slice starting after the counts of the row's
+// earlier slices.  Inside a selection the index scan adds the first digit while it writes the
+// scores (digit0_done: the histograms are cleared before the scan, and the first histogram
+// kernel is skipped).
 constexpr int kSlice = 4096, kSliceT = 256;
 
 struct SlicedWs {
