@@ -157,13 +157,14 @@ def test_tile_attention_skips_unselected_tiles_and_ignores_order():
     gc.compare_attention(W, rows, O, lse, O_or, lse_or)
 
 
-def test_decode_selection_fills_its_first_digit_in_the_index_scan():
+@pytest.mark.parametrize("hidx,didx,kdt", [(16, 64, E4M3), (32, 128, BF16), (64, 128, E4M3)])
+def test_decode_selection_fills_its_first_digit_in_the_index_scan(hidx, didx, kdt):
     # Few long rows take the sliced top-k, whose first radix digit the index scan adds while it
     # writes the scores: the selection still matches the oracle, a row shorter than k lists all
     # its positions, a NaN key at a visible position is reported and one past kv_len is not read.
     def work():
-        return sa_synth.custom(seed=71, B=3, n_q=1, n_kv=9000, Hq=2, Hkv=2, d_qk=64, d_v=64, Hidx=16, d_idx=64,
-                               kidx_dtype=E4M3, k=256, lens=[9000, 8500, 200], q_pos0=[8999, 8499, 199])
+        return sa_synth.custom(seed=71 + hidx, B=3, n_q=1, n_kv=9000, Hq=2, Hkv=2, d_qk=64, d_v=64, Hidx=hidx,
+                               d_idx=didx, kidx_dtype=kdt, k=256, lens=[9000, 8500, 200], q_pos0=[8999, 8499, 199])
     W = work()
     rows = np.arange(3, dtype=np.int32)
     idx, _, _, st = gc.gpu_select_attend(W)
@@ -176,6 +177,6 @@ def test_decode_selection_fills_its_first_digit_in_the_index_scan():
     for b, j, want in [(0, 1234, sa.SA_ERR_NONFINITE), (1, 8700, sa.SA_OK)]:
         W = work()
         W["k_idx"] = W["k_idx"].copy()
-        W["k_idx"][b, j, 3] = 0x7F  # e4m3 NaN
+        W["k_idx"][b, j, 3] = 0x7F if kdt == E4M3 else 0x7FC0  # NaN
         _, _, _, st = gc.gpu_select_attend(W)
         assert st == want, (b, j)
